@@ -1,0 +1,87 @@
+// Device helpers shared by the gfx950 kernels of libinfllm.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace infllm {
+
+typedef uint16_t bf16_t;  // bf16 stored as its 16-bit pattern
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+// ---------------------------------------------------------------- scalars
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float((uint32_t)x << 16); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
+  __bf16 h = (__bf16)x;  // round to nearest even (v_cvt_pk_bf16_f32)
+  return __builtin_bit_cast(bf16_t, h);
+}
+
+// Unit table and eligibility, host and device.  Unit u is absolute block
+// j = u + floor(n_init/B) with keys [max(j*B, n_init), (j+1)*B).
+__host__ __device__ __forceinline__ int64_t unit_first_key(int64_t u, int B, int n_init) {
+  int64_t j = u + n_init / B;
+  int64_t lo = j * B;
+  return lo > n_init ? lo : n_init;
+}
+
+// Units whose first key lies at or before t_last - W (a prefix of [0, U)).
+// lo(0) = n_init and lo(u) = (u + n_init/B)*B for u >= 1.
+__host__ __device__ __forceinline__ int64_t eligible_units(int64_t t_last, int64_t U, int B,
+                                                          int n_init, int W) {
+  int64_t x = t_last - W;
+  if (U <= 0 || x < n_init) return 0;
+  int64_t e = x / B - n_init / B + 1;
+  return e < U ? e : U;
+}
+
+// ------------------------------------------------------------ lane shuffles
+// DPP controls (gfx9 encoding): quad_perm [1,0,3,2], [2,3,0,1]; row_half_mirror;
+// row_mirror.  Applied in this order they all-reduce a 16-lane row.
+#define INFLLM_DPP_XOR1 0xB1
+#define INFLLM_DPP_XOR2 0x4E
+#define INFLLM_DPP_HALF_MIRROR 0x141
+#define INFLLM_DPP_MIRROR 0x140
+
+template <int CTRL> __device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over the 16 lanes of a DPP row; every lane of the row gets the sum.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_f32<INFLLM_DPP_XOR1>(x);
+  x += dpp_f32<INFLLM_DPP_XOR2>(x);
+  x += dpp_f32<INFLLM_DPP_HALF_MIRROR>(x);
+  x += dpp_f32<INFLLM_DPP_MIRROR>(x);
+  return x;
+}
+
+__device__ __forceinline__ double shfl_xor_f64(double x, int m) {
+  int lo = __double2loint(x), hi = __double2hiint(x);
+  lo = __shfl_xor(lo, m);
+  hi = __shfl_xor(hi, m);
+  return __hiloint2double(hi, lo);
+}
+
+__device__ __forceinline__ double wave_sum_f64(double x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += shfl_xor_f64(x, m);
+  return x;
+}
+
+// Order-preserving map of an fp32 to uint32 (larger float -> larger key);
+// -0 and +0 map to the same key.
+__device__ __forceinline__ uint32_t orderable(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace infllm

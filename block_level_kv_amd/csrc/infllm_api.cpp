@@ -1,0 +1,266 @@
+// C ABI of libinfllm.so (declared in include/infllm.h): host-side argument
+// validation, workspace sizing and kernel dispatch.  Validation never touches
+// the device, so every error path can be exercised without a GPU.
+#include "../../include/infllm.h"
+
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+#include "kernels.h"
+
+using namespace infllm;
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+infllm_status check_config(const infllm_config* c) {
+  if (!c) return INFLLM_ERR_INVALID_ARG;
+  if (c->n_q_heads < 1 || c->n_kv_heads < 1 || c->n_q_heads % c->n_kv_heads != 0)
+    return INFLLM_ERR_INVALID_ARG;
+  if (c->head_dim < 1 || c->block < 1 || c->n_init < 0 || c->window < 1 || c->top_k < 0)
+    return INFLLM_ERR_INVALID_ARG;
+  if (c->rep_mode != INFLLM_REP_TOKENS && c->rep_mode != INFLLM_REP_MEAN)
+    return INFLLM_ERR_INVALID_ARG;
+  if (c->dtype != INFLLM_F32 && c->dtype != INFLLM_BF16) return INFLLM_ERR_INVALID_ARG;
+  if (c->rep_mode == INFLLM_REP_TOKENS && (c->rep_k < 1 || c->rep_k > c->block))
+    return INFLLM_ERR_INVALID_ARG;
+  const int G = c->n_q_heads / c->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return INFLLM_ERR_UNSUPPORTED;
+  if (c->head_dim != 64 && c->head_dim != 128) return INFLLM_ERR_UNSUPPORTED;
+  if (c->block % 64 != 0 || c->block > 1024) return INFLLM_ERR_UNSUPPORTED;
+  if (c->top_k > kMaxTopK) return INFLLM_ERR_UNSUPPORTED;
+  return INFLLM_OK;
+}
+
+int64_t num_units(const infllm_config* c, int64_t n) {
+  const int64_t u = n / c->block - c->n_init / c->block;
+  return u > 0 ? u : 0;
+}
+
+infllm_status launched(hipError_t e) { return e == hipSuccess ? INFLLM_OK : INFLLM_ERR_HIP; }
+
+BuildArgs build_args(const infllm_config* c, int32_t batch, int64_t n_ctx) {
+  BuildArgs a{};
+  a.batch = batch;
+  a.Hq = c->n_q_heads;
+  a.Hkv = c->n_kv_heads;
+  a.d = c->head_dim;
+  a.B = c->block;
+  a.n_init = c->n_init;
+  a.W = c->window;
+  a.r_k = c->rep_k;
+  a.rep_mode = c->rep_mode;
+  a.bf16 = c->dtype == INFLLM_BF16;
+  a.n_ctx = n_ctx;
+  a.U = (int)num_units(c, n_ctx);
+  return a;
+}
+
+AttendArgs attend_args(const infllm_config* c, int32_t batch, int32_t chunk_len, int32_t n_chunks) {
+  AttendArgs a{};
+  a.batch = batch;
+  a.Hq = c->n_q_heads;
+  a.Hkv = c->n_kv_heads;
+  a.d = c->head_dim;
+  a.B = c->block;
+  a.n_init = c->n_init;
+  a.W = c->window;
+  a.k_m = c->top_k;
+  a.L = chunk_len;
+  a.n_chunks = n_chunks;
+  a.n_pos = chunk_len * n_chunks;
+  a.bf16 = c->dtype == INFLLM_BF16;
+  return a;
+}
+
+// Which attention path runs, and its split-K factor.
+void attend_plan(const AttendArgs& a, bool* mfma, int* splits) {
+  *mfma = prefill_supported(a);
+  *splits = *mfma ? prefill_num_splits(a) : rows_num_splits(a);
+}
+
+size_t attend_ws_bytes(const AttendArgs& a) {
+  bool mfma;
+  int splits;
+  attend_plan(a, &mfma, &splits);
+  if (splits <= 1) return 0;
+  const size_t rows = (size_t)splits * a.batch * a.Hq * a.n_pos;
+  const size_t o = rows * a.d * sizeof(float);
+  return ((o + 255) & ~(size_t)255) + rows * 2 * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t infllm_abi_version(void) { return INFLLM_ABI_VERSION; }
+
+const char* infllm_status_string(int32_t s) {
+  switch (s) {
+    case INFLLM_OK: return "ok";
+    case INFLLM_ERR_INVALID_ARG: return "invalid argument";
+    case INFLLM_ERR_UNSUPPORTED: return "unsupported configuration";
+    case INFLLM_ERR_WORKSPACE: return "workspace missing or too small";
+    case INFLLM_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int32_t infllm_num_units(const infllm_config* cfg, int64_t n_ctx) {
+  if (check_config(cfg) != INFLLM_OK || n_ctx < 0) return -1;
+  const int64_t u = num_units(cfg, n_ctx);
+  return u > INT32_MAX ? -1 : (int32_t)u;
+}
+
+int32_t infllm_num_eligible(const infllm_config* cfg, int64_t t_last, int32_t n_units) {
+  if (check_config(cfg) != INFLLM_OK || n_units < 0) return -1;
+  return (int32_t)eligible_units(t_last, n_units, cfg->block, cfg->n_init, cfg->window);
+}
+
+size_t infllm_workspace_size(const infllm_config* cfg, int32_t call, int32_t batch, int64_t n,
+                             int32_t chunk_len, int32_t n_chunks) {
+  if (check_config(cfg) != INFLLM_OK || batch < 1) return 0;
+  switch (call) {
+    case INFLLM_CALL_BUILD:
+      return n < 1 ? 0 : build_workspace_bytes(build_args(cfg, batch, n));
+    case INFLLM_CALL_ATTEND:
+      if (chunk_len < 1 || n_chunks < 1) return 0;
+      return attend_ws_bytes(attend_args(cfg, batch, chunk_len, n_chunks));
+    default:
+      return 0;
+  }
+}
+
+infllm_status infllm_build_units(const infllm_config* cfg, int32_t batch, const void* q,
+                                 int64_t q_cap, const void* k, int64_t kv_cap, int64_t n_ctx,
+                                 int32_t* rep_idx, float* unit_repr, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  infllm_status st = check_config(cfg);
+  if (st != INFLLM_OK) return st;
+  if (batch < 1 || n_ctx < 1 || q_cap < n_ctx || kv_cap < n_ctx) return INFLLM_ERR_INVALID_ARG;
+  const bool tokens = cfg->rep_mode == INFLLM_REP_TOKENS;
+  if (!k || !aligned16(k) || (tokens && (!q || !aligned16(q)))) return INFLLM_ERR_INVALID_ARG;
+  BuildArgs a = build_args(cfg, batch, n_ctx);
+  if (a.U > 0) {
+    if (!unit_repr || !aligned16(unit_repr)) return INFLLM_ERR_INVALID_ARG;
+    if (tokens && (!rep_idx || !aligned16(rep_idx))) return INFLLM_ERR_INVALID_ARG;
+  }
+  const size_t need = build_workspace_bytes(a);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return INFLLM_ERR_WORKSPACE;
+  a.q = q;
+  a.q_cap = q_cap;
+  a.k = k;
+  a.kv_cap = kv_cap;
+  a.rep_idx = rep_idx;
+  a.unit_repr = unit_repr;
+  a.ws = workspace;
+  return launched(launch_build(a, (hipStream_t)stream));
+}
+
+infllm_status infllm_score_units(const infllm_config* cfg, int32_t batch, const void* q,
+                                 int64_t q_cap, int64_t q_off, int64_t q_pos, int32_t chunk_len,
+                                 int32_t n_chunks, const float* unit_repr, int32_t n_units,
+                                 float* scores, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  infllm_status st = check_config(cfg);
+  if (st != INFLLM_OK) return st;
+  if (batch < 1 || chunk_len < 1 || n_chunks < 1 || n_units < 0 || q_off < 0 || q_pos < 0)
+    return INFLLM_ERR_INVALID_ARG;
+  if (q_off + (int64_t)chunk_len * n_chunks > q_cap) return INFLLM_ERR_INVALID_ARG;
+  if ((int64_t)n_chunks * cfg->n_kv_heads > 65535) return INFLLM_ERR_UNSUPPORTED;
+  if (!q || !aligned16(q)) return INFLLM_ERR_INVALID_ARG;
+  if (n_units > 0 && (!unit_repr || !scores || !aligned16(unit_repr) || !aligned16(scores)))
+    return INFLLM_ERR_INVALID_ARG;
+  ScoreArgs a{};
+  a.batch = batch;
+  a.Hq = cfg->n_q_heads;
+  a.Hkv = cfg->n_kv_heads;
+  a.d = cfg->head_dim;
+  a.B = cfg->block;
+  a.n_init = cfg->n_init;
+  a.W = cfg->window;
+  a.L = chunk_len;
+  a.n_chunks = n_chunks;
+  a.U = n_units;
+  a.bf16 = cfg->dtype == INFLLM_BF16;
+  a.q = q;
+  a.q_cap = q_cap;
+  a.q_off = q_off;
+  a.q_pos = q_pos;
+  a.repr = unit_repr;
+  a.scores = scores;
+  return launched(launch_score(a, (hipStream_t)stream));
+}
+
+infllm_status infllm_topk_units(const infllm_config* cfg, int32_t batch, int32_t n_chunks,
+                                const float* scores, int32_t n_units, int32_t* sel,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  infllm_status st = check_config(cfg);
+  if (st != INFLLM_OK) return st;
+  if (batch < 1 || n_chunks < 1 || n_units < 0) return INFLLM_ERR_INVALID_ARG;
+  if (cfg->top_k == 0) return INFLLM_OK;
+  if (!sel || !aligned16(sel) || (n_units > 0 && (!scores || !aligned16(scores))))
+    return INFLLM_ERR_INVALID_ARG;
+  TopkArgs a{};
+  a.batch = batch;
+  a.Hkv = cfg->n_kv_heads;
+  a.n_chunks = n_chunks;
+  a.U = n_units;
+  a.k_m = cfg->top_k;
+  a.scores = scores;
+  a.sel = sel;
+  return launched(launch_topk(a, (hipStream_t)stream));
+}
+
+infllm_status infllm_attend(const infllm_config* cfg, int32_t batch, const void* q, int64_t q_cap,
+                            int64_t q_off, int64_t q_pos, int32_t chunk_len, int32_t n_chunks,
+                            const void* k, const void* v, int64_t kv_cap, const int32_t* sel,
+                            void* out, float* lse, int64_t out_cap, int64_t out_off,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  infllm_status st = check_config(cfg);
+  if (st != INFLLM_OK) return st;
+  if (batch < 1 || chunk_len < 1 || n_chunks < 1 || q_off < 0 || q_pos < 0 || out_off < 0)
+    return INFLLM_ERR_INVALID_ARG;
+  const int64_t n_pos = (int64_t)chunk_len * n_chunks;
+  if (n_pos > 65535 || (int64_t)batch * cfg->n_kv_heads > 65535) return INFLLM_ERR_UNSUPPORTED;
+  if (q_off + n_pos > q_cap || q_pos + n_pos > kv_cap || out_off + n_pos > out_cap)
+    return INFLLM_ERR_INVALID_ARG;
+  if (!q || !k || !v || !out || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return INFLLM_ERR_INVALID_ARG;
+  if (cfg->top_k > 0 && (!sel || !aligned16(sel))) return INFLLM_ERR_INVALID_ARG;
+  AttendArgs a = attend_args(cfg, batch, chunk_len, n_chunks);
+  bool mfma;
+  int splits;
+  attend_plan(a, &mfma, &splits);
+  const size_t need = attend_ws_bytes(a);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return INFLLM_ERR_WORKSPACE;
+  a.q = q;
+  a.q_cap = q_cap;
+  a.q_off = q_off;
+  a.q_pos = q_pos;
+  a.k = k;
+  a.v = v;
+  a.kv_cap = kv_cap;
+  a.sel = cfg->top_k > 0 ? sel : nullptr;
+  a.out = out;
+  a.lse = lse;
+  a.out_cap = out_cap;
+  a.out_off = out_off;
+  if (need > 0) {
+    const size_t rows = (size_t)splits * a.batch * a.Hq * a.n_pos;
+    const size_t o = rows * a.d * sizeof(float);
+    a.ws_o = (float*)workspace;
+    a.ws_ml = (float*)((char*)workspace + ((o + 255) & ~(size_t)255));
+  }
+  hipStream_t s = (hipStream_t)stream;
+  return launched(mfma ? launch_attend_prefill(a, splits, s) : launch_attend_rows(a, splits, s));
+}
+
+}  // extern "C"

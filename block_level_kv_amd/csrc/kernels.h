@@ -1,0 +1,69 @@
+// Internal launch interface between the C-ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace infllm {
+
+constexpr int kMaxTopK = 256;
+
+struct BuildArgs {
+  int batch, Hq, Hkv, d, B, n_init, W, r_k, rep_mode, U;
+  bool bf16;
+  const void* q;
+  int64_t q_cap;
+  const void* k;
+  int64_t kv_cap, n_ctx;
+  int32_t* rep_idx;
+  float* unit_repr;
+  void* ws;
+};
+
+struct ScoreArgs {
+  int batch, Hq, Hkv, d, B, n_init, W, L, n_chunks, U;
+  bool bf16;
+  const void* q;
+  int64_t q_cap, q_off, q_pos;
+  const float* repr;
+  float* scores;
+};
+
+struct TopkArgs {
+  int batch, Hkv, n_chunks, U, k_m;
+  const float* scores;
+  int32_t* sel;
+};
+
+struct AttendArgs {
+  int batch, Hq, Hkv, d, B, n_init, W, k_m, L, n_chunks, n_pos;
+  bool bf16;
+  const void* q;
+  int64_t q_cap, q_off, q_pos;
+  const void* k;
+  const void* v;
+  int64_t kv_cap;
+  const int32_t* sel;
+  void* out;
+  float* lse;
+  int64_t out_cap, out_off;
+  float* ws_o;   // split-K partial outputs
+  float* ws_ml;  // split-K partial (max, sum) pairs
+};
+
+size_t build_workspace_bytes(const BuildArgs& a);
+hipError_t launch_build(const BuildArgs& a, hipStream_t st);
+hipError_t launch_score(const ScoreArgs& a, hipStream_t st);
+hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
+
+// vector-ALU attention, one query position per workgroup
+int rows_num_splits(const AttendArgs& a);
+hipError_t launch_attend_rows(const AttendArgs& a, int splits, hipStream_t st);
+
+// bf16 MFMA attention tiles for query chunks (head_dim 128)
+bool prefill_supported(const AttendArgs& a);
+int prefill_num_splits(const AttendArgs& a);
+hipError_t launch_attend_prefill(const AttendArgs& a, int splits, hipStream_t st);
+
+}  // namespace infllm

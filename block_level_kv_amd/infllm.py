@@ -1,0 +1,211 @@
+"""ctypes binding of libinfllm.so (include/infllm.h), same call names.
+
+Argument marshalling only: shapes and dtypes of torch tensors are checked,
+then data pointers, sizes and the current HIP stream are handed to the C
+ABI, which does every step of the work in HIP kernels.  There is no
+fallback: if the library is missing or a call fails, an exception says so.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libinfllm.so")
+
+INFLLM_OK, INFLLM_ERR_INVALID_ARG, INFLLM_ERR_UNSUPPORTED, INFLLM_ERR_WORKSPACE, INFLLM_ERR_HIP = \
+    0, -1, -2, -3, -4
+INFLLM_F32, INFLLM_BF16 = 0, 1
+INFLLM_REP_TOKENS, INFLLM_REP_MEAN = 0, 1
+INFLLM_CALL_BUILD, INFLLM_CALL_SCORE, INFLLM_CALL_TOPK, INFLLM_CALL_ATTEND = 0, 1, 2, 3
+
+EXPORTED = ("infllm_num_units", "infllm_num_eligible", "infllm_workspace_size",
+            "infllm_build_units", "infllm_score_units", "infllm_topk_units", "infllm_attend",
+            "infllm_status_string", "infllm_abi_version")
+
+
+class infllm_config(ctypes.Structure):
+    _fields_ = [("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("block", ctypes.c_int32),
+                ("n_init", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("rep_k", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("rep_mode", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class InfllmError(RuntimeError):
+    def __init__(self, call: str, status: int):
+        self.status = status
+        super().__init__("%s failed: %s (%d)" % (call, status_string(status), status))
+
+
+_i32, _i64, _sz, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+_cfgp = ctypes.POINTER(infllm_config)
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libinfllm.so is not built (run: python -m block_level_kv_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.infllm_num_units.restype = _i32
+        L.infllm_num_units.argtypes = [_cfgp, _i64]
+        L.infllm_num_eligible.restype = _i32
+        L.infllm_num_eligible.argtypes = [_cfgp, _i64, _i32]
+        L.infllm_workspace_size.restype = _sz
+        L.infllm_workspace_size.argtypes = [_cfgp, _i32, _i32, _i64, _i32, _i32]
+        L.infllm_build_units.restype = _i32
+        L.infllm_build_units.argtypes = [_cfgp, _i32, _vp, _i64, _vp, _i64, _i64, _vp, _vp, _vp,
+                                         _sz, _vp]
+        L.infllm_score_units.restype = _i32
+        L.infllm_score_units.argtypes = [_cfgp, _i32, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _i32,
+                                         _vp, _vp, _sz, _vp]
+        L.infllm_topk_units.restype = _i32
+        L.infllm_topk_units.argtypes = [_cfgp, _i32, _i32, _vp, _i32, _vp, _vp, _sz, _vp]
+        L.infllm_attend.restype = _i32
+        L.infllm_attend.argtypes = [_cfgp, _i32, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _i64,
+                                    _vp, _vp, _vp, _i64, _i64, _vp, _sz, _vp]
+        L.infllm_status_string.restype = ctypes.c_char_p
+        L.infllm_status_string.argtypes = [_i32]
+        L.infllm_abi_version.restype = _i32
+        _LIB = L
+    return _LIB
+
+
+def status_string(status: int) -> str:
+    return lib().infllm_status_string(status).decode()
+
+
+def make_config(*, n_q_heads: int, n_kv_heads: int, head_dim: int, block: int, n_init: int,
+                window: int, rep_k: int, top_k: int, rep_mode: int = INFLLM_REP_TOKENS,
+                dtype: int = INFLLM_BF16) -> infllm_config:
+    return infllm_config(n_q_heads, n_kv_heads, head_dim, block, n_init, window, rep_k, top_k,
+                         rep_mode, dtype)
+
+
+# ------------------------------------------------------------------ helpers
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _dtype_of(cfg: infllm_config) -> torch.dtype:
+    return torch.bfloat16 if cfg.dtype == INFLLM_BF16 else torch.float32
+
+
+def _check(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a tensor" % name)
+    if t.dtype != dtype or t.dim() != ndim or not t.is_contiguous() or t.device.type != "cuda":
+        raise ValueError("%s must be a contiguous %dD %s CUDA/HIP tensor, got %s %s %s" %
+                         (name, ndim, dtype, t.dtype, tuple(t.shape), t.device))
+
+
+def _ws(t: torch.Tensor | None) -> tuple[int | None, int]:
+    if t is None:
+        return None, 0
+    return t.data_ptr(), t.numel() * t.element_size()
+
+
+def _raise(call: str, status: int) -> None:
+    if status != INFLLM_OK:
+        raise InfllmError(call, status)
+
+
+# ------------------------------------------------------------------ calls
+def infllm_num_units(cfg: infllm_config, n_ctx: int) -> int:
+    return int(lib().infllm_num_units(ctypes.byref(cfg), n_ctx))
+
+
+def infllm_num_eligible(cfg: infllm_config, t_last: int, n_units: int) -> int:
+    return int(lib().infllm_num_eligible(ctypes.byref(cfg), t_last, n_units))
+
+
+def infllm_workspace_size(cfg: infllm_config, call: int, batch: int, n: int = 0,
+                          chunk_len: int = 0, n_chunks: int = 0) -> int:
+    return int(lib().infllm_workspace_size(ctypes.byref(cfg), call, batch, n, chunk_len, n_chunks))
+
+
+def workspace(cfg: infllm_config, call: int, batch: int, n: int = 0, chunk_len: int = 0,
+              n_chunks: int = 0, device="cuda") -> torch.Tensor | None:
+    """A caller-owned workspace tensor of the size `call` needs (None if 0)."""
+    size = infllm_workspace_size(cfg, call, batch, n, chunk_len, n_chunks)
+    if size == 0:
+        return None
+    return torch.empty(size, dtype=torch.uint8, device=device)
+
+
+def infllm_build_units(cfg, q, k, n_ctx: int, rep_idx, unit_repr, ws=None, stream=None) -> None:
+    dt = _dtype_of(cfg)
+    if cfg.rep_mode == INFLLM_REP_TOKENS:
+        _check(q, "q", dt, 4)
+        _check(rep_idx, "rep_idx", torch.int32, 4)
+    _check(k, "k", dt, 4)
+    _check(unit_repr, "unit_repr", torch.float32, 4)
+    batch = k.shape[0]
+    U = infllm_num_units(cfg, n_ctx)
+    if tuple(unit_repr.shape) != (batch, cfg.n_kv_heads, U, cfg.head_dim):
+        raise ValueError("unit_repr must be [batch, H_kv, U=%d, d]" % U)
+    if rep_idx is not None and tuple(rep_idx.shape) != (batch, cfg.n_kv_heads, U, cfg.rep_k):
+        raise ValueError("rep_idx must be [batch, H_kv, U=%d, r_k]" % U)
+    q_cap = q.shape[2] if q is not None else 0
+    wp, wb = _ws(ws)
+    _raise("infllm_build_units", lib().infllm_build_units(
+        ctypes.byref(cfg), batch, _ptr(q), q_cap, k.data_ptr(), k.shape[2], n_ctx,
+        _ptr(rep_idx), unit_repr.data_ptr(), wp, wb, _stream(stream)))
+
+
+def infllm_score_units(cfg, q, q_off: int, q_pos: int, chunk_len: int, n_chunks: int, unit_repr,
+                       scores, ws=None, stream=None) -> None:
+    _check(q, "q", _dtype_of(cfg), 4)
+    _check(unit_repr, "unit_repr", torch.float32, 4)
+    _check(scores, "scores", torch.float32, 4)
+    batch, U = q.shape[0], unit_repr.shape[2]
+    if tuple(scores.shape) != (batch, cfg.n_kv_heads, n_chunks, U):
+        raise ValueError("scores must be [batch, H_kv, n_chunks, U]")
+    wp, wb = _ws(ws)
+    _raise("infllm_score_units", lib().infllm_score_units(
+        ctypes.byref(cfg), batch, q.data_ptr(), q.shape[2], q_off, q_pos, chunk_len, n_chunks,
+        unit_repr.data_ptr(), U, scores.data_ptr(), wp, wb, _stream(stream)))
+
+
+def infllm_topk_units(cfg, scores, sel, ws=None, stream=None) -> None:
+    _check(scores, "scores", torch.float32, 4)
+    _check(sel, "sel", torch.int32, 4)
+    batch, _, n_chunks, U = scores.shape
+    if tuple(sel.shape) != (batch, cfg.n_kv_heads, n_chunks, cfg.top_k):
+        raise ValueError("sel must be [batch, H_kv, n_chunks, k_m]")
+    wp, wb = _ws(ws)
+    _raise("infllm_topk_units", lib().infllm_topk_units(
+        ctypes.byref(cfg), batch, n_chunks, scores.data_ptr(), U, sel.data_ptr(), wp, wb,
+        _stream(stream)))
+
+
+def infllm_attend(cfg, q, q_off: int, q_pos: int, chunk_len: int, n_chunks: int, k, v, sel, out,
+                  lse=None, out_off: int = 0, ws=None, stream=None) -> None:
+    dt = _dtype_of(cfg)
+    _check(q, "q", dt, 4)
+    _check(k, "k", dt, 4)
+    _check(v, "v", dt, 4)
+    _check(out, "out", dt, 4)
+    if sel is not None:
+        _check(sel, "sel", torch.int32, 4)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, 3)
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    wp, wb = _ws(ws)
+    _raise("infllm_attend", lib().infllm_attend(
+        ctypes.byref(cfg), q.shape[0], q.data_ptr(), q.shape[2], q_off, q_pos, chunk_len, n_chunks,
+        k.data_ptr(), v.data_ptr(), k.shape[2], _ptr(sel), out.data_ptr(), _ptr(lse),
+        out.shape[2], out_off, wp, wb, _stream(stream)))

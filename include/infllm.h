@@ -1,0 +1,223 @@
+/*
+ * infllm.h -- C ABI of libinfllm.so: InfLLM's context-memory attention step
+ * on one AMD Instinct MI355X (gfx950).
+ *
+ * The method (InfLLM: Training-Free Long-Context Extrapolation for LLMs with
+ * an Efficient Context Memory; summary page, "Approach"; InfLLM Guide blog,
+ * "Core Innovation 1" and "Core Innovation 2"): the distant part of the KV
+ * cache is cut into fixed-size memory units; each unit is represented by its
+ * top-scoring representative keys (or by the mean of its keys); every query
+ * chunk scores all units, keeps the best k_m per KV head, and attends over
+ * the initial tokens, the retrieved units and a local sliding window.
+ *
+ * The four calls mirror that statement:
+ *   infllm_build_units  -- representative-token selection per unit
+ *   infllm_score_units  -- chunk-query . unit-representation scores
+ *   infllm_topk_units   -- top-k_m units per (sequence, KV head, chunk)
+ *   infllm_attend       -- exact softmax attention over the working context
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  Layout.  Q is [batch, n_q_heads, q_cap, head_dim] and K, V are
+ *    [batch, n_kv_heads, kv_cap, head_dim], dense row-major, element type
+ *    cfg->dtype (fp32, or bf16 stored as its 16-bit pattern).  Row t of a
+ *    K/V head is absolute position t.  Query head g reads KV head g / G with
+ *    G = n_q_heads / n_kv_heads.
+ *  Pointers.  Every tensor pointer is a device pointer, 16-byte aligned.
+ *    The library never dereferences them on the host.
+ *  Ownership.  The caller allocates every buffer, including the workspace
+ *    (size from infllm_workspace_size).  The library allocates nothing,
+ *    keeps no state between calls and is re-entrant.
+ *  Asynchrony.  Each call validates its arguments on the host, then only
+ *    enqueues kernels on `stream` (a hipStream_t; NULL = the null stream)
+ *    and returns; it never synchronises.  Device faults surface at the
+ *    caller's next synchronisation.
+ *  Errors.  Invalid arguments return INFLLM_ERR_INVALID_ARG (or
+ *    INFLLM_ERR_UNSUPPORTED / INFLLM_ERR_WORKSPACE) before any device
+ *    work is enqueued; a failed launch returns INFLLM_ERR_HIP.  Nothing is
+ *    thrown across the ABI.
+ *  Units.  Unit u is absolute block j = u + floor(n_init / block); its keys
+ *    are positions [max(j*block, n_init), (j+1)*block).  A context of n_ctx
+ *    tokens holds floor(n_ctx/block) - floor(n_init/block) units (blocks
+ *    aligned to multiples of the unit size, as in the guide's figure of a
+ *    unit spanning tokens 1024..1151).
+ *  Chunks.  The query-chunk calls take `n_chunks` consecutive chunks of
+ *    `chunk_len` queries: chunk c holds rows q_off + c*chunk_len ... of the
+ *    Q buffer, at absolute positions q_pos + c*chunk_len ....  Each chunk has
+ *    its own unit selection (retrieval during pre-filling is done per block
+ *    of queries: authors' rebuttal, "Comparison to Well-trained Long LLM").
+ *    A decode step is one chunk of length 1.
+ */
+#ifndef INFLLM_H
+#define INFLLM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define INFLLM_ABI_VERSION 1
+
+#if defined(__GNUC__) || defined(__clang__)
+#define INFLLM_API __attribute__((visibility("default")))
+#else
+#define INFLLM_API
+#endif
+
+typedef enum {
+  INFLLM_OK = 0,
+  INFLLM_ERR_INVALID_ARG = -1, /* a pointer, size or config field is invalid */
+  INFLLM_ERR_UNSUPPORTED = -2, /* valid, but outside what the kernels handle */
+  INFLLM_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+  INFLLM_ERR_HIP = -4          /* a HIP launch failed */
+} infllm_status;
+
+typedef enum { INFLLM_F32 = 0, INFLLM_BF16 = 1 } infllm_dtype;
+
+/* Unit representation: top-r_k representative tokens (summed), or the mean
+ * of the unit's keys (summary page, "Measured effects": representative
+ * tokens versus mean key vectors). */
+typedef enum { INFLLM_REP_TOKENS = 0, INFLLM_REP_MEAN = 1 } infllm_rep_mode;
+
+typedef enum {
+  INFLLM_CALL_BUILD = 0,
+  INFLLM_CALL_SCORE = 1,
+  INFLLM_CALL_TOPK = 2,
+  INFLLM_CALL_ATTEND = 3
+} infllm_call;
+
+typedef struct {
+  int32_t n_q_heads;  /* H_q >= 1, multiple of n_kv_heads                  */
+  int32_t n_kv_heads; /* H_kv >= 1                                          */
+  int32_t head_dim;   /* d: 64 or 128                                       */
+  int32_t block;      /* unit size B: multiple of 64, 64..1024              */
+  int32_t n_init;     /* initial (sink) tokens, >= 0                        */
+  int32_t window;     /* local window W >= 1: query t sees t-W+1 .. t       */
+  int32_t rep_k;      /* representative tokens per unit, 1..block (TOKENS)  */
+  int32_t top_k;      /* units retrieved per chunk k_m, 0..256              */
+  int32_t rep_mode;   /* infllm_rep_mode                                    */
+  int32_t dtype;      /* infllm_dtype of Q, K, V and the attention output  */
+} infllm_config;
+
+/* Units held by a context of n_ctx tokens: floor(n_ctx/B) - floor(n_init/B),
+ * or 0.  Returns -1 for an invalid config. */
+INFLLM_API int32_t infllm_num_units(const infllm_config *cfg, int64_t n_ctx);
+
+/* Units eligible for a chunk whose last query is at position t_last: those
+ * whose first key lies at or before t_last - W (a unit key is attended only
+ * while it is outside the local window).  They form the prefix
+ * [0, result) of [0, n_units).  Returns -1 for an invalid config. */
+INFLLM_API int32_t infllm_num_eligible(const infllm_config *cfg, int64_t t_last, int32_t n_units);
+
+/* Workspace bytes `call` needs for the given sizes (0 if none).  For BUILD
+ * pass n = n_ctx; for SCORE/TOPK/ATTEND pass the chunk geometry (n unused
+ * for TOPK, which takes n_units in `n`). */
+INFLLM_API size_t infllm_workspace_size(const infllm_config *cfg, int32_t call, int32_t batch, int64_t n,
+                             int32_t chunk_len, int32_t n_chunks);
+
+/*
+ * infllm_build_units -- unit representations for a context of n_ctx tokens.
+ *
+ * TOKENS (summary page, "Approach": each unit is represented by its top-
+ * scoring tokens chosen with attention-based scores; authors' rebuttal,
+ * "Representative Tokens": the model selects discrete tokens).  Key p of
+ * KV head h scores
+ *     s_p = sum_{g in group(h)} sum_{i = p+1}^{min(p+W, n_ctx-1)} q_i^(g) . k_p
+ * (raw, unscaled; the queries that follow it inside one local window).
+ * Per unit the r_k keys with the highest s_p are kept (ties: lower
+ * position), listed in ascending position in rep_idx, and the unit is
+ * represented by their sum.  Scores are accumulated in fp64.
+ * MEAN: the representation is the mean of the unit's keys; rep_idx unused.
+ *
+ *   q          [batch, H_q, q_cap, d]  queries of positions 0 .. n_ctx-1
+ *   k          [batch, H_kv, kv_cap, d]
+ *   n_ctx      context tokens, 1 <= n_ctx <= min(q_cap, kv_cap)
+ *   rep_idx    out [batch, H_kv, U, r_k] int32 absolute positions, -1 pads
+ *              (TOKENS; may be NULL for MEAN)
+ *   unit_repr  out [batch, H_kv, U, d] fp32, U = infllm_num_units(n_ctx)
+ *   workspace  >= infllm_workspace_size(cfg, INFLLM_CALL_BUILD, batch, n_ctx, 0, 0)
+ */
+INFLLM_API infllm_status infllm_build_units(const infllm_config *cfg, int32_t batch, const void *q,
+                                 int64_t q_cap, const void *k, int64_t kv_cap, int64_t n_ctx,
+                                 int32_t *rep_idx, float *unit_repr, void *workspace,
+                                 size_t workspace_bytes, void *stream);
+
+/*
+ * infllm_score_units -- relevance of every unit to each query chunk.
+ *
+ * (InfLLM Guide, "Core Innovation 2", item 2: a dot product of the query
+ * against every unit representation; authors' rebuttal, "Latency Across
+ * Different Context Windows": the lookup takes the dot product with all unit
+ * representations.)  For chunk c and KV head h:
+ *     score[u] = (sum over the chunk's queries and the group's query heads
+ *                 of q) . unit_repr[u]              for u < e_c,
+ *     score[u] = -inf                               otherwise,
+ * with e_c = infllm_num_eligible(position of the chunk's last query).  The
+ * query sum and the dot product are accumulated in fp64.
+ *
+ *   q          [batch, H_q, q_cap, d]; rows q_off .. q_off + n_chunks*chunk_len - 1
+ *   q_pos      absolute position of row q_off
+ *   unit_repr  [batch, H_kv, n_units, d] fp32 (from infllm_build_units)
+ *   scores     out [batch, H_kv, n_chunks, n_units] fp32
+ */
+INFLLM_API infllm_status infllm_score_units(const infllm_config *cfg, int32_t batch, const void *q,
+                                 int64_t q_cap, int64_t q_off, int64_t q_pos, int32_t chunk_len,
+                                 int32_t n_chunks, const float *unit_repr, int32_t n_units,
+                                 float *scores, void *workspace, size_t workspace_bytes,
+                                 void *stream);
+
+/*
+ * infllm_topk_units -- keep the k_m best units per (sequence, KV head,
+ * chunk) (InfLLM Guide, "Core Innovation 2", item 2: the top-k highest-
+ * scoring units are loaded for exact attention).
+ *
+ * Among the finite scores, min(k_m, #finite) units are kept by (score
+ * descending, unit index ascending) and written in ascending index order;
+ * remaining slots are -1.  -inf marks an ineligible unit and is never kept.
+ *
+ *   scores  [batch, H_kv, n_chunks, n_units] fp32, no NaN
+ *   sel     out [batch, H_kv, n_chunks, k_m] int32
+ */
+INFLLM_API infllm_status infllm_topk_units(const infllm_config *cfg, int32_t batch, int32_t n_chunks,
+                                const float *scores, int32_t n_units, int32_t *sel,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * infllm_attend -- exact attention over the working context (InfLLM Guide,
+ * "Core Innovation 2", item 3, the Working Context equation: sinks, the
+ * retrieved units and the local window; "Core Innovation 1", items 1-2).
+ *
+ * Query t (chunk c) of query head g attends the keys p <= t with
+ *     p < n_init                                  (initial tokens), or
+ *     t - W < p                                   (local window, t included), or
+ *     n_init <= p <= t - W and unit(p) in sel_c   (retrieved units),
+ * softmax(q.k_p / sqrt(d)) . V, fp32 online softmax (bf16 MFMA products for
+ * bf16 inputs).  The output is rounded to the input dtype.
+ *
+ *   q        [batch, H_q, q_cap, d]; rows q_off .., positions q_pos ..
+ *   k, v     [batch, H_kv, kv_cap, d]; must hold every attended position
+ *            (q_pos + n_chunks*chunk_len <= kv_cap)
+ *   sel      [batch, H_kv, n_chunks, k_m] int32 unit ids (-1 = empty slot),
+ *            e.g. from infllm_topk_units; ids must be < the number of units
+ *            the K/V context holds (not checked on the device)
+ *   out      out [batch, H_q, out_cap, d], rows out_off .. out_off +
+ *            n_chunks*chunk_len - 1, cfg->dtype
+ *   lse      optional out [batch, H_q, out_cap] fp32 natural-log
+ *            sum-exp of the scaled logits, same rows; may be NULL
+ */
+INFLLM_API infllm_status infllm_attend(const infllm_config *cfg, int32_t batch, const void *q, int64_t q_cap,
+                            int64_t q_off, int64_t q_pos, int32_t chunk_len, int32_t n_chunks,
+                            const void *k, const void *v, int64_t kv_cap, const int32_t *sel,
+                            void *out, float *lse, int64_t out_cap, int64_t out_off,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+INFLLM_API const char *infllm_status_string(int32_t status);
+INFLLM_API int32_t infllm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* INFLLM_H */

@@ -1,0 +1,270 @@
+"""GPU parity: every C-ABI stage against the fp64 oracle on the same seeded
+inputs, at sizes the oracle finishes in seconds (several tiles, ragged
+tails), plus edge cases.  Stage-isolated: each stage gets identical inputs on
+both sides; the full pipeline is compared stage by stage on the GPU's own
+upstream outputs."""
+import numpy as np
+import pytest
+import torch
+
+from block_level_kv_amd import infllm as F
+from block_level_kv_amd import synth
+from gpu_helpers import (assert_close, cfg_of, check_rep_idx, check_selection, gpu_attend,
+                         gpu_build, gpu_score, gpu_topk, tolerance)
+
+pytestmark = pytest.mark.gpu
+
+LL = synth.WORKLOADS["llama3_8b_32k_encode"]
+CASES = {
+    # bf16, G=4, d=128, W a multiple of B, ragged context (not a multiple of B)
+    "bf16_g4": LL.replace(n_ctx=3136, n_q_heads=8, n_kv_heads=2, window=512, top_k=4, chunk=256),
+    # fp32, G=1, d=64, sinks not a multiple of B (partial unit 0), planted block
+    "f32_g1": synth.WORKLOADS["tiny_f32"].replace(n_ctx=2048),
+    # bf16, G=8, W not a multiple of B, sinks 100, chunk 192
+    "bf16_g8_ragged": LL.replace(n_ctx=2500, n_q_heads=8, n_kv_heads=1, window=300, n_init=100,
+                                 top_k=5, chunk=192),
+    # bf16, mean-of-keys units, clustered keys
+    "bf16_mean": synth.WORKLOADS["mistral_7b_64k_mean"].replace(
+        n_ctx=3072, n_q_heads=8, n_kv_heads=2, window=512, top_k=6, chunk=256, decode_steps=0),
+    # bf16, G=2, d=64
+    "bf16_g2_d64": LL.replace(n_ctx=2304, n_q_heads=4, n_kv_heads=2, head_dim=64, window=256,
+                              top_k=3, chunk=128, scale=0.125),
+}
+
+
+@pytest.fixture(scope="module")
+def data():
+    cache = {}
+
+    def get(name):
+        if name not in cache:
+            w = CASES[name]
+            inp = synth.make_inputs(w)
+            dev = {k: (v.cuda() if isinstance(v, torch.Tensor) and k != "planted_units" else v)
+                   for k, v in inp.items()}
+            cache[name] = (w, inp, dev)
+        return cache[name]
+    return get
+
+
+def oracle_build(orc, w, inp):
+    return orc.build_units_all(inp["q"], inp["k"], w.n_ctx, B=w.block, n_init=w.n_init,
+                               W=w.window, r_k=w.rep_k, mode=w.rep_mode)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_build_parity(orc, data, name):
+    w, inp, dev = data(name)
+    cfg = cfg_of(w)
+    rep_g, repr_g = gpu_build(cfg, dev["q"], dev["k"], w.n_ctx)
+    torch.cuda.synchronize()
+    rep_o, repr_o, ks_o = oracle_build(orc, w, inp)
+    rg = repr_g.cpu().numpy()
+    if w.rep_mode == "mean":
+        np.testing.assert_array_equal(rg, repr_o.astype(np.float32))
+        return
+    ex = check_rep_idx(rep_g.cpu().numpy(), rep_o, ks_o, w.block, w.n_init)
+    assert len(ex) <= max(2, rep_o.shape[2] // 50)
+    same = np.all(rep_g.cpu().numpy() == rep_o, axis=-1)
+    # same representatives -> the fp64 sum rounded once: bit-identical
+    np.testing.assert_array_equal(rg[same], repr_o.astype(np.float32)[same])
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_score_and_topk_parity(orc, data, name):
+    w, inp, dev = data(name)
+    cfg = cfg_of(w)
+    U = orc.num_units(w.n_ctx, w.block, w.n_init)
+    gen = torch.Generator().manual_seed(7)
+    repr32 = (torch.randn((w.batch, w.n_kv_heads, U, w.head_dim), generator=gen)).float()
+    n_chunks = w.n_ctx // w.chunk
+    scores = gpu_score(cfg, dev["q"], 0, 0, w.chunk, n_chunks, repr32.cuda())
+    # the same chunks one call at a time give bit-identical scores
+    s1 = gpu_score(cfg, dev["q"], w.chunk, w.chunk, w.chunk, 1, repr32.cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(scores[:, :, 1:2], s1)
+    sg = scores.cpu().numpy()
+    sel_g = gpu_topk(cfg, scores).cpu().numpy()
+    G = w.group
+    for c in range(n_chunks):
+        t0 = c * w.chunk
+        e = orc.num_eligible(t0 + w.chunk - 1, U, w.block, w.n_init, w.window)
+        assert F.infllm_num_eligible(cfg, t0 + w.chunk - 1, U) == e
+        for bi in range(w.batch):
+            for h in range(w.n_kv_heads):
+                so = orc.score_units(inp["q"][bi, h * G:(h + 1) * G, t0:t0 + w.chunk],
+                                     repr32[bi, h].double().numpy(), e)
+                fin = np.isfinite(so)
+                assert (np.isfinite(sg[bi, h, c]) == fin).all()
+                np.testing.assert_allclose(sg[bi, h, c][fin], so[fin], rtol=1e-6,
+                                           atol=1e-6 * np.abs(so[fin]).max(initial=1.0))
+                # top-k on the GPU's fp32 scores: exact against the oracle on
+                # the same (widened) values
+                so32 = sg[bi, h, c].astype(np.float64)
+                assert sel_g[bi, h, c].tolist() == orc.topk(so32, e, w.top_k).tolist()
+                # and within the near-tie rule of the oracle's own fp64 scores
+                check_selection(sel_g[bi, h, c], orc.topk(so, e, w.top_k), so)
+
+
+@pytest.mark.parametrize("U,k_m,ties", [(1, 4, False), (7, 3, True), (255, 16, True),
+                                        (1023, 32, False), (8191, 32, True), (8191, 256, False),
+                                        (40, 64, False), (300, 1, True)])
+def test_topk_exact(orc, U, k_m, ties):
+    gen = torch.Generator().manual_seed(U * 131 + k_m)
+    nc = 3
+    if ties:
+        s = torch.randint(-6, 6, (2, 2, nc, U), generator=gen).float() * 0.5
+    else:
+        s = torch.randn((2, 2, nc, U), generator=gen)
+    s[..., U - U // 5:] = -float("inf")                       # an ineligible tail
+    s[1, 1, 2] = -float("inf")                                # nothing eligible
+    s[0, 1, 1, :3] = torch.tensor([0.0, -0.0, 0.0])[:min(3, U)]
+    cfg = F.make_config(n_q_heads=4, n_kv_heads=2, head_dim=128, block=128, n_init=128,
+                        window=512, rep_k=4, top_k=k_m)
+    sel = gpu_topk(cfg, s.cuda()).cpu().numpy()
+    for idx in np.ndindex(s.shape[:3]):
+        row = s[idx].double().numpy()
+        e = int(np.argmax(~np.isfinite(row))) if not np.isfinite(row).all() else U
+        assert sel[idx].tolist() == orc.topk(row, e, k_m).tolist(), idx
+
+
+def _oracle_selection(orc, w, inp, t0, L, repr_o):
+    _, sel, e = orc.select_all(inp["q"][:, :, t0:t0 + L], t0, repr_o, B=w.block, n_init=w.n_init,
+                               W=w.window, k_m=w.top_k)
+    return sel
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_attend_chunks_parity(orc, data, name):
+    """Chunked encoding: every chunk in one call (per-chunk selections)."""
+    w, inp, dev = data(name)
+    cfg = cfg_of(w)
+    _, repr_o, _ = oracle_build(orc, w, inp)
+    n_chunks = w.n_ctx // w.chunk
+    sels = np.stack([_oracle_selection(orc, w, inp, c * w.chunk, w.chunk, repr_o)
+                     for c in range(n_chunks)], axis=2)            # [b, H_kv, nc, k_m]
+    out, lse = gpu_attend(cfg, dev["q"], 0, 0, w.chunk, n_chunks, dev["k"], dev["v"],
+                          torch.from_numpy(sels).cuda())
+    torch.cuda.synchronize()
+    # oracle on a sample of chunks: first, one in the middle, the last
+    for c in sorted({0, n_chunks // 2, n_chunks - 1}):
+        t0 = c * w.chunk
+        o_ref, l_ref = orc.attend_all(inp["q"][:, :, t0:t0 + w.chunk], t0, inp["k"], inp["v"],
+                                      sels[:, :, c], B=w.block, n_init=w.n_init, W=w.window)
+        tol = tolerance(inp["q"].dtype, o_ref)
+        assert_close(out[:, :, t0:t0 + w.chunk], o_ref, tol, "%s chunk %d out" % (name, c))
+        assert_close(lse[:, :, t0:t0 + w.chunk], l_ref, 1e-3, "%s chunk %d lse" % (name, c))
+
+
+@pytest.mark.parametrize("name", ["bf16_g4", "f32_g1", "bf16_g8_ragged"])
+def test_attend_edge_cases(orc, data, name):
+    w, inp, dev = data(name)
+    U = orc.num_units(w.n_ctx, w.block, w.n_init)
+    G = w.group
+    # (a) k_m = 0: sinks + window only; (b) every unit selected: dense causal;
+    # (c) a ragged chunk of 37 queries straddling the first eligible unit;
+    # (d) decode-like single positions, including t < n_init
+    cases = [("no_units", cfg_of(w, top_k=0), np.zeros((w.batch, w.n_kv_heads, 1, 0), np.int32),
+              w.n_ctx - 100, 100),
+             ("all_units", cfg_of(w, top_k=min(U, 256)),
+              np.broadcast_to(np.arange(min(U, 256), dtype=np.int32),
+                              (w.batch, w.n_kv_heads, 1, min(U, 256))).copy(), w.n_ctx - 64, 64),
+             ("ragged", cfg_of(w), None, w.window + w.n_init - 20, 37),
+             ("early", cfg_of(w), None, 0, 1),
+             ("late_single", cfg_of(w), None, w.n_ctx - 1, 1)]
+    _, repr_o, _ = oracle_build(orc, w, inp)
+    for label, cfg, sel, t0, L in cases:
+        if sel is None:
+            sel = _oracle_selection(orc, w, inp, t0, L, repr_o)[:, :, None, :]
+        sel_t = torch.from_numpy(np.ascontiguousarray(sel)).cuda() if sel.shape[-1] > 0 else None
+        out, lse = gpu_attend(cfg, dev["q"], t0, t0, L, 1, dev["k"], dev["v"], sel_t)
+        torch.cuda.synchronize()
+        s0 = sel[:, :, 0] if sel.shape[-1] > 0 else np.zeros((w.batch, w.n_kv_heads, 0), np.int32)
+        o_ref, l_ref = orc.attend_all(inp["q"][:, :, t0:t0 + L], t0, inp["k"], inp["v"], s0,
+                                      B=w.block, n_init=w.n_init, W=w.window)
+        tol = tolerance(inp["q"].dtype, o_ref)
+        assert_close(out, o_ref, tol, "%s %s out" % (name, label))
+        assert_close(lse, l_ref, 1e-3, "%s %s lse" % (name, label))
+
+
+def test_empty_unit_pool(orc):
+    """A context shorter than one unit: no units, nothing eligible, sel all -1."""
+    w = CASES["bf16_g4"].replace(n_ctx=200)
+    cfg = cfg_of(w)
+    inp = synth.make_inputs(w)
+    q, k = inp["q"].cuda(), inp["k"].cuda()
+    rep_idx, repr_ = gpu_build(cfg, q, k, w.n_ctx)
+    assert repr_.shape[2] == 0
+    scores = gpu_score(cfg, q, 100, 100, 100, 1, repr_)
+    sel = gpu_topk(cfg, scores)
+    torch.cuda.synchronize()
+    assert (sel.cpu() == -1).all()
+
+
+def test_decode_steps_parity(orc):
+    """Decode: per step score(L=1) -> top-k -> attend, against the oracle."""
+    w = synth.WORKLOADS["llama3_8b_128k_decode"].replace(n_ctx=6144, batch=2, n_q_heads=8,
+                                                         n_kv_heads=2, decode_steps=6, top_k=8,
+                                                         window=1024)
+    cfg = cfg_of(w)
+    inp = synth.make_inputs(w)
+    dev = {k: v.cuda() for k, v in inp.items() if isinstance(v, torch.Tensor)}
+    _, repr_g = gpu_build(cfg, dev["q"], dev["k"], w.n_ctx)
+    repr_np = repr_g.cpu().double().numpy()
+    U = repr_np.shape[2]
+    G = w.group
+    for s in range(w.decode_steps):
+        t = w.n_ctx + s
+        scores = gpu_score(cfg, dev["q_dec"], s, t, 1, 1, repr_g)
+        sel = gpu_topk(cfg, scores)
+        out, lse = gpu_attend(cfg, dev["q_dec"], s, t, 1, 1, dev["k"], dev["v"], sel)
+        torch.cuda.synchronize()
+        e = orc.num_eligible(t, U, w.block, w.n_init, w.window)
+        sg = sel.cpu().numpy()
+        for bi in range(w.batch):
+            for h in range(w.n_kv_heads):
+                so = orc.score_units(inp["q_dec"][bi, h * G:(h + 1) * G, s:s + 1], repr_np[bi, h], e)
+                check_selection(sg[bi, h, 0], orc.topk(so, e, w.top_k), so)
+        o_ref, l_ref = orc.attend_all(inp["q_dec"][:, :, s:s + 1], t, inp["k"], inp["v"],
+                                      sg[:, :, 0], B=w.block, n_init=w.n_init, W=w.window)
+        assert_close(out, o_ref, tolerance(torch.bfloat16, o_ref), "decode step %d" % s)
+        assert_close(lse, l_ref, 1e-3, "decode lse step %d" % s)
+
+
+def test_tiny_workload_pipeline(orc):
+    """The tiny fp32 workload end to end (4,096 tokens, 16 chunks of 256,
+    calls issued one chunk at a time), stage by stage, plus planted-unit
+    recall equal to the oracle's."""
+    w = synth.WORKLOADS["tiny_f32"]
+    cfg = cfg_of(w)
+    inp = synth.make_inputs(w)
+    dev = {k: v.cuda() for k, v in inp.items() if isinstance(v, torch.Tensor) and k != "planted_units"}
+    rep_g, repr_g = gpu_build(cfg, dev["q"], dev["k"], w.n_ctx)
+    torch.cuda.synchronize()
+    rep_o, repr_o, ks_o = oracle_build(orc, w, inp)
+    check_rep_idx(rep_g.cpu().numpy(), rep_o, ks_o, w.block, w.n_init)
+    repr_np = repr_g.cpu().double().numpy()
+    U = repr_np.shape[2]
+    pu = w.planted_block - w.n_init // w.block
+    hits_g = hits_o = n_elig = 0
+    for c in range(w.n_ctx // w.chunk):
+        t0 = c * w.chunk
+        scores = gpu_score(cfg, dev["q"], t0, t0, w.chunk, 1, repr_g)
+        sel = gpu_topk(cfg, scores)
+        out, lse = gpu_attend(cfg, dev["q"], t0, t0, w.chunk, 1, dev["k"], dev["v"], sel)
+        torch.cuda.synchronize()
+        e = orc.num_eligible(t0 + w.chunk - 1, U, w.block, w.n_init, w.window)
+        so = orc.score_units(inp["q"][0, :, t0:t0 + w.chunk], repr_np[0, 0], e)
+        so_sel = orc.topk(so, e, w.top_k)
+        sg = sel.cpu().numpy()[0, 0, 0]
+        check_selection(sg, so_sel, so)
+        if e > pu:
+            n_elig += 1
+            hits_g += pu in sg.tolist()
+            hits_o += pu in so_sel.tolist()
+        o_ref, l_ref = orc.attend_all(inp["q"][:, :, t0:t0 + w.chunk], t0, inp["k"], inp["v"],
+                                      sel.cpu().numpy()[:, :, 0], B=w.block, n_init=w.n_init,
+                                      W=w.window)
+        assert_close(out, o_ref, 1e-4, "tiny chunk %d" % c)
+        assert_close(lse, l_ref, 1e-4, "tiny lse chunk %d" % c)
+    assert n_elig == 10 and hits_g == hits_o
