@@ -249,11 +249,24 @@ int rows_num_splits(const AttendArgs& a) {
   return s < 1 ? 1 : (int)s;
 }
 
+hipError_t launch_combine(const AttendArgs& a, int splits, hipStream_t st) {
+  const dim3 grid(a.n_pos, a.Hq, a.batch);
+  if (a.bf16) {
+    if (a.d == 128) k_combine<bf16_t, 128><<<grid, 128, 0, st>>>(a, splits);
+    else k_combine<bf16_t, 64><<<grid, 64, 0, st>>>(a, splits);
+  } else {
+    if (a.d == 128) k_combine<float, 128><<<grid, 128, 0, st>>>(a, splits);
+    else k_combine<float, 64><<<grid, 64, 0, st>>>(a, splits);
+  }
+  return hipGetLastError();
+}
+
 template <typename T, int D, int G>
 static hipError_t launch_rows_tdg(const AttendArgs& a, int splits, hipStream_t st) {
   k_attend_rows<T, D, G><<<dim3(splits, a.n_pos, a.batch * a.Hkv), kRowsThreads, 0, st>>>(a);
-  if (splits > 1) k_combine<T, D><<<dim3(a.n_pos, a.Hq, a.batch), D, 0, st>>>(a, splits);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  return launch_combine(a, splits, st);
 }
 
 template <typename T, int D>

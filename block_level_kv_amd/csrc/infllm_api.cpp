@@ -40,6 +40,21 @@ int64_t num_units(const infllm_config* c, int64_t n) {
 
 infllm_status launched(hipError_t e) { return e == hipSuccess ? INFLLM_OK : INFLLM_ERR_HIP; }
 
+ScoreArgs score_args(const infllm_config* c, int32_t batch, int32_t chunk_len, int32_t n_chunks) {
+  ScoreArgs a{};
+  a.batch = batch;
+  a.Hq = c->n_q_heads;
+  a.Hkv = c->n_kv_heads;
+  a.d = c->head_dim;
+  a.B = c->block;
+  a.n_init = c->n_init;
+  a.W = c->window;
+  a.L = chunk_len;
+  a.n_chunks = n_chunks;
+  a.bf16 = c->dtype == INFLLM_BF16;
+  return a;
+}
+
 BuildArgs build_args(const infllm_config* c, int32_t batch, int64_t n_ctx) {
   BuildArgs a{};
   a.batch = batch;
@@ -80,15 +95,28 @@ void attend_plan(const AttendArgs& a, bool* mfma, int* splits) {
   *splits = *mfma ? prefill_num_splits(a) : rows_num_splits(a);
 }
 
-size_t attend_ws_bytes(const AttendArgs& a) {
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Attention workspace: [split-K counters][partial outputs][partial (max, sum)].
+struct AttendWs {
+  size_t count_bytes, o_bytes, ml_bytes;
+  size_t total() const { return count_bytes + o_bytes + ml_bytes; }
+};
+
+AttendWs attend_ws_layout(const AttendArgs& a) {
   bool mfma;
   int splits;
   attend_plan(a, &mfma, &splits);
-  if (splits <= 1) return 0;
+  AttendWs w{0, 0, 0};
+  if (splits <= 1) return w;
   const size_t rows = (size_t)splits * a.batch * a.Hq * a.n_pos;
-  const size_t o = rows * a.d * sizeof(float);
-  return ((o + 255) & ~(size_t)255) + rows * 2 * sizeof(float);
+  if (mfma) w.count_bytes = round256((size_t)prefill_num_counters(a) * sizeof(int));
+  w.o_bytes = round256(rows * a.d * sizeof(float));
+  w.ml_bytes = rows * 2 * sizeof(float);
+  return w;
 }
+
+size_t attend_ws_bytes(const AttendArgs& a) { return attend_ws_layout(a).total(); }
 
 }  // namespace
 
@@ -124,6 +152,9 @@ size_t infllm_workspace_size(const infllm_config* cfg, int32_t call, int32_t bat
   switch (call) {
     case INFLLM_CALL_BUILD:
       return n < 1 ? 0 : build_workspace_bytes(build_args(cfg, batch, n));
+    case INFLLM_CALL_SCORE:
+      if (chunk_len < 1 || n_chunks < 1) return 0;
+      return score_workspace_bytes(score_args(cfg, batch, chunk_len, n_chunks));
     case INFLLM_CALL_ATTEND:
       if (chunk_len < 1 || n_chunks < 1) return 0;
       return attend_ws_bytes(attend_args(cfg, batch, chunk_len, n_chunks));
@@ -164,8 +195,6 @@ infllm_status infllm_score_units(const infllm_config* cfg, int32_t batch, const 
                                  int32_t n_chunks, const float* unit_repr, int32_t n_units,
                                  float* scores, void* workspace, size_t workspace_bytes,
                                  void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   infllm_status st = check_config(cfg);
   if (st != INFLLM_OK) return st;
   if (batch < 1 || chunk_len < 1 || n_chunks < 1 || n_units < 0 || q_off < 0 || q_pos < 0)
@@ -175,18 +204,12 @@ infllm_status infllm_score_units(const infllm_config* cfg, int32_t batch, const 
   if (!q || !aligned16(q)) return INFLLM_ERR_INVALID_ARG;
   if (n_units > 0 && (!unit_repr || !scores || !aligned16(unit_repr) || !aligned16(scores)))
     return INFLLM_ERR_INVALID_ARG;
-  ScoreArgs a{};
-  a.batch = batch;
-  a.Hq = cfg->n_q_heads;
-  a.Hkv = cfg->n_kv_heads;
-  a.d = cfg->head_dim;
-  a.B = cfg->block;
-  a.n_init = cfg->n_init;
-  a.W = cfg->window;
-  a.L = chunk_len;
-  a.n_chunks = n_chunks;
+  ScoreArgs a = score_args(cfg, batch, chunk_len, n_chunks);
   a.U = n_units;
-  a.bf16 = cfg->dtype == INFLLM_BF16;
+  const size_t need = score_workspace_bytes(a);
+  if (n_units > 0 && need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return INFLLM_ERR_WORKSPACE;
+  a.ws = workspace;
   a.q = q;
   a.q_cap = q_cap;
   a.q_off = q_off;
@@ -231,6 +254,7 @@ infllm_status infllm_attend(const infllm_config* cfg, int32_t batch, const void*
   if (n_pos > 65535 || (int64_t)batch * cfg->n_kv_heads > 65535) return INFLLM_ERR_UNSUPPORTED;
   if (q_off + n_pos > q_cap || q_pos + n_pos > kv_cap || out_off + n_pos > out_cap)
     return INFLLM_ERR_INVALID_ARG;
+  if (q_pos + n_pos > ((int64_t)1 << 31) - 128) return INFLLM_ERR_UNSUPPORTED;
   if (!q || !k || !v || !out || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return INFLLM_ERR_INVALID_ARG;
   if (cfg->top_k > 0 && (!sel || !aligned16(sel))) return INFLLM_ERR_INVALID_ARG;
@@ -254,10 +278,10 @@ infllm_status infllm_attend(const infllm_config* cfg, int32_t batch, const void*
   a.out_cap = out_cap;
   a.out_off = out_off;
   if (need > 0) {
-    const size_t rows = (size_t)splits * a.batch * a.Hq * a.n_pos;
-    const size_t o = rows * a.d * sizeof(float);
-    a.ws_o = (float*)workspace;
-    a.ws_ml = (float*)((char*)workspace + ((o + 255) & ~(size_t)255));
+    const AttendWs lay = attend_ws_layout(a);
+    a.ws_count = (int*)workspace;
+    a.ws_o = (float*)((char*)workspace + lay.count_bytes);
+    a.ws_ml = (float*)((char*)workspace + lay.count_bytes + lay.o_bytes);
   }
   hipStream_t s = (hipStream_t)stream;
   return launched(mfma ? launch_attend_prefill(a, splits, s) : launch_attend_rows(a, splits, s));

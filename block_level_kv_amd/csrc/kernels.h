@@ -28,6 +28,7 @@ struct ScoreArgs {
   int64_t q_cap, q_off, q_pos;
   const float* repr;
   float* scores;
+  void* ws;  // fp64 partial query sums of long chunks
 };
 
 struct TopkArgs {
@@ -50,20 +51,25 @@ struct AttendArgs {
   int64_t out_cap, out_off;
   float* ws_o;   // split-K partial outputs
   float* ws_ml;  // split-K partial (max, sum) pairs
+  int* ws_count; // split-K arrival counters (zero between calls)
 };
 
 size_t build_workspace_bytes(const BuildArgs& a);
 hipError_t launch_build(const BuildArgs& a, hipStream_t st);
+size_t score_workspace_bytes(const ScoreArgs& a);
 hipError_t launch_score(const ScoreArgs& a, hipStream_t st);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 
 // vector-ALU attention, one query position per workgroup
 int rows_num_splits(const AttendArgs& a);
 hipError_t launch_attend_rows(const AttendArgs& a, int splits, hipStream_t st);
+// merge of split-K partial rows (shared by both attention paths)
+hipError_t launch_combine(const AttendArgs& a, int splits, hipStream_t st);
 
 // bf16 MFMA attention tiles for query chunks (head_dim 128)
 bool prefill_supported(const AttendArgs& a);
 int prefill_num_splits(const AttendArgs& a);
+int64_t prefill_num_counters(const AttendArgs& a);
 hipError_t launch_attend_prefill(const AttendArgs& a, int splits, hipStream_t st);
 
 }  // namespace infllm

@@ -5,9 +5,13 @@
 // sum and the dot products accumulate in fp64, so the ranking that follows
 // is decided on scores accurate far below the near-tie margin.
 //
-// A workgroup handles one (chunk, KV head, sequence) and a slice of up to
-// kUnitsPerWG units: the chunk query sum is formed once in LDS, then each
-// wave scores one unit at a time with a coalesced read of its fp32 row.
+// Long chunks: k_chunk_qsum spreads the query sum over many workgroups
+// (16-byte loads, kQsumRows query rows each) and writes fp64 partial sums;
+// k_score_units adds them in a fixed order, so results do not depend on
+// scheduling.  Short chunks (decode: one query x G heads) skip the first
+// pass and sum their few rows directly.  k_score_units then scores a slice
+// of up to kUnitsPerWG units, one wave per unit at a time with a coalesced
+// read of its fp32 representation.
 #include "common.h"
 #include "kernels.h"
 
@@ -15,21 +19,85 @@ namespace infllm {
 
 constexpr int kScoreThreads = 256;
 constexpr int kUnitsPerWG = 512;
+constexpr int kQsumRows = 32;        // chunk rows per partial sum
+constexpr int kDirectRows = 64;      // L*G up to this: sum in the scoring kernel
+
+template <typename T> struct Load8;
+template <> struct Load8<bf16_t> {
+  static __device__ __forceinline__ void add(const bf16_t* p, double* acc) {
+    const u32x4 w = *(const u32x4*)p;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] += (double)__uint_as_float(w[i] << 16);
+      acc[2 * i + 1] += (double)__uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+template <> struct Load8<float> {
+  static __device__ __forceinline__ void add(const float* p, double* acc) {
+    const float4 a = ((const float4*)p)[0], b = ((const float4*)p)[1];
+    acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+    acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+  }
+};
+
+int score_num_parts(int L, int G) {
+  return L * G <= kDirectRows ? 0 : (L + kQsumRows - 1) / kQsumRows;
+}
+
+// Partial query sums: part p of chunk c covers rows [p*kQsumRows, ...) of
+// the chunk, all G heads.  grid (parts, H_kv, batch * n_chunks).
+template <typename T>
+__global__ __launch_bounds__(kScoreThreads) void k_chunk_qsum(
+    const T* __restrict__ q, int64_t q_cap, int64_t q_off, int L, int Hq, int Hkv, int d,
+    int n_chunks, double* __restrict__ parts) {
+  const int part = blockIdx.x, h = blockIdx.y;
+  const int ch = blockIdx.z % n_chunks, bi = blockIdx.z / n_chunks;
+  const int G = Hq / Hkv;
+  const int cgs = d / 8;                            // 8-column groups per row
+  const int cg = threadIdx.x % cgs, rl = threadIdx.x / cgs, nrl = kScoreThreads / cgs;
+  const int r0 = part * kQsumRows;
+  const int r1 = r0 + kQsumRows < L ? r0 + kQsumRows : L;
+  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int g = 0; g < G; ++g) {
+    const T* qh = q + (((int64_t)bi * Hq + (int64_t)h * G + g) * q_cap + q_off +
+                       (int64_t)ch * L) * d + cg * 8;
+    for (int i = r0 + rl; i < r1; i += nrl) Load8<T>::add(qh + (int64_t)i * d, acc);
+  }
+  __shared__ double sm[kScoreThreads / 8][128];     // [row lane][column]
+#pragma unroll
+  for (int j = 0; j < 8; ++j) sm[rl][cg * 8 + j] = acc[j];
+  __syncthreads();
+  if (threadIdx.x < d) {
+    double s = 0.0;
+    for (int r = 0; r < nrl; ++r) s += sm[r][threadIdx.x];
+    const int n_parts = gridDim.x;
+    parts[((((int64_t)bi * Hkv + h) * n_chunks + ch) * n_parts + part) * d + threadIdx.x] = s;
+  }
+}
 
 template <typename T>
 __global__ __launch_bounds__(kScoreThreads) void k_score_units(
     const T* __restrict__ q, int64_t q_cap, int64_t q_off, int64_t q_pos, int L, int Hq, int Hkv,
     int d, int B, int n_init, int W, const float* __restrict__ repr, int U,
-    float* __restrict__ scores, int n_chunks) {
+    float* __restrict__ scores, int n_chunks, const double* __restrict__ parts, int n_parts) {
   const int slice = blockIdx.x;
   const int ch = blockIdx.y % n_chunks, h = blockIdx.y / n_chunks, bi = blockIdx.z;
   const int G = Hq / Hkv;
   const int tid = threadIdx.x;
-  __shared__ double part[kScoreThreads];
+  __shared__ double part_sm[kScoreThreads];
   __shared__ double qsum[128];
 
-  // chunk query sum, fp64: thread -> (column, row phase)
-  {
+  if (n_parts > 0) {
+    if (tid < d) {
+      const double* pp = parts + (((int64_t)bi * Hkv + h) * n_chunks + ch) * n_parts * d + tid;
+      double s = 0.0;
+      for (int p = 0; p < n_parts; ++p) s += pp[(int64_t)p * d];
+      qsum[tid] = s;
+    }
+    __syncthreads();
+  } else {
+    // few rows: thread -> (column, row phase)
     const int c = tid % d, phase = tid / d, nph = kScoreThreads / d;
     double acc = 0.0;
     const int64_t row0 = q_off + (int64_t)ch * L;
@@ -37,10 +105,10 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_units(
       const T* qh = q + (((int64_t)bi * Hq + (int64_t)h * G + g) * q_cap + row0) * d + c;
       for (int i = phase; i < L; i += nph) acc += (double)to_f32(qh[(int64_t)i * d]);
     }
-    part[tid] = acc;
+    part_sm[tid] = acc;
     __syncthreads();
     if (phase == 0) {
-      for (int p = 1; p < nph; ++p) acc += part[p * d + c];
+      for (int p = 1; p < nph; ++p) acc += part_sm[p * d + c];
       qsum[c] = acc;
     }
     __syncthreads();
@@ -65,18 +133,28 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_units(
   }
 }
 
+size_t score_workspace_bytes(const ScoreArgs& a) {
+  const int parts = score_num_parts(a.L, a.Hq / a.Hkv);
+  return (size_t)parts * a.batch * a.Hkv * a.n_chunks * a.d * sizeof(double);
+}
+
+template <typename T>
+static hipError_t launch_score_t(const ScoreArgs& a, hipStream_t st) {
+  const int parts = score_num_parts(a.L, a.Hq / a.Hkv);
+  double* pw = (double*)a.ws;
+  if (parts > 0)
+    k_chunk_qsum<T><<<dim3(parts, a.Hkv, a.batch * a.n_chunks), kScoreThreads, 0, st>>>(
+        (const T*)a.q, a.q_cap, a.q_off, a.L, a.Hq, a.Hkv, a.d, a.n_chunks, pw);
+  dim3 grid((a.U + kUnitsPerWG - 1) / kUnitsPerWG, a.n_chunks * a.Hkv, a.batch);
+  k_score_units<T><<<grid, kScoreThreads, 0, st>>>(
+      (const T*)a.q, a.q_cap, a.q_off, a.q_pos, a.L, a.Hq, a.Hkv, a.d, a.B, a.n_init, a.W, a.repr,
+      a.U, a.scores, a.n_chunks, pw, parts);
+  return hipGetLastError();
+}
+
 hipError_t launch_score(const ScoreArgs& a, hipStream_t st) {
   if (a.U <= 0 || a.n_chunks <= 0) return hipSuccess;
-  dim3 grid((a.U + kUnitsPerWG - 1) / kUnitsPerWG, a.n_chunks * a.Hkv, a.batch);
-  if (a.bf16)
-    k_score_units<bf16_t><<<grid, kScoreThreads, 0, st>>>(
-        (const bf16_t*)a.q, a.q_cap, a.q_off, a.q_pos, a.L, a.Hq, a.Hkv, a.d, a.B, a.n_init, a.W,
-        a.repr, a.U, a.scores, a.n_chunks);
-  else
-    k_score_units<float><<<grid, kScoreThreads, 0, st>>>(
-        (const float*)a.q, a.q_cap, a.q_off, a.q_pos, a.L, a.Hq, a.Hkv, a.d, a.B, a.n_init, a.W,
-        a.repr, a.U, a.scores, a.n_chunks);
-  return hipGetLastError();
+  return a.bf16 ? launch_score_t<bf16_t>(a, st) : launch_score_t<float>(a, st);
 }
 
 }  // namespace infllm

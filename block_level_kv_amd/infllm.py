@@ -138,11 +138,13 @@ def infllm_workspace_size(cfg: infllm_config, call: int, batch: int, n: int = 0,
 
 def workspace(cfg: infllm_config, call: int, batch: int, n: int = 0, chunk_len: int = 0,
               n_chunks: int = 0, device="cuda") -> torch.Tensor | None:
-    """A caller-owned workspace tensor of the size `call` needs (None if 0)."""
+    """A caller-owned, zero-filled workspace tensor of the size `call` needs
+    (None if 0).  Zero-filled because the attention workspace carries
+    split-K counters that must start at zero (and stay zero between calls)."""
     size = infllm_workspace_size(cfg, call, batch, n, chunk_len, n_chunks)
     if size == 0:
         return None
-    return torch.empty(size, dtype=torch.uint8, device=device)
+    return torch.zeros(size, dtype=torch.uint8, device=device)
 
 
 def infllm_build_units(cfg, q, k, n_ctx: int, rep_idx, unit_repr, ws=None, stream=None) -> None:

@@ -161,6 +161,8 @@ INFLLM_API infllm_status infllm_build_units(const infllm_config *cfg, int32_t ba
  *   q_pos      absolute position of row q_off
  *   unit_repr  [batch, H_kv, n_units, d] fp32 (from infllm_build_units)
  *   scores     out [batch, H_kv, n_chunks, n_units] fp32
+ *   workspace  >= infllm_workspace_size(cfg, INFLLM_CALL_SCORE, batch, 0,
+ *              chunk_len, n_chunks) (fp64 partial query sums; 0 for short chunks)
  */
 INFLLM_API infllm_status infllm_score_units(const infllm_config *cfg, int32_t batch, const void *q,
                                  int64_t q_cap, int64_t q_off, int64_t q_pos, int32_t chunk_len,
@@ -206,6 +208,10 @@ INFLLM_API infllm_status infllm_topk_units(const infllm_config *cfg, int32_t bat
  *            n_chunks*chunk_len - 1, cfg->dtype
  *   lse      optional out [batch, H_q, out_cap] fp32 natural-log
  *            sum-exp of the scaled logits, same rows; may be NULL
+ *   workspace >= infllm_workspace_size(cfg, INFLLM_CALL_ATTEND, batch, 0,
+ *            chunk_len, n_chunks).  It must be zero-filled before its first
+ *            use: it holds split-K arrival counters, which every call leaves
+ *            at zero again.  Calls that share a workspace must not overlap.
  */
 INFLLM_API infllm_status infllm_attend(const infllm_config *cfg, int32_t batch, const void *q, int64_t q_cap,
                             int64_t q_off, int64_t q_pos, int32_t chunk_len, int32_t n_chunks,

@@ -55,7 +55,8 @@ def gpu_score(cfg, q, q_off, q_pos, L, n_chunks, repr_):
     b = q.shape[0]
     scores = torch.empty((b, cfg.n_kv_heads, n_chunks, repr_.shape[2]), dtype=torch.float32,
                          device=q.device)
-    F.infllm_score_units(cfg, q, q_off, q_pos, L, n_chunks, repr_, scores)
+    ws = F.workspace(cfg, F.INFLLM_CALL_SCORE, b, 0, L, n_chunks, device=q.device)
+    F.infllm_score_units(cfg, q, q_off, q_pos, L, n_chunks, repr_, scores, ws)
     return scores
 
 

@@ -268,3 +268,73 @@ def test_tiny_workload_pipeline(orc):
         assert_close(out, o_ref, 1e-4, "tiny chunk %d" % c)
         assert_close(lse, l_ref, 1e-4, "tiny lse chunk %d" % c)
     assert n_elig == 10 and hits_g == hits_o
+
+
+PREFILL_VARIANTS = [
+    # (G, n_init, W, chunk, n_ctx, top_k)
+    (1, 128, 512, 256, 2048, 4),
+    (2, 100, 200, 100, 1900, 3),
+    (8, 0, 64, 512, 2560, 6),
+    (4, 200, 300, 16, 1600, 2),
+    (4, 64, 4096, 512, 3072, 8),       # window longer than the context: dense
+]
+
+
+@pytest.mark.parametrize("G,n_init,W,chunk,n_ctx,top_k", PREFILL_VARIANTS)
+@pytest.mark.parametrize("splits", ["auto", "1", "3"])
+def test_prefill_mfma_variants(orc, monkeypatch, G, n_init, W, chunk, n_ctx, top_k, splits):
+    if splits != "auto":
+        monkeypatch.setenv("INFLLM_PREFILL_SPLITS", splits)
+    w = LL.replace(n_ctx=n_ctx, n_q_heads=2 * G, n_kv_heads=2, window=W, n_init=n_init,
+                   top_k=top_k, chunk=chunk, seed=G * 1000 + n_init)
+    cfg = cfg_of(w)
+    inp = synth.make_inputs(w)
+    dev = {k: v.cuda() for k, v in inp.items() if isinstance(v, torch.Tensor)}
+    _, repr_o, _ = oracle_build(orc, w, inp)
+    n_chunks = n_ctx // chunk
+    sels = np.stack([_oracle_selection(orc, w, inp, c * chunk, chunk, repr_o)
+                     for c in range(n_chunks)], axis=2)
+    out, lse = gpu_attend(cfg, dev["q"], 0, 0, chunk, n_chunks, dev["k"], dev["v"],
+                          torch.from_numpy(sels).cuda())
+    torch.cuda.synchronize()
+    for c in sorted({0, 1, n_chunks // 2, n_chunks - 1}):
+        t0 = c * chunk
+        o_ref, l_ref = orc.attend_all(inp["q"][:, :, t0:t0 + chunk], t0, inp["k"], inp["v"],
+                                      sels[:, :, c], B=w.block, n_init=n_init, W=W)
+        assert_close(out[:, :, t0:t0 + chunk], o_ref, tolerance(torch.bfloat16, o_ref),
+                     "G%d chunk %d out" % (G, c))
+        assert_close(lse[:, :, t0:t0 + chunk], l_ref, 1e-3, "G%d chunk %d lse" % (G, c))
+
+
+def test_prefill_deterministic_and_sequential_equals_batched(orc):
+    """Two runs are bitwise equal, and one chunk per call equals all chunks
+    in one call (same kernels, same reduction order)."""
+    w = CASES["bf16_g4"]
+    cfg = cfg_of(w)
+    inp = synth.make_inputs(w)
+    dev = {k: v.cuda() for k, v in inp.items() if isinstance(v, torch.Tensor)}
+    _, repr_g = gpu_build(cfg, dev["q"], dev["k"], w.n_ctx)
+    n_chunks = w.n_ctx // w.chunk
+    scores = gpu_score(cfg, dev["q"], 0, 0, w.chunk, n_chunks, repr_g)
+    sel = gpu_topk(cfg, scores)
+    o1, l1 = gpu_attend(cfg, dev["q"], 0, 0, w.chunk, n_chunks, dev["k"], dev["v"], sel)
+    o2, l2 = gpu_attend(cfg, dev["q"], 0, 0, w.chunk, n_chunks, dev["k"], dev["v"], sel)
+    torch.cuda.synchronize()
+    diff = (o1.float() - o2.float()).abs().max().item()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2), diff
+    # split-K counters are back at zero after a call on a shared workspace
+    ws = F.workspace(cfg, F.INFLLM_CALL_ATTEND, w.batch, 0, w.chunk, n_chunks)
+    out = torch.empty_like(o1)
+    for _ in range(3):
+        F.infllm_attend(cfg, dev["q"], 0, 0, w.chunk, n_chunks, dev["k"], dev["v"], sel, out,
+                        None, 0, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, o1)
+    if ws is not None:
+        n_counters = -(-w.chunk // (128 // w.group)) * n_chunks * w.n_kv_heads * w.batch
+        assert int(ws[:4 * n_counters].view(torch.int32).abs().sum()) == 0
+    c = n_chunks - 2
+    oc, lc = gpu_attend(cfg, dev["q"], c * w.chunk, c * w.chunk, w.chunk, 1, dev["k"], dev["v"],
+                        sel[:, :, c:c + 1].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(oc, o1[:, :, c * w.chunk:(c + 1) * w.chunk])
