@@ -7,17 +7,20 @@ Default workload: a Llama-3-8B-shaped layer (32 query / 8 KV heads, head_dim
 processed one after another: one step = build the unit pool over the context
 (representative tokens, r_k = 4), then for each chunk score every unit,
 keep the top 16 per KV head and attend over 128 initial tokens + 16 units +
-a 4,096-token window.  Decode workloads (--workload llama3_8b_128k_decode,
-llama3_8b_1m_decode, mistral_7b_64k_*): the unit pool is built once
-beforehand; one step = 256 consecutive single-token decode steps.
+a 4,096-token window.  Other workloads (--workload): the 128K and 1M decode
+layers (unit pool built once beforehand; one step = 256 consecutive
+single-token decode steps) and the Mistral-7B 64K layer (one step = build +
+128 encoding chunks + 256 decode steps).
 
 Prints ONE JSON line.  `value` is attended KV tokens per second over the
-whole step (sum over sequences and query positions of the number of keys
-each query attends).  `roofline` is for the attention kernel: algorithmic
-work per launch (MFMA flops 4*d*H_q*sum|A(t)| for chunks; K/V + query +
-output bytes for decode) divided by its average launch time, measured with
-HIP events on the launch stream inside the timed region.  `cpu_baseline` is
-the fp64 oracle on a bounded sample of the same work on the host cores.
+whole step (over sequences and query positions, the number of keys each
+query attends, averaged over KV heads).  `roofline` is for the attention
+kernel of the dominant pass (chunked encoding if the workload has one):
+algorithmic work per launch -- MFMA flops 4*d*H_q*sum|A(t)| for chunks, or
+the K/V rows, queries and outputs it must move for decode -- divided by its
+average launch time, measured with HIP events on the launch stream inside
+the timed region.  `cpu_baseline` is the fp64 oracle on a bounded sample of
+the same work on the host cores.
 """
 from __future__ import annotations
 
@@ -71,7 +74,10 @@ def attended_counts(w: synth.Workload, t0: int, L: int, sel: np.ndarray) -> np.n
 
 
 class Pipeline:
-    """Buffers and call sequence of one workload on the GPU."""
+    """Buffers and call sequence of one workload on the GPU.  The encoding
+    pass (if w.chunk > 0) builds the unit pool and runs every chunk; the
+    decode pass (if w.decode_steps > 0) runs single-token steps against the
+    pool.  Selections and outputs of the last step are kept for checking."""
 
     def __init__(self, w: synth.Workload, dev: str = "cuda"):
         self.w, self.cfg, self.dev = w, cfg_of(w), dev
@@ -80,71 +86,93 @@ class Pipeline:
         torch.cuda.synchronize()
         self.gen_s = time.time() - t
         b, Hkv, d = w.batch, w.n_kv_heads, w.head_dim
-        self.U = F.infllm_num_units(self.cfg, w.n_ctx)
+        cfg = self.cfg
+        self.encode = w.chunk > 0
+        self.decode = w.decode_steps > 0
+        self.U = F.infllm_num_units(cfg, w.n_ctx)
         self.repr = torch.empty((b, Hkv, self.U, d), dtype=torch.float32, device=dev)
         self.rep_idx = (torch.empty((b, Hkv, self.U, w.rep_k), dtype=torch.int32, device=dev)
                         if w.rep_mode == "tokens" else None)
-        self.build_ws = F.workspace(self.cfg, F.INFLLM_CALL_BUILD, b, w.n_ctx, device=dev)
+        self.build_ws = F.workspace(cfg, F.INFLLM_CALL_BUILD, b, w.n_ctx, device=dev)
         self.scores = torch.empty((b, Hkv, 1, self.U), dtype=torch.float32, device=dev)
-        L = w.chunk if (w.chunk > 0 and w.decode_steps == 0) else 1
-        self.score_ws = F.workspace(self.cfg, F.INFLLM_CALL_SCORE, b, 0, L, 1, device=dev)
-        self.sel = torch.empty((b, Hkv, 1, w.top_k), dtype=torch.int32, device=dev)
-        self.encode = w.chunk > 0 and w.decode_steps == 0
         if self.encode:
             self.n_chunks = w.n_ctx // w.chunk
-            self.out = torch.empty_like(self.inp["q"])
-            self.attn_ws = F.workspace(self.cfg, F.INFLLM_CALL_ATTEND, b, 0, w.chunk, 1, device=dev)
-            self.sel_log = torch.empty((self.n_chunks, b, Hkv, w.top_k), dtype=torch.int32,
+            self.enc_score_ws = F.workspace(cfg, F.INFLLM_CALL_SCORE, b, 0, w.chunk, 1, device=dev)
+            self.enc_attn_ws = F.workspace(cfg, F.INFLLM_CALL_ATTEND, b, 0, w.chunk, 1, device=dev)
+            self.sel_enc = torch.empty((self.n_chunks, b, Hkv, 1, w.top_k), dtype=torch.int32,
                                        device=dev)
-        else:
-            self.out = torch.empty_like(self.inp["q_dec"])
-            self.attn_ws = F.workspace(self.cfg, F.INFLLM_CALL_ATTEND, b, 0, 1, 1, device=dev)
-            self.sel_log = torch.empty((w.decode_steps, b, Hkv, w.top_k), dtype=torch.int32,
+            self.out_enc = torch.empty_like(self.inp["q"])
+        if self.decode:
+            self.dec_score_ws = F.workspace(cfg, F.INFLLM_CALL_SCORE, b, 0, 1, 1, device=dev)
+            self.dec_attn_ws = F.workspace(cfg, F.INFLLM_CALL_ATTEND, b, 0, 1, 1, device=dev)
+            self.sel_dec = torch.empty((w.decode_steps, b, Hkv, 1, w.top_k), dtype=torch.int32,
                                        device=dev)
+            self.out_dec = torch.empty_like(self.inp["q_dec"])
 
     def build(self):
-        w = self.w
-        F.infllm_build_units(self.cfg, self.inp["q"], self.inp["k"], w.n_ctx, self.rep_idx,
+        F.infllm_build_units(self.cfg, self.inp["q"], self.inp["k"], self.w.n_ctx, self.rep_idx,
                              self.repr, self.build_ws)
 
-    def step(self, events=None):
-        """One pass of the hot path; `events` collects (start, end) pairs
-        around each attention call."""
-        w, cfg, inp = self.w, self.cfg, self.inp
+    def _select_attend(self, q, q_off, pos, L, sel, out, score_ws, attn_ws, events):
+        cfg, inp = self.cfg, self.inp
+        F.infllm_score_units(cfg, q, q_off, pos, L, 1, self.repr, self.scores, score_ws)
+        F.infllm_topk_units(cfg, self.scores, sel)
+        if events is not None:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+        F.infllm_attend(cfg, q, q_off, pos, L, 1, inp["k"], inp["v"], sel, out, None, q_off,
+                        attn_ws)
+        if events is not None:
+            e1.record()
+            events.append((e0, e1))
+
+    def step(self, enc_events=None, dec_events=None, pass_events=None):
+        """One pass of the hot path; the event lists collect (start, end)
+        pairs around each attention call of each pass; pass_events gets one
+        event recorded between the encoding and the decode pass."""
+        w = self.w
         if self.encode:
             self.build()
-            q, L, items = inp["q"], w.chunk, [(c, c * w.chunk, c * w.chunk)
-                                               for c in range(self.n_chunks)]
-        else:
-            q, L, items = inp["q_dec"], 1, [(s, s, w.n_ctx + s) for s in range(w.decode_steps)]
-        for i, q_off, pos in items:
-            F.infllm_score_units(cfg, q, q_off, pos, L, 1, self.repr, self.scores, self.score_ws)
-            sel = self.sel_log[i].unsqueeze(2)
-            F.infllm_topk_units(cfg, self.scores, sel)
-            if events is not None:
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-            F.infllm_attend(cfg, q, q_off, pos, L, 1, inp["k"], inp["v"], sel, self.out, None,
-                            q_off, self.attn_ws)
-            if events is not None:
-                e1.record()
-                events.append((e0, e1))
+            for c in range(self.n_chunks):
+                t0 = c * w.chunk
+                self._select_attend(self.inp["q"], t0, t0, w.chunk, self.sel_enc[c], self.out_enc,
+                                    self.enc_score_ws, self.enc_attn_ws, enc_events)
+        if pass_events is not None:
+            e = torch.cuda.Event(enable_timing=True)
+            e.record()
+            pass_events.append(e)
+        if self.decode:
+            for s in range(w.decode_steps):
+                self._select_attend(self.inp["q_dec"], s, w.n_ctx + s, 1, self.sel_dec[s],
+                                    self.out_dec, self.dec_score_ws, self.dec_attn_ws, dec_events)
+        if pass_events is not None:
+            e = torch.cuda.Event(enable_timing=True)
+            e.record()
+            pass_events.append(e)
 
     def work(self):
-        """(attended KV tokens, attention flops, attention bytes) of one step."""
+        """Per pass: (attended KV tokens, attention flops, attention bytes)."""
         w = self.w
-        sel = self.sel_log.cpu().numpy()
-        tokens = flops = 0
-        nbytes = 0
         esz = 2 if w.dtype == "bf16" else 4
-        for i in range(sel.shape[0]):
-            t0, L = (i * w.chunk, w.chunk) if self.encode else (w.n_ctx + i, 1)
-            cnt = attended_counts(w, t0, L, sel[i])                 # [b, H_kv, L]
-            tokens += int(cnt.sum()) // w.n_kv_heads                # mean over KV heads
-            flops += 4 * w.head_dim * w.group * int(cnt.sum())
-            nbytes += int(cnt.sum()) * 2 * w.head_dim * esz         # K and V rows read
-            nbytes += 2 * w.batch * w.n_q_heads * L * w.head_dim * esz  # q in, out
-        return tokens, flops, nbytes
+        res = {}
+        passes = []
+        if self.encode:
+            passes.append(("encode", self.sel_enc, [(c * w.chunk, w.chunk)
+                                                    for c in range(self.n_chunks)]))
+        if self.decode:
+            passes.append(("decode", self.sel_dec, [(w.n_ctx + s, 1)
+                                                    for s in range(w.decode_steps)]))
+        for name, sel_log, items in passes:
+            sel = sel_log.cpu().numpy()[:, :, :, 0]
+            tokens = flops = nbytes = 0
+            for i, (t0, L) in enumerate(items):
+                cnt = attended_counts(w, t0, L, sel[i])             # [b, H_kv, L]
+                tokens += int(cnt.sum()) // w.n_kv_heads             # mean over KV heads
+                flops += 4 * w.head_dim * w.group * int(cnt.sum())
+                nbytes += int(cnt.sum()) * 2 * w.head_dim * esz      # K and V rows read
+                nbytes += 2 * w.batch * w.n_q_heads * L * w.head_dim * esz  # q in, out
+            res[name] = (tokens, flops, nbytes)
+        return res
 
 
 def cpu_baseline(w: synth.Workload, pipe: Pipeline) -> dict:
@@ -152,42 +180,68 @@ def cpu_baseline(w: synth.Workload, pipe: Pipeline) -> dict:
     top-k and attention plus that chunk's share of the unit build; for
     decode, two decode steps.  Value in attended KV tokens per second."""
     from oracle import oracle as orc
-    inp = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in pipe.inp.items()}
     B, n_init, W = w.block, w.n_init, w.window
     G = w.group
+    repr_ = pipe.repr.cpu().double().numpy()
+    k0, v0 = pipe.inp["k"][:1].cpu(), pipe.inp["v"][:1].cpu()
     t_start = time.time()
     tokens = 0
     if pipe.encode:
+        q0 = pipe.inp["q"][:1].cpu()
         n_chunks = w.n_ctx // w.chunk
         U = orc.num_units(w.n_ctx, B, n_init)
         share = max(1, math.ceil(U / n_chunks))          # units per chunk of the build
         for h in range(w.n_kv_heads):
             if w.rep_mode == "mean":
-                orc.build_mean(inp["k"][0, h], B, n_init, 0, share)
+                orc.build_mean(k0[0, h], B, n_init, 0, share)
             else:
-                orc.build_tokens(inp["q"][0, h * G:(h + 1) * G], inp["k"][0, h], w.n_ctx, B,
-                                 n_init, W, w.rep_k, 0, share)
-        repr_ = pipe.repr.cpu().double().numpy()
+                orc.build_tokens(q0[0, h * G:(h + 1) * G], k0[0, h], w.n_ctx, B, n_init, W,
+                                 w.rep_k, 0, share)
         t0 = w.n_ctx - w.chunk
-        qc = inp["q"][:1, :, t0:]
+        qc = q0[:, :, t0:]
         _, sel, _ = orc.select_all(qc, t0, repr_[:1], B=B, n_init=n_init, W=W, k_m=w.top_k)
-        orc.attend_all(qc, t0, inp["k"][:1], inp["v"][:1], sel, B=B, n_init=n_init, W=W)
-        tokens = int(attended_counts(w, t0, w.chunk, sel)[0, 0].sum())
-        sample = ("1 of %d chunks (512 queries x %d heads, sequence 0) plus that chunk's share "
-                  "(%d units x %d KV heads) of the unit build" % (n_chunks, w.n_q_heads, share,
-                                                                   w.n_kv_heads))
+        orc.attend_all(qc, t0, k0, v0, sel, B=B, n_init=n_init, W=W)
+        tokens = int(attended_counts(w, t0, w.chunk, sel).sum()) // w.n_kv_heads
+        sample = ("1 of %d chunks (%d queries x %d heads, sequence 0) plus that chunk's share "
+                  "(%d units x %d KV heads) of the unit build" % (n_chunks, w.chunk, w.n_q_heads,
+                                                                   share, w.n_kv_heads))
     else:
-        repr_ = pipe.repr.cpu().double().numpy()
+        qd0 = pipe.inp["q_dec"][:1].cpu()
         for s in range(2):
             t = w.n_ctx + s
-            qd = inp["q_dec"][:1, :, s:s + 1]
+            qd = qd0[:, :, s:s + 1]
             _, sel, _ = orc.select_all(qd, t, repr_[:1], B=B, n_init=n_init, W=W, k_m=w.top_k)
-            orc.attend_all(qd, t, inp["k"][:1], inp["v"][:1], sel, B=B, n_init=n_init, W=W)
-            tokens += int(attended_counts(w, t, 1, sel)[0, 0].sum())
+            orc.attend_all(qd, t, k0, v0, sel, B=B, n_init=n_init, W=W)
+            tokens += int(attended_counts(w, t, 1, sel).sum()) // w.n_kv_heads
         sample = "2 of %d decode steps, sequence 0 of %d" % (w.decode_steps, w.batch)
     dt = time.time() - t_start
-    return {"value": tokens / dt, "unit": "attended KV tokens/s", "cores": orc.num_threads(),
-            "kind": "oracle", "sample": sample, "seconds": round(dt, 2)}
+    return {"value": round(tokens / dt, 1), "unit": "attended KV tokens/s",
+            "cores": orc.num_threads(), "kind": "oracle", "sample": sample,
+            "seconds": round(dt, 2)}
+
+
+def roofline(w: synth.Workload, phase: str, work, events, steps: int) -> dict:
+    tokens, flops, nbytes = work
+    n_calls = len(events) // steps
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in events]))
+    if phase == "encode" and w.dtype == "bf16":
+        achieved = flops / n_calls / (attn_ms * 1e-3) / 1e12
+        r = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+             "unit": "TFLOP/s"}
+    elif phase == "encode":
+        achieved = flops / n_calls / (attn_ms * 1e-3) / 1e12
+        r = {"bound": "alu", "achieved": round(achieved, 2), "peak": PEAK_F32_TFLOPS,
+             "unit": "TFLOP/s"}
+    else:
+        achieved = nbytes / n_calls / (attn_ms * 1e-3) / 1e9
+        r = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    r["frac"] = round(achieved / r["peak"], 4)
+    r["traffic"] = None
+    r["kernel"] = "infllm_attend (%s)" % ("k_attend_prefill" if phase == "encode" and
+                                          w.dtype == "bf16" else "k_attend_rows")
+    r["avg_launch_us"] = round(attn_ms * 1e3, 2)
+    r["launches_per_step"] = n_calls
+    return r
 
 
 def main():
@@ -207,39 +261,27 @@ def main():
     w = synth.WORKLOADS[args.workload]
     pipe = Pipeline(w)
     if not pipe.encode:
-        pipe.build()
+        pipe.build()            # decode-only: the pool is built once, beforehand
     for _ in range(args.warmup):
         pipe.step()
     torch.cuda.synchronize()
 
-    events = []
+    enc_ev, dec_ev, pass_ev = [], [], []
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for _ in range(args.steps):
-        pipe.step(events)
+        pipe.step(enc_ev, dec_ev, pass_ev)
     end.record()
     torch.cuda.synchronize()
-    ms_total = start.elapsed_time(end)
-    ms_step = ms_total / args.steps
-    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in events]))
+    ms_step = start.elapsed_time(end) / args.steps
+    # decode-pass time per step: between the two pass-boundary events of a step
+    ms_decode = float(np.mean([pass_ev[2 * i].elapsed_time(pass_ev[2 * i + 1])
+                               for i in range(args.steps)]))
 
-    tokens, flops, nbytes = pipe.work()
-    n_calls = len(events) // args.steps
-    if pipe.encode:
-        achieved = flops / n_calls / (attn_ms * 1e-3) / 1e12
-        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-        roof = {"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": round(achieved, 2),
-                "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                "traffic": None}
-    else:
-        achieved = nbytes / n_calls / (attn_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
-    roof["kernel"] = "infllm_attend"
-    roof["avg_launch_us"] = round(attn_ms * 1e3, 2)
-    roof["launches_per_step"] = n_calls
-
+    work = pipe.work()
+    tokens = sum(v[0] for v in work.values())
+    phase = "encode" if pipe.encode else "decode"
     line = {
         "metric": "attended KV tokens/s (InfLLM attention step, Llama-3-8B layer)",
         "value": round(tokens / (ms_step * 1e-3), 1),
@@ -254,10 +296,17 @@ def main():
                    "chunk": w.chunk, "decode_steps": w.decode_steps, "block": w.block,
                    "n_init": w.n_init, "window": w.window, "rep_k": w.rep_k, "top_k": w.top_k,
                    "rep_mode": w.rep_mode, "attended_tokens_per_step": tokens},
-        "roofline": roof,
+        "roofline": roofline(w, phase, work[phase], enc_ev if phase == "encode" else dec_ev,
+                             args.steps),
     }
-    if not pipe.encode:
-        line["ms_per_decode_step"] = round(ms_step / w.decode_steps, 5)
+    if pipe.decode:
+        # one decode step = score + top-k + attention for one token position
+        line["ms_per_decode_step"] = round((ms_decode if pipe.encode else ms_step) /
+                                           w.decode_steps, 5)
+        line["decode_tokens_per_s"] = round(work["decode"][0] / (
+            (ms_decode if pipe.encode else ms_step) * 1e-3), 1)
+        if pipe.encode:
+            line["decode_roofline"] = roofline(w, "decode", work["decode"], dec_ev, args.steps)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, pipe)
     print(json.dumps(line), flush=True)

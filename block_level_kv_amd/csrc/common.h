@@ -54,6 +54,12 @@ template <int CTRL> __device__ __forceinline__ float dpp_f32(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 
+template <int CTRL> __device__ __forceinline__ double dpp_f64(double x) {
+  const int lo = __builtin_amdgcn_mov_dpp(__double2loint(x), CTRL, 0xF, 0xF, true);
+  const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(x), CTRL, 0xF, 0xF, true);
+  return __hiloint2double(hi, lo);
+}
+
 // Sum over the 16 lanes of a DPP row; every lane of the row gets the sum.
 __device__ __forceinline__ float row16_sum(float x) {
   x += dpp_f32<INFLLM_DPP_XOR1>(x);

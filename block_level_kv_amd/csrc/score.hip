@@ -121,15 +121,32 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_units(
   const int u1 = u0 + kUnitsPerWG < U ? u0 + kUnitsPerWG : U;
   const float* rb = repr + ((int64_t)bi * Hkv + h) * U * d;
   float* sb = scores + (((int64_t)bi * Hkv + h) * n_chunks + ch) * U;
-  for (int u = u0 + wave; u < u1; u += kScoreThreads / 64) {
-    if (u >= e) {
-      if (lane == 0) sb[u] = -INFINITY;
-      continue;
-    }
+  // d/8 lanes per unit (a DPP row or half row), 8 columns each
+  const int lpu = d / 8, upw = 64 / lpu;
+  const int sub = lane / lpu, cg = lane % lpu;
+  double qv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) qv[j] = qsum[cg * 8 + j];
+  for (int ub = u0 + wave * upw; ub < u1; ub += (kScoreThreads / 64) * upw) {
+    const int u = ub + sub;
     double s = 0.0;
-    for (int c = lane; c < d; c += 64) s += (double)rb[(int64_t)u * d + c] * qsum[c];
-    s = wave_sum_f64(s);
-    if (lane == 0) sb[u] = (float)s;
+    if (u < u1 && u < e) {
+      const float4* rp = (const float4*)(rb + (int64_t)u * d + cg * 8);
+      const float4 x = rp[0], y = rp[1];
+      s = fma((double)x.x, qv[0], s);
+      s = fma((double)x.y, qv[1], s);
+      s = fma((double)x.z, qv[2], s);
+      s = fma((double)x.w, qv[3], s);
+      s = fma((double)y.x, qv[4], s);
+      s = fma((double)y.y, qv[5], s);
+      s = fma((double)y.z, qv[6], s);
+      s = fma((double)y.w, qv[7], s);
+    }
+    s += dpp_f64<INFLLM_DPP_XOR1>(s);
+    s += dpp_f64<INFLLM_DPP_XOR2>(s);
+    s += dpp_f64<INFLLM_DPP_HALF_MIRROR>(s);
+    if (lpu == 16) s += dpp_f64<INFLLM_DPP_MIRROR>(s);
+    if (u < u1 && cg == 0) sb[u] = u < e ? (float)s : -INFINITY;
   }
 }
 
