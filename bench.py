@@ -175,10 +175,15 @@ class Pipeline:
         return res
 
 
+CPU_SAMPLE_SECONDS = 10.0
+
+
 def cpu_baseline(w: synth.Workload, pipe: Pipeline) -> dict:
-    """The oracle on a bounded sample: for chunked encoding, one chunk's score,
-    top-k and attention plus that chunk's share of the unit build; for
-    decode, two decode steps.  Value in attended KV tokens per second."""
+    """The oracle on a bounded sample of the same work, about
+    CPU_SAMPLE_SECONDS long: for chunked encoding, whole chunks (score, top-k,
+    attention, sequence 0) from the last backwards, each with its share of
+    the unit build; for decode, consecutive decode steps of sequence 0.
+    Value in attended KV tokens per second."""
     from oracle import oracle as orc
     B, n_init, W = w.block, w.n_init, w.window
     G = w.group
@@ -191,33 +196,64 @@ def cpu_baseline(w: synth.Workload, pipe: Pipeline) -> dict:
         n_chunks = w.n_ctx // w.chunk
         U = orc.num_units(w.n_ctx, B, n_init)
         share = max(1, math.ceil(U / n_chunks))          # units per chunk of the build
-        for h in range(w.n_kv_heads):
-            if w.rep_mode == "mean":
-                orc.build_mean(k0[0, h], B, n_init, 0, share)
-            else:
-                orc.build_tokens(q0[0, h * G:(h + 1) * G], k0[0, h], w.n_ctx, B, n_init, W,
-                                 w.rep_k, 0, share)
-        t0 = w.n_ctx - w.chunk
-        qc = q0[:, :, t0:]
-        _, sel, _ = orc.select_all(qc, t0, repr_[:1], B=B, n_init=n_init, W=W, k_m=w.top_k)
-        orc.attend_all(qc, t0, k0, v0, sel, B=B, n_init=n_init, W=W)
-        tokens = int(attended_counts(w, t0, w.chunk, sel).sum()) // w.n_kv_heads
-        sample = ("1 of %d chunks (%d queries x %d heads, sequence 0) plus that chunk's share "
-                  "(%d units x %d KV heads) of the unit build" % (n_chunks, w.chunk, w.n_q_heads,
-                                                                   share, w.n_kv_heads))
+        done = 0
+        while done < n_chunks and time.time() - t_start < CPU_SAMPLE_SECONDS:
+            u0 = min(done * share, max(U - share, 0))
+            for h in range(w.n_kv_heads):
+                if w.rep_mode == "mean":
+                    orc.build_mean(k0[0, h], B, n_init, u0, min(u0 + share, U))
+                else:
+                    orc.build_tokens(q0[0, h * G:(h + 1) * G], k0[0, h], w.n_ctx, B, n_init, W,
+                                     w.rep_k, u0, min(u0 + share, U))
+            t0 = w.n_ctx - (done + 1) * w.chunk
+            qc = q0[:, :, t0:t0 + w.chunk]
+            _, sel, _ = orc.select_all(qc, t0, repr_[:1], B=B, n_init=n_init, W=W, k_m=w.top_k)
+            orc.attend_all(qc, t0, k0, v0, sel, B=B, n_init=n_init, W=W)
+            tokens += int(attended_counts(w, t0, w.chunk, sel).sum()) // w.n_kv_heads
+            done += 1
+        sample = ("%d of %d chunks (%d queries x %d heads each, sequence 0), each with its share "
+                  "(%d units x %d KV heads) of the unit build" % (done, n_chunks, w.chunk,
+                                                                   w.n_q_heads, share,
+                                                                   w.n_kv_heads))
     else:
         qd0 = pipe.inp["q_dec"][:1].cpu()
-        for s in range(2):
+        done = 0
+        while done < w.decode_steps and time.time() - t_start < CPU_SAMPLE_SECONDS:
+            s = done
             t = w.n_ctx + s
             qd = qd0[:, :, s:s + 1]
             _, sel, _ = orc.select_all(qd, t, repr_[:1], B=B, n_init=n_init, W=W, k_m=w.top_k)
             orc.attend_all(qd, t, k0, v0, sel, B=B, n_init=n_init, W=W)
             tokens += int(attended_counts(w, t, 1, sel).sum()) // w.n_kv_heads
-        sample = "2 of %d decode steps, sequence 0 of %d" % (w.decode_steps, w.batch)
+            done += 1
+        sample = "%d of %d decode steps (score, top-k, attention), sequence 0 of %d" % (
+            done, w.decode_steps, w.batch)
     dt = time.time() - t_start
     return {"value": round(tokens / dt, 1), "unit": "attended KV tokens/s",
             "cores": orc.num_threads(), "kind": "oracle", "sample": sample,
             "seconds": round(dt, 2)}
+
+
+def stored_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (profiles/<kernel>_<workload>.md), or None if there is none or the
+    kernel's source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "%s_%s.md" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if line.startswith("- ") and ":" in line:
+            key, val = line[2:].split(":", 1)
+            fields[key.strip()] = val.strip()
+    try:
+        src = os.path.join(ROOT, fields["kernel_source"])
+        if hashlib.sha256(open(src, "rb").read()).hexdigest() != fields["kernel_source_sha256"]:
+            return None
+        return int(fields["hbm_bytes_per_launch"])
+    except (KeyError, OSError, ValueError):
+        return None
 
 
 def roofline(w: synth.Workload, phase: str, work, events, steps: int) -> dict:
@@ -236,9 +272,9 @@ def roofline(w: synth.Workload, phase: str, work, events, steps: int) -> dict:
         achieved = nbytes / n_calls / (attn_ms * 1e-3) / 1e9
         r = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     r["frac"] = round(achieved / r["peak"], 4)
-    r["traffic"] = None
-    r["kernel"] = "infllm_attend (%s)" % ("k_attend_prefill" if phase == "encode" and
-                                          w.dtype == "bf16" else "k_attend_rows")
+    kernel = "k_attend_prefill" if phase == "encode" and w.dtype == "bf16" else "k_attend_rows"
+    r["traffic"] = stored_traffic(kernel, w.name)
+    r["kernel"] = "infllm_attend (%s)" % kernel
     r["avg_launch_us"] = round(attn_ms * 1e3, 2)
     r["launches_per_step"] = n_calls
     return r
@@ -251,6 +287,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="llama3_8b_32k_encode", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
+                    help="after timing, run one plain device copy of MIB MiB (untimed), the "
+                         "reference kernel for scaling HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the path runs on a single MI355X with the whole unit "
@@ -307,6 +346,14 @@ def main():
             (ms_decode if pipe.encode else ms_step) * 1e-3), 1)
         if pipe.encode:
             line["decode_roofline"] = roofline(w, "decode", work["decode"], dec_ev, args.steps)
+    if args.calibration_copy > 0:
+        n = args.calibration_copy << 20
+        src = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)                       # reads n bytes, writes n bytes
+        torch.cuda.synchronize()
+        line["calibration_copy_bytes"] = n
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, pipe)
     print(json.dumps(line), flush=True)
