@@ -10,11 +10,15 @@
 //     [first_key(u), min(end(u), t-W+1))        each selected unit u
 //     [max(n_init, t-W+1), t+1)                 local window (t included)
 // so no per-key mask is needed.  The intervals' keys are numbered 0..n-1 and
-// split evenly over gridDim.x workgroups (split-K); each writes a partial
-// (max, sum, unnormalised output) that k_combine merges.  Within a workgroup
-// 16 lanes share a key (each holds D/16 columns: one coalesced 16-byte load
-// per lane for bf16, D = 128) and the 16 key lanes run independent online
-// softmaxes that are merged through LDS at the end.
+// split evenly over gridDim.x workgroups (split-K).  Within a workgroup 16
+// lanes share a key (each holds D/16 columns: one coalesced 16-byte load per
+// lane for bf16, D = 128); the 16 key lanes run independent online softmaxes
+// merged through LDS, and the next group of keys is loaded while the current
+// one is reduced.  Splits publish partial (max, sum, unnormalised output)
+// rows; the last one to arrive merges them in split order (see common.h for
+// the publication protocol), so one launch produces the output.
+#include <stdlib.h>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -25,10 +29,11 @@ constexpr int kMaxIntervals = kMaxTopK + 2;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-template <typename T, int CPT> struct RowLoad;
-template <> struct RowLoad<bf16_t, 8> {
-  static __device__ __forceinline__ void load(const bf16_t* p, float* o) {
-    const u32x4 w = *(const u32x4*)p;
+template <typename T, int CPT> struct RowRaw;   // CPT columns of one row, raw bits
+template <> struct RowRaw<bf16_t, 8> {
+  u32x4 w;
+  __device__ __forceinline__ void load(const bf16_t* p) { w = *(const u32x4*)p; }
+  __device__ __forceinline__ void to_f32(float* o) const {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       o[2 * i] = __uint_as_float(w[i] << 16);
@@ -36,69 +41,108 @@ template <> struct RowLoad<bf16_t, 8> {
     }
   }
 };
-template <> struct RowLoad<bf16_t, 4> {
-  static __device__ __forceinline__ void load(const bf16_t* p, float* o) {
-    const uint2 w = *(const uint2*)p;
+template <> struct RowRaw<bf16_t, 4> {
+  uint2 w;
+  __device__ __forceinline__ void load(const bf16_t* p) { w = *(const uint2*)p; }
+  __device__ __forceinline__ void to_f32(float* o) const {
     o[0] = __uint_as_float(w.x << 16);
     o[1] = __uint_as_float(w.x & 0xffff0000u);
     o[2] = __uint_as_float(w.y << 16);
     o[3] = __uint_as_float(w.y & 0xffff0000u);
   }
 };
-template <> struct RowLoad<float, 8> {
-  static __device__ __forceinline__ void load(const float* p, float* o) {
-    const float4 a = ((const float4*)p)[0], b = ((const float4*)p)[1];
+template <> struct RowRaw<float, 8> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = ((const float4*)p)[0];
+    b = ((const float4*)p)[1];
+  }
+  __device__ __forceinline__ void to_f32(float* o) const {
     o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
     o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
   }
 };
-template <> struct RowLoad<float, 4> {
-  static __device__ __forceinline__ void load(const float* p, float* o) {
-    const float4 a = *(const float4*)p;
+template <> struct RowRaw<float, 4> {
+  float4 a;
+  __device__ __forceinline__ void load(const float* p) { a = *(const float4*)p; }
+  __device__ __forceinline__ void to_f32(float* o) const {
     o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
   }
 };
 
 constexpr int kKeysPerIter = 4;  // keys per lane between softmax rescales
+constexpr int kMaxSplits = 64;
 
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kRowsThreads) void k_attend_rows(AttendArgs a) {
   constexpr int CPT = D / 16;
   const int split = blockIdx.x, pos = blockIdx.y;
   const int h = blockIdx.z % a.Hkv, bi = blockIdx.z / a.Hkv;
-  const int tid = threadIdx.x, seg = tid % 16, kl = tid / 16;
+  const int tid = threadIdx.x, lane = tid % 64, seg = tid % 16, kl = tid / 16;
   const int ch = pos / a.L;
   const int64_t t = a.q_pos + pos;
 
   __shared__ int64_t iv_lo[kMaxIntervals];
-  __shared__ int64_t iv_end[kMaxIntervals + 1];  // exclusive prefix of lengths
-  __shared__ int n_iv;
-  if (tid == 0) {
-    int n = 0;
-    int64_t total = 0;
-    auto add = [&](int64_t lo, int64_t hi) {
-      if (hi > lo) {
-        iv_lo[n] = lo;
-        total += hi - lo;
-        iv_end[n] = total;
-        ++n;
-      }
-    };
-    add(0, a.n_init < t + 1 ? a.n_init : t + 1);
+  __shared__ int64_t iv_first[kMaxIntervals + 1];  // first key index of each interval
+  __shared__ int wave_tot[kRowsThreads / 64];
+  __shared__ int last_sh;
+
+  // query rows first: their loads overlap the interval scan below
+  RowRaw<T, CPT> qraw[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+    qraw[g].load((const T*)a.q +
+                 (((int64_t)bi * a.Hq + (int64_t)h * G + g) * a.q_cap + a.q_off + pos) * D +
+                 seg * CPT);
+
+  // ---------------------------------------------------------- key intervals
+  // slot 0: initial tokens; slots 1..k_m: units (sel order); slot k_m+1:
+  // window.  Thread m computes unit m's length; a block scan gives offsets.
+  const int niv = a.k_m + 2;
+  {
     const int64_t unit_cap = t - a.W + 1;
-    for (int m = 0; m < a.k_m; ++m) {
-      const int32_t u = a.sel[(((int64_t)bi * a.Hkv + h) * a.n_chunks + ch) * a.k_m + m];
-      if (u < 0) continue;
-      const int64_t lo = unit_first_key(u, a.B, a.n_init);
-      const int64_t hi = ((int64_t)u + a.n_init / a.B + 1) * a.B;
-      add(lo, hi < unit_cap ? hi : unit_cap);
+    const int64_t init_len = a.n_init < t + 1 ? a.n_init : t + 1;
+    const int64_t win_lo = a.n_init > unit_cap ? a.n_init : unit_cap;
+    const int64_t win_len = t + 1 - win_lo > 0 ? t + 1 - win_lo : 0;
+    int64_t lo = 0, len = 0;
+    if (tid < a.k_m) {
+      const int32_t u = a.sel[(((int64_t)bi * a.Hkv + h) * a.n_chunks + ch) * a.k_m + tid];
+      if (u >= 0) {
+        lo = unit_first_key(u, a.B, a.n_init);
+        const int64_t hi = ((int64_t)u + a.n_init / a.B + 1) * a.B;
+        len = (hi < unit_cap ? hi : unit_cap) - lo;
+        len = len > 0 ? len : 0;
+      }
     }
-    add(a.n_init > unit_cap ? a.n_init : unit_cap, t + 1);
-    n_iv = n;
+    // inclusive scan of the unit lengths (each <= B)
+    int x = (int)len;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const int y = __shfl_up(x, m);
+      if (lane >= m) x += y;
+    }
+    if (lane == 63) wave_tot[tid / 64] = x;
+    __syncthreads();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < kRowsThreads / 64; ++w2) {
+      before += w2 < tid / 64 ? wave_tot[w2] : 0;
+      all += wave_tot[w2];
+    }
+    if (tid < a.k_m) {
+      iv_lo[tid + 1] = lo;
+      iv_first[tid + 1] = init_len + before + x - len;
+    }
+    if (tid == 0) {
+      iv_lo[0] = 0;
+      iv_first[0] = 0;
+      iv_lo[niv - 1] = win_lo;
+      iv_first[niv - 1] = init_len + all;
+      iv_first[niv] = init_len + all + win_len;
+    }
   }
   __syncthreads();
-  const int niv = n_iv;
-  const int64_t n_keys = niv > 0 ? iv_end[niv - 1] : 0;
+  const int64_t n_keys = iv_first[niv];
   const int64_t per = (n_keys + gridDim.x - 1) / gridDim.x;
   const int64_t k_begin = (int64_t)split * per;
   const int64_t k_stop = k_begin + per < n_keys ? k_begin + per : n_keys;
@@ -109,10 +153,7 @@ __global__ __launch_bounds__(kRowsThreads) void k_attend_rows(AttendArgs a) {
   float qv[G][CPT];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const T* qp = (const T*)a.q +
-                  (((int64_t)bi * a.Hq + (int64_t)h * G + g) * a.q_cap + a.q_off + pos) * D +
-                  seg * CPT;
-    RowLoad<T, CPT>::load(qp, qv[g]);
+    qraw[g].to_f32(qv[g]);
 #pragma unroll
     for (int c = 0; c < CPT; ++c) qv[g][c] *= qscale;
   }
@@ -125,54 +166,81 @@ __global__ __launch_bounds__(kRowsThreads) void k_attend_rows(AttendArgs a) {
     for (int c = 0; c < CPT; ++c) acc[g][c] = 0.f;
   }
 
+  // key index -> position; each lane's indices only grow, so a cursor works
   int cur = 0;
   auto key_pos = [&](int64_t idx) -> int64_t {
-    while (idx >= iv_end[cur]) ++cur;
-    return iv_lo[cur] + (idx - (cur ? iv_end[cur - 1] : 0));
+    while (idx >= iv_first[cur + 1]) ++cur;
+    return iv_lo[cur] + (idx - iv_first[cur]);
   };
-
-  for (int64_t base = k_begin; base < k_stop; base += 16 * kKeysPerIter) {
-    float kr[kKeysPerIter][CPT], vr[kKeysPerIter][CPT];
-    bool ok[kKeysPerIter];
+  RowRaw<T, CPT> kn[kKeysPerIter], vn[kKeysPerIter];
+  bool okn[kKeysPerIter];
+  auto fetch = [&](int64_t base) {
 #pragma unroll
     for (int j = 0; j < kKeysPerIter; ++j) {
       const int64_t idx = base + kl + 16 * j;
-      ok[j] = idx < k_stop;
-      const int64_t p = ok[j] ? key_pos(idx) : 0;
-      RowLoad<T, CPT>::load(kb + p * D, kr[j]);
-      RowLoad<T, CPT>::load(vb + p * D, vr[j]);
+      okn[j] = idx < k_stop;
+      const int64_t p = okn[j] ? key_pos(idx) : 0;
+      kn[j].load(kb + p * D);
+      vn[j].load(vb + p * D);
     }
+  };
+  if (k_begin < k_stop) fetch(k_begin);
+  for (int64_t base = k_begin; base < k_stop; base += 16 * kKeysPerIter) {
+    RowRaw<T, CPT> kc[kKeysPerIter], vc[kKeysPerIter];
+    bool ok[kKeysPerIter];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float s[kKeysPerIter];
-      float mx = m[g];
+    for (int j = 0; j < kKeysPerIter; ++j) {
+      kc[j] = kn[j];
+      vc[j] = vn[j];
+      ok[j] = okn[j];
+    }
+    if (base + 16 * kKeysPerIter < k_stop) fetch(base + 16 * kKeysPerIter);  // in flight
+    // logits of the current keys for every head (each key row converted once)
+    float s[G][kKeysPerIter];
 #pragma unroll
-      for (int j = 0; j < kKeysPerIter; ++j) {
+    for (int j = 0; j < kKeysPerIter; ++j) {
+      float kf[CPT];
+      kc[j].to_f32(kf);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
         float d0 = 0.f;
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) d0 = fmaf(qv[g][c], kr[j][c], d0);
+        for (int c = 0; c < CPT; ++c) d0 = fmaf(qv[g][c], kf[c], d0);
         const float r = row16_sum(d0);  // the 16 lanes of a row share key j
-        s[j] = ok[j] ? r : -INFINITY;
-        mx = fmaxf(mx, s[j]);
+        s[g][j] = ok[j] ? r : -INFINITY;
       }
-      if (mx == -INFINITY) continue;  // no valid key yet for this lane group
-      const float alpha = exp2f(m[g] - mx);
+    }
+    // online softmax update per head; s becomes the weights p
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float mx = m[g];
+#pragma unroll
+      for (int j = 0; j < kKeysPerIter; ++j) mx = fmaxf(mx, s[g][j]);
+      const float mu = mx == -INFINITY ? 0.f : mx;   // no valid key yet: weights 0
+      const float alpha = __builtin_amdgcn_exp2f(m[g] - mu);
       m[g] = mx;
       float lsum = l[g] * alpha;
 #pragma unroll
       for (int c = 0; c < CPT; ++c) acc[g][c] *= alpha;
 #pragma unroll
       for (int j = 0; j < kKeysPerIter; ++j) {
-        const float p = exp2f(s[j] - mx);
-        lsum += p;
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) acc[g][c] = fmaf(p, vr[j][c], acc[g][c]);
+        s[g][j] = __builtin_amdgcn_exp2f(s[g][j] - mu);
+        lsum += s[g][j];
       }
       l[g] = lsum;
     }
+#pragma unroll
+    for (int j = 0; j < kKeysPerIter; ++j) {
+      float vf[CPT];
+      vc[j].to_f32(vf);
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) acc[g][c] = fmaf(s[g][j], vf[c], acc[g][c]);
+    }
   }
 
-  // merge the 16 key lanes
+  // ---------------------------------------------------------- merge 16 key lanes
   __shared__ float sm_m[16][G], sm_l[16][G];
   __shared__ float sm_o[16][G][D];
 #pragma unroll
@@ -185,88 +253,135 @@ __global__ __launch_bounds__(kRowsThreads) void k_attend_rows(AttendArgs a) {
     for (int c = 0; c < CPT; ++c) sm_o[kl][g][seg * CPT + c] = acc[g][c];
   }
   __syncthreads();
-  for (int o = tid; o < G * D; o += kRowsThreads) {
+  constexpr int kOut = (G * D + kRowsThreads - 1) / kRowsThreads;  // outputs per thread
+  float Mv[kOut], Lv[kOut], Ov[kOut];
+#pragma unroll
+  for (int i = 0; i < kOut; ++i) {
+    const int o = tid + i * kRowsThreads;
+    Mv[i] = -INFINITY;
+    Lv[i] = 0.f;
+    Ov[i] = 0.f;
+    if (o >= G * D) continue;
     const int g = o / D, col = o % D;
-    float M = -INFINITY;
-    for (int r = 0; r < 16; ++r) M = fmaxf(M, sm_m[r][g]);
-    float Lsum = 0.f, O = 0.f;
-    if (M != -INFINITY) {
+    for (int r = 0; r < 16; ++r) Mv[i] = fmaxf(Mv[i], sm_m[r][g]);
+    if (Mv[i] != -INFINITY) {
       for (int r = 0; r < 16; ++r) {
-        const float w = exp2f(sm_m[r][g] - M);
-        Lsum += sm_l[r][g] * w;
-        O += sm_o[r][g][col] * w;
-      }
-    }
-    const int64_t qh = (int64_t)bi * a.Hq + (int64_t)h * G + g;
-    if (gridDim.x == 1) {
-      T* out = (T*)a.out + (qh * a.out_cap + a.out_off + pos) * D + col;
-      *out = from_f32<T>(O / Lsum);
-      if (a.lse && col == 0) a.lse[qh * a.out_cap + a.out_off + pos] = (M + log2f(Lsum)) * kLn2;
-    } else {
-      const int64_t row = (((int64_t)split * a.batch * a.Hq) + qh) * a.n_pos + pos;
-      a.ws_o[row * D + col] = O;
-      if (col == 0) {
-        a.ws_ml[2 * row] = M;
-        a.ws_ml[2 * row + 1] = Lsum;
+        const float w = __builtin_amdgcn_exp2f(sm_m[r][g] - Mv[i]);
+        Lv[i] = fmaf(sm_l[r][g], w, Lv[i]);
+        Ov[i] = fmaf(sm_o[r][g][col], w, Ov[i]);
       }
     }
   }
-}
 
-// Merge split-K partials: o = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
-// grid (n_pos, H_q, batch), D threads.
-template <typename T, int D>
-__global__ void k_combine(AttendArgs a, int n_splits) {
-  const int pos = blockIdx.x, qh_in = blockIdx.y, bi = blockIdx.z, col = threadIdx.x;
-  const int64_t qh = (int64_t)bi * a.Hq + qh_in;
-  float M = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) {
-    const int64_t row = ((int64_t)s * a.batch * a.Hq + qh) * a.n_pos + pos;
-    M = fmaxf(M, a.ws_ml[2 * row]);
+  // ---------------------------------------------------------- split-K merge
+  const int splits = gridDim.x;
+  const int64_t qh0 = (int64_t)bi * a.Hq + (int64_t)h * G;
+  if (splits > 1) {
+#pragma unroll
+    for (int i = 0; i < kOut; ++i) {
+      const int o = tid + i * kRowsThreads;
+      if (o >= G * D) continue;
+      const int g = o / D, col = o % D;
+      const int64_t row = ((int64_t)split * a.batch * a.Hq + qh0 + g) * a.n_pos + pos;
+      st_dev(a.ws_o + row * D + col, Ov[i]);
+      if (col == 0) {
+        st_dev(a.ws_ml + 2 * row, Mv[i]);
+        st_dev(a.ws_ml + 2 * row + 1, Lv[i]);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    if (tid == 0) {
+      int* ctr = a.ws_count + ((int64_t)bi * a.Hkv + h) * a.n_pos + pos;
+      const int done = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last_sh = done == splits - 1;
+      if (last_sh) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!last_sh) return;
+    // Merge every split's published rows (this one's included) in split
+    // order.  (max, sum) pairs are staged in LDS with one load per thread;
+    // each head's weights 2^(m_s - M) are formed once; output columns then
+    // sum their splits with independent loads.
+    float* sm_w = &sm_o[0][0][0];                  // reuse: [splits][G] weights
+    float* sm_sl = sm_w + kMaxSplits * G;          // [splits][G] sums
+    for (int idx = tid; idx < splits * G; idx += kRowsThreads) {
+      const int s = idx / G, g = idx % G;
+      const int64_t row = ((int64_t)s * a.batch * a.Hq + qh0 + g) * a.n_pos + pos;
+      sm_w[idx] = ld_dev(a.ws_ml + 2 * row);
+      sm_sl[idx] = ld_dev(a.ws_ml + 2 * row + 1);
+    }
+    __syncthreads();
+    __shared__ float sm_M[G], sm_L[G];
+    if (tid < G) {
+      float M = -INFINITY;
+      for (int s = 0; s < splits; ++s) M = fmaxf(M, sm_w[s * G + tid]);
+      float Ls = 0.f;
+      for (int s = 0; s < splits; ++s) {
+        const float ms = sm_w[s * G + tid];
+        const float w = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+        sm_w[s * G + tid] = w;
+        Ls = fmaf(sm_sl[s * G + tid], w, Ls);
+      }
+      sm_M[tid] = M;
+      sm_L[tid] = Ls;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kOut; ++i) {
+      const int o = tid + i * kRowsThreads;
+      if (o >= G * D) continue;
+      const int g = o / D, col = o % D;
+      const float* base = a.ws_o + ((qh0 + g) * a.n_pos + pos) * D + col;
+      const int64_t stride = (int64_t)a.batch * a.Hq * a.n_pos * D;   // between splits
+      float Os = 0.f;
+      for (int s0 = 0; s0 < splits; s0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = s0 + j < splits ? ld_dev(base + (s0 + j) * stride) : 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (s0 + j < splits) Os = fmaf(v[j], sm_w[(s0 + j) * G + g], Os);
+      }
+      Mv[i] = sm_M[g];
+      Lv[i] = sm_L[g];
+      Ov[i] = Os;
+    }
   }
-  float Lsum = 0.f, O = 0.f;
-  for (int s = 0; s < n_splits; ++s) {
-    const int64_t row = ((int64_t)s * a.batch * a.Hq + qh) * a.n_pos + pos;
-    const float ms = a.ws_ml[2 * row];
-    if (ms == -INFINITY) continue;
-    const float w = exp2f(ms - M);
-    Lsum += a.ws_ml[2 * row + 1] * w;
-    O += a.ws_o[row * D + col] * w;
+#pragma unroll
+  for (int i = 0; i < kOut; ++i) {
+    const int o = tid + i * kRowsThreads;
+    if (o >= G * D) continue;
+    const int g = o / D, col = o % D;
+    const int64_t qh = qh0 + g;
+    T* out = (T*)a.out + (qh * a.out_cap + a.out_off + pos) * D + col;
+    *out = from_f32<T>(Ov[i] / Lv[i]);
+    if (a.lse && col == 0) a.lse[qh * a.out_cap + a.out_off + pos] = (Mv[i] + log2f(Lv[i])) * kLn2;
   }
-  T* out = (T*)a.out + (qh * a.out_cap + a.out_off + pos) * D + col;
-  *out = from_f32<T>(O / Lsum);
-  if (a.lse && col == 0) a.lse[qh * a.out_cap + a.out_off + pos] = (M + log2f(Lsum)) * kLn2;
 }
 
 int rows_num_splits(const AttendArgs& a) {
-  // enough workgroups to cover the chip twice, at least ~256 keys per split
+  // enough workgroups to cover the chip several times, >= ~256 keys each
   const int64_t max_keys = (int64_t)a.n_init + (int64_t)a.k_m * a.B + a.W;
   const int64_t wgs = (int64_t)a.n_pos * a.batch * a.Hkv;
-  int64_t s = (512 + wgs - 1) / wgs;
+  int64_t target = 512;
+  if (const char* e = getenv("INFLLM_ROWS_WGS")) {  // tuning override
+    const int v = atoi(e);
+    if (v >= 1 && v <= 65536) target = v;
+  }
+  int64_t s = (target + wgs - 1) / wgs;
   const int64_t cap = (max_keys + 255) / 256;
   if (s > cap) s = cap;
-  if (s > 64) s = 64;
+  if (s > kMaxSplits) s = kMaxSplits;
   return s < 1 ? 1 : (int)s;
 }
 
-hipError_t launch_combine(const AttendArgs& a, int splits, hipStream_t st) {
-  const dim3 grid(a.n_pos, a.Hq, a.batch);
-  if (a.bf16) {
-    if (a.d == 128) k_combine<bf16_t, 128><<<grid, 128, 0, st>>>(a, splits);
-    else k_combine<bf16_t, 64><<<grid, 64, 0, st>>>(a, splits);
-  } else {
-    if (a.d == 128) k_combine<float, 128><<<grid, 128, 0, st>>>(a, splits);
-    else k_combine<float, 64><<<grid, 64, 0, st>>>(a, splits);
-  }
-  return hipGetLastError();
-}
+int64_t rows_num_counters(const AttendArgs& a) { return (int64_t)a.n_pos * a.batch * a.Hkv; }
 
 template <typename T, int D, int G>
 static hipError_t launch_rows_tdg(const AttendArgs& a, int splits, hipStream_t st) {
   k_attend_rows<T, D, G><<<dim3(splits, a.n_pos, a.batch * a.Hkv), kRowsThreads, 0, st>>>(a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || splits == 1) return e;
-  return launch_combine(a, splits, st);
+  return hipGetLastError();
 }
 
 template <typename T, int D>

@@ -82,6 +82,36 @@ __device__ __forceinline__ double wave_sum_f64(double x) {
   return x;
 }
 
+// ------------------------------------------------ cross-workgroup publication
+// Split-K partial results are handed from one workgroup to another without
+// device-scope fences (on gfx950 a __threadfence() writes back and
+// invalidates the L2, evicting what other workgroups share there).  Writers
+// use device-scope (sc1) stores and drain them with s_waitcnt vmcnt(0)
+// before the barrier that precedes their arrival-counter increment; the
+// last arriver reads with device-scope loads.
+
+// s_waitcnt immediate (gfx9 encoding) for vmcnt(0), expcnt/lgkmcnt untouched
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// 16-byte device-scope accesses through a raw buffer resource (cache policy
+// sc1); `bytes` bounds the range, checked by the hardware.
+constexpr int kCachePolicySc1 = 16;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dev_rsrc(const float* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void st4_dev(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kCachePolicySc1);
+}
+__device__ __forceinline__ f32x4 ld4_dev(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCachePolicySc1));
+}
+
 // Order-preserving map of an fp32 to uint32 (larger float -> larger key);
 // -0 and +0 map to the same key.
 __device__ __forceinline__ uint32_t orderable(float f) {

@@ -63,8 +63,7 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 // vector-ALU attention, one query position per workgroup
 int rows_num_splits(const AttendArgs& a);
 hipError_t launch_attend_rows(const AttendArgs& a, int splits, hipStream_t st);
-// merge of split-K partial rows (shared by both attention paths)
-hipError_t launch_combine(const AttendArgs& a, int splits, hipStream_t st);
+int64_t rows_num_counters(const AttendArgs& a);
 
 // bf16 MFMA attention tiles for query chunks (head_dim 128)
 bool prefill_supported(const AttendArgs& a);

@@ -18,7 +18,7 @@
 namespace infllm {
 
 constexpr int kScoreThreads = 256;
-constexpr int kUnitsPerWG = 512;
+constexpr int kUnitsPerWG = 64;
 constexpr int kQsumRows = 32;        // chunk rows per partial sum
 constexpr int kDirectRows = 64;      // L*G up to this: sum in the scoring kernel
 
