@@ -1,8 +1,8 @@
 // Working-context attention for query chunks on bf16 MFMA (gfx950,
 // head_dim 128): the chunked-encoding hot loop.
 //
-// A workgroup owns 128 query rows of one KV head -- the G query heads that
-// share that KV head times 128/G consecutive queries of one chunk -- and
+// A workgroup owns 256 query rows of one KV head -- the G query heads that
+// share that KV head times 256/G consecutive queries of one chunk -- and
 // walks a list of 64-key tiles: the initial tokens, each selected unit's
 // block, and the local-window band of its queries (InfLLM Guide, "Core
 // Innovation 2", item 3, Working Context).  Tiles that straddle a boundary
@@ -10,22 +10,26 @@
 //     initial tokens:  p < n_init, p <= t
 //     unit keys:       p >= n_init, p <= t - W
 //     window keys:     p >= n_init, t - W < p <= t
-// all other tiles run mask-free.  Each of the 4 waves holds 32 rows:
+// all other tiles run mask-free.  Each of the 8 waves holds 32 rows:
 //     S^T = K Q^T   (v_mfma_f32_32x32x16_bf16; A = K rows from LDS,
 //                    B = the wave's Q rows kept in registers)
 //     online softmax in fp32 (exp2, log2-scaled logits)
-//     O^T += V^T P^T (A = V^T from LDS, B = P^T straight from the S^T
-//                    accumulators, rounded to bf16)
+//     O^T += V^T P^T (A = V^T read from row-major V with the transposing
+//                    LDS load, B = P^T straight from the S^T accumulators,
+//                    rounded to bf16)
 // The rows of K fed to the first product are permuted (bits 2 and 3 of the
 // row index swapped) so that each lane's S^T values come out as runs of 8
-// consecutive keys: exactly the B-operand layout of the second product.  V
-// is transposed into LDS while it is staged; both tiles are double-buffered
-// and the next tile's global loads are in flight during the current tile's
-// math.  To fill the chip the tile list is split over several workgroups
-// (split-K): each publishes its partial (max, sum, unnormalised output) rows
-// and the last one to finish, found with a per-tile counter in the
-// workspace, merges them and writes the output.  The counters return to
-// zero at the end of every call.
+// consecutive keys: exactly the B-operand layout of the second product.
+//
+// K and V tiles travel from global memory straight into LDS (16-byte
+// global_load_lds per lane, no register staging) through a ring of four
+// buffers, three tiles ahead of the math.  Within a row the 16-byte chunks
+// are XOR-swizzled so that both the K operand reads and the transposing V
+// reads are free of bank conflicts.  To fill the chip the tile list is
+// split over several workgroups (split-K): each publishes its partial
+// (max, sum, unnormalised output) rows and the last one to finish, found
+// with a per-tile counter in the workspace, merges them and writes the
+// output.  The counters return to zero at the end of every call.
 #include <stdlib.h>
 
 #include "common.h"
@@ -34,23 +38,37 @@
 namespace infllm {
 
 constexpr int kD = 128;
-constexpr int kRows = 128;            // query rows per workgroup
+constexpr int kRows = 256;            // query rows per workgroup (32 per wave)
 constexpr int kKT = 64;               // keys per tile
-constexpr int kKsStride = kD + 8;     // bf16 per K row in LDS (272 B)
-constexpr int kVtStride = kKT + 8;    // bf16 per V^T row in LDS (144 B)
-constexpr int kKsElems = kKT * kKsStride;
-constexpr int kVtElems = kD * kVtStride;
+constexpr int kTileElems = kKT * kD;  // one K or V tile in LDS: 64 rows of 256 B
+constexpr int kStages = 4;            // LDS ring depth
 constexpr int kMaxTiles = 1024;
 constexpr int kXcds = 8;             // MI355X: 8 XCDs, each with its own L2
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
 
 enum : int { kTileInit = 0, kTileUnit = 1, kTileWin = 2, kTileMask = 4 };
 
 constexpr float kLog2eP = 1.4426950408889634f;
+// s_waitcnt vmcnt(4 (kStages - 2)) lgkmcnt(0): the loads of the next tile
+// have landed and no LDS read of this wave is still in flight
+constexpr int kWaitRing = 0x0078;
+static_assert(kStages == 4, "kWaitRing encodes 4 loads x 2 tiles in flight");
 
 __device__ __forceinline__ int swap_bits23(int m) {
   return (m & ~0xC) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
+
+// 16-byte chunk position of chunk c of row r within its 256-byte LDS row.
+// K rows are read 16 rows x one chunk at a time: XOR with r % 16 spreads
+// them over all banks.  V rows are read through the transposing load, four
+// consecutive keys x four chunks per 16 lanes: XOR with 4 (r % 4).
+__device__ __forceinline__ int k_pos(int r, int c) { return c ^ (r & 15); }
+__device__ __forceinline__ int v_pos(int r, int c) { return c ^ ((r & 3) << 2); }
+
+typedef short short4_t __attribute__((ext_vector_type(4)));
+#define INFLLM_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+#define INFLLM_GLOBAL(p) ((const __attribute__((address_space(1))) void*)(p))
 
 // Workgroup -> work mapping.  The hardware hands workgroup i to XCD i % 8;
 // when the (sequence, KV head) groups divide evenly over the XCDs, every
@@ -106,8 +124,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_prefill(AttendArgs a, Pr
   const int64_t ta = a.q_pos + (int64_t)ch * a.L + q_first;  // first query position
   const int64_t tb = ta + nq - 1;                            // last valid query position
 
-  __shared__ __attribute__((aligned(16))) bf16_t lds_k[2][kKsElems];
-  __shared__ __attribute__((aligned(16))) bf16_t lds_vt[2][kVtElems];
+  // the ring: one variable per stage and operand, so that the compiler can
+  // tell the buffer being read from the buffers being loaded
+  __shared__ __attribute__((aligned(16))) bf16_t lds_k0[kTileElems], lds_k1[kTileElems],
+      lds_k2[kTileElems], lds_k3[kTileElems];
+  __shared__ __attribute__((aligned(16))) bf16_t lds_v0[kTileElems], lds_v1[kTileElems],
+      lds_v2[kTileElems], lds_v3[kTileElems];
   __shared__ int tiles[kMaxTiles];
   __shared__ int n_tiles_sh;
   __shared__ int last_sh;
@@ -193,79 +215,91 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_prefill(AttendArgs a, Pr
   }
 
   // ---------------------------------------------------------- staging
+  // One global_load_lds instruction of a wave fills 1 KB of LDS: four rows,
+  // lane l writing position l % 16 of row l / 16.  Wave w fills row groups w
+  // and w + 8 of the K tile and of the V tile; each lane fetches the chunk
+  // that the swizzle puts at its position (rows past the cache end are
+  // clamped to the last row: those keys are always masked).
   const bf16_t* Kg = (const bf16_t*)a.k + ((int64_t)bi * a.Hkv + h) * a.kv_cap * kD;
   const bf16_t* Vg = (const bf16_t*)a.v + ((int64_t)bi * a.Hkv + h) * a.kv_cap * kD;
   const int64_t last_row = a.kv_cap - 1;
-  u32x4 pk[4], pv[4];
-  // K: thread -> (key = tid/16 + 16 i, 16-byte chunk tid%16), coalesced rows
-  // V: thread -> (key pair kp = tid%32, 8-column group dg = tid/32 + 8 i)
-  auto load_tile = [&](int desc) {
-    const int64_t p0 = desc & ~7;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int64_t r = p0 + tid / 16 + 16 * i;
-      r = r < last_row ? r : last_row;
-      pk[i] = *(const u32x4*)(Kg + r * kD + (tid % 16) * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int dg = tid / 32 + 8 * i, kp = tid % 32;
-      int64_t r0 = p0 + 2 * kp, r1 = r0 + 1;
-      r0 = r0 < last_row ? r0 : last_row;
-      r1 = r1 < last_row ? r1 : last_row;
-      pv[2 * i] = *(const u32x4*)(Vg + r0 * kD + dg * 8);
-      pv[2 * i + 1] = *(const u32x4*)(Vg + r1 * kD + dg * 8);
-    }
-  };
-  auto store_tile = [&](int buf) {
-    bf16_t* ks = lds_k[buf];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *(u32x4*)(ks + (tid / 16 + 16 * i) * kKsStride + (tid % 16) * 8) = pk[i];
-    uint32_t* vt = (uint32_t*)lds_vt[buf];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int dg = tid / 32 + 8 * i, kp = tid % 32;
-      const u32x4 x = pv[2 * i], y = pv[2 * i + 1];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        // columns 8dg+2j and 8dg+2j+1 of keys 2kp and 2kp+1
-        const uint32_t lo = (x[j] & 0xffffu) | (y[j] << 16);
-        const uint32_t hi = (x[j] >> 16) | (y[j] & 0xffff0000u);
-        vt[((8 * dg + 2 * j) * kVtStride) / 2 + kp] = lo;
-        vt[((8 * dg + 2 * j + 1) * kVtStride) / 2 + kp] = hi;
-      }
-    }
-  };
-
   f32x16 acc[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
   const float c = kLog2eP / sqrtf((float)kD);
   const int kperm = swap_bits23(n);   // key row this lane feeds to S^T
+  // transposing V reads: within each 16 lanes, lane s supplies key
+  // 4h + s/4 (of the 8-key run) and 4 columns starting at vcol; the lane
+  // then receives column kperm(n) of the four keys 4h .. 4h+3
+  const int vs = lane % 16;
+  const int vcol = 16 * ((lane % 32) / 16) + 4 * (((vs & 1) << 1) | ((vs >> 1) & 1));
+  const int vkey = 8 * half + (vs >> 2);
 
-  if (tile_begin < tile_end) {
-    load_tile(tiles[tile_begin]);
-    store_tile(0);
+  // Ring of kStages buffers, loads kStages-1 tiles ahead.  Every iteration
+  // issues the loads of one tile (a repeat of the last tile past the end,
+  // into a buffer nobody reads) so that each lane always has the same
+  // number of loads in flight, and "tile i+1 has landed" is
+  // s_waitcnt vmcnt(4 * (kStages - 2)).
+  const int nt = tile_end - tile_begin;
+  // wave w fills row groups w and w + 8 of a tile: one global_load_lds
+  // fills four rows (1 KB), lane l writing position l % 16 of row l / 16
+  // with the chunk that the swizzle puts there; rows past the cache end are
+  // clamped to the last row (those keys are always masked)
+  auto load_tile = [&](int desc, bf16_t* kn, bf16_t* vn) {
+    const int64_t p0 = desc & ~7;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int grp = wave + kWaves * j;
+      const int r = 4 * grp + lane / 16, pos = lane % 16;
+      int64_t row = p0 + r;
+      row = row < last_row ? row : last_row;
+      __builtin_amdgcn_global_load_lds(INFLLM_GLOBAL(Kg + row * kD + 8 * k_pos(r, pos)),
+                                       INFLLM_LDS(kn + grp * 4 * kD), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(INFLLM_GLOBAL(Vg + row * kD + 8 * v_pos(r, pos)),
+                                       INFLLM_LDS(vn + grp * 4 * kD), 16, 0, 0);
+    }
+  };
+  // Between tiles: tile i+1 has landed (this lane's loads; vmcnt counts the
+  // direct-to-LDS loads in issue order) and every LDS read of tile i has
+  // returned (lgkmcnt), so after the barrier all lanes' parts of tile i+1
+  // are visible and buffer i can be refilled.  A plain s_barrier:
+  // __syncthreads' fence would also wait for the loads of tiles i+2 and
+  // i+3.  The empty asm statements keep the compiler from moving LDS
+  // accesses across it.
+  auto ring_barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt(kWaitRing);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  if (nt > 0) {
+    const int* tl = tiles + tile_begin;
+    load_tile(tl[0], lds_k0, lds_v0);
+    load_tile(tl[1 < nt ? 1 : nt - 1], lds_k1, lds_v1);
+    load_tile(tl[2 < nt ? 2 : nt - 1], lds_k2, lds_v2);
   }
-  __syncthreads();
+  ring_barrier();   // tile 0 landed
 
-  for (int tix = tile_begin; tix < tile_end; ++tix) {
-    const int buf = (tix - tile_begin) & 1;
-    const int desc = tiles[tix];
-    const bool more = tix + 1 < tile_end;
-    if (more) load_tile(tiles[tix + 1]);
+  // One tile: issue the loads of tile i+3, then the math on tile i.  The
+  // ring buffers are separate variables and the loop below is unrolled over
+  // the ring, so every LDS read names a buffer that the compiler can tell
+  // apart from the ones being loaded (otherwise it would make every LDS read
+  // wait for all loads in flight).
+  auto tile_step = [&](const int* tl, const bf16_t* kb, const bf16_t* vb, bf16_t* kn,
+                       bf16_t* vn, int i) {
+    const int desc = tl[i];
+    load_tile(tl[i + kStages - 1 < nt ? i + kStages - 1 : nt - 1], kn, vn);
 
     // S^T = K Q^T for 64 keys x 32 rows: two 32-key sub-tiles
     f32x16 s0 = f32x16{}, s1 = f32x16{};
     {
-      const bf16_t* k0 = lds_k[buf] + kperm * kKsStride + half * 8;
-      const bf16_t* k1 = k0 + 32 * kKsStride;
+      const int r0 = kperm, r1 = 32 + kperm;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 a0 = *(const bf16x8*)(k0 + ks * 16);
-        const bf16x8 a1 = *(const bf16x8*)(k1 + ks * 16);
+        const int cch = 2 * ks + half;
+        const bf16x8 a0 = *(const bf16x8*)(kb + r0 * kD + 8 * k_pos(r0, cch));
+        const bf16x8 a1 = *(const bf16x8*)(kb + r1 * kD + 8 * k_pos(r1, cch));
         s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[ks], s0, 0, 0, 0);
         s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[ks], s1, 0, 0, 0);
       }
@@ -286,7 +320,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_prefill(AttendArgs a, Pr
     float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    {
+      // the other half of the wave holds the row's other keys
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                       false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
     const float m_new = fmaxf(m_run, mx * c);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     if (__any(m_new != m_run)) {   // rescale only when some row's max moved
@@ -308,21 +347,52 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_prefill(AttendArgs a, Pr
     }
     l_run += psum;
 
-    // O^T += V^T P^T: 4 key steps of 16 x 4 d-tiles of 32
+    // O^T += V^T P^T: 4 key steps of 16 x 4 d-tiles of 32; the V^T operand
+    // (column kperm(n) + 32 dt, keys 16 sp + 8 half + j) comes from two
+    // transposing reads of four keys each
     {
-      const bf16_t* vt = lds_vt[buf] + kperm * kVtStride + half * 8;
 #pragma unroll
       for (int sp = 0; sp < 4; ++sp) {
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          const bf16x8 av = *(const bf16x8*)(vt + (32 * dt) * kVtStride + sp * 16);
+          const int col = 32 * dt + vcol;
+          const int k0 = 16 * sp + vkey, k1 = k0 + 4;
+          const short4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) short4_t*)(vb + k0 * kD + 8 * v_pos(k0, col / 8) + col % 8));
+          const short4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) short4_t*)(vb + k1 * kD + 8 * v_pos(k1, col / 8) + col % 8));
+          // whole-vector concatenation and bit cast: building the operand
+          // element by element makes the compiler splat element 0
+          const bf16x8 av = __builtin_bit_cast(
+              bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
           acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[sp], acc[dt], 0, 0, 0);
         }
       }
     }
-    if (more) store_tile(buf ^ 1);
-    __syncthreads();
+  };
+
+  // unrolled over the ring so that every copy names fixed buffers; after
+  // each tile: tile i+1 landed (this lane's part), and the barrier makes
+  // all parts visible and frees buffer i for the loads of the next tile
+  {
+    const int* tl = tiles + tile_begin;
+    for (int i = 0; i < nt; i += kStages) {
+      tile_step(tl, lds_k0, lds_v0, lds_k3, lds_v3, i);
+      ring_barrier();
+      if (i + 1 >= nt) break;
+      tile_step(tl, lds_k1, lds_v1, lds_k0, lds_v0, i + 1);
+      ring_barrier();
+      if (i + 2 >= nt) break;
+      tile_step(tl, lds_k2, lds_v2, lds_k1, lds_v1, i + 2);
+      ring_barrier();
+      if (i + 3 >= nt) break;
+      tile_step(tl, lds_k3, lds_v3, lds_k2, lds_v2, i + 3);
+      ring_barrier();
+    }
   }
+  // the repeat loads past the end must land before the workgroup's LDS can
+  // be handed to another workgroup
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   // ---------------------------------------------------------- epilogue
   float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -457,7 +527,7 @@ int prefill_num_splits(const AttendArgs& a) {
   const int64_t wgs = (int64_t)((a.L + TQ - 1) / TQ) * a.n_chunks * a.Hkv * a.batch;
   const int tiles = max_tiles(a, TQ);
   int s = 1;
-  while (wgs * s < 512 && tiles / (2 * s) >= 8 && s < 8) s *= 2;
+  while (wgs * s < 256 && tiles / (2 * s) >= 8 && s < 8) s *= 2;
   return s;
 }
 
