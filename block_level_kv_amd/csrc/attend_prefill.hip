@@ -76,6 +76,7 @@ typedef short short4_t __attribute__((ext_vector_type(4)));
 // are shared through that XCD's L2.
 struct PrefillGeom {
   int n_qtiles, TQ, splits;
+  int n_items;     // work items (query tile x chunk x sequence x KV head) per split
   int per_group;   // workgroups per (sequence, KV head): chunks x query tiles x splits
   int xcd_groups;  // 1: group g runs on XCD g % 8
 };
@@ -200,7 +201,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_prefill(AttendArgs a, Pr
   const int tile_end = (int)((int64_t)n_tiles * (split + 1) / geo.splits);
 
   // ---------------------------------------------------------- this lane's row
-  const int row = wave * 32 + n;            // 0..127
+  const int row = wave * 32 + n;            // 0..255
   const int g = row / TQ, qi = row % TQ;    // head within the group, query within tile
   const bool row_ok = qi < nq;
   const int64_t t_row = ta + qi;
@@ -396,7 +397,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_prefill(AttendArgs a, Pr
 
   // ---------------------------------------------------------- epilogue
   float l_tot = l_run + __shfl_xor(l_run, 32);
-  const int64_t pos = (int64_t)ch * a.L + q_first + qi;     // row within this call
   // register r of d-tile dt holds column 32dt + 16(r/8) + 8 half + r%8
   if (geo.splits > 1) {
     // Every split publishes its partial rows; the last split to finish
@@ -404,19 +404,18 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_prefill(AttendArgs a, Pr
     // s_waitcnt vmcnt(0) before the barrier that precedes the arrival
     // counter; the merger reads with device-scope loads.  No L2 writeback or
     // invalidate is needed, so the K/V lines other workgroups share in L2
-    // survive.
-    const int64_t wrow = ((int64_t)split * a.batch * a.Hq + qh) * a.n_pos + pos;
-    // this workgroup's rows of split s start at region_row(s); lane offsets
-    // (head g, query qi, column) stay below G * n_pos rows
-    const int64_t qh0 = (int64_t)bi * a.Hq + (int64_t)h * G;
-    const int64_t pos0 = (int64_t)ch * a.L + q_first;
+    // survive.  Only a workgroup with this same row-to-lane mapping reads
+    // the partials back, so they are stored lane-major -- [split][work
+    // item][16-byte chunk][thread] -- and every store and load instruction
+    // covers 1 KB per wave; (max, sum) pairs are stored per row.
+    const int64_t item = (((int64_t)bi * a.Hkv + h) * a.n_chunks + ch) * geo.n_qtiles + qt;
     auto region = [&](int s) {
-      return dev_rsrc(a.ws_o + (((int64_t)s * a.batch * a.Hq + qh0) * a.n_pos + pos0) * kD,
-                      (uint32_t)((int64_t)G * a.n_pos * kD * sizeof(float)));
+      return dev_rsrc(a.ws_o + ((int64_t)s * geo.n_items + item) * (kRows * kD),
+                      (uint32_t)(kRows * kD * sizeof(float)));
     };
-    const uint32_t lane_off =
-        (uint32_t)((((int64_t)g * a.n_pos + qi) * kD + half * 8) * sizeof(float));
-    if (row_ok) {
+    auto ml_at = [&](int s) { return a.ws_ml + 2 * (((int64_t)s * geo.n_items + item) * kRows + row); };
+    const uint32_t lane_off = (uint32_t)tid * 16;
+    {
       const __amdgpu_buffer_rsrc_t r = region(split);
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
@@ -425,33 +424,28 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_prefill(AttendArgs a, Pr
           f32x4 v;
 #pragma unroll
           for (int j = 0; j < 4; ++j) v[j] = acc[dt][4 * q4 + j];
-          // registers 4q4..4q4+3 hold columns 32dt + 16(q4/2) + 8half + 4(q4%2) + j
-          st4_dev(r, lane_off + (32 * dt + 16 * (q4 / 2) + 4 * (q4 % 2)) * 4, v);
+          st4_dev(r, lane_off + (uint32_t)((4 * dt + q4) * kThreads * 16), v);
         }
       if (half == 0) {
-        st_dev(&a.ws_ml[2 * wrow], m_run);
-        st_dev(&a.ws_ml[2 * wrow + 1], l_tot);
+        st_dev(ml_at(split), m_run);
+        st_dev(ml_at(split) + 1, l_tot);
       }
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     if (tid == 0) {
-      const int64_t tile_id = (((int64_t)bi * a.Hkv + h) * a.n_chunks + ch) * geo.n_qtiles + qt;
-      const int done = __hip_atomic_fetch_add(&a.ws_count[tile_id], 1, __ATOMIC_RELAXED,
+      const int done = __hip_atomic_fetch_add(&a.ws_count[item], 1, __ATOMIC_RELAXED,
                                               __HIP_MEMORY_SCOPE_AGENT);
       last_sh = done == geo.splits - 1;
       if (last_sh)   // ready for the next call
-        __hip_atomic_store(&a.ws_count[tile_id], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&a.ws_count[item], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
     if (!last_sh || !row_ok) return;
     // merge: own registers + the other splits' published rows
     float M = m_run;
-    for (int s = 0; s < geo.splits; ++s) {
-      if (s == split) continue;
-      const int64_t r2 = ((int64_t)s * a.batch * a.Hq + qh) * a.n_pos + pos;
-      M = fmaxf(M, ld_dev(&a.ws_ml[2 * r2]));
-    }
+    for (int s2 = 0; s2 < geo.splits; ++s2)
+      if (s2 != split) M = fmaxf(M, ld_dev(ml_at(s2)));
     // splits are summed in index order whichever one merges, so the result
     // does not depend on arrival order
     const float mu = M == -INFINITY ? 0.f : M;
@@ -459,8 +453,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_prefill(AttendArgs a, Pr
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) res[dt] = f32x16{};
     float l_sum = 0.f;
-    for (int s = 0; s < geo.splits; ++s) {
-      if (s == split) {
+    for (int s2 = 0; s2 < geo.splits; ++s2) {
+      if (s2 == split) {
         const float w = __builtin_amdgcn_exp2f(m_run - mu);
         l_sum = fmaf(l_tot, w, l_sum);
 #pragma unroll
@@ -469,16 +463,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_prefill(AttendArgs a, Pr
           for (int j = 0; j < 16; ++j) res[dt][j] = fmaf(acc[dt][j], w, res[dt][j]);
         continue;
       }
-      const int64_t r2 = ((int64_t)s * a.batch * a.Hq + qh) * a.n_pos + pos;
-      const float ms = ld_dev(&a.ws_ml[2 * r2]);
-      const float w = __builtin_amdgcn_exp2f(ms - mu);
-      l_sum = fmaf(ld_dev(&a.ws_ml[2 * r2 + 1]), w, l_sum);
-      const __amdgpu_buffer_rsrc_t r = region(s);
+      const float w = __builtin_amdgcn_exp2f(ld_dev(ml_at(s2)) - mu);
+      l_sum = fmaf(ld_dev(ml_at(s2) + 1), w, l_sum);
+      const __amdgpu_buffer_rsrc_t r = region(s2);
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const f32x4 v = ld4_dev(r, lane_off + (32 * dt + 16 * (q4 / 2) + 4 * (q4 % 2)) * 4);
+          const f32x4 v = ld4_dev(r, lane_off + (uint32_t)((4 * dt + q4) * kThreads * 16));
 #pragma unroll
           for (int j = 0; j < 4; ++j) res[dt][4 * q4 + j] = fmaf(v[j], w, res[dt][4 * q4 + j]);
         }
@@ -488,6 +480,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_prefill(AttendArgs a, Pr
     l_tot = l_sum;
     m_run = M;
   }
+  const int64_t pos = (int64_t)ch * a.L + q_first + qi;     // row within this call
   if (!row_ok) return;
   const float inv = 1.f / l_tot;
   bf16_t* o = (bf16_t*)a.out + (qh * a.out_cap + a.out_off + pos) * kD + half * 8;
@@ -531,6 +524,8 @@ int prefill_num_splits(const AttendArgs& a) {
   return s;
 }
 
+int64_t prefill_partial_rows(const AttendArgs& a) { return prefill_num_counters(a) * kRows; }
+
 int64_t prefill_num_counters(const AttendArgs& a) {
   const int TQ = kRows / (a.Hq / a.Hkv);
   return (int64_t)((a.L + TQ - 1) / TQ) * a.n_chunks * a.Hkv * a.batch;
@@ -545,6 +540,7 @@ static void launch_g(const AttendArgs& a, int splits, hipStream_t st) {
   geo.splits = splits;
   geo.per_group = geo.n_qtiles * a.n_chunks * splits;
   const int groups = a.Hkv * a.batch;
+  geo.n_items = geo.n_qtiles * a.n_chunks * groups;
   geo.xcd_groups = groups % kXcds == 0;
   k_attend_prefill<G><<<dim3(geo.per_group * groups), kThreads, 0, st>>>(a, geo);
 }

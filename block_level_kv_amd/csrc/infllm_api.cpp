@@ -109,7 +109,8 @@ AttendWs attend_ws_layout(const AttendArgs& a) {
   attend_plan(a, &mfma, &splits);
   AttendWs w{0, 0, 0};
   if (splits <= 1) return w;
-  const size_t rows = (size_t)splits * a.batch * a.Hq * a.n_pos;
+  const size_t rows =
+      (size_t)splits * (mfma ? (size_t)prefill_partial_rows(a) : (size_t)a.batch * a.Hq * a.n_pos);
   const int64_t counters = mfma ? prefill_num_counters(a) : rows_num_counters(a);
   w.count_bytes = round256((size_t)counters * sizeof(int));
   w.o_bytes = round256(rows * a.d * sizeof(float));

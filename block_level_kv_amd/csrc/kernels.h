@@ -69,6 +69,7 @@ int64_t rows_num_counters(const AttendArgs& a);
 bool prefill_supported(const AttendArgs& a);
 int prefill_num_splits(const AttendArgs& a);
 int64_t prefill_num_counters(const AttendArgs& a);
+int64_t prefill_partial_rows(const AttendArgs& a);   // per split
 hipError_t launch_attend_prefill(const AttendArgs& a, int splits, hipStream_t st);
 
 }  // namespace infllm
