@@ -271,22 +271,24 @@ def test_tiny_workload_pipeline(orc):
 
 
 PREFILL_VARIANTS = [
-    # (G, n_init, W, chunk, n_ctx, top_k)
-    (1, 128, 512, 256, 2048, 4),
-    (2, 100, 200, 100, 1900, 3),
-    (8, 0, 64, 512, 2560, 6),
-    (4, 200, 300, 16, 1600, 2),
-    (4, 64, 4096, 512, 3072, 8),       # window longer than the context: dense
+    # (G, n_init, W, chunk, n_ctx, top_k, KV heads)
+    (1, 128, 512, 256, 2048, 4, 2),
+    (2, 100, 200, 100, 1900, 3, 2),
+    (8, 0, 64, 512, 2560, 6, 2),
+    (4, 200, 300, 16, 1600, 2, 2),
+    (4, 64, 4096, 512, 3072, 8, 2),    # window longer than the context: dense
+    # 8 (sequence, KV head) groups: the splits of a work item share an XCD
+    (2, 128, 384, 192, 1536, 4, 8),
 ]
 
 
-@pytest.mark.parametrize("G,n_init,W,chunk,n_ctx,top_k", PREFILL_VARIANTS)
+@pytest.mark.parametrize("G,n_init,W,chunk,n_ctx,top_k,Hkv", PREFILL_VARIANTS)
 @pytest.mark.parametrize("splits", ["auto", "1", "3"])
-def test_prefill_mfma_variants(orc, monkeypatch, G, n_init, W, chunk, n_ctx, top_k, splits):
+def test_prefill_mfma_variants(orc, monkeypatch, G, n_init, W, chunk, n_ctx, top_k, Hkv, splits):
     if splits != "auto":
         monkeypatch.setenv("INFLLM_PREFILL_SPLITS", splits)
-    w = LL.replace(n_ctx=n_ctx, n_q_heads=2 * G, n_kv_heads=2, window=W, n_init=n_init,
-                   top_k=top_k, chunk=chunk, seed=G * 1000 + n_init)
+    w = LL.replace(n_ctx=n_ctx, n_q_heads=Hkv * G, n_kv_heads=Hkv, window=W, n_init=n_init,
+                   top_k=top_k, chunk=chunk, seed=G * 1000 + n_init + Hkv)
     cfg = cfg_of(w)
     inp = synth.make_inputs(w)
     dev = {k: v.cuda() for k, v in inp.items() if isinstance(v, torch.Tensor)}
