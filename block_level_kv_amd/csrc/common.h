@@ -82,6 +82,21 @@ __device__ __forceinline__ double wave_sum_f64(double x) {
   return x;
 }
 
+// Sum over the wave in a fixed order without LDS round trips: DPP sums
+// within each 16-lane row, then the four row sums read into scalars.
+__device__ __forceinline__ double readlane_f64(double x, int l) {
+  const int lo = __builtin_amdgcn_readlane(__double2loint(x), l);
+  const int hi = __builtin_amdgcn_readlane(__double2hiint(x), l);
+  return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ double wave_sum_f64_dpp(double x) {
+  x += dpp_f64<INFLLM_DPP_XOR1>(x);
+  x += dpp_f64<INFLLM_DPP_XOR2>(x);
+  x += dpp_f64<INFLLM_DPP_HALF_MIRROR>(x);
+  x += dpp_f64<INFLLM_DPP_MIRROR>(x);
+  return (readlane_f64(x, 0) + readlane_f64(x, 16)) + (readlane_f64(x, 32) + readlane_f64(x, 48));
+}
+
 // ------------------------------------------------ cross-workgroup publication
 // Split-K partial results are handed from one workgroup to another without
 // device-scope fences (on gfx950 a __threadfence() writes back and
