@@ -5,7 +5,8 @@
 // sum and the dot products accumulate in fp64, so the ranking that follows
 // is decided on scores accurate far below the near-tie margin.
 //
-// Long chunks: k_chunk_qsum spreads the query sum over many workgroups
+// Long chunks (unit count above kFusedMaxUnits; smaller counts take the
+// one-launch k_score_fused below): k_chunk_qsum spreads the query sum over many workgroups
 // (16-byte loads, kQsumRows query rows each) and writes fp64 partial sums;
 // k_score_units adds them in a fixed order, so results do not depend on
 // scheduling.  Short chunks (decode: one query x G heads) skip the first
@@ -150,15 +151,125 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_units(
   }
 }
 
+// Long chunks with a moderate unit count, in one launch: each workgroup
+// sums kQsumRows query rows of one chunk (all G heads) in fp64 and publishes
+// the partial sum with device-scope stores; the last workgroup of a
+// (sequence, KV head, chunk) to arrive -- found with a counter in the
+// workspace, which it resets -- adds the partial sums in part order (so the
+// result does not depend on arrival order) and scores every unit.
+// grid (parts, H_kv, batch * n_chunks).
+constexpr int kFusedMaxUnits = 2048;
+
+template <typename T>
+__global__ __launch_bounds__(kScoreThreads) void k_score_fused(
+    const T* __restrict__ q, int64_t q_cap, int64_t q_off, int64_t q_pos, int L, int Hq, int Hkv,
+    int d, int B, int n_init, int W, const float* __restrict__ repr, int U,
+    float* __restrict__ scores, int n_chunks, double* __restrict__ parts, int* __restrict__ count) {
+  const int part = blockIdx.x, h = blockIdx.y;
+  const int ch = blockIdx.z % n_chunks, bi = blockIdx.z / n_chunks;
+  const int n_parts = gridDim.x;
+  const int G = Hq / Hkv;
+  const int tid = threadIdx.x;
+  const int cgs = d / 8;
+  const int cg = tid % cgs, rl = tid / cgs, nrl = kScoreThreads / cgs;
+  const int r0 = part * kQsumRows;
+  const int r1 = r0 + kQsumRows < L ? r0 + kQsumRows : L;
+  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int g = 0; g < G; ++g) {
+    const T* qh = q + (((int64_t)bi * Hq + (int64_t)h * G + g) * q_cap + q_off +
+                       (int64_t)ch * L) * d + cg * 8;
+    for (int i = r0 + rl; i < r1; i += nrl) Load8<T>::add(qh + (int64_t)i * d, acc);
+  }
+  __shared__ double sm[kScoreThreads / 8][128];     // [row lane][column]
+  __shared__ double qsum[128];
+  __shared__ int last_sh;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) sm[rl][cg * 8 + j] = acc[j];
+  __syncthreads();
+  const int64_t prob = ((int64_t)bi * Hkv + h) * n_chunks + ch;
+  double* pp = parts + prob * n_parts * d;
+  if (tid < d) {
+    double t = 0.0;
+    for (int r = 0; r < nrl; ++r) t += sm[r][tid];
+    __hip_atomic_store(&pp[(int64_t)part * d + tid], t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  if (tid == 0) {
+    const int done = __hip_atomic_fetch_add(&count[prob], 1, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+    last_sh = done == n_parts - 1;
+    if (last_sh)   // ready for the next call
+      __hip_atomic_store(&count[prob], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!last_sh) return;
+  if (tid < d) {
+    double t = 0.0;
+    for (int p = 0; p < n_parts; ++p)
+      t += __hip_atomic_load(&pp[(int64_t)p * d + tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    qsum[tid] = t;
+  }
+  __syncthreads();
+  const int64_t t_last = q_pos + (int64_t)ch * L + L - 1;
+  const int64_t e = eligible_units(t_last, U, B, n_init, W);
+  const int wave = tid / 64, lane = tid % 64;
+  const float* rb = repr + ((int64_t)bi * Hkv + h) * U * d;
+  float* sb = scores + prob * U;
+  const int lpu = d / 8, upw = 64 / lpu;
+  const int sub = lane / lpu, cgl = lane % lpu;
+  double qv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) qv[j] = qsum[cgl * 8 + j];
+  for (int ub = wave * upw; ub < U; ub += (kScoreThreads / 64) * upw) {
+    const int u = ub + sub;
+    double t = 0.0;
+    if (u < U && u < e) {
+      const float4* rp = (const float4*)(rb + (int64_t)u * d + cgl * 8);
+      const float4 x = rp[0], y = rp[1];
+      t = fma((double)x.x, qv[0], t);
+      t = fma((double)x.y, qv[1], t);
+      t = fma((double)x.z, qv[2], t);
+      t = fma((double)x.w, qv[3], t);
+      t = fma((double)y.x, qv[4], t);
+      t = fma((double)y.y, qv[5], t);
+      t = fma((double)y.z, qv[6], t);
+      t = fma((double)y.w, qv[7], t);
+    }
+    t += dpp_f64<INFLLM_DPP_XOR1>(t);
+    t += dpp_f64<INFLLM_DPP_XOR2>(t);
+    t += dpp_f64<INFLLM_DPP_HALF_MIRROR>(t);
+    if (lpu == 16) t += dpp_f64<INFLLM_DPP_MIRROR>(t);
+    if (u < U && cgl == 0) sb[u] = u < e ? (float)t : -INFINITY;
+  }
+}
+
+static bool score_fused(const ScoreArgs& a) {
+  return score_num_parts(a.L, a.Hq / a.Hkv) > 0 && a.U <= kFusedMaxUnits;
+}
+
+static size_t score_counter_bytes(const ScoreArgs& a) {
+  return ((size_t)a.batch * a.Hkv * a.n_chunks * sizeof(int) + 255) & ~(size_t)255;
+}
+
+// [arrival counters, 256-byte aligned][fp64 partial query sums]; sized for
+// either path (the unit count is not known here)
 size_t score_workspace_bytes(const ScoreArgs& a) {
   const int parts = score_num_parts(a.L, a.Hq / a.Hkv);
-  return (size_t)parts * a.batch * a.Hkv * a.n_chunks * a.d * sizeof(double);
+  if (parts == 0) return 0;
+  return score_counter_bytes(a) + (size_t)parts * a.batch * a.Hkv * a.n_chunks * a.d * sizeof(double);
 }
 
 template <typename T>
 static hipError_t launch_score_t(const ScoreArgs& a, hipStream_t st) {
   const int parts = score_num_parts(a.L, a.Hq / a.Hkv);
-  double* pw = (double*)a.ws;
+  double* pw = parts > 0 ? (double*)((char*)a.ws + score_counter_bytes(a)) : nullptr;
+  if (score_fused(a)) {
+    k_score_fused<T><<<dim3(parts, a.Hkv, a.batch * a.n_chunks), kScoreThreads, 0, st>>>(
+        (const T*)a.q, a.q_cap, a.q_off, a.q_pos, a.L, a.Hq, a.Hkv, a.d, a.B, a.n_init, a.W,
+        a.repr, a.U, a.scores, a.n_chunks, pw, (int*)a.ws);
+    return hipGetLastError();
+  }
   if (parts > 0)
     k_chunk_qsum<T><<<dim3(parts, a.Hkv, a.batch * a.n_chunks), kScoreThreads, 0, st>>>(
         (const T*)a.q, a.q_cap, a.q_off, a.L, a.Hq, a.Hkv, a.d, a.n_chunks, pw);

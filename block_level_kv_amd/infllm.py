@@ -139,8 +139,9 @@ def infllm_workspace_size(cfg: infllm_config, call: int, batch: int, n: int = 0,
 def workspace(cfg: infllm_config, call: int, batch: int, n: int = 0, chunk_len: int = 0,
               n_chunks: int = 0, device="cuda") -> torch.Tensor | None:
     """A caller-owned, zero-filled workspace tensor of the size `call` needs
-    (None if 0).  Zero-filled because the attention workspace carries
-    split-K counters that must start at zero (and stay zero between calls)."""
+    (None if 0).  Zero-filled because the score and attention workspaces
+    carry arrival counters that must start at zero (and stay zero between
+    calls)."""
     size = infllm_workspace_size(cfg, call, batch, n, chunk_len, n_chunks)
     if size == 0:
         return None

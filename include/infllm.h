@@ -162,7 +162,10 @@ INFLLM_API infllm_status infllm_build_units(const infllm_config *cfg, int32_t ba
  *   unit_repr  [batch, H_kv, n_units, d] fp32 (from infllm_build_units)
  *   scores     out [batch, H_kv, n_chunks, n_units] fp32
  *   workspace  >= infllm_workspace_size(cfg, INFLLM_CALL_SCORE, batch, 0,
- *              chunk_len, n_chunks) (fp64 partial query sums; 0 for short chunks)
+ *              chunk_len, n_chunks): arrival counters and fp64 partial query
+ *              sums (0 bytes for short chunks).  It must be zero-filled before
+ *              its first use; every call leaves the counters at zero again,
+ *              and calls that share a workspace must not overlap in time.
  */
 INFLLM_API infllm_status infllm_score_units(const infllm_config *cfg, int32_t batch, const void *q,
                                  int64_t q_cap, int64_t q_off, int64_t q_pos, int32_t chunk_len,

@@ -340,3 +340,36 @@ def test_prefill_deterministic_and_sequential_equals_batched(orc):
                         sel[:, :, c:c + 1].contiguous())
     torch.cuda.synchronize()
     assert torch.equal(oc, o1[:, :, c * w.chunk:(c + 1) * w.chunk])
+
+
+@pytest.mark.parametrize("U_big", [False, True])
+def test_score_shared_workspace_repeatable(U_big):
+    """Long-chunk scoring on one shared workspace: repeated calls give
+    bitwise-equal scores and leave the arrival counters at zero.  U_big
+    takes the two-launch path (more units than one workgroup scores)."""
+    w = CASES["bf16_g4"]
+    cfg = cfg_of(w)
+    inp = synth.make_inputs(w)
+    q = inp["q"].cuda()
+    U = 2600 if U_big else 24
+    gen = torch.Generator().manual_seed(7)
+    repr_ = torch.randn((w.batch, w.n_kv_heads, U, w.head_dim), generator=gen).cuda()
+    n_chunks = 4
+    ws = F.workspace(cfg, F.INFLLM_CALL_SCORE, w.batch, 0, w.chunk, n_chunks)
+    outs = []
+    for _ in range(3):
+        sc = torch.empty((w.batch, w.n_kv_heads, n_chunks, U), dtype=torch.float32, device="cuda")
+        F.infllm_score_units(cfg, q, 0, 10 ** 6, w.chunk, n_chunks, repr_, sc, ws)
+        outs.append(sc)
+    torch.cuda.synchronize()
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
+    n_prob = w.batch * w.n_kv_heads * n_chunks
+    assert int(ws[:4 * n_prob].view(torch.int32).abs().sum().item()) == 0
+    # against a float64 evaluation of the definition
+    qs = inp["q"].double().view(w.batch, w.n_kv_heads, w.group, -1, w.head_dim)
+    for c in range(n_chunks):
+        qsum = qs[:, :, :, c * w.chunk:(c + 1) * w.chunk].sum(dim=(2, 3))
+        ref = torch.einsum("bhd,bhud->bhu", qsum, repr_.double().cpu())
+        got = outs[0][:, :, c].double().cpu()
+        fin = torch.isfinite(got)
+        assert torch.allclose(got[fin], ref[fin].float().double(), rtol=1e-6, atol=1e-6)
