@@ -5,9 +5,10 @@
 Default workload: a Llama-3-8B-shaped layer (32 query / 8 KV heads, head_dim
 128, bf16), 32,768-token context, chunked encoding in 512-query chunks
 processed one after another: one step = build the unit pool over the context
-(representative tokens, r_k = 4), then for each chunk score every unit,
-keep the top 16 per KV head and attend over 128 initial tokens + 16 units +
-a 4,096-token window.  Other workloads (--workload): the 128K and 1M decode
+(representative tokens, r_k = 4), then for each chunk score every unit and
+keep the top 16 per KV head, then for each chunk attend over 128 initial
+tokens + 16 units + a 4,096-token window (selection never depends on
+attention outputs, so the attention launches run back to back).  Other workloads (--workload): the 128K and 1M decode
 layers (unit pool built once beforehand; one step = 256 consecutive
 single-token decode steps) and the Mistral-7B 64K layer (one step = build +
 128 encoding chunks + 256 decode steps).
@@ -18,8 +19,8 @@ query attends, averaged over KV heads).  `roofline` is for the attention
 kernel of the dominant pass (chunked encoding if the workload has one):
 algorithmic work per launch -- MFMA flops 4*d*H_q*sum|A(t)| for chunks, or
 the K/V rows, queries and outputs it must move for decode -- divided by its
-average launch time, measured with HIP events on the launch stream inside
-the timed region.  `cpu_baseline` is the fp64 oracle on a bounded sample of
+average launch time: HIP events on the launch stream, inside the timed
+region, around each step's run of attention launches.  `cpu_baseline` is the fp64 oracle on a bounded sample of
 the same work on the host cores.
 """
 from __future__ import annotations
@@ -113,42 +114,49 @@ class Pipeline:
         F.infllm_build_units(self.cfg, self.inp["q"], self.inp["k"], self.w.n_ctx, self.rep_idx,
                              self.repr, self.build_ws)
 
-    def _select_attend(self, q, q_off, pos, L, sel, out, score_ws, attn_ws, events):
-        cfg, inp = self.cfg, self.inp
-        F.infllm_score_units(cfg, q, q_off, pos, L, 1, self.repr, self.scores, score_ws)
-        F.infllm_topk_units(cfg, self.scores, sel)
-        if events is not None:
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-        F.infllm_attend(cfg, q, q_off, pos, L, 1, inp["k"], inp["v"], sel, out, None, q_off,
-                        attn_ws)
-        if events is not None:
-            e1.record()
-            events.append((e0, e1))
+    def _select(self, q, q_off, pos, L, sel, score_ws):
+        F.infllm_score_units(self.cfg, q, q_off, pos, L, 1, self.repr, self.scores, score_ws)
+        F.infllm_topk_units(self.cfg, self.scores, sel)
 
-    def step(self, enc_events=None, dec_events=None, pass_events=None):
-        """One pass of the hot path; the event lists collect (start, end)
-        pairs around each attention call of each pass; pass_events gets one
-        event recorded between the encoding and the decode pass."""
-        w = self.w
+    def _attend(self, q, q_off, pos, L, sel, out, attn_ws):
+        F.infllm_attend(self.cfg, q, q_off, pos, L, 1, self.inp["k"], self.inp["v"], sel, out,
+                        None, q_off, attn_ws)
+
+    @staticmethod
+    def _mark(marks, key):
+        if marks is not None:
+            e = torch.cuda.Event(enable_timing=True)
+            e.record()
+            marks.setdefault(key, []).append(e)
+
+    def step(self, marks=None):
+        """One pass of the hot path.  Each pass first scores and selects units
+        for all of its query chunks (or decode positions), then runs all of
+        their attention launches back to back: selection depends only on the
+        built units, never on attention outputs.  With a dict, events are
+        recorded at the phase boundaries: 'enc_sel' / 'enc_end' around the
+        encoding attention launches, 'dec_sel' / 'dec_end' around the decode
+        ones."""
+        w, inp = self.w, self.inp
         if self.encode:
             self.build()
             for c in range(self.n_chunks):
                 t0 = c * w.chunk
-                self._select_attend(self.inp["q"], t0, t0, w.chunk, self.sel_enc[c], self.out_enc,
-                                    self.enc_score_ws, self.enc_attn_ws, enc_events)
-        if pass_events is not None:
-            e = torch.cuda.Event(enable_timing=True)
-            e.record()
-            pass_events.append(e)
+                self._select(inp["q"], t0, t0, w.chunk, self.sel_enc[c], self.enc_score_ws)
+            self._mark(marks, "enc_sel")
+            for c in range(self.n_chunks):
+                t0 = c * w.chunk
+                self._attend(inp["q"], t0, t0, w.chunk, self.sel_enc[c], self.out_enc,
+                             self.enc_attn_ws)
+            self._mark(marks, "enc_end")
         if self.decode:
             for s in range(w.decode_steps):
-                self._select_attend(self.inp["q_dec"], s, w.n_ctx + s, 1, self.sel_dec[s],
-                                    self.out_dec, self.dec_score_ws, self.dec_attn_ws, dec_events)
-        if pass_events is not None:
-            e = torch.cuda.Event(enable_timing=True)
-            e.record()
-            pass_events.append(e)
+                self._select(inp["q_dec"], s, w.n_ctx + s, 1, self.sel_dec[s], self.dec_score_ws)
+            self._mark(marks, "dec_sel")
+            for s in range(w.decode_steps):
+                self._attend(inp["q_dec"], s, w.n_ctx + s, 1, self.sel_dec[s], self.out_dec,
+                             self.dec_attn_ws)
+            self._mark(marks, "dec_end")
 
     def work(self):
         """Per pass: (attended KV tokens, attention flops, attention bytes)."""
@@ -256,10 +264,9 @@ def stored_traffic(kernel: str, workload: str):
         return None
 
 
-def roofline(w: synth.Workload, phase: str, work, events, steps: int) -> dict:
+def roofline(w: synth.Workload, phase: str, work, attn_ms: float, n_calls: int) -> dict:
+    """attn_ms: average duration of one attention launch, in ms."""
     tokens, flops, nbytes = work
-    n_calls = len(events) // steps
-    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in events]))
     if phase == "encode" and w.dtype == "bf16":
         achieved = flops / n_calls / (attn_ms * 1e-3) / 1e12
         r = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
@@ -277,7 +284,9 @@ def roofline(w: synth.Workload, phase: str, work, events, steps: int) -> dict:
     r["kernel"] = "infllm_attend (%s)" % kernel
     r["avg_launch_us"] = round(attn_ms * 1e3, 2)
     r["launches_per_step"] = n_calls
-    r["launch_timing"] = "HIP events around each launch, one step after the timed steps"
+    r["launch_timing"] = ("HIP events on the launch stream around each timed step's run of "
+                          "back-to-back attention launches, divided by the launch count "
+                          "(dispatch gaps between launches included)")
     return r
 
 
@@ -306,24 +315,20 @@ def main():
         pipe.step()
     torch.cuda.synchronize()
 
-    # The timed steps carry no per-launch events (each timing event costs the
-    # stream several microseconds); only the pass boundaries are marked.
-    pass_ev = []
+    # The timed steps carry events only at their phase boundaries; each
+    # event costs the stream a few microseconds, a few per step.
+    marks = {}
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for _ in range(args.steps):
-        pipe.step(None, None, pass_ev)
+        pipe.step(marks)
     end.record()
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / args.steps
-    # decode-pass time per step: between the two pass-boundary events of a step
-    ms_decode = float(np.mean([pass_ev[2 * i].elapsed_time(pass_ev[2 * i + 1])
-                               for i in range(args.steps)]))
-    # attention launch durations: one more step with events around each launch
-    enc_ev, dec_ev = [], []
-    pipe.step(enc_ev, dec_ev, None)
-    torch.cuda.synchronize()
+
+    def span_ms(a, b):
+        return float(np.mean([x.elapsed_time(y) for x, y in zip(marks[a], marks[b])]))
 
     work = pipe.work()
     tokens = sum(v[0] for v in work.values())
@@ -342,16 +347,22 @@ def main():
                    "chunk": w.chunk, "decode_steps": w.decode_steps, "block": w.block,
                    "n_init": w.n_init, "window": w.window, "rep_k": w.rep_k, "top_k": w.top_k,
                    "rep_mode": w.rep_mode, "attended_tokens_per_step": tokens},
-        "roofline": roofline(w, phase, work[phase], enc_ev if phase == "encode" else dec_ev, 1),
+        "roofline": (roofline(w, "encode", work["encode"],
+                              span_ms("enc_sel", "enc_end") / pipe.n_chunks, pipe.n_chunks)
+                     if phase == "encode" else
+                     roofline(w, "decode", work["decode"],
+                              span_ms("dec_sel", "dec_end") / w.decode_steps, w.decode_steps)),
     }
     if pipe.decode:
         # one decode step = score + top-k + attention for one token position
-        line["ms_per_decode_step"] = round((ms_decode if pipe.encode else ms_step) /
-                                           w.decode_steps, 5)
-        line["decode_tokens_per_s"] = round(work["decode"][0] / (
-            (ms_decode if pipe.encode else ms_step) * 1e-3), 1)
+        # the decode pass of a step: from the end of its encoding pass
+        ms_decode = span_ms("enc_end", "dec_end") if pipe.encode else ms_step
+        line["ms_per_decode_step"] = round(ms_decode / w.decode_steps, 5)
+        line["decode_tokens_per_s"] = round(work["decode"][0] / (ms_decode * 1e-3), 1)
         if pipe.encode:
-            line["decode_roofline"] = roofline(w, "decode", work["decode"], dec_ev, 1)
+            line["decode_roofline"] = roofline(w, "decode", work["decode"],
+                                               span_ms("dec_sel", "dec_end") / w.decode_steps,
+                                               w.decode_steps)
     if args.calibration_copy > 0:
         n = args.calibration_copy << 20
         src = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda")

@@ -299,53 +299,98 @@ __global__ __launch_bounds__(kRowsThreads) void k_attend_rows(AttendArgs a) {
     }
     __syncthreads();
     if (!last_sh) return;
-    // Merge every split's published rows (this one's included) in split
-    // order.  (max, sum) pairs are staged in LDS with one load per thread;
-    // each head's weights 2^(m_s - M) are formed once; output columns then
-    // sum their splits with independent loads.
-    float* sm_w = &sm_o[0][0][0];                  // reuse: [splits][G] weights
-    float* sm_sl = sm_w + kMaxSplits * G;          // [splits][G] sums
-    for (int idx = tid; idx < splits * G; idx += kRowsThreads) {
+    // Merge every split's published rows (this one's included).  Each
+    // thread's (max, sum) pairs and its output columns' first batch of split
+    // values are requested together: one memory round trip when the splits
+    // fit a batch.  The (max, sum) table is padded to kMaxSplits with
+    // (-inf, 0), so the weight pass and the weighted sums run without
+    // per-split branches (padding weights are 0 and padding loads return 0).
+    float* sm_w = &sm_o[0][0][0];                  // reuse: [kMaxSplits][G] weights
+    float* sm_sl = sm_w + kMaxSplits * G;          // [kMaxSplits][G] sums
+    constexpr int kMlPer = (kMaxSplits * G + kRowsThreads - 1) / kRowsThreads;
+    constexpr int kBatch = kOut <= 2 ? 32 : (kOut <= 64 ? 64 / kOut : 1);  // splits per batch
+    static_assert(kMaxSplits <= 64 && kMaxSplits % kBatch == 0, "one split per lane of wave 0");
+    const int64_t stride = (int64_t)a.batch * a.Hq * a.n_pos * D;   // between splits
+    float mlm[kMlPer], mll[kMlPer];
+#pragma unroll
+    for (int j = 0; j < kMlPer; ++j) {
+      const int idx = tid + j * kRowsThreads;
       const int s = idx / G, g = idx % G;
       const int64_t row = ((int64_t)s * a.batch * a.Hq + qh0 + g) * a.n_pos + pos;
-      sm_w[idx] = ld_dev(a.ws_ml + 2 * row);
-      sm_sl[idx] = ld_dev(a.ws_ml + 2 * row + 1);
+      mlm[j] = idx < splits * G ? ld_dev(a.ws_ml + 2 * row) : -INFINITY;
+      mll[j] = idx < splits * G ? ld_dev(a.ws_ml + 2 * row + 1) : 0.f;
     }
-    __syncthreads();
-    __shared__ float sm_M[G], sm_L[G];
-    if (tid < G) {
-      float M = -INFINITY;
-      for (int s = 0; s < splits; ++s) M = fmaxf(M, sm_w[s * G + tid]);
-      float Ls = 0.f;
-      for (int s = 0; s < splits; ++s) {
-        const float ms = sm_w[s * G + tid];
-        const float w = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-        sm_w[s * G + tid] = w;
-        Ls = fmaf(sm_sl[s * G + tid], w, Ls);
+    // Output columns through a buffer resource that ends at the last
+    // split: loads of splits beyond it return 0, so a batch is issued
+    // without branches (the workspace of a split-K launch stays far below
+    // 4 GiB, so byte offsets fit 32 bits).
+    const __amdgpu_buffer_rsrc_t ro = dev_rsrc(a.ws_o, (uint32_t)(splits * stride * 4));
+    float vb[kOut][kBatch];
+    auto load_batch = [&](int s0) {
+#pragma unroll
+      for (int i = 0; i < kOut; ++i) {
+        const int o = tid + i * kRowsThreads;
+        const int g = (o < G * D ? o : 0) / D, col = o % D;
+        const uint32_t base = (uint32_t)(((qh0 + g) * a.n_pos + pos) * D + col);
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j)
+          vb[i][j] = ld1_dev(ro, (base + (uint32_t)((s0 + j) * stride)) * 4u);
       }
-      sm_M[tid] = M;
-      sm_L[tid] = Ls;
+    };
+    load_batch(0);
+#pragma unroll
+    for (int j = 0; j < kMlPer; ++j) {
+      const int idx = tid + j * kRowsThreads;
+      if (idx < kMaxSplits * G) {
+        sm_w[idx] = mlm[j];
+        sm_sl[idx] = mll[j];
+      }
     }
     __syncthreads();
+    // wave 0, one split per lane: M = max_s m_s, w_s = 2^(m_s - M),
+    // L = sum_s l_s w_s (fixed reduction tree)
+    __shared__ float sm_M[G], sm_L[G];
+    if (tid < 64) {
+      float mv[G], lv[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        mv[g] = sm_w[lane * G + g];
+        lv[g] = sm_sl[lane * G + g];
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float M = wave_max_f32(mv[g]);
+        const float w = mv[g] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mv[g] - M);
+        const float Ls = wave_sum_f32(lv[g] * w);
+        sm_w[lane * G + g] = w;
+        if (lane == 0) {
+          sm_M[g] = M;
+          sm_L[g] = Ls;
+        }
+      }
+    }
+    __syncthreads();
+    float Os[kOut];
+#pragma unroll
+    for (int i = 0; i < kOut; ++i) Os[i] = 0.f;
+    for (int s0 = 0; s0 < splits; s0 += kBatch) {
+      if (s0 > 0) load_batch(s0);
+#pragma unroll
+      for (int i = 0; i < kOut; ++i) {
+        const int o = tid + i * kRowsThreads;
+        const int g = (o < G * D ? o : 0) / D;
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) Os[i] = fmaf(vb[i][j], sm_w[(s0 + j) * G + g], Os[i]);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < kOut; ++i) {
       const int o = tid + i * kRowsThreads;
       if (o >= G * D) continue;
-      const int g = o / D, col = o % D;
-      const float* base = a.ws_o + ((qh0 + g) * a.n_pos + pos) * D + col;
-      const int64_t stride = (int64_t)a.batch * a.Hq * a.n_pos * D;   // between splits
-      float Os = 0.f;
-      for (int s0 = 0; s0 < splits; s0 += 8) {
-        float v[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = s0 + j < splits ? ld_dev(base + (s0 + j) * stride) : 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (s0 + j < splits) Os = fmaf(v[j], sm_w[(s0 + j) * G + g], Os);
-      }
+      const int g = o / D;
       Mv[i] = sm_M[g];
       Lv[i] = sm_L[g];
-      Ov[i] = Os;
+      Ov[i] = Os[i];
     }
   }
 #pragma unroll

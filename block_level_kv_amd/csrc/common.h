@@ -82,6 +82,28 @@ __device__ __forceinline__ double wave_sum_f64(double x) {
   return x;
 }
 
+// Max / sum over the wave: DPP within each 16-lane row, then the four row
+// results read into scalars (a fixed order: deterministic sums).
+__device__ __forceinline__ float wave_max_f32(float x) {
+  x = fmaxf(x, dpp_f32<INFLLM_DPP_XOR1>(x));
+  x = fmaxf(x, dpp_f32<INFLLM_DPP_XOR2>(x));
+  x = fmaxf(x, dpp_f32<INFLLM_DPP_HALF_MIRROR>(x));
+  x = fmaxf(x, dpp_f32<INFLLM_DPP_MIRROR>(x));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+__device__ __forceinline__ float wave_sum_f32(float x) {
+  x = row16_sum(x);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
 // Sum over the wave in a fixed order without LDS round trips: DPP sums
 // within each 16-lane row, then the four row sums read into scalars.
 __device__ __forceinline__ double readlane_f64(double x, int l) {
@@ -122,6 +144,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t dev_rsrc(const float* base, ui
 }
 __device__ __forceinline__ void st4_dev(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kCachePolicySc1);
+}
+__device__ __forceinline__ float ld1_dev(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  // past the resource's range the hardware returns 0 (no fault)
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kCachePolicySc1));
 }
 __device__ __forceinline__ f32x4 ld4_dev(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCachePolicySc1));
