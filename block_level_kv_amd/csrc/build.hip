@@ -49,37 +49,6 @@ template <> struct Cols8<float> {
 
 // Raw 8-column piece of a row: loaded first, widened later, so that a batch
 // of loads is in flight before any of them is waited on.
-template <typename T> struct Raw8;
-template <> struct Raw8<bf16_t> {
-  u32x4 w;
-  __device__ __forceinline__ void load(const bf16_t* p) { w = *(const u32x4*)p; }
-  __device__ __forceinline__ void add(double* acc) const {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[2 * i] += (double)__uint_as_float(w[i] << 16);
-      acc[2 * i + 1] += (double)__uint_as_float(w[i] & 0xffff0000u);
-    }
-  }
-  __device__ __forceinline__ double get(int i) const {
-    return (double)__uint_as_float(i & 1 ? w[i / 2] & 0xffff0000u : w[i / 2] << 16);
-  }
-};
-template <> struct Raw8<float> {
-  float4 x, y;
-  __device__ __forceinline__ void load(const float* p) {
-    x = ((const float4*)p)[0];
-    y = ((const float4*)p)[1];
-  }
-  __device__ __forceinline__ void add(double* acc) const {
-    acc[0] += x.x; acc[1] += x.y; acc[2] += x.z; acc[3] += x.w;
-    acc[4] += y.x; acc[5] += y.y; acc[6] += y.z; acc[7] += y.w;
-  }
-  __device__ __forceinline__ double get(int i) const {
-    const float v[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
-    return (double)v[i];
-  }
-};
-
 // S[b][h][j][c] = sum over rows of block j (clipped to n_ctx) and over the
 // group's query heads of q[.][c], fp64.  grid (n_blocks, H_kv, batch), 256
 // threads: thread -> (8-column group, row phase), 16-byte loads.

@@ -42,6 +42,38 @@ __host__ __device__ __forceinline__ int64_t eligible_units(int64_t t_last, int64
   return e < U ? e : U;
 }
 
+// Eight consecutive columns of a row, raw bits, widened to fp64 on use.
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16_t> {
+  u32x4 w;
+  __device__ __forceinline__ void load(const bf16_t* p) { w = *(const u32x4*)p; }
+  __device__ __forceinline__ void add(double* acc) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] += (double)__uint_as_float(w[i] << 16);
+      acc[2 * i + 1] += (double)__uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ __forceinline__ double get(int i) const {
+    return (double)__uint_as_float(i & 1 ? w[i / 2] & 0xffff0000u : w[i / 2] << 16);
+  }
+};
+template <> struct Raw8<float> {
+  float4 x, y;
+  __device__ __forceinline__ void load(const float* p) {
+    x = ((const float4*)p)[0];
+    y = ((const float4*)p)[1];
+  }
+  __device__ __forceinline__ void add(double* acc) const {
+    acc[0] += x.x; acc[1] += x.y; acc[2] += x.z; acc[3] += x.w;
+    acc[4] += y.x; acc[5] += y.y; acc[6] += y.z; acc[7] += y.w;
+  }
+  __device__ __forceinline__ double get(int i) const {
+    const float v[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+    return (double)v[i];
+  }
+};
+
 // ------------------------------------------------------------ lane shuffles
 // DPP controls (gfx9 encoding): quad_perm [1,0,3,2], [2,3,0,1]; row_half_mirror;
 // row_mirror.  Applied in this order they all-reduce a 16-lane row.
@@ -139,8 +171,8 @@ __device__ __forceinline__ float ld_dev(const float* p) {
 // 16-byte device-scope accesses through a raw buffer resource (cache policy
 // sc1); `bytes` bounds the range, checked by the hardware.
 constexpr int kCachePolicySc1 = 16;
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t dev_rsrc(const float* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, (int)bytes, 0x00020000);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dev_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
 __device__ __forceinline__ void st4_dev(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kCachePolicySc1);
@@ -148,6 +180,9 @@ __device__ __forceinline__ void st4_dev(__amdgpu_buffer_rsrc_t r, uint32_t off, 
 __device__ __forceinline__ float ld1_dev(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   // past the resource's range the hardware returns 0 (no fault)
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kCachePolicySc1));
+}
+__device__ __forceinline__ double ld1_dev_f64(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCachePolicySc1));
 }
 __device__ __forceinline__ f32x4 ld4_dev(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCachePolicySc1));

@@ -5,14 +5,18 @@
 // sum and the dot products accumulate in fp64, so the ranking that follows
 // is decided on scores accurate far below the near-tie margin.
 //
-// Long chunks (unit count above kFusedMaxUnits; smaller counts take the
-// one-launch k_score_fused below): k_chunk_qsum spreads the query sum over many workgroups
-// (16-byte loads, kQsumRows query rows each) and writes fp64 partial sums;
-// k_score_units adds them in a fixed order, so results do not depend on
-// scheduling.  Short chunks (decode: one query x G heads) skip the first
-// pass and sum their few rows directly.  k_score_units then scores a slice
-// of up to kUnitsPerWG units, one wave per unit at a time with a coalesced
-// read of its fp32 representation.
+// Long chunks: the query sum is spread over workgroups of kQsumRows rows
+// each (16-byte loads, all G heads), whose fp64 partial sums are added in
+// part order, so results do not depend on scheduling.  Up to
+// kFusedMaxUnits units this is one launch (k_score_fused: the last
+// workgroup of a chunk to arrive adds the parts and scores every unit);
+// beyond, k_chunk_qsum writes the parts and k_score_units adds them.
+// Short chunks (decode: one query x G heads) skip the parts and sum their
+// few rows directly in k_score_units, which scores a slice of kUnitsPerWG
+// units.  Each unit is read as one coalesced fp32 row by D/8 lanes.  Every
+// phase issues all of its loads before it uses any of them (clamped
+// indices or bounds-checked buffer loads instead of branches), so a phase
+// costs one memory round trip.
 #include "common.h"
 #include "kernels.h"
 
@@ -22,94 +26,176 @@ constexpr int kScoreThreads = 256;
 constexpr int kUnitsPerWG = 64;
 constexpr int kQsumRows = 32;        // chunk rows per partial sum
 constexpr int kDirectRows = 64;      // L*G up to this: sum in the scoring kernel
-
-template <typename T> struct Load8;
-template <> struct Load8<bf16_t> {
-  static __device__ __forceinline__ void add(const bf16_t* p, double* acc) {
-    const u32x4 w = *(const u32x4*)p;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[2 * i] += (double)__uint_as_float(w[i] << 16);
-      acc[2 * i + 1] += (double)__uint_as_float(w[i] & 0xffff0000u);
-    }
-  }
-};
-template <> struct Load8<float> {
-  static __device__ __forceinline__ void add(const float* p, double* acc) {
-    const float4 a = ((const float4*)p)[0], b = ((const float4*)p)[1];
-    acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
-    acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
-  }
-};
+constexpr int kFusedMaxUnits = 2048;
+constexpr int kPartBatch = 16;       // partial sums requested together
+constexpr int kBatchUnits = 256;     // units whose rows the fused kernel requests together
 
 int score_num_parts(int L, int G) {
   return L * G <= kDirectRows ? 0 : (L + kQsumRows - 1) / kQsumRows;
 }
 
-// Partial query sums: part p of chunk c covers rows [p*kQsumRows, ...) of
-// the chunk, all G heads.  grid (parts, H_kv, batch * n_chunks).
-template <typename T>
-__global__ __launch_bounds__(kScoreThreads) void k_chunk_qsum(
-    const T* __restrict__ q, int64_t q_cap, int64_t q_off, int L, int Hq, int Hkv, int d,
-    int n_chunks, double* __restrict__ parts) {
-  const int part = blockIdx.x, h = blockIdx.y;
-  const int ch = blockIdx.z % n_chunks, bi = blockIdx.z / n_chunks;
-  const int G = Hq / Hkv;
-  const int cgs = d / 8;                            // 8-column groups per row
-  const int cg = threadIdx.x % cgs, rl = threadIdx.x / cgs, nrl = kScoreThreads / cgs;
-  const int r0 = part * kQsumRows;
-  const int r1 = r0 + kQsumRows < L ? r0 + kQsumRows : L;
+// Column sums of rows [r0, r1) of one chunk over the G heads of a KV head,
+// fp64: thread (8-column group, row lane) adds its rows head by head, then
+// the row lanes are added in order through LDS.  qb points at row 0 of the
+// chunk in the first head; heads are hs elements apart.  Threads tid < D
+// return column tid's sum.
+template <typename T, int G, int D>
+__device__ __forceinline__ double rows_colsum(const T* __restrict__ qb, int64_t hs, int r0, int r1,
+                                              double (*sm)[D]) {
+  constexpr int kCgs = D / 8, kNrl = kScoreThreads / kCgs;
+  constexpr int kIt = (kQsumRows + kNrl - 1) / kNrl;
+  const int tid = threadIdx.x, cg = tid % kCgs, rl = tid / kCgs;
+  Raw8<T> raw[G][kIt];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int i = r0 + rl + it * kNrl;
+      raw[g][it].load(qb + g * hs + (int64_t)(i < r1 ? i : r1 - 1) * D + cg * 8);
+    }
   double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int g = 0; g < G; ++g) {
-    const T* qh = q + (((int64_t)bi * Hq + (int64_t)h * G + g) * q_cap + q_off +
-                       (int64_t)ch * L) * d + cg * 8;
-    for (int i = r0 + rl; i < r1; i += nrl) Load8<T>::add(qh + (int64_t)i * d, acc);
-  }
-  __shared__ double sm[kScoreThreads / 8][128];     // [row lane][column]
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int it = 0; it < kIt; ++it)
+      if (r0 + rl + it * kNrl < r1) raw[g][it].add(acc);
 #pragma unroll
   for (int j = 0; j < 8; ++j) sm[rl][cg * 8 + j] = acc[j];
   __syncthreads();
-  if (threadIdx.x < d) {
-    double s = 0.0;
-    for (int r = 0; r < nrl; ++r) s += sm[r][threadIdx.x];
+  double t = 0.0;
+  if (tid < D) {
+#pragma unroll
+    for (int r = 0; r < kNrl; ++r) t += sm[r][tid];
+  }
+  return t;
+}
+
+// Sum of the n_parts partial sums of column c (part p at pp[p*D + c]), in
+// part order.  Loads past the last part return 0 and leave the sum as is.
+template <int D>
+__device__ __forceinline__ double sum_parts(const double* pp, int n_parts, int c) {
+  const __amdgpu_buffer_rsrc_t r = dev_rsrc(pp, (uint32_t)((int64_t)n_parts * D * 8));
+  double t = 0.0;
+  for (int p0 = 0; p0 < n_parts; p0 += kPartBatch) {
+    double v[kPartBatch];
+#pragma unroll
+    for (int j = 0; j < kPartBatch; ++j) v[j] = ld1_dev_f64(r, (uint32_t)(((p0 + j) * D + c) * 8));
+#pragma unroll
+    for (int j = 0; j < kPartBatch; ++j) t += v[j];
+  }
+  return t;
+}
+
+// Unit rows for scoring: D/8 lanes per unit, 8 columns each; slot s of
+// wave w holds units base + s*(4*upw) + w*upw + lane/(D/8).  Indices past
+// the last unit are clamped (their scores are not stored).
+template <int D, int kSlots>
+struct UnitRows {
+  static constexpr int kLpu = D / 8, kUpw = 64 / kLpu, kPerSlot = (kScoreThreads / 64) * kUpw;
+  Raw8<float> x[kSlots];
+  __device__ __forceinline__ static int unit(int base, int s) {
+    const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+    return base + s * kPerSlot + wave * kUpw + lane / kLpu;
+  }
+  __device__ __forceinline__ void load(const float* rb, int U, int base) {
+    const int cg = threadIdx.x % 64 % kLpu;
+#pragma unroll
+    for (int s = 0; s < kSlots; ++s) {
+      const int u = unit(base, s);
+      x[s].load(rb + (int64_t)(u < U ? u : U - 1) * D + cg * 8);
+    }
+  }
+  // score[u] = qsum . repr[u] (fp64), -inf for u >= e; units in [base, u1)
+  __device__ __forceinline__ void score(const double* qv, int base, int u1, int64_t e,
+                                        float* sb) const {
+    const int cg = threadIdx.x % 64 % kLpu;
+#pragma unroll
+    for (int s = 0; s < kSlots; ++s) {
+      const int u = unit(base, s);
+      double t = 0.0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) t = fma(x[s].get(j), qv[j], t);
+      t += dpp_f64<INFLLM_DPP_XOR1>(t);
+      t += dpp_f64<INFLLM_DPP_XOR2>(t);
+      t += dpp_f64<INFLLM_DPP_HALF_MIRROR>(t);
+      if (kLpu == 16) t += dpp_f64<INFLLM_DPP_MIRROR>(t);
+      if (u < u1 && cg == 0) sb[u] = u < e ? (float)t : -INFINITY;
+    }
+  }
+};
+
+// Partial query sums: part p of chunk c covers rows [p*kQsumRows, ...) of
+// the chunk, all G heads.  grid (parts, H_kv, batch * n_chunks).
+template <typename T, int G, int D>
+__global__ __launch_bounds__(kScoreThreads) void k_chunk_qsum(
+    const T* __restrict__ q, int64_t q_cap, int64_t q_off, int L, int Hq, int Hkv, int n_chunks,
+    double* __restrict__ parts) {
+  const int part = blockIdx.x, h = blockIdx.y;
+  const int ch = blockIdx.z % n_chunks, bi = blockIdx.z / n_chunks;
+  __shared__ double sm[kScoreThreads / (D / 8)][D];
+  const T* qb = q + (((int64_t)bi * Hq + (int64_t)h * G) * q_cap + q_off + (int64_t)ch * L) * D;
+  const int r0 = part * kQsumRows;
+  const int r1 = r0 + kQsumRows < L ? r0 + kQsumRows : L;
+  const double t = rows_colsum<T, G, D>(qb, q_cap * D, r0, r1, sm);
+  if (threadIdx.x < D) {
     const int n_parts = gridDim.x;
-    parts[((((int64_t)bi * Hkv + h) * n_chunks + ch) * n_parts + part) * d + threadIdx.x] = s;
+    parts[((((int64_t)bi * Hkv + h) * n_chunks + ch) * n_parts + part) * D + threadIdx.x] = t;
   }
 }
 
-template <typename T>
+// Scores of a slice of kUnitsPerWG units.  grid (slices, n_chunks * H_kv, batch).
+template <typename T, int G, int D>
 __global__ __launch_bounds__(kScoreThreads) void k_score_units(
     const T* __restrict__ q, int64_t q_cap, int64_t q_off, int64_t q_pos, int L, int Hq, int Hkv,
-    int d, int B, int n_init, int W, const float* __restrict__ repr, int U,
-    float* __restrict__ scores, int n_chunks, const double* __restrict__ parts, int n_parts) {
+    int B, int n_init, int W, const float* __restrict__ repr, int U, float* __restrict__ scores,
+    int n_chunks, const double* __restrict__ parts, int n_parts) {
+  using Rows = UnitRows<D, kUnitsPerWG / UnitRows<D, 1>::kPerSlot>;
   const int slice = blockIdx.x;
   const int ch = blockIdx.y % n_chunks, h = blockIdx.y / n_chunks, bi = blockIdx.z;
-  const int G = Hq / Hkv;
   const int tid = threadIdx.x;
   __shared__ double part_sm[kScoreThreads];
-  __shared__ double qsum[128];
+  __shared__ double qsum[D];
+  const int u0 = slice * kUnitsPerWG;
+  const int u1 = u0 + kUnitsPerWG < U ? u0 + kUnitsPerWG : U;
+  const float* rb = repr + ((int64_t)bi * Hkv + h) * U * D;
+  Rows rows;
+  rows.load(rb, U, u0);              // in flight while the query sum forms
 
   if (n_parts > 0) {
-    if (tid < d) {
-      const double* pp = parts + (((int64_t)bi * Hkv + h) * n_chunks + ch) * n_parts * d + tid;
-      double s = 0.0;
-      for (int p = 0; p < n_parts; ++p) s += pp[(int64_t)p * d];
-      qsum[tid] = s;
-    }
+    const double* pp = parts + (((int64_t)bi * Hkv + h) * n_chunks + ch) * n_parts * D;
+    const double t = sum_parts<D>(pp, n_parts, tid % D);
+    if (tid < D) qsum[tid] = t;
     __syncthreads();
   } else {
-    // few rows: thread -> (column, row phase)
-    const int c = tid % d, phase = tid / d, nph = kScoreThreads / d;
-    double acc = 0.0;
-    const int64_t row0 = q_off + (int64_t)ch * L;
-    for (int g = 0; g < G; ++g) {
-      const T* qh = q + (((int64_t)bi * Hq + (int64_t)h * G + g) * q_cap + row0) * d + c;
-      for (int i = phase; i < L; i += nph) acc += (double)to_f32(qh[(int64_t)i * d]);
+    // few rows (L*G <= kDirectRows): thread -> (column, row phase)
+    constexpr int kNph = kScoreThreads / D;
+    constexpr int kIt = (kDirectRows / G + kNph - 1) / kNph;
+    const int c = tid % D, phase = tid / D;
+    const T* qb = q + (((int64_t)bi * Hq + (int64_t)h * G) * q_cap + q_off + (int64_t)ch * L) * D + c;
+    const int n_it = (L + kNph - 1) / kNph;     // row iterations the chunk needs
+    T v[G][kIt];
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      if (it >= n_it) break;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int i = phase + it * kNph;
+        v[g][it] = qb[g * q_cap * D + (int64_t)(i < L ? i : L - 1) * D];
+      }
     }
+    double acc = 0.0;
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int it = 0; it < kIt; ++it) {
+        if (it >= n_it) break;
+        if (phase + it * kNph < L) acc += (double)to_f32(v[g][it]);
+      }
     part_sm[tid] = acc;
     __syncthreads();
     if (phase == 0) {
-      for (int p = 1; p < nph; ++p) acc += part_sm[p * d + c];
+#pragma unroll
+      for (int p = 1; p < kNph; ++p) acc += part_sm[p * D + c];
       qsum[c] = acc;
     }
     __syncthreads();
@@ -117,38 +203,11 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_units(
 
   const int64_t t_last = q_pos + (int64_t)ch * L + L - 1;
   const int64_t e = eligible_units(t_last, U, B, n_init, W);
-  const int wave = tid / 64, lane = tid % 64;
-  const int u0 = slice * kUnitsPerWG;
-  const int u1 = u0 + kUnitsPerWG < U ? u0 + kUnitsPerWG : U;
-  const float* rb = repr + ((int64_t)bi * Hkv + h) * U * d;
-  float* sb = scores + (((int64_t)bi * Hkv + h) * n_chunks + ch) * U;
-  // d/8 lanes per unit (a DPP row or half row), 8 columns each
-  const int lpu = d / 8, upw = 64 / lpu;
-  const int sub = lane / lpu, cg = lane % lpu;
+  const int cg = tid % 64 % (D / 8);
   double qv[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) qv[j] = qsum[cg * 8 + j];
-  for (int ub = u0 + wave * upw; ub < u1; ub += (kScoreThreads / 64) * upw) {
-    const int u = ub + sub;
-    double s = 0.0;
-    if (u < u1 && u < e) {
-      const float4* rp = (const float4*)(rb + (int64_t)u * d + cg * 8);
-      const float4 x = rp[0], y = rp[1];
-      s = fma((double)x.x, qv[0], s);
-      s = fma((double)x.y, qv[1], s);
-      s = fma((double)x.z, qv[2], s);
-      s = fma((double)x.w, qv[3], s);
-      s = fma((double)y.x, qv[4], s);
-      s = fma((double)y.y, qv[5], s);
-      s = fma((double)y.z, qv[6], s);
-      s = fma((double)y.w, qv[7], s);
-    }
-    s += dpp_f64<INFLLM_DPP_XOR1>(s);
-    s += dpp_f64<INFLLM_DPP_XOR2>(s);
-    s += dpp_f64<INFLLM_DPP_HALF_MIRROR>(s);
-    if (lpu == 16) s += dpp_f64<INFLLM_DPP_MIRROR>(s);
-    if (u < u1 && cg == 0) sb[u] = u < e ? (float)s : -INFINITY;
-  }
+  rows.score(qv, u0, u1, e, scores + (((int64_t)bi * Hkv + h) * n_chunks + ch) * U);
 }
 
 // Long chunks with a moderate unit count, in one launch: each workgroup
@@ -156,43 +215,30 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_units(
 // the partial sum with device-scope stores; the last workgroup of a
 // (sequence, KV head, chunk) to arrive -- found with a counter in the
 // workspace, which it resets -- adds the partial sums in part order (so the
-// result does not depend on arrival order) and scores every unit.
+// result does not depend on arrival order) and scores every unit.  Its
+// part loads and its first batch of unit rows are requested together.
 // grid (parts, H_kv, batch * n_chunks).
-constexpr int kFusedMaxUnits = 2048;
-
-template <typename T>
+template <typename T, int G, int D>
 __global__ __launch_bounds__(kScoreThreads) void k_score_fused(
     const T* __restrict__ q, int64_t q_cap, int64_t q_off, int64_t q_pos, int L, int Hq, int Hkv,
-    int d, int B, int n_init, int W, const float* __restrict__ repr, int U,
-    float* __restrict__ scores, int n_chunks, double* __restrict__ parts, int* __restrict__ count) {
+    int B, int n_init, int W, const float* __restrict__ repr, int U, float* __restrict__ scores,
+    int n_chunks, double* __restrict__ parts, int* __restrict__ count) {
+  using Rows = UnitRows<D, kBatchUnits / UnitRows<D, 1>::kPerSlot>;
   const int part = blockIdx.x, h = blockIdx.y;
   const int ch = blockIdx.z % n_chunks, bi = blockIdx.z / n_chunks;
   const int n_parts = gridDim.x;
-  const int G = Hq / Hkv;
   const int tid = threadIdx.x;
-  const int cgs = d / 8;
-  const int cg = tid % cgs, rl = tid / cgs, nrl = kScoreThreads / cgs;
+  __shared__ double sm[kScoreThreads / (D / 8)][D];
+  __shared__ double qsum[D];
+  __shared__ int last_sh;
+  const T* qb = q + (((int64_t)bi * Hq + (int64_t)h * G) * q_cap + q_off + (int64_t)ch * L) * D;
   const int r0 = part * kQsumRows;
   const int r1 = r0 + kQsumRows < L ? r0 + kQsumRows : L;
-  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int g = 0; g < G; ++g) {
-    const T* qh = q + (((int64_t)bi * Hq + (int64_t)h * G + g) * q_cap + q_off +
-                       (int64_t)ch * L) * d + cg * 8;
-    for (int i = r0 + rl; i < r1; i += nrl) Load8<T>::add(qh + (int64_t)i * d, acc);
-  }
-  __shared__ double sm[kScoreThreads / 8][128];     // [row lane][column]
-  __shared__ double qsum[128];
-  __shared__ int last_sh;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) sm[rl][cg * 8 + j] = acc[j];
-  __syncthreads();
+  const double t = rows_colsum<T, G, D>(qb, q_cap * D, r0, r1, sm);
   const int64_t prob = ((int64_t)bi * Hkv + h) * n_chunks + ch;
-  double* pp = parts + prob * n_parts * d;
-  if (tid < d) {
-    double t = 0.0;
-    for (int r = 0; r < nrl; ++r) t += sm[r][tid];
-    __hip_atomic_store(&pp[(int64_t)part * d + tid], t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  double* pp = parts + prob * n_parts * D;
+  if (tid < D)
+    __hip_atomic_store(&pp[(int64_t)part * D + tid], t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
   if (tid == 0) {
@@ -204,43 +250,22 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_fused(
   }
   __syncthreads();
   if (!last_sh) return;
-  if (tid < d) {
-    double t = 0.0;
-    for (int p = 0; p < n_parts; ++p)
-      t += __hip_atomic_load(&pp[(int64_t)p * d + tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    qsum[tid] = t;
-  }
+  const float* rb = repr + ((int64_t)bi * Hkv + h) * U * D;
+  Rows rows;
+  rows.load(rb, U, 0);
+  const double qs = sum_parts<D>(pp, n_parts, tid % D);
+  if (tid < D) qsum[tid] = qs;
   __syncthreads();
   const int64_t t_last = q_pos + (int64_t)ch * L + L - 1;
   const int64_t e = eligible_units(t_last, U, B, n_init, W);
-  const int wave = tid / 64, lane = tid % 64;
-  const float* rb = repr + ((int64_t)bi * Hkv + h) * U * d;
-  float* sb = scores + prob * U;
-  const int lpu = d / 8, upw = 64 / lpu;
-  const int sub = lane / lpu, cgl = lane % lpu;
+  const int cg = tid % 64 % (D / 8);
   double qv[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) qv[j] = qsum[cgl * 8 + j];
-  for (int ub = wave * upw; ub < U; ub += (kScoreThreads / 64) * upw) {
-    const int u = ub + sub;
-    double t = 0.0;
-    if (u < U && u < e) {
-      const float4* rp = (const float4*)(rb + (int64_t)u * d + cgl * 8);
-      const float4 x = rp[0], y = rp[1];
-      t = fma((double)x.x, qv[0], t);
-      t = fma((double)x.y, qv[1], t);
-      t = fma((double)x.z, qv[2], t);
-      t = fma((double)x.w, qv[3], t);
-      t = fma((double)y.x, qv[4], t);
-      t = fma((double)y.y, qv[5], t);
-      t = fma((double)y.z, qv[6], t);
-      t = fma((double)y.w, qv[7], t);
-    }
-    t += dpp_f64<INFLLM_DPP_XOR1>(t);
-    t += dpp_f64<INFLLM_DPP_XOR2>(t);
-    t += dpp_f64<INFLLM_DPP_HALF_MIRROR>(t);
-    if (lpu == 16) t += dpp_f64<INFLLM_DPP_MIRROR>(t);
-    if (u < U && cgl == 0) sb[u] = u < e ? (float)t : -INFINITY;
+  for (int j = 0; j < 8; ++j) qv[j] = qsum[cg * 8 + j];
+  float* sb = scores + prob * U;
+  for (int base = 0; base < U; base += kBatchUnits) {
+    if (base > 0) rows.load(rb, U, base);
+    rows.score(qv, base, U, e, sb);
   }
 }
 
@@ -260,24 +285,40 @@ size_t score_workspace_bytes(const ScoreArgs& a) {
   return score_counter_bytes(a) + (size_t)parts * a.batch * a.Hkv * a.n_chunks * a.d * sizeof(double);
 }
 
-template <typename T>
-static hipError_t launch_score_t(const ScoreArgs& a, hipStream_t st) {
-  const int parts = score_num_parts(a.L, a.Hq / a.Hkv);
+template <typename T, int G, int D>
+static hipError_t launch_score_tgd(const ScoreArgs& a, hipStream_t st) {
+  const int parts = score_num_parts(a.L, G);
   double* pw = parts > 0 ? (double*)((char*)a.ws + score_counter_bytes(a)) : nullptr;
   if (score_fused(a)) {
-    k_score_fused<T><<<dim3(parts, a.Hkv, a.batch * a.n_chunks), kScoreThreads, 0, st>>>(
-        (const T*)a.q, a.q_cap, a.q_off, a.q_pos, a.L, a.Hq, a.Hkv, a.d, a.B, a.n_init, a.W,
-        a.repr, a.U, a.scores, a.n_chunks, pw, (int*)a.ws);
+    k_score_fused<T, G, D><<<dim3(parts, a.Hkv, a.batch * a.n_chunks), kScoreThreads, 0, st>>>(
+        (const T*)a.q, a.q_cap, a.q_off, a.q_pos, a.L, a.Hq, a.Hkv, a.B, a.n_init, a.W, a.repr,
+        a.U, a.scores, a.n_chunks, pw, (int*)a.ws);
     return hipGetLastError();
   }
   if (parts > 0)
-    k_chunk_qsum<T><<<dim3(parts, a.Hkv, a.batch * a.n_chunks), kScoreThreads, 0, st>>>(
-        (const T*)a.q, a.q_cap, a.q_off, a.L, a.Hq, a.Hkv, a.d, a.n_chunks, pw);
+    k_chunk_qsum<T, G, D><<<dim3(parts, a.Hkv, a.batch * a.n_chunks), kScoreThreads, 0, st>>>(
+        (const T*)a.q, a.q_cap, a.q_off, a.L, a.Hq, a.Hkv, a.n_chunks, pw);
   dim3 grid((a.U + kUnitsPerWG - 1) / kUnitsPerWG, a.n_chunks * a.Hkv, a.batch);
-  k_score_units<T><<<grid, kScoreThreads, 0, st>>>(
-      (const T*)a.q, a.q_cap, a.q_off, a.q_pos, a.L, a.Hq, a.Hkv, a.d, a.B, a.n_init, a.W, a.repr,
-      a.U, a.scores, a.n_chunks, pw, parts);
+  k_score_units<T, G, D><<<grid, kScoreThreads, 0, st>>>(
+      (const T*)a.q, a.q_cap, a.q_off, a.q_pos, a.L, a.Hq, a.Hkv, a.B, a.n_init, a.W, a.repr, a.U,
+      a.scores, a.n_chunks, pw, parts);
   return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_score_td(const ScoreArgs& a, hipStream_t st) {
+  switch (a.Hq / a.Hkv) {
+    case 1: return launch_score_tgd<T, 1, D>(a, st);
+    case 2: return launch_score_tgd<T, 2, D>(a, st);
+    case 4: return launch_score_tgd<T, 4, D>(a, st);
+    case 8: return launch_score_tgd<T, 8, D>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+static hipError_t launch_score_t(const ScoreArgs& a, hipStream_t st) {
+  return a.d == 128 ? launch_score_td<T, 128>(a, st) : launch_score_td<T, 64>(a, st);
 }
 
 hipError_t launch_score(const ScoreArgs& a, hipStream_t st) {

@@ -108,7 +108,9 @@ def test_score_and_topk_parity(orc, data, name):
 
 @pytest.mark.parametrize("U,k_m,ties", [(1, 4, False), (7, 3, True), (255, 16, True),
                                         (1023, 32, False), (8191, 32, True), (8191, 256, False),
-                                        (40, 64, False), (300, 1, True)])
+                                        (40, 64, False), (300, 1, True), (2048, 32, True),
+                                        (2049, 5, True), (16000, 32, True), (20000, 8, False),
+                                        (64, 64, False), (4096, 256, True)])
 def test_topk_exact(orc, U, k_m, ties):
     gen = torch.Generator().manual_seed(U * 131 + k_m)
     nc = 3
