@@ -5,10 +5,11 @@
 Default workload: a Llama-3-8B-shaped layer (32 query / 8 KV heads, head_dim
 128, bf16), 32,768-token context, chunked encoding in 512-query chunks
 processed one after another: one step = build the unit pool over the context
-(representative tokens, r_k = 4), then for each chunk score every unit and
-keep the top 16 per KV head, then for each chunk attend over 128 initial
-tokens + 16 units + a 4,096-token window (selection never depends on
-attention outputs, so the attention launches run back to back).  Other workloads (--workload): the 128K and 1M decode
+(representative tokens, r_k = 4), then for every chunk score every unit and
+keep the top 16 per KV head, then for every chunk attend over 128 initial
+tokens + 16 units + a 4,096-token window.  Selection never depends on
+attention outputs, so each of the three stages covers all 64 chunks in one
+call.  Other workloads (--workload): the 128K and 1M decode
 layers (unit pool built once beforehand; one step = 256 consecutive
 single-token decode steps) and the Mistral-7B 64K layer (one step = build +
 128 encoding chunks + 256 decode steps).
@@ -20,7 +21,7 @@ kernel of the dominant pass (chunked encoding if the workload has one):
 algorithmic work per launch -- MFMA flops 4*d*H_q*sum|A(t)| for chunks, or
 the K/V rows, queries and outputs it must move for decode -- divided by its
 average launch time: HIP events on the launch stream, inside the timed
-region, around each step's run of attention launches.  `cpu_baseline` is the fp64 oracle on a bounded sample of
+region, around each step's attention launches.  `cpu_baseline` is the fp64 oracle on a bounded sample of
 the same work on the host cores.
 """
 from __future__ import annotations
@@ -97,11 +98,13 @@ class Pipeline:
         self.build_ws = F.workspace(cfg, F.INFLLM_CALL_BUILD, b, w.n_ctx, device=dev)
         self.scores = torch.empty((b, Hkv, 1, self.U), dtype=torch.float32, device=dev)
         if self.encode:
-            self.n_chunks = w.n_ctx // w.chunk
-            self.enc_score_ws = F.workspace(cfg, F.INFLLM_CALL_SCORE, b, 0, w.chunk, 1, device=dev)
-            self.enc_attn_ws = F.workspace(cfg, F.INFLLM_CALL_ATTEND, b, 0, w.chunk, 1, device=dev)
-            self.sel_enc = torch.empty((self.n_chunks, b, Hkv, 1, w.top_k), dtype=torch.int32,
-                                       device=dev)
+            nc = self.n_chunks = w.n_ctx // w.chunk
+            self.enc_scores = torch.empty((b, Hkv, nc, self.U), dtype=torch.float32, device=dev)
+            self.enc_score_ws = F.workspace(cfg, F.INFLLM_CALL_SCORE, b, 0, w.chunk, nc, device=dev)
+            self.enc_attn_ws = F.workspace(cfg, F.INFLLM_CALL_ATTEND, b, 0, w.chunk, nc, device=dev)
+            self.enc_sel = torch.empty((b, Hkv, nc, w.top_k), dtype=torch.int32, device=dev)
+            # per-chunk view [chunk, b, H_kv, 1, k_m]
+            self.sel_enc = self.enc_sel.permute(2, 0, 1, 3).unsqueeze(3)
             self.out_enc = torch.empty_like(self.inp["q"])
         if self.decode:
             self.dec_score_ws = F.workspace(cfg, F.INFLLM_CALL_SCORE, b, 0, 1, 1, device=dev)
@@ -130,24 +133,26 @@ class Pipeline:
             marks.setdefault(key, []).append(e)
 
     def step(self, marks=None):
-        """One pass of the hot path.  Each pass first scores and selects units
-        for all of its query chunks (or decode positions), then runs all of
-        their attention launches back to back: selection depends only on the
-        built units, never on attention outputs.  With a dict, events are
-        recorded at the phase boundaries: 'enc_sel' / 'enc_end' around the
-        encoding attention launches, 'dec_sel' / 'dec_end' around the decode
-        ones."""
-        w, inp = self.w, self.inp
+        """One pass of the hot path.  Selection depends only on the built
+        units, never on attention outputs, so each pass first scores and
+        selects units for all of its query chunks (or decode positions) and
+        then attends: the encoding pass with one call per kind covering all
+        chunks, the decode pass one call per position (each decode step
+        follows the previous one).  With a dict, events are recorded at the
+        phase boundaries: 'enc_sel' / 'enc_end' around the encoding
+        attention launch, 'dec_sel' / 'dec_end' around the decode ones."""
+        w, inp, cfg = self.w, self.inp, self.cfg
         if self.encode:
+            # the whole encoding pass: every chunk in one call of each kind
+            # (chunk c covers queries [c*chunk, (c+1)*chunk), positions equal)
             self.build()
-            for c in range(self.n_chunks):
-                t0 = c * w.chunk
-                self._select(inp["q"], t0, t0, w.chunk, self.sel_enc[c], self.enc_score_ws)
+            nc = self.n_chunks
+            F.infllm_score_units(cfg, inp["q"], 0, 0, w.chunk, nc, self.repr, self.enc_scores,
+                                 self.enc_score_ws)
+            F.infllm_topk_units(cfg, self.enc_scores, self.enc_sel)
             self._mark(marks, "enc_sel")
-            for c in range(self.n_chunks):
-                t0 = c * w.chunk
-                self._attend(inp["q"], t0, t0, w.chunk, self.sel_enc[c], self.out_enc,
-                             self.enc_attn_ws)
+            F.infllm_attend(cfg, inp["q"], 0, 0, w.chunk, nc, inp["k"], inp["v"], self.enc_sel,
+                            self.out_enc, None, 0, self.enc_attn_ws)
             self._mark(marks, "enc_end")
         if self.decode:
             for s in range(w.decode_steps):
@@ -284,9 +289,9 @@ def roofline(w: synth.Workload, phase: str, work, attn_ms: float, n_calls: int) 
     r["kernel"] = "infllm_attend (%s)" % kernel
     r["avg_launch_us"] = round(attn_ms * 1e3, 2)
     r["launches_per_step"] = n_calls
-    r["launch_timing"] = ("HIP events on the launch stream around each timed step's run of "
-                          "back-to-back attention launches, divided by the launch count "
-                          "(dispatch gaps between launches included)")
+    r["launch_timing"] = ("HIP events on the launch stream around each timed step's "
+                          "attention launches (back to back), divided by their count; "
+                          "dispatch gaps between launches included")
     return r
 
 
@@ -347,8 +352,7 @@ def main():
                    "chunk": w.chunk, "decode_steps": w.decode_steps, "block": w.block,
                    "n_init": w.n_init, "window": w.window, "rep_k": w.rep_k, "top_k": w.top_k,
                    "rep_mode": w.rep_mode, "attended_tokens_per_step": tokens},
-        "roofline": (roofline(w, "encode", work["encode"],
-                              span_ms("enc_sel", "enc_end") / pipe.n_chunks, pipe.n_chunks)
+        "roofline": (roofline(w, "encode", work["encode"], span_ms("enc_sel", "enc_end"), 1)
                      if phase == "encode" else
                      roofline(w, "decode", work["decode"],
                               span_ms("dec_sel", "dec_end") / w.decode_steps, w.decode_steps)),

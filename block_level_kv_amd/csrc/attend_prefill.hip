@@ -118,7 +118,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_prefill(AttendArgs a, Pr
   const int h = gidx % a.Hkv, bi = gidx / a.Hkv;
   const int split = item % geo.splits;
   item /= geo.splits;
-  const int qt = item % geo.n_qtiles, ch = item / geo.n_qtiles;
+  // chunks in reverse order: later chunks have the longer tile lists, and
+  // the short ones dispatched last fill the tail of the launch
+  const int qt = item % geo.n_qtiles, ch = a.n_chunks - 1 - item / geo.n_qtiles;
 
   const int q_first = qt * TQ;                          // within the chunk
   const int nq = a.L - q_first < TQ ? a.L - q_first : TQ;

@@ -253,7 +253,7 @@ infllm_status infllm_attend(const infllm_config* cfg, int32_t batch, const void*
   if (batch < 1 || chunk_len < 1 || n_chunks < 1 || q_off < 0 || q_pos < 0 || out_off < 0)
     return INFLLM_ERR_INVALID_ARG;
   const int64_t n_pos = (int64_t)chunk_len * n_chunks;
-  if (n_pos > 65535 || (int64_t)batch * cfg->n_kv_heads > 65535) return INFLLM_ERR_UNSUPPORTED;
+  if ((int64_t)batch * cfg->n_kv_heads > 65535) return INFLLM_ERR_UNSUPPORTED;
   if (q_off + n_pos > q_cap || q_pos + n_pos > kv_cap || out_off + n_pos > out_cap)
     return INFLLM_ERR_INVALID_ARG;
   if (q_pos + n_pos > ((int64_t)1 << 31) - 128) return INFLLM_ERR_UNSUPPORTED;
@@ -264,6 +264,7 @@ infllm_status infllm_attend(const infllm_config* cfg, int32_t batch, const void*
   bool mfma;
   int splits;
   attend_plan(a, &mfma, &splits);
+  if (!mfma && n_pos > 65535) return INFLLM_ERR_UNSUPPORTED;   // one grid row per position
   const size_t need = attend_ws_bytes(a);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return INFLLM_ERR_WORKSPACE;

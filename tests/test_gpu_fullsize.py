@@ -1,6 +1,6 @@
 """GPU parity at the workloads' full sizes, in the launch configuration
-bench.py times (bench.Pipeline: one score/top-k/attend call per chunk or
-decode step).  The oracle checks what it can afford one by one:
+bench.py times (bench.Pipeline: one score/top-k/attend call covering all
+chunks of the encoding pass, one per decode step).  The oracle checks what it can afford one by one:
   - the unit build on contiguous samples of units (start, middle and end of
     the context, where the representative window is truncated);
   - every chunk's and every decode step's selection, re-derived from the
