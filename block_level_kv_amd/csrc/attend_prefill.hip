@@ -50,6 +50,14 @@ constexpr int kWaves = kThreads / 64;
 enum : int { kTileInit = 0, kTileUnit = 1, kTileWin = 2, kTileMask = 4 };
 
 constexpr float kLog2eP = 1.4426950408889634f;
+constexpr float kSlack = 8.f;         // weights below 2^8 between rescales
+
+// max of three floats in one instruction (no NaN reaches it)
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float d;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
 // s_waitcnt vmcnt(4 (kStages - 2)) lgkmcnt(0): the loads of the next tile
 // have landed and no LDS read of this wave is still in flight
 constexpr int kWaitRing = 0x0078;
@@ -322,22 +330,27 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_prefill(AttendArgs a, Pr
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+    for (int r = 0; r < 16; ++r) mx = max3(mx, s0[r], s1[r]);
     {
       // the other half of the wave holds the row's other keys
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                        false, false);
       mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     }
-    const float m_new = fmaxf(m_run, mx * c);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    if (__any(m_new != m_run)) {   // rescale only when some row's max moved
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    // m_run is a reference maximum, not necessarily the running one: the
+    // accumulators are rescaled only when some row's tile maximum exceeds
+    // its reference by more than kSlack (log2 units), so weights stay
+    // below 2^kSlack and most tiles skip the rescale
+    const float mxs = mx * c;
+    if (__any(mxs > m_run + kSlack)) {
+      const float m_new = fmaxf(m_run, mxs);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
       l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) acc[dt] *= alpha;
+      m_run = m_new;
     }
-    m_run = m_new;
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
     float psum = 0.f;
     bf16x8 pb[4];
 #pragma unroll
