@@ -91,9 +91,18 @@ def _ptr(t: torch.Tensor | None) -> int | None:
     return None if t is None else t.data_ptr()
 
 
-def _stream(stream) -> int | None:
+# the raw current-stream handle of a device, without building a Stream
+# object (a few microseconds per call otherwise)
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(stream, t: torch.Tensor) -> int | None:
+    """The stream to launch on: `stream` if given, else the current stream of
+    tensor t's device."""
     if stream is None:
-        return torch.cuda.current_stream().cuda_stream
+        if _raw_stream is not None:
+            return _raw_stream(t.get_device())
+        return torch.cuda.current_stream(t.device).cuda_stream
     if isinstance(stream, torch.cuda.Stream):
         return stream.cuda_stream
     return int(stream)
@@ -106,7 +115,7 @@ def _dtype_of(cfg: infllm_config) -> torch.dtype:
 def _check(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int) -> None:
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a tensor" % name)
-    if t.dtype != dtype or t.dim() != ndim or not t.is_contiguous() or t.device.type != "cuda":
+    if t.dtype != dtype or t.dim() != ndim or not t.is_cuda or not t.is_contiguous():
         raise ValueError("%s must be a contiguous %dD %s CUDA/HIP tensor, got %s %s %s" %
                          (name, ndim, dtype, t.dtype, tuple(t.shape), t.device))
 
@@ -165,7 +174,7 @@ def infllm_build_units(cfg, q, k, n_ctx: int, rep_idx, unit_repr, ws=None, strea
     wp, wb = _ws(ws)
     _raise("infllm_build_units", lib().infllm_build_units(
         ctypes.byref(cfg), batch, _ptr(q), q_cap, k.data_ptr(), k.shape[2], n_ctx,
-        _ptr(rep_idx), unit_repr.data_ptr(), wp, wb, _stream(stream)))
+        _ptr(rep_idx), unit_repr.data_ptr(), wp, wb, _stream(stream, k)))
 
 
 def infllm_score_units(cfg, q, q_off: int, q_pos: int, chunk_len: int, n_chunks: int, unit_repr,
@@ -179,7 +188,7 @@ def infllm_score_units(cfg, q, q_off: int, q_pos: int, chunk_len: int, n_chunks:
     wp, wb = _ws(ws)
     _raise("infllm_score_units", lib().infllm_score_units(
         ctypes.byref(cfg), batch, q.data_ptr(), q.shape[2], q_off, q_pos, chunk_len, n_chunks,
-        unit_repr.data_ptr(), U, scores.data_ptr(), wp, wb, _stream(stream)))
+        unit_repr.data_ptr(), U, scores.data_ptr(), wp, wb, _stream(stream, q)))
 
 
 def infllm_topk_units(cfg, scores, sel, ws=None, stream=None) -> None:
@@ -191,7 +200,7 @@ def infllm_topk_units(cfg, scores, sel, ws=None, stream=None) -> None:
     wp, wb = _ws(ws)
     _raise("infllm_topk_units", lib().infllm_topk_units(
         ctypes.byref(cfg), batch, n_chunks, scores.data_ptr(), U, sel.data_ptr(), wp, wb,
-        _stream(stream)))
+        _stream(stream, scores)))
 
 
 def infllm_attend(cfg, q, q_off: int, q_pos: int, chunk_len: int, n_chunks: int, k, v, sel, out,
@@ -211,4 +220,4 @@ def infllm_attend(cfg, q, q_off: int, q_pos: int, chunk_len: int, n_chunks: int,
     _raise("infllm_attend", lib().infllm_attend(
         ctypes.byref(cfg), q.shape[0], q.data_ptr(), q.shape[2], q_off, q_pos, chunk_len, n_chunks,
         k.data_ptr(), v.data_ptr(), k.shape[2], _ptr(sel), out.data_ptr(), _ptr(lse),
-        out.shape[2], out_off, wp, wb, _stream(stream)))
+        out.shape[2], out_off, wp, wb, _stream(stream, q)))
