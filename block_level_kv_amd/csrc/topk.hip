@@ -17,16 +17,20 @@
 // mbcnt over the keep ballot, column by column, so the kept indices are
 // written in ascending order without a scan.
 //
-// U <= 64*32: one wave per problem (four problems per workgroup).  Larger
-// U: one workgroup of four waves per problem, one barrier per round; keys
-// in registers up to 4*64*64 units, beyond that re-read every round.
+// Up to 256 units (or up to 2,048 with many problems): one wave per
+// problem, four problems per workgroup, the bit-by-bit search.  Otherwise
+// one workgroup of 16 waves per problem and a radix search (8 bits per
+// pass, LDS histograms); keys in registers up to 16*64*32 units, beyond
+// that re-read every pass.
 #include "common.h"
 #include "kernels.h"
 
 namespace infllm {
 
-constexpr int kTopkThreads = 256;
+constexpr int kTopkThreads = 256;                  // wave variant: 4 problems per workgroup
 constexpr int kTopkWaves = kTopkThreads / 64;
+constexpr int kBlockThreads = 1024;                // workgroup variant: 16 waves per problem
+constexpr int kBlockWaves = kBlockThreads / 64;
 
 __device__ __forceinline__ uint32_t score_key(float f) {
   return f > -INFINITY ? orderable(f) : 0u;
@@ -39,22 +43,23 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
                                         __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    const uint32_t y = (uint32_t)__shfl_xor((int)x, m);
-    x = y > x ? y : x;
-  }
-  return x;
+// max / min over the wave: DPP within 16-lane rows, then the four rows'
+// results through scalar registers
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_ext_u32(uint32_t x) {
+  auto pick = [](uint32_t a, uint32_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
+  x = pick(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, INFLLM_DPP_XOR1, 0xF, 0xF, true));
+  x = pick(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, INFLLM_DPP_XOR2, 0xF, 0xF, true));
+  x = pick(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, INFLLM_DPP_HALF_MIRROR, 0xF, 0xF, true));
+  x = pick(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, INFLLM_DPP_MIRROR, 0xF, 0xF, true));
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+  return pick(pick(r0, r1), pick(r2, r3));
 }
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    const uint32_t y = (uint32_t)__shfl_xor((int)x, m);
-    x = y < x ? y : x;
-  }
-  return x;
-}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) { return wave_ext_u32<true>(x); }
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) { return wave_ext_u32<false>(x); }
 
 // The keys of one wave's index range [base, base + 64*VPT) (clipped to U).
 // VPT == 0: keys are re-read from memory at every use.
@@ -200,20 +205,83 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_wave(const float* __restr
   for (int m = K + lane; m < k_m; m += 64) out[m] = -1;
 }
 
+// Radix form of the same search, for a workgroup: 8 bits of the threshold
+// per pass instead of one.  Among the keys that share the bits above `top`
+// with the threshold found so far, an LDS histogram of the next 8 bits
+// gives the digit that holds the krem-th largest key; krem then becomes its
+// rank inside that digit.  Three barriers per pass, at most four passes
+// (fewer after skipping the common leading bits of the largest and
+// smallest finite key).
+constexpr int kRadixBins = 256;
+template <typename Keys>
+__device__ __forceinline__ uint32_t radix_tau(const Keys& keys, int K, int n_valid, uint32_t hi,
+                                              uint32_t lo, int* hist, int* pick) {
+  if (K == n_valid || hi == lo) return lo;       // every finite key is kept, or all equal
+  const int tid = threadIdx.x, lane = tid % 64;
+  int top = 31 - __builtin_clz(hi ^ lo);         // highest bit where keys can differ
+  uint32_t prefix = top == 31 ? 0u : hi & ~((2u << top) - 1u);
+  int krem = K;
+  while (top >= 0) {
+    const int shift = top >= 7 ? top - 7 : 0;
+    const uint32_t dmask = (2u << (top - shift)) - 1u;
+    for (int i = tid; i < kRadixBins; i += blockDim.x) hist[i] = 0;
+    __syncthreads();
+    for (int i = 0; i < keys.n_cols(); ++i) {
+      const uint32_t x = keys.key(i);
+      const bool in = x != 0u && (top == 31 || (x >> (top + 1)) == (prefix >> (top + 1)));
+      if (in) atomicAdd(&hist[(x >> shift) & dmask], 1);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      // lane l holds bins 4l .. 4l+3; keys above a bin = later bins
+      int h[4], own = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        h[j] = hist[4 * lane + j];
+        own += h[j];
+      }
+      int suf = own;   // inclusive suffix sum over lanes lane .. 63
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) {
+        const int y = __shfl_down(suf, m);
+        if (lane + m < 64) suf += y;
+      }
+      int above = suf - own;   // keys in the bins of later lanes
+#pragma unroll
+      for (int j = 3; j >= 0; --j) {
+        if (above < krem && above + h[j] >= krem) {
+          pick[0] = 4 * lane + j;
+          pick[1] = above;
+        }
+        above += h[j];
+      }
+    }
+    __syncthreads();
+    const int d = pick[0];
+    krem -= pick[1];
+    prefix |= (uint32_t)d << shift;
+    top = shift - 1;
+  }
+  return prefix;
+}
+
 // -------------------------------------------------------- workgroup variant
 // Wave w owns indices [w*R, (w+1)*R), R a multiple of 64.  Per-wave values
-// meet in LDS, double-buffered: one barrier per exchange.
+// meet in LDS, double-buffered: one barrier per exchange; the threshold
+// comes from the radix search.
 template <int VPT>
-__global__ __launch_bounds__(kTopkThreads) void k_topk_block(const float* __restrict__ scores,
+__global__ __launch_bounds__(kBlockThreads) void k_topk_block(const float* __restrict__ scores,
                                                              int U, int k_m,
                                                              int32_t* __restrict__ sel) {
   const int64_t prob = blockIdx.x;
   int32_t* out = sel + prob * k_m;
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
-  const int R = ((U + kTopkWaves - 1) / kTopkWaves + 63) / 64 * 64;
+  const int R = ((U + kBlockWaves - 1) / kBlockWaves + 63) / 64 * 64;
   const int b0 = wave * R < U ? wave * R : U;
   const int b1 = b0 + R < U ? b0 + R : U;
-  __shared__ uint32_t xch[2][3][kTopkWaves];
+  __shared__ uint32_t xch[2][3][kBlockWaves];
+  __shared__ int hist[kRadixBins];
+  __shared__ int pick[2];
   int phase = 0;
   // all-reduce of one value per wave (sum, max or min)
   auto exchange = [&](uint32_t v, int slot) {
@@ -237,30 +305,14 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_block(const float* __rest
   int n_valid = 0;
   uint32_t hi = 0u, lo = 0xffffffffu;
 #pragma unroll
-  for (int w = 0; w < kTopkWaves; ++w) {
+  for (int w = 0; w < kBlockWaves; ++w) {
     n_valid += (int)got(0, w);
     hi = got(1, w) > hi ? got(1, w) : hi;
     lo = got(2, w) < lo ? got(2, w) : lo;
   }
   const int K = k_m < n_valid ? k_m : n_valid;
   if (K > 0) {
-    auto sum = [&](int c) {
-      exchange((uint32_t)c, 0);
-      sync();
-      int t = 0;
-#pragma unroll
-      for (int w = 0; w < kTopkWaves; ++w) t += (int)got(0, w);
-      return t;
-    };
-    auto min_all = [&](uint32_t m) {
-      exchange(m, 0);
-      sync();
-      uint32_t t = 0xffffffffu;
-#pragma unroll
-      for (int w = 0; w < kTopkWaves; ++w) t = got(0, w) < t ? got(0, w) : t;
-      return t;
-    };
-    const uint32_t tau = find_tau(keys, K, n_valid, hi, lo, sum, min_all);
+    const uint32_t tau = radix_tau(keys, K, n_valid, hi, lo, hist, pick);
     int n_gt, n_eq;
     keys.split(tau, n_gt, n_eq);
     exchange((uint32_t)n_gt, 0);
@@ -268,11 +320,11 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_block(const float* __rest
     sync();
     int gt_all = 0;
 #pragma unroll
-    for (int w = 0; w < kTopkWaves; ++w) gt_all += (int)got(0, w);
+    for (int w = 0; w < kBlockWaves; ++w) gt_all += (int)got(0, w);
     const int rem = K - gt_all;                // ties kept, lowest indices first
     int slot = 0, tie_rank = 0;
 #pragma unroll
-    for (int w = 0; w < kTopkWaves; ++w) {
+    for (int w = 0; w < kBlockWaves; ++w) {
       if (w >= wave) break;
       const int eq_w = (int)got(1, w);
       const int kept_eq = rem - tie_rank < 0 ? 0 : (rem - tie_rank < eq_w ? rem - tie_rank : eq_w);
@@ -281,14 +333,16 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_block(const float* __rest
     }
     keys.emit(tau, rem, tie_rank, slot, out);
   }
-  for (int m = K + tid; m < k_m; m += kTopkThreads) out[m] = -1;
+  for (int m = K + tid; m < k_m; m += kBlockThreads) out[m] = -1;
 }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   const int64_t problems = (int64_t)a.batch * a.Hkv * a.n_chunks;
   if (problems <= 0 || a.k_m <= 0) return hipSuccess;
   const int cols = (a.U + 63) / 64;
-  if (cols <= 32) {
+  // few columns: a wave per problem; more: a workgroup of 16 waves (each
+  // threshold round then costs one ballot column or a few per wave)
+  if (cols <= 4 || (cols <= 32 && problems >= 1024)) {
     const dim3 wgrid((unsigned)((problems + kTopkWaves - 1) / kTopkWaves));
     if (cols <= 4)
       k_topk_wave<4><<<wgrid, kTopkThreads, 0, st>>>(a.scores, problems, a.U, a.k_m, a.sel);
@@ -299,11 +353,11 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
     return hipGetLastError();
   }
   const dim3 grid((unsigned)problems);
-  const int wcols = (cols + kTopkWaves - 1) / kTopkWaves;   // columns per wave
-  if (wcols <= 16) k_topk_block<16><<<grid, kTopkThreads, 0, st>>>(a.scores, a.U, a.k_m, a.sel);
-  else if (wcols <= 32) k_topk_block<32><<<grid, kTopkThreads, 0, st>>>(a.scores, a.U, a.k_m, a.sel);
-  else if (wcols <= 64) k_topk_block<64><<<grid, kTopkThreads, 0, st>>>(a.scores, a.U, a.k_m, a.sel);
-  else k_topk_block<0><<<grid, kTopkThreads, 0, st>>>(a.scores, a.U, a.k_m, a.sel);
+  const int wcols = (cols + kBlockWaves - 1) / kBlockWaves;   // columns per wave
+  if (wcols <= 2) k_topk_block<2><<<grid, kBlockThreads, 0, st>>>(a.scores, a.U, a.k_m, a.sel);
+  else if (wcols <= 8) k_topk_block<8><<<grid, kBlockThreads, 0, st>>>(a.scores, a.U, a.k_m, a.sel);
+  else if (wcols <= 32) k_topk_block<32><<<grid, kBlockThreads, 0, st>>>(a.scores, a.U, a.k_m, a.sel);
+  else k_topk_block<0><<<grid, kBlockThreads, 0, st>>>(a.scores, a.U, a.k_m, a.sel);
   return hipGetLastError();
 }
 

@@ -110,10 +110,12 @@ def test_score_and_topk_parity(orc, data, name):
                                         (1023, 32, False), (8191, 32, True), (8191, 256, False),
                                         (40, 64, False), (300, 1, True), (2048, 32, True),
                                         (2049, 5, True), (16000, 32, True), (20000, 8, False),
-                                        (64, 64, False), (4096, 256, True)])
+                                        (64, 64, False), (4096, 256, True), (40000, 16, True),
+                                        (1500, 32, True), (600, 8, False)])
 def test_topk_exact(orc, U, k_m, ties):
     gen = torch.Generator().manual_seed(U * 131 + k_m)
-    nc = 3
+    # 1500 and 600 units: enough problems (2 x 2 x 256) for the one-wave variant
+    nc = 256 if U in (1500, 600) else 3
     if ties:
         s = torch.randint(-6, 6, (2, 2, nc, U), generator=gen).float() * 0.5
     else:
