@@ -192,30 +192,35 @@ __global__ __launch_bounds__(64 * kRepWaves) void k_rep_select(
     }
   }
   // starting sums F(lo), F(e_lo): block prefix + the in-block rows (the
-  // block prefix holds every head of the group: only slot 0 takes it)
+  // block prefix holds every head of the group: only slot 0 takes it).
+  // F(n_ctx - 1) is the prefix past the last block.  In-block rows are
+  // added in batches whose loads are all in flight together.
   double fp[8], fe[8];
   {
     const int64_t e = lo + W < last ? lo + W : last;
-    const int64_t be = e / B;
+    const bool e_end = e == last;
+    const int64_t be = e_end ? n_blocks : e / B;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       fp[i] = slot == 0 ? bp[j * d + i] : 0.0;
       fe[i] = slot == 0 ? bp[be * d + i] : 0.0;
     }
+    auto add_rows = [&](int64_t r0, int64_t r1, double* acc) {   // rows r0 .. r1
+      for (int64_t i0 = r0; i0 <= r1; i0 += kPass1Batch) {
+        Raw8<T> r[kPass1Batch][HPL];
 #pragma unroll
-    for (int x = 0; x < HPL; ++x) {
-      if (!hv[x]) continue;
-      for (int64_t i = j * B; i <= lo; ++i) {
-        Raw8<T> r;
-        r.load(qh[x] + i * d);
-        r.add(fp);
+        for (int y = 0; y < kPass1Batch; ++y)
+#pragma unroll
+          for (int x = 0; x < HPL; ++x) r[y][x].load(qh[x] + (i0 + y <= r1 ? i0 + y : r1) * d);
+#pragma unroll
+        for (int y = 0; y < kPass1Batch; ++y)
+#pragma unroll
+          for (int x = 0; x < HPL; ++x)
+            if (hv[x] && i0 + y <= r1) r[y][x].add(acc);
       }
-      for (int64_t i = be * B; i <= e; ++i) {
-        Raw8<T> r;
-        r.load(qh[x] + i * d);
-        r.add(fe);
-      }
-    }
+    };
+    add_rows(j * B, lo, fp);
+    if (!e_end) add_rows(be * B, e, fe);
   }
   __syncthreads();
   for (int w2 = 0; w2 < wave; ++w2)
@@ -278,18 +283,31 @@ __global__ __launch_bounds__(64 * kRepWaves) void k_rep_select(
   __syncthreads();
   const int64_t out_row = ((int64_t)bi * Hkv + h) * U + u;
   int32_t* ri = rep_idx + out_row * r_k;
+  __shared__ int chosen[kMaxBlock];     // kept key offsets, ascending
   for (int a = c; a < nk; a += blockDim.x) {
     if (picked[a]) {
       int at = 0;
       for (int b2 = 0; b2 < a; ++b2) at += picked[b2];
       ri[at] = (int32_t)(lo + a);
+      chosen[at] = a;
     }
   }
   for (int s = nk + c; s < r_k; s += blockDim.x) ri[s] = -1;  // fewer keys than r_k
+  __syncthreads();
+  // the representation: kept keys summed in ascending position, their rows
+  // requested together
+  const int n_kept = nk < r_k ? nk : r_k;
   if (c < d) {
     double acc = 0.0;
-    for (int a = 0; a < nk; ++a)
-      if (picked[a]) acc += (double)to_f32(kb[(lo + a) * d + c]);
+    for (int a0 = 0; a0 < n_kept; a0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int y = 0; y < 8; ++y)
+        v[y] = to_f32(kb[(lo + chosen[a0 + y < n_kept ? a0 + y : n_kept - 1]) * d + c]);
+#pragma unroll
+      for (int y = 0; y < 8; ++y)
+        if (a0 + y < n_kept) acc += (double)v[y];
+    }
     unit_repr[out_row * d + c] = (float)acc;
   }
 }

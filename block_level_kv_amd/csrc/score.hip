@@ -28,7 +28,7 @@ constexpr int kQsumRows = 32;        // chunk rows per partial sum
 constexpr int kDirectRows = 64;      // L*G up to this: sum in the scoring kernel
 constexpr int kFusedMaxUnits = 2048;
 constexpr int kPartBatch = 16;       // partial sums requested together
-constexpr int kBatchUnits = 256;     // units whose rows the fused kernel requests together
+constexpr int kBatchUnits = 64;      // units whose rows the fused kernel requests together
 
 int score_num_parts(int L, int G) {
   return L * G <= kDirectRows ? 0 : (L + kQsumRows - 1) / kQsumRows;
