@@ -10,9 +10,12 @@ keep the top 16 per KV head, then for every chunk attend over 128 initial
 tokens + 16 units + a 4,096-token window.  Selection never depends on
 attention outputs, so each of the three stages covers all 64 chunks in one
 call.  Other workloads (--workload): the 128K and 1M decode
-layers (unit pool built once beforehand; one step = 256 consecutive
-single-token decode steps) and the Mistral-7B 64K layer (one step = build +
-128 encoding chunks + 256 decode steps).
+layers (unit pools built once beforehand; one step = 256 consecutive
+single-token decode steps, rotating over 4 layers' K/V and unit pools as a
+model's layers follow one another, so no step finds its K/V still in the
+256 MB last-level cache; --layers 1 gives the single-layer figure) and the
+Mistral-7B 64K layer (one step = build + 128 encoding chunks + 256 decode
+steps).
 
 Prints ONE JSON line.  `value` is attended KV tokens per second over the
 whole step (over sequences and query positions, the number of keys each
@@ -81,7 +84,7 @@ class Pipeline:
     decode pass (if w.decode_steps > 0) runs single-token steps against the
     pool.  Selections and outputs of the last step are kept for checking."""
 
-    def __init__(self, w: synth.Workload, dev: str = "cuda"):
+    def __init__(self, w: synth.Workload, dev: str = "cuda", layers: int = 1):
         self.w, self.cfg, self.dev = w, cfg_of(w), dev
         t = time.time()
         self.inp = synth.make_inputs(w, device=dev)
@@ -112,18 +115,35 @@ class Pipeline:
             self.sel_dec = torch.empty((w.decode_steps, b, Hkv, 1, w.top_k), dtype=torch.int32,
                                        device=dev)
             self.out_dec = torch.empty_like(self.inp["q_dec"])
+        # Layer 0 is the workload's own K/V; further layers (decode only)
+        # have their own K/V, unit pool and selections, over the same queries
+        self.layers = [dict(k=self.inp["k"], v=self.inp["v"], repr=self.repr,
+                            rep_idx=self.rep_idx)]
+        for li in range(1, layers):
+            k, v = synth.make_layer_kv(w, li, device=dev)
+            self.layers.append(dict(k=k, v=v, repr=torch.empty_like(self.repr),
+                                    rep_idx=None if self.rep_idx is None
+                                    else torch.empty_like(self.rep_idx)))
+        torch.cuda.synchronize()
 
-    def build(self):
-        F.infllm_build_units(self.cfg, self.inp["q"], self.inp["k"], self.w.n_ctx, self.rep_idx,
-                             self.repr, self.build_ws)
+    def build(self, layer: int = 0):
+        ly = self.layers[layer]
+        F.infllm_build_units(self.cfg, self.inp["q"], ly["k"], self.w.n_ctx, ly["rep_idx"],
+                             ly["repr"], self.build_ws)
 
-    def _select(self, q, q_off, pos, L, sel, score_ws):
-        F.infllm_score_units(self.cfg, q, q_off, pos, L, 1, self.repr, self.scores, score_ws)
+    def build_all(self):
+        for li in range(len(self.layers)):
+            self.build(li)
+
+    def _select(self, q, q_off, pos, L, sel, score_ws, layer=0):
+        F.infllm_score_units(self.cfg, q, q_off, pos, L, 1, self.layers[layer]["repr"],
+                             self.scores, score_ws)
         F.infllm_topk_units(self.cfg, self.scores, sel)
 
-    def _attend(self, q, q_off, pos, L, sel, out, attn_ws):
-        F.infllm_attend(self.cfg, q, q_off, pos, L, 1, self.inp["k"], self.inp["v"], sel, out,
-                        None, q_off, attn_ws)
+    def _attend(self, q, q_off, pos, L, sel, out, attn_ws, layer=0):
+        ly = self.layers[layer]
+        F.infllm_attend(self.cfg, q, q_off, pos, L, 1, ly["k"], ly["v"], sel, out, None, q_off,
+                        attn_ws)
 
     @staticmethod
     def _mark(marks, key):
@@ -155,12 +175,16 @@ class Pipeline:
                             self.out_enc, None, 0, self.enc_attn_ws)
             self._mark(marks, "enc_end")
         if self.decode:
+            # decode step s runs on layer s mod L, as a model's layers follow
+            # one another
+            nl = len(self.layers)
             for s in range(w.decode_steps):
-                self._select(inp["q_dec"], s, w.n_ctx + s, 1, self.sel_dec[s], self.dec_score_ws)
+                self._select(inp["q_dec"], s, w.n_ctx + s, 1, self.sel_dec[s], self.dec_score_ws,
+                             s % nl)
             self._mark(marks, "dec_sel")
             for s in range(w.decode_steps):
                 self._attend(inp["q_dec"], s, w.n_ctx + s, 1, self.sel_dec[s], self.out_dec,
-                             self.dec_attn_ws)
+                             self.dec_attn_ws, s % nl)
             self._mark(marks, "dec_end")
 
     def work(self):
@@ -302,6 +326,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="llama3_8b_32k_encode", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layers", type=int, default=None,
+                    help="decode workloads: rotate the decode steps over this many layers' "
+                         "K/V and unit pools (default 4, so that a step's K/V is not still in "
+                         "the 256 MB last-level cache from the step before; 1 for the "
+                         "single-layer figure); encoding workloads use one layer")
     ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
                     help="after timing, run one plain device copy of MIB MiB (untimed), the "
                          "reference kernel for scaling HBM byte counters")
@@ -313,9 +342,11 @@ def main():
         sys.exit(2)
     torch.cuda.set_device(0)
     w = synth.WORKLOADS[args.workload]
-    pipe = Pipeline(w)
+    decode_only = w.chunk == 0
+    layers = (args.layers or 4) if decode_only else 1
+    pipe = Pipeline(w, layers=layers)
     if not pipe.encode:
-        pipe.build()            # decode-only: the pool is built once, beforehand
+        pipe.build_all()        # decode-only: the pools are built once, beforehand
     for _ in range(args.warmup):
         pipe.step()
     torch.cuda.synchronize()
@@ -351,7 +382,8 @@ def main():
                    "heads": "%dq/%dkv" % (w.n_q_heads, w.n_kv_heads), "head_dim": w.head_dim,
                    "chunk": w.chunk, "decode_steps": w.decode_steps, "block": w.block,
                    "n_init": w.n_init, "window": w.window, "rep_k": w.rep_k, "top_k": w.top_k,
-                   "rep_mode": w.rep_mode, "attended_tokens_per_step": tokens},
+                   "rep_mode": w.rep_mode, "layers": layers,
+                   "attended_tokens_per_step": tokens},
         "roofline": (roofline(w, "encode", work["encode"], span_ms("enc_sel", "enc_end"), 1)
                      if phase == "encode" else
                      roofline(w, "decode", work["decode"],

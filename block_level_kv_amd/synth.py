@@ -176,6 +176,29 @@ def make_inputs(w: Workload, device: str | torch.device = "cpu") -> dict:
     return dict(q=q, k=k, v=v, q_dec=q_dec, planted_units=planted)
 
 
+def make_layer_kv(w: Workload, layer: int, device: str | torch.device = "cpu"):
+    """K and V [b, H_kv, n_ctx + steps, d] of another layer of the same
+    workload: the same distribution, an independent seed per layer (no
+    planted blocks).  Decode benchmarks rotate over several layers so that
+    one step's K/V is not still cached from the previous step."""
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed * 1000 + layer)
+    dt = w.torch_dtype
+    b, Hkv, d, cap = w.batch, w.n_kv_heads, w.head_dim, w.n_cap
+    k = torch.empty((b, Hkv, cap, d), dtype=dt, device=dev)
+    v = torch.empty((b, Hkv, cap, d), dtype=dt, device=dev)
+    for bi in range(b):
+        for h in range(Hkv):
+            if w.kv_dist == "mixture":
+                k[bi, h] = _mixture(cap, d, gen, dev, w.scale).to(dt)
+                v[bi, h] = _mixture(cap, d, gen, dev, w.scale).to(dt)
+            else:
+                k[bi, h] = _normal((cap, d), gen, dev, w.scale).to(dt)
+                v[bi, h] = _normal((cap, d), gen, dev, w.scale).to(dt)
+    return k, v
+
+
 def plant_dominant_block(k: torch.Tensor, block: int, B: int, direction: torch.Tensor,
                          margin: float = 1.5) -> None:
     """Overwrite every key of absolute block `block` (all sequences and heads
