@@ -293,7 +293,38 @@ def stored_traffic(kernel: str, workload: str):
         return None
 
 
-def roofline(w: synth.Workload, phase: str, work, attn_ms: float, n_calls: int) -> dict:
+def measure_peaks() -> dict:
+    """What plain library kernels reach on this GPU, as context for the
+    published peaks: a 2 GiB device copy (bytes read + written) and a bf16
+    8192^3 GEMM (hipBLASLt through torch.matmul).  Best of 5 runs each."""
+    def best_ms(f, reps=5):
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            f()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return min(ts)
+    x = torch.ones((1 << 29,), dtype=torch.float32, device="cuda")       # 2 GiB
+    y = torch.empty_like(x)
+    y.copy_(x)
+    copy_ms = best_ms(lambda: y.copy_(x))                                 # 2 GiB in, 2 GiB out
+    del x, y
+    n = 8192
+    a = torch.randn((n, n), dtype=torch.bfloat16, device="cuda")
+    b = torch.randn((n, n), dtype=torch.bfloat16, device="cuda")
+    torch.matmul(a, b)
+    gemm_ms = best_ms(lambda: torch.matmul(a, b))
+    del a, b
+    torch.cuda.empty_cache()
+    return {"hbm_copy_GBs": round((1 << 32) / (copy_ms * 1e-3) / 1e9, 1),
+            "bf16_gemm_TFLOPs": round(2 * n ** 3 / (gemm_ms * 1e-3) / 1e12, 1)}
+
+
+def roofline(w: synth.Workload, phase: str, work, attn_ms: float, n_calls: int,
+             peaks: dict | None = None) -> dict:
     """attn_ms: average duration of one attention launch, in ms."""
     tokens, flops, nbytes = work
     if phase == "encode" and w.dtype == "bf16":
@@ -308,6 +339,15 @@ def roofline(w: synth.Workload, phase: str, work, attn_ms: float, n_calls: int) 
         achieved = nbytes / n_calls / (attn_ms * 1e-3) / 1e9
         r = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     r["frac"] = round(achieved / r["peak"], 4)
+    if peaks:   # the same work against what plain library kernels reach here
+        if r["bound"] == "hbm":
+            r["measured_peak"] = peaks["hbm_copy_GBs"]
+            r["measured_peak_kernel"] = "2 GiB device copy, bytes read + written (torch copy_)"
+        elif r["bound"] == "mfma":
+            r["measured_peak"] = peaks["bf16_gemm_TFLOPs"]
+            r["measured_peak_kernel"] = "bf16 8192^3 GEMM (hipBLASLt via torch.matmul)"
+        if "measured_peak" in r:
+            r["frac_of_measured"] = round(achieved / r["measured_peak"], 4)
     kernel = "k_attend_prefill" if phase == "encode" and w.dtype == "bf16" else "k_attend_rows"
     r["traffic"] = stored_traffic(kernel, w.name)
     r["kernel"] = "infllm_attend (%s)" % kernel
@@ -326,6 +366,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="llama3_8b_32k_encode", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip measuring what plain library kernels reach (read, GEMM)")
     ap.add_argument("--layers", type=int, default=None,
                     help="decode workloads: rotate the decode steps over this many layers' "
                          "K/V and unit pools (default 4, so that a step's K/V is not still in "
@@ -367,6 +409,7 @@ def main():
         return float(np.mean([x.elapsed_time(y) for x, y in zip(marks[a], marks[b])]))
 
     work = pipe.work()
+    peaks = None if args.no_peaks else measure_peaks()
     tokens = sum(v[0] for v in work.values())
     phase = "encode" if pipe.encode else "decode"
     line = {
@@ -384,10 +427,12 @@ def main():
                    "n_init": w.n_init, "window": w.window, "rep_k": w.rep_k, "top_k": w.top_k,
                    "rep_mode": w.rep_mode, "layers": layers,
                    "attended_tokens_per_step": tokens},
-        "roofline": (roofline(w, "encode", work["encode"], span_ms("enc_sel", "enc_end"), 1)
+        "roofline": (roofline(w, "encode", work["encode"], span_ms("enc_sel", "enc_end"), 1,
+                              peaks)
                      if phase == "encode" else
                      roofline(w, "decode", work["decode"],
-                              span_ms("dec_sel", "dec_end") / w.decode_steps, w.decode_steps)),
+                              span_ms("dec_sel", "dec_end") / w.decode_steps, w.decode_steps,
+                              peaks)),
     }
     if pipe.decode:
         # one decode step = score + top-k + attention for one token position
@@ -398,7 +443,7 @@ def main():
         if pipe.encode:
             line["decode_roofline"] = roofline(w, "decode", work["decode"],
                                                span_ms("dec_sel", "dec_end") / w.decode_steps,
-                                               w.decode_steps)
+                                               w.decode_steps, peaks)
     if args.calibration_copy > 0:
         n = args.calibration_copy << 20
         src = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda")
