@@ -125,6 +125,30 @@ struct WaveKeys {
     hi = wave_max_u32(h);
     lo = wave_min_u32(l);
   }
+  // A lower bound on the K-th largest key from this wave's four 16-lane
+  // rows: their maxima are distinct keys, so with `rows` nonempty rows
+  // (summed over the problem's waves) >= K, the smallest row maximum is at
+  // or below the K-th largest key.  Empty rows give (0 rows, ~0u).
+  __device__ __forceinline__ void row_bound(int& rows, uint32_t& lb) const {
+    uint32_t h = 0u;
+    for (int i = 0; i < n_cols(); ++i) {
+      const uint32_t x = key(i);
+      h = x > h ? x : h;
+    }
+    auto mx = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+    h = mx(h, (uint32_t)__builtin_amdgcn_mov_dpp((int)h, INFLLM_DPP_XOR1, 0xF, 0xF, true));
+    h = mx(h, (uint32_t)__builtin_amdgcn_mov_dpp((int)h, INFLLM_DPP_XOR2, 0xF, 0xF, true));
+    h = mx(h, (uint32_t)__builtin_amdgcn_mov_dpp((int)h, INFLLM_DPP_HALF_MIRROR, 0xF, 0xF, true));
+    h = mx(h, (uint32_t)__builtin_amdgcn_mov_dpp((int)h, INFLLM_DPP_MIRROR, 0xF, 0xF, true));
+    rows = 0;
+    lb = 0xffffffffu;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t m = (uint32_t)__builtin_amdgcn_readlane((int)h, 16 * r);
+      rows += m != 0u;
+      lb = m != 0u && m < lb ? m : lb;
+    }
+  }
   // smallest key >= c (c >= 1)
   __device__ __forceinline__ uint32_t min_ge(uint32_t c) const {
     uint32_t l = 0xffffffffu;
@@ -213,12 +237,15 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_wave(const float* __restr
 // (fewer after skipping the common leading bits of the largest and
 // smallest finite key).
 constexpr int kRadixBins = 256;
+// lb: a lower bound on the K-th largest key (the smallest finite key, or a
+// tighter bound); only the bits where hi and lb differ are searched.
 template <typename Keys>
 __device__ __forceinline__ uint32_t radix_tau(const Keys& keys, int K, int n_valid, uint32_t hi,
-                                              uint32_t lo, int* hist, int* pick) {
-  if (K == n_valid || hi == lo) return lo;       // every finite key is kept, or all equal
+                                              uint32_t lo, uint32_t lb, int* hist, int* pick) {
+  if (K == n_valid) return lo;                   // every finite key is kept
+  if (hi == lb) return hi;                       // K keys at the maximum
   const int tid = threadIdx.x, lane = tid % 64;
-  int top = 31 - __builtin_clz(hi ^ lo);         // highest bit where keys can differ
+  int top = 31 - __builtin_clz(hi ^ lb);         // highest bit where hi and the bound differ
   uint32_t prefix = top == 31 ? 0u : hi & ~((2u << top) - 1u);
   int krem = K;
   while (top >= 0) {
@@ -279,7 +306,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_topk_block(const float* __res
   const int R = ((U + kBlockWaves - 1) / kBlockWaves + 63) / 64 * 64;
   const int b0 = wave * R < U ? wave * R : U;
   const int b1 = b0 + R < U ? b0 + R : U;
-  __shared__ uint32_t xch[2][3][kBlockWaves];
+  __shared__ uint32_t xch[2][5][kBlockWaves];
   __shared__ int hist[kRadixBins];
   __shared__ int pick[2];
   int phase = 0;
@@ -298,21 +325,28 @@ __global__ __launch_bounds__(kBlockThreads) void k_topk_block(const float* __res
   int nv_w;
   uint32_t hi_w, lo_w;
   keys.stats(nv_w, hi_w, lo_w);
+  int rows_w;
+  uint32_t lb_w;
+  keys.row_bound(rows_w, lb_w);
   exchange((uint32_t)nv_w, 0);
   exchange(hi_w, 1);
   exchange(lo_w, 2);
+  exchange((uint32_t)rows_w, 3);
+  exchange(lb_w, 4);
   sync();
-  int n_valid = 0;
-  uint32_t hi = 0u, lo = 0xffffffffu;
+  int n_valid = 0, rows = 0;
+  uint32_t hi = 0u, lo = 0xffffffffu, lb = 0xffffffffu;
 #pragma unroll
   for (int w = 0; w < kBlockWaves; ++w) {
     n_valid += (int)got(0, w);
     hi = got(1, w) > hi ? got(1, w) : hi;
     lo = got(2, w) < lo ? got(2, w) : lo;
+    rows += (int)got(3, w);
+    lb = got(4, w) < lb ? got(4, w) : lb;
   }
   const int K = k_m < n_valid ? k_m : n_valid;
   if (K > 0) {
-    const uint32_t tau = radix_tau(keys, K, n_valid, hi, lo, hist, pick);
+    const uint32_t tau = radix_tau(keys, K, n_valid, hi, lo, rows >= K ? lb : lo, hist, pick);
     int n_gt, n_eq;
     keys.split(tau, n_gt, n_eq);
     exchange((uint32_t)n_gt, 0);
