@@ -5,7 +5,7 @@
 // sum and the dot products accumulate in fp64, so the ranking that follows
 // is decided on scores accurate far below the near-tie margin.
 //
-// Long chunks: the query sum is spread over workgroups of kQsumRows rows
+// Long chunks: the query sum is spread over workgroups of ROWS rows
 // each (16-byte loads, all G heads), whose fp64 partial sums are added in
 // part order, so results do not depend on scheduling.  Up to
 // kFusedMaxUnits units this is one launch (k_score_fused: the last
@@ -24,14 +24,22 @@ namespace infllm {
 
 constexpr int kScoreThreads = 256;
 constexpr int kUnitsPerWG = 64;
-constexpr int kQsumRows = 32;        // chunk rows per partial sum
+// chunk rows per partial sum: 128 when a call has enough of them to fill
+// the chip (fewer, longer workgroups amortize the publication), else 32
+constexpr int kRowsShort = 32, kRowsLong = 128;
 constexpr int kDirectRows = 64;      // L*G up to this: sum in the scoring kernel
 constexpr int kFusedMaxUnits = 2048;
 constexpr int kPartBatch = 16;       // partial sums requested together
 constexpr int kBatchUnits = 64;      // units whose rows the fused kernel requests together
 
-int score_num_parts(int L, int G) {
-  return L * G <= kDirectRows ? 0 : (L + kQsumRows - 1) / kQsumRows;
+static int score_rows(const ScoreArgs& a) {
+  const int64_t long_parts = (int64_t)a.batch * a.Hkv * a.n_chunks * ((a.L + kRowsLong - 1) / kRowsLong);
+  return long_parts >= 512 ? kRowsLong : kRowsShort;
+}
+
+static int score_num_parts(const ScoreArgs& a) {
+  const int G = a.Hq / a.Hkv, rows = score_rows(a);
+  return a.L * G <= kDirectRows ? 0 : (a.L + rows - 1) / rows;
 }
 
 // Column sums of rows [r0, r1) of one chunk over the G heads of a KV head,
@@ -39,11 +47,11 @@ int score_num_parts(int L, int G) {
 // the row lanes are added in order through LDS.  qb points at row 0 of the
 // chunk in the first head; heads are hs elements apart.  Threads tid < D
 // return column tid's sum.
-template <typename T, int G, int D>
+template <typename T, int G, int D, int ROWS>
 __device__ __forceinline__ double rows_colsum(const T* __restrict__ qb, int64_t hs, int r0, int r1,
                                               double (*sm)[D]) {
   constexpr int kCgs = D / 8, kNrl = kScoreThreads / kCgs;
-  constexpr int kIt = (kQsumRows + kNrl - 1) / kNrl;
+  constexpr int kIt = (ROWS + kNrl - 1) / kNrl;
   const int tid = threadIdx.x, cg = tid % kCgs, rl = tid / kCgs;
   Raw8<T> raw[G][kIt];
 #pragma unroll
@@ -124,9 +132,9 @@ struct UnitRows {
   }
 };
 
-// Partial query sums: part p of chunk c covers rows [p*kQsumRows, ...) of
-// the chunk, all G heads.  grid (parts, H_kv, batch * n_chunks).
-template <typename T, int G, int D>
+// Partial query sums: part p of chunk c covers rows [p*ROWS, ...) of the
+// chunk, all G heads.  grid (parts, H_kv, batch * n_chunks).
+template <typename T, int G, int D, int ROWS>
 __global__ __launch_bounds__(kScoreThreads) void k_chunk_qsum(
     const T* __restrict__ q, int64_t q_cap, int64_t q_off, int L, int Hq, int Hkv, int n_chunks,
     double* __restrict__ parts) {
@@ -134,9 +142,9 @@ __global__ __launch_bounds__(kScoreThreads) void k_chunk_qsum(
   const int ch = blockIdx.z % n_chunks, bi = blockIdx.z / n_chunks;
   __shared__ double sm[kScoreThreads / (D / 8)][D];
   const T* qb = q + (((int64_t)bi * Hq + (int64_t)h * G) * q_cap + q_off + (int64_t)ch * L) * D;
-  const int r0 = part * kQsumRows;
-  const int r1 = r0 + kQsumRows < L ? r0 + kQsumRows : L;
-  const double t = rows_colsum<T, G, D>(qb, q_cap * D, r0, r1, sm);
+  const int r0 = part * ROWS;
+  const int r1 = r0 + ROWS < L ? r0 + ROWS : L;
+  const double t = rows_colsum<T, G, D, ROWS>(qb, q_cap * D, r0, r1, sm);
   if (threadIdx.x < D) {
     const int n_parts = gridDim.x;
     parts[((((int64_t)bi * Hkv + h) * n_chunks + ch) * n_parts + part) * D + threadIdx.x] = t;
@@ -211,14 +219,14 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_units(
 }
 
 // Long chunks with a moderate unit count, in one launch: each workgroup
-// sums kQsumRows query rows of one chunk (all G heads) in fp64 and publishes
+// sums ROWS query rows of one chunk (all G heads) in fp64 and publishes
 // the partial sum with device-scope stores; the last workgroup of a
 // (sequence, KV head, chunk) to arrive -- found with a counter in the
 // workspace, which it resets -- adds the partial sums in part order (so the
 // result does not depend on arrival order) and scores every unit.  Its
 // part loads and its first batch of unit rows are requested together.
 // grid (parts, H_kv, batch * n_chunks).
-template <typename T, int G, int D>
+template <typename T, int G, int D, int ROWS>
 __global__ __launch_bounds__(kScoreThreads) void k_score_fused(
     const T* __restrict__ q, int64_t q_cap, int64_t q_off, int64_t q_pos, int L, int Hq, int Hkv,
     int B, int n_init, int W, const float* __restrict__ repr, int U, float* __restrict__ scores,
@@ -232,9 +240,9 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_fused(
   __shared__ double qsum[D];
   __shared__ int last_sh;
   const T* qb = q + (((int64_t)bi * Hq + (int64_t)h * G) * q_cap + q_off + (int64_t)ch * L) * D;
-  const int r0 = part * kQsumRows;
-  const int r1 = r0 + kQsumRows < L ? r0 + kQsumRows : L;
-  const double t = rows_colsum<T, G, D>(qb, q_cap * D, r0, r1, sm);
+  const int r0 = part * ROWS;
+  const int r1 = r0 + ROWS < L ? r0 + ROWS : L;
+  const double t = rows_colsum<T, G, D, ROWS>(qb, q_cap * D, r0, r1, sm);
   const int64_t prob = ((int64_t)bi * Hkv + h) * n_chunks + ch;
   double* pp = parts + prob * n_parts * D;
   if (tid < D)
@@ -270,7 +278,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_fused(
 }
 
 static bool score_fused(const ScoreArgs& a) {
-  return score_num_parts(a.L, a.Hq / a.Hkv) > 0 && a.U <= kFusedMaxUnits;
+  return score_num_parts(a) > 0 && a.U <= kFusedMaxUnits;
 }
 
 static size_t score_counter_bytes(const ScoreArgs& a) {
@@ -280,24 +288,32 @@ static size_t score_counter_bytes(const ScoreArgs& a) {
 // [arrival counters, 256-byte aligned][fp64 partial query sums]; sized for
 // either path (the unit count is not known here)
 size_t score_workspace_bytes(const ScoreArgs& a) {
-  const int parts = score_num_parts(a.L, a.Hq / a.Hkv);
+  const int parts = score_num_parts(a);
   if (parts == 0) return 0;
   return score_counter_bytes(a) + (size_t)parts * a.batch * a.Hkv * a.n_chunks * a.d * sizeof(double);
 }
 
-template <typename T, int G, int D>
-static hipError_t launch_score_tgd(const ScoreArgs& a, hipStream_t st) {
-  const int parts = score_num_parts(a.L, G);
-  double* pw = parts > 0 ? (double*)((char*)a.ws + score_counter_bytes(a)) : nullptr;
-  if (score_fused(a)) {
-    k_score_fused<T, G, D><<<dim3(parts, a.Hkv, a.batch * a.n_chunks), kScoreThreads, 0, st>>>(
+template <typename T, int G, int D, int ROWS>
+static void launch_parts(const ScoreArgs& a, int parts, double* pw, hipStream_t st) {
+  const dim3 grid(parts, a.Hkv, a.batch * a.n_chunks);
+  if (score_fused(a))
+    k_score_fused<T, G, D, ROWS><<<grid, kScoreThreads, 0, st>>>(
         (const T*)a.q, a.q_cap, a.q_off, a.q_pos, a.L, a.Hq, a.Hkv, a.B, a.n_init, a.W, a.repr,
         a.U, a.scores, a.n_chunks, pw, (int*)a.ws);
-    return hipGetLastError();
-  }
-  if (parts > 0)
-    k_chunk_qsum<T, G, D><<<dim3(parts, a.Hkv, a.batch * a.n_chunks), kScoreThreads, 0, st>>>(
+  else
+    k_chunk_qsum<T, G, D, ROWS><<<grid, kScoreThreads, 0, st>>>(
         (const T*)a.q, a.q_cap, a.q_off, a.L, a.Hq, a.Hkv, a.n_chunks, pw);
+}
+
+template <typename T, int G, int D>
+static hipError_t launch_score_tgd(const ScoreArgs& a, hipStream_t st) {
+  const int parts = score_num_parts(a);
+  double* pw = parts > 0 ? (double*)((char*)a.ws + score_counter_bytes(a)) : nullptr;
+  if (parts > 0) {
+    if (score_rows(a) == kRowsLong) launch_parts<T, G, D, kRowsLong>(a, parts, pw, st);
+    else launch_parts<T, G, D, kRowsShort>(a, parts, pw, st);
+    if (score_fused(a)) return hipGetLastError();
+  }
   dim3 grid((a.U + kUnitsPerWG - 1) / kUnitsPerWG, a.n_chunks * a.Hkv, a.batch);
   k_score_units<T, G, D><<<grid, kScoreThreads, 0, st>>>(
       (const T*)a.q, a.q_cap, a.q_off, a.q_pos, a.L, a.Hq, a.Hkv, a.B, a.n_init, a.W, a.repr, a.U,
