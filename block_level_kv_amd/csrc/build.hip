@@ -15,68 +15,66 @@
 namespace infllm {
 
 // Eight consecutive columns of a row, widened to fp64 and added to acc.
-template <typename T> struct Cols8;
-template <> struct Cols8<bf16_t> {
-  static __device__ __forceinline__ void add(const bf16_t* p, double* acc) {
-    const u32x4 w = *(const u32x4*)p;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[2 * i] += (double)__uint_as_float(w[i] << 16);
-      acc[2 * i + 1] += (double)__uint_as_float(w[i] & 0xffff0000u);
-    }
-  }
-  static __device__ __forceinline__ void get(const bf16_t* p, double* v) {
-    const u32x4 w = *(const u32x4*)p;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = (double)__uint_as_float(w[i] << 16);
-      v[2 * i + 1] = (double)__uint_as_float(w[i] & 0xffff0000u);
-    }
-  }
-};
-template <> struct Cols8<float> {
-  static __device__ __forceinline__ void add(const float* p, double* acc) {
-    const float4 x = ((const float4*)p)[0], y = ((const float4*)p)[1];
-    acc[0] += x.x; acc[1] += x.y; acc[2] += x.z; acc[3] += x.w;
-    acc[4] += y.x; acc[5] += y.y; acc[6] += y.z; acc[7] += y.w;
-  }
-  static __device__ __forceinline__ void get(const float* p, double* v) {
-    const float4 x = ((const float4*)p)[0], y = ((const float4*)p)[1];
-    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
-    v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
-  }
-};
-
-// Raw 8-column piece of a row: loaded first, widened later, so that a batch
-// of loads is in flight before any of them is waited on.
 // S[b][h][j][c] = sum over rows of block j (clipped to n_ctx) and over the
-// group's query heads of q[.][c], fp64.  grid (n_blocks, H_kv, batch), 256
-// threads: thread -> (8-column group, row phase), 16-byte loads.
+// group's query heads of q[.][c], fp64.  With NSUB = 4 (blocks of 128 rows)
+// the sums of the block's four 32-row sub-blocks are stored too
+// (S32[b][h][j][s][c]) and S[j] is their sum in order.  grid (n_blocks,
+// H_kv, batch), 256 threads: thread -> (8-column group, row phase); each
+// thread requests 8 rows of a head at a time before adding any.
 constexpr int kSumThreads = 256;
-template <typename T>
+template <typename T, int NSUB>
 __global__ __launch_bounds__(kSumThreads) void k_block_sums(const T* __restrict__ q, int64_t q_cap,
                                                             int Hq, int Hkv, int d, int B,
                                                             int64_t n_ctx, int n_blocks,
-                                                            double* __restrict__ S) {
+                                                            double* __restrict__ S,
+                                                            double* __restrict__ S32) {
   const int j = blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
   const int G = Hq / Hkv;
   const int cgs = d / 8, cg = threadIdx.x % cgs, ph = threadIdx.x / cgs, nph = kSumThreads / cgs;
   const int64_t r0 = (int64_t)j * B;
   const int64_t r1 = r0 + B < n_ctx ? r0 + B : n_ctx;
-  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  const int sub_rows = B / NSUB;
+  double acc[NSUB][8];
+#pragma unroll
+  for (int s2 = 0; s2 < NSUB; ++s2)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[s2][i] = 0.0;
   for (int g = 0; g < G; ++g) {
     const T* qh = q + ((int64_t)bi * Hq + (int64_t)h * G + g) * q_cap * d + cg * 8;
-    for (int64_t r = r0 + ph; r < r1; r += nph) Cols8<T>::add(qh + r * d, acc);
+    for (int64_t rb = r0 + ph; rb < r1; rb += 8 * nph) {
+      Raw8<T> raw[8];
+#pragma unroll
+      for (int y = 0; y < 8; ++y) {
+        const int64_t r = rb + (int64_t)y * nph;
+        raw[y].load(qh + (r < r1 ? r : r1 - 1) * d);
+      }
+#pragma unroll
+      for (int y = 0; y < 8; ++y) {
+        const int64_t r = rb + (int64_t)y * nph;
+        if (r >= r1) break;
+        const int sb = NSUB == 1 ? 0 : (int)((r - r0) / sub_rows);
+#pragma unroll
+        for (int s2 = 0; s2 < NSUB; ++s2)
+          if (s2 == sb) raw[y].add(acc[s2]);
+      }
+    }
   }
   __shared__ double part[kSumThreads / 8][128];   // [phase][column]
+  double blk = 0.0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) part[ph][cg * 8 + i] = acc[i];
-  __syncthreads();
-  if (threadIdx.x < d) {
-    double t = 0.0;
-    for (int p2 = 0; p2 < nph; ++p2) t += part[p2][threadIdx.x];
-    S[(((int64_t)bi * Hkv + h) * n_blocks + j) * d + threadIdx.x] = t;
+  for (int s2 = 0; s2 < NSUB; ++s2) {
+    if (s2 > 0) __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) part[ph][cg * 8 + i] = acc[s2][i];
+    __syncthreads();
+    if (threadIdx.x < d) {
+      double t = 0.0;
+      for (int p2 = 0; p2 < nph; ++p2) t += part[p2][threadIdx.x];
+      if (NSUB > 1) S32[((((int64_t)bi * Hkv + h) * n_blocks + j) * NSUB + s2) * d + threadIdx.x] = t;
+      blk += t;
+    }
   }
+  if (threadIdx.x < d) S[(((int64_t)bi * Hkv + h) * n_blocks + j) * d + threadIdx.x] = blk;
 }
 
 // BP[b][h][j][c] = sum_{j' < j} S[b][h][j'][c] for j = 0..n_blocks.
@@ -125,7 +123,8 @@ template <typename T, int HPL>
 __global__ __launch_bounds__(64 * kRepWaves) void k_rep_select(
     const T* __restrict__ q, int64_t q_cap, const T* __restrict__ k, int64_t kv_cap, int Hq,
     int Hkv, int d, int B, int n_init, int W, int r_k, int64_t n_ctx, int U, int n_blocks,
-    const double* __restrict__ BP, int32_t* __restrict__ rep_idx, float* __restrict__ unit_repr) {
+    const double* __restrict__ BP, const double* __restrict__ S32, int32_t* __restrict__ rep_idx,
+    float* __restrict__ unit_repr) {
   const int u = blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
   const int G = Hq / Hkv;
   const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
@@ -156,10 +155,27 @@ __global__ __launch_bounds__(64 * kRepWaves) void k_rep_select(
   const int k0 = wave * per < nk ? wave * per : nk;
   const int k1 = k0 + per < nk ? k0 + per : nk;
 
+  // Without pass 1: for a 128-key unit aligned to its block, with W a
+  // multiple of 32 and 32-row sub-block sums at hand, every wave's keys
+  // start at a 32-row boundary, so the sums before them are block prefixes
+  // plus sub-block sums: F(32x - 1) = BP[x / 4] + sum_{s < x % 4} S32[x / 4][s].
+  const bool sub = S32 != nullptr && nk == B && lo == j * B && B == 4 * 32 && W % 32 == 0;
+  auto f_at = [&](int64_t x, double* out) {   // F(32x - 1), slot 0 only; x <= 32 n_blocks
+    const int64_t blk = x / 4;
+    const int s_in = (int)(x % 4);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out[i] = slot == 0 ? bp[blk * d + i] : 0.0;
+    if (slot == 0) {
+      const double* sp = S32 + ((((int64_t)bi * Hkv + h) * n_blocks + blk) * 4) * d + cg * 8;
+      for (int s2 = 0; s2 < s_in; ++s2)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) out[i] += sp[s2 * d + i];
+    }
+  };
   // pass 1: rows that keys k0..k1-1 add (key lo adds none: its sums are
   // the starting values); rows past the context are loaded clamped and
   // not added
-  {
+  if (!sub) {
     double sl[8] = {0, 0, 0, 0, 0, 0, 0, 0}, su[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int o0 = k0 > 0 ? k0 : 1; o0 < k1; o0 += kPass1Batch) {
       Raw8<T> rl[kPass1Batch][HPL], ru[kPass1Batch][HPL];
@@ -223,12 +239,24 @@ __global__ __launch_bounds__(64 * kRepWaves) void k_rep_select(
     if (!e_end) add_rows(be * B, e, fe);
   }
   __syncthreads();
-  for (int w2 = 0; w2 < wave; ++w2)
+  if (!sub) {
+    for (int w2 = 0; w2 < wave; ++w2)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      fp[i] += seg[0][w2][lane][i];
-      fe[i] += seg[1][w2][lane][i];
+      for (int i = 0; i < 8; ++i) {
+        fp[i] += seg[0][w2][lane][i];
+        fe[i] += seg[1][w2][lane][i];
+      }
+  } else if (k0 > 0) {
+    // F(lo + k0 - 1) and F(min(lo + k0 - 1 + W, last)); the in-block rows
+    // of the starting sums above belong to wave 0 only
+    f_at((lo + k0) / 32, fp);
+    if (lo + k0 - 1 + W >= last) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) fe[i] = slot == 0 ? bp[(int64_t)n_blocks * d + i] : 0.0;
+    } else {
+      f_at((lo + k0 + W) / 32, fe);
     }
+  }
   // pass 2: walk the keys; a batch's rows are loaded first, and its
   // reductions overlap
   for (int o0 = k0; o0 < k1; o0 += kPass2Batch) {
@@ -325,12 +353,24 @@ __global__ void k_mean_repr(const T* __restrict__ k, int64_t kv_cap, int Hkv, in
   unit_repr[(((int64_t)bi * Hkv + h) * U + u) * d + c] = (float)(acc / (double)(hi - lo));
 }
 
+// [block sums S][block prefix BP][32-row sub-block sums S32 (128-row blocks only)]
+struct BuildWs {
+  size_t s, bp, s32;
+};
+static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+static BuildWs build_ws_layout(const BuildArgs& a) {
+  const int64_t nb = (a.n_ctx + a.B - 1) / a.B;
+  BuildWs w;
+  w.s = round256((size_t)a.batch * a.Hkv * nb * a.d * sizeof(double));
+  w.bp = round256((size_t)a.batch * a.Hkv * (nb + 1) * a.d * sizeof(double));
+  w.s32 = a.B == 128 ? (size_t)a.batch * a.Hkv * nb * 4 * a.d * sizeof(double) : 0;
+  return w;
+}
+
 size_t build_workspace_bytes(const BuildArgs& a) {
   if (a.rep_mode != 0) return 0;
-  const int64_t nb = (a.n_ctx + a.B - 1) / a.B;
-  const size_t s = (size_t)a.batch * a.Hkv * nb * a.d * sizeof(double);
-  const size_t bp = (size_t)a.batch * a.Hkv * (nb + 1) * a.d * sizeof(double);
-  return ((s + 255) & ~(size_t)255) + bp;
+  const BuildWs w = build_ws_layout(a);
+  return w.s + w.bp + w.s32;
 }
 
 template <typename T>
@@ -344,11 +384,17 @@ static hipError_t launch_build_t(const BuildArgs& a, hipStream_t st) {
     return hipGetLastError();
   }
   const int nb = (int)((a.n_ctx + a.B - 1) / a.B);
+  const BuildWs lay = build_ws_layout(a);
   double* S = (double*)a.ws;
-  const size_t s_bytes = (size_t)a.batch * a.Hkv * nb * a.d * sizeof(double);
-  double* BP = (double*)((char*)a.ws + ((s_bytes + 255) & ~(size_t)255));
-  k_block_sums<T><<<dim3(nb, a.Hkv, a.batch), kSumThreads, 0, st>>>(q, a.q_cap, a.Hq, a.Hkv, a.d, a.B,
-                                                            a.n_ctx, nb, S);
+  double* BP = (double*)((char*)a.ws + lay.s);
+  double* S32 = lay.s32 > 0 ? (double*)((char*)a.ws + lay.s + lay.bp) : nullptr;
+  const dim3 sgrid(nb, a.Hkv, a.batch);
+  if (S32)
+    k_block_sums<T, 4><<<sgrid, kSumThreads, 0, st>>>(q, a.q_cap, a.Hq, a.Hkv, a.d, a.B, a.n_ctx,
+                                                      nb, S, S32);
+  else
+    k_block_sums<T, 1><<<sgrid, kSumThreads, 0, st>>>(q, a.q_cap, a.Hq, a.Hkv, a.d, a.B, a.n_ctx,
+                                                      nb, S, nullptr);
   k_block_prefix<<<dim3(a.Hkv, a.batch), a.d, 0, st>>>(S, BP, a.Hkv, a.d, nb);
   // heads per lane: 64 / (d / 8) head slots per wave
   const int hs = 64 / (a.d / 8), G = a.Hq / a.Hkv;
@@ -356,11 +402,11 @@ static hipError_t launch_build_t(const BuildArgs& a, hipStream_t st) {
   if (G <= hs)
     k_rep_select<T, 1><<<grid, 64 * kRepWaves, 0, st>>>(
         q, a.q_cap, k, a.kv_cap, a.Hq, a.Hkv, a.d, a.B, a.n_init, a.W, a.r_k, a.n_ctx, a.U, nb,
-        BP, a.rep_idx, a.unit_repr);
+        BP, S32, a.rep_idx, a.unit_repr);
   else if (G <= 2 * hs)
     k_rep_select<T, 2><<<grid, 64 * kRepWaves, 0, st>>>(
         q, a.q_cap, k, a.kv_cap, a.Hq, a.Hkv, a.d, a.B, a.n_init, a.W, a.r_k, a.n_ctx, a.U, nb,
-        BP, a.rep_idx, a.unit_repr);
+        BP, S32, a.rep_idx, a.unit_repr);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
