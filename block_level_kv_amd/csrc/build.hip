@@ -117,7 +117,7 @@ __global__ void k_block_prefix(const double* __restrict__ S, double* __restrict_
 constexpr int kMaxBlock = 1024;
 constexpr int kRepWaves = 4;
 constexpr int kPass1Batch = 8;
-constexpr int kPass2Batch = 4;
+constexpr int kPass2Batch = 8;
 
 template <typename T, int HPL>
 __global__ __launch_bounds__(64 * kRepWaves) void k_rep_select(
