@@ -18,17 +18,19 @@ namespace infllm {
 // S[b][h][j][c] = sum over rows of block j (clipped to n_ctx) and over the
 // group's query heads of q[.][c], fp64.  With NSUB = 4 (blocks of 128 rows)
 // the sums of the block's four 32-row sub-blocks are stored too
-// (S32[b][h][j][s][c]) and S[j] is their sum in order.  grid (n_blocks,
-// H_kv, batch), 256 threads: thread -> (8-column group, row phase); each
-// thread requests 8 rows of a head at a time before adding any.
+// (S32[b][h][j][s][c]) and S[j] is their sum in order.  Blocks jb0 ..
+// jb0 + n_blocks - 1 are summed, stored at local index j - jb0.  grid
+// (n_blocks, H_kv, batch), 256 threads: thread -> (8-column group, row
+// phase); each thread requests 8 rows of a head at a time before adding any.
 constexpr int kSumThreads = 256;
 template <typename T, int NSUB>
 __global__ __launch_bounds__(kSumThreads) void k_block_sums(const T* __restrict__ q, int64_t q_cap,
                                                             int Hq, int Hkv, int d, int B,
-                                                            int64_t n_ctx, int n_blocks,
-                                                            double* __restrict__ S,
+                                                            int64_t n_ctx, int64_t jb0,
+                                                            int n_blocks, double* __restrict__ S,
                                                             double* __restrict__ S32) {
-  const int j = blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
+  const int jl = blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
+  const int64_t j = jb0 + jl;
   const int G = Hq / Hkv;
   const int cgs = d / 8, cg = threadIdx.x % cgs, ph = threadIdx.x / cgs, nph = kSumThreads / cgs;
   const int64_t r0 = (int64_t)j * B;
@@ -70,11 +72,11 @@ __global__ __launch_bounds__(kSumThreads) void k_block_sums(const T* __restrict_
     if (threadIdx.x < d) {
       double t = 0.0;
       for (int p2 = 0; p2 < nph; ++p2) t += part[p2][threadIdx.x];
-      if (NSUB > 1) S32[((((int64_t)bi * Hkv + h) * n_blocks + j) * NSUB + s2) * d + threadIdx.x] = t;
+      if (NSUB > 1) S32[((((int64_t)bi * Hkv + h) * n_blocks + jl) * NSUB + s2) * d + threadIdx.x] = t;
       blk += t;
     }
   }
-  if (threadIdx.x < d) S[(((int64_t)bi * Hkv + h) * n_blocks + j) * d + threadIdx.x] = blk;
+  if (threadIdx.x < d) S[(((int64_t)bi * Hkv + h) * n_blocks + jl) * d + threadIdx.x] = blk;
 }
 
 // BP[b][h][j][c] = sum_{j' < j} S[b][h][j'][c] for j = 0..n_blocks.
@@ -122,10 +124,10 @@ constexpr int kPass2Batch = 8;
 template <typename T, int HPL>
 __global__ __launch_bounds__(64 * kRepWaves) void k_rep_select(
     const T* __restrict__ q, int64_t q_cap, const T* __restrict__ k, int64_t kv_cap, int Hq,
-    int Hkv, int d, int B, int n_init, int W, int r_k, int64_t n_ctx, int U, int n_blocks,
-    const double* __restrict__ BP, const double* __restrict__ S32, int32_t* __restrict__ rep_idx,
-    float* __restrict__ unit_repr) {
-  const int u = blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
+    int Hkv, int d, int B, int n_init, int W, int r_k, int64_t n_ctx, int u_begin, int u_stride,
+    int64_t jb0, int n_blocks, const double* __restrict__ BP, const double* __restrict__ S32,
+    int32_t* __restrict__ rep_idx, float* __restrict__ unit_repr) {
+  const int u = u_begin + (int)blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
   const int G = Hq / Hkv;
   const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
   const int c = tid;   // column owner in the final phases (c < d)
@@ -160,8 +162,8 @@ __global__ __launch_bounds__(64 * kRepWaves) void k_rep_select(
   // start at a 32-row boundary, so the sums before them are block prefixes
   // plus sub-block sums: F(32x - 1) = BP[x / 4] + sum_{s < x % 4} S32[x / 4][s].
   const bool sub = S32 != nullptr && nk == B && lo == j * B && B == 4 * 32 && W % 32 == 0;
-  auto f_at = [&](int64_t x, double* out) {   // F(32x - 1), slot 0 only; x <= 32 n_blocks
-    const int64_t blk = x / 4;
+  auto f_at = [&](int64_t x, double* out) {   // F(32x - 1) (local prefix), slot 0 only
+    const int64_t blk = x / 4 - jb0;
     const int s_in = (int)(x % 4);
 #pragma unroll
     for (int i = 0; i < 8; ++i) out[i] = slot == 0 ? bp[blk * d + i] : 0.0;
@@ -215,11 +217,11 @@ __global__ __launch_bounds__(64 * kRepWaves) void k_rep_select(
   {
     const int64_t e = lo + W < last ? lo + W : last;
     const bool e_end = e == last;
-    const int64_t be = e_end ? n_blocks : e / B;
+    const int64_t be = e_end ? jb0 + n_blocks : e / B;   // absolute block
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      fp[i] = slot == 0 ? bp[j * d + i] : 0.0;
-      fe[i] = slot == 0 ? bp[be * d + i] : 0.0;
+      fp[i] = slot == 0 ? bp[(j - jb0) * d + i] : 0.0;
+      fe[i] = slot == 0 ? bp[(be - jb0) * d + i] : 0.0;
     }
     auto add_rows = [&](int64_t r0, int64_t r1, double* acc) {   // rows r0 .. r1
       for (int64_t i0 = r0; i0 <= r1; i0 += kPass1Batch) {
@@ -252,7 +254,7 @@ __global__ __launch_bounds__(64 * kRepWaves) void k_rep_select(
     f_at((lo + k0) / 32, fp);
     if (lo + k0 - 1 + W >= last) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) fe[i] = slot == 0 ? bp[(int64_t)n_blocks * d + i] : 0.0;
+      for (int i = 0; i < 8; ++i) fe[i] = slot == 0 ? bp[(int64_t)n_blocks * d + i] : 0.0;   // F(last)
     } else {
       f_at((lo + k0 + W) / 32, fe);
     }
@@ -309,7 +311,7 @@ __global__ __launch_bounds__(64 * kRepWaves) void k_rep_select(
     picked[a] = rank < r_k;
   }
   __syncthreads();
-  const int64_t out_row = ((int64_t)bi * Hkv + h) * U + u;
+  const int64_t out_row = ((int64_t)bi * Hkv + h) * u_stride + u;
   int32_t* ri = rep_idx + out_row * r_k;
   __shared__ int chosen[kMaxBlock];     // kept key offsets, ascending
   for (int a = c; a < nk; a += blockDim.x) {
@@ -344,13 +346,33 @@ __global__ __launch_bounds__(64 * kRepWaves) void k_rep_select(
 // vector representations).  grid (U, H_kv, batch), d threads.
 template <typename T>
 __global__ void k_mean_repr(const T* __restrict__ k, int64_t kv_cap, int Hkv, int d, int B,
-                            int n_init, int U, float* __restrict__ unit_repr) {
-  const int u = blockIdx.x, h = blockIdx.y, bi = blockIdx.z, c = threadIdx.x;
+                            int n_init, int u_begin, int u_stride, float* __restrict__ unit_repr) {
+  const int u = u_begin + (int)blockIdx.x, h = blockIdx.y, bi = blockIdx.z, c = threadIdx.x;
   const int64_t lo = unit_first_key(u, B, n_init), hi = (u + n_init / B + 1) * (int64_t)B;
   const T* kb = k + ((int64_t)bi * Hkv + h) * kv_cap * d + c;
   double acc = 0.0;
-  for (int64_t p = lo; p < hi; ++p) acc += (double)to_f32(kb[p * d]);
-  unit_repr[(((int64_t)bi * Hkv + h) * U + u) * d + c] = (float)(acc / (double)(hi - lo));
+  for (int64_t p0 = lo; p0 < hi; p0 += 16) {   // 16 rows requested before any is added
+    T v[16];
+#pragma unroll
+    for (int y = 0; y < 16; ++y) v[y] = kb[(p0 + y < hi ? p0 + y : hi - 1) * d];
+#pragma unroll
+    for (int y = 0; y < 16; ++y)
+      if (p0 + y < hi) acc += (double)to_f32(v[y]);
+  }
+  unit_repr[(((int64_t)bi * Hkv + h) * u_stride + u) * d + c] = (float)(acc / (double)(hi - lo));
+}
+
+// Blocks that units u_begin .. u_end-1 read: from the first unit's block to
+// ceil(W/B) + 2 blocks past the last one's (its keys' windows), clipped to
+// the context.  Sums and prefixes are local to this range: only differences
+// of the prefix enter a score.
+static void build_blocks(const BuildArgs& a, int64_t* jb0, int64_t* nbl) {
+  const int64_t nb = (a.n_ctx + a.B - 1) / a.B;
+  const int64_t j0 = a.n_init / a.B;
+  *jb0 = a.u_begin + j0;
+  int64_t jb1 = (int64_t)(a.u_end - 1) + j0 + (a.W + a.B - 1) / a.B + 2;
+  jb1 = jb1 < nb ? jb1 : nb;
+  *nbl = jb1 - *jb0;
 }
 
 // [block sums S][block prefix BP][32-row sub-block sums S32 (128-row blocks only)]
@@ -358,55 +380,65 @@ struct BuildWs {
   size_t s, bp, s32;
 };
 static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
-static BuildWs build_ws_layout(const BuildArgs& a) {
-  const int64_t nb = (a.n_ctx + a.B - 1) / a.B;
+static BuildWs build_ws_layout(const BuildArgs& a, int64_t nbl) {
   BuildWs w;
-  w.s = round256((size_t)a.batch * a.Hkv * nb * a.d * sizeof(double));
-  w.bp = round256((size_t)a.batch * a.Hkv * (nb + 1) * a.d * sizeof(double));
-  w.s32 = a.B == 128 ? (size_t)a.batch * a.Hkv * nb * 4 * a.d * sizeof(double) : 0;
+  w.s = round256((size_t)a.batch * a.Hkv * nbl * a.d * sizeof(double));
+  w.bp = round256((size_t)a.batch * a.Hkv * (nbl + 1) * a.d * sizeof(double));
+  w.s32 = a.B == 128 ? (size_t)a.batch * a.Hkv * nbl * 4 * a.d * sizeof(double) : 0;
   return w;
 }
+static size_t ws_total(const BuildWs& w) { return w.s + w.bp + w.s32; }
 
 size_t build_workspace_bytes(const BuildArgs& a) {
-  if (a.rep_mode != 0) return 0;
-  const BuildWs w = build_ws_layout(a);
-  return w.s + w.bp + w.s32;
+  if (a.rep_mode != 0 || a.u_end <= a.u_begin) return 0;
+  int64_t jb0, nbl;
+  build_blocks(a, &jb0, &nbl);
+  return ws_total(build_ws_layout(a, nbl));
+}
+
+size_t build_range_workspace_bytes(const BuildArgs& a, int64_t n_units) {
+  if (a.rep_mode != 0 || n_units < 1) return 0;
+  return ws_total(build_ws_layout(a, n_units + (a.W + a.B - 1) / a.B + 2));
 }
 
 template <typename T>
 static hipError_t launch_build_t(const BuildArgs& a, hipStream_t st) {
   const T* q = (const T*)a.q;
   const T* k = (const T*)a.k;
-  if (a.U <= 0) return hipSuccess;
+  const int n_u = a.u_end - a.u_begin;
+  if (n_u <= 0) return hipSuccess;
   if (a.rep_mode != 0) {
-    k_mean_repr<T><<<dim3(a.U, a.Hkv, a.batch), a.d, 0, st>>>(k, a.kv_cap, a.Hkv, a.d, a.B,
-                                                              a.n_init, a.U, a.unit_repr);
+    k_mean_repr<T><<<dim3(n_u, a.Hkv, a.batch), a.d, 0, st>>>(k, a.kv_cap, a.Hkv, a.d, a.B,
+                                                              a.n_init, a.u_begin, a.u_stride,
+                                                              a.unit_repr);
     return hipGetLastError();
   }
-  const int nb = (int)((a.n_ctx + a.B - 1) / a.B);
-  const BuildWs lay = build_ws_layout(a);
+  int64_t jb0, nbl;
+  build_blocks(a, &jb0, &nbl);
+  const BuildWs lay = build_ws_layout(a, nbl);
   double* S = (double*)a.ws;
   double* BP = (double*)((char*)a.ws + lay.s);
   double* S32 = lay.s32 > 0 ? (double*)((char*)a.ws + lay.s + lay.bp) : nullptr;
+  const int nb = (int)nbl;
   const dim3 sgrid(nb, a.Hkv, a.batch);
   if (S32)
     k_block_sums<T, 4><<<sgrid, kSumThreads, 0, st>>>(q, a.q_cap, a.Hq, a.Hkv, a.d, a.B, a.n_ctx,
-                                                      nb, S, S32);
+                                                      jb0, nb, S, S32);
   else
     k_block_sums<T, 1><<<sgrid, kSumThreads, 0, st>>>(q, a.q_cap, a.Hq, a.Hkv, a.d, a.B, a.n_ctx,
-                                                      nb, S, nullptr);
+                                                      jb0, nb, S, nullptr);
   k_block_prefix<<<dim3(a.Hkv, a.batch), a.d, 0, st>>>(S, BP, a.Hkv, a.d, nb);
   // heads per lane: 64 / (d / 8) head slots per wave
   const int hs = 64 / (a.d / 8), G = a.Hq / a.Hkv;
-  const dim3 grid(a.U, a.Hkv, a.batch);
+  const dim3 grid(n_u, a.Hkv, a.batch);
   if (G <= hs)
     k_rep_select<T, 1><<<grid, 64 * kRepWaves, 0, st>>>(
-        q, a.q_cap, k, a.kv_cap, a.Hq, a.Hkv, a.d, a.B, a.n_init, a.W, a.r_k, a.n_ctx, a.U, nb,
-        BP, S32, a.rep_idx, a.unit_repr);
+        q, a.q_cap, k, a.kv_cap, a.Hq, a.Hkv, a.d, a.B, a.n_init, a.W, a.r_k, a.n_ctx, a.u_begin,
+        a.u_stride, jb0, nb, BP, S32, a.rep_idx, a.unit_repr);
   else if (G <= 2 * hs)
     k_rep_select<T, 2><<<grid, 64 * kRepWaves, 0, st>>>(
-        q, a.q_cap, k, a.kv_cap, a.Hq, a.Hkv, a.d, a.B, a.n_init, a.W, a.r_k, a.n_ctx, a.U, nb,
-        BP, S32, a.rep_idx, a.unit_repr);
+        q, a.q_cap, k, a.kv_cap, a.Hq, a.Hkv, a.d, a.B, a.n_init, a.W, a.r_k, a.n_ctx, a.u_begin,
+        a.u_stride, jb0, nb, BP, S32, a.rep_idx, a.unit_repr);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -69,6 +69,9 @@ BuildArgs build_args(const infllm_config* c, int32_t batch, int64_t n_ctx) {
   a.bf16 = c->dtype == INFLLM_BF16;
   a.n_ctx = n_ctx;
   a.U = (int)num_units(c, n_ctx);
+  a.u_begin = 0;
+  a.u_end = a.U;
+  a.u_stride = a.U;
   return a;
 }
 
@@ -154,6 +157,8 @@ size_t infllm_workspace_size(const infllm_config* cfg, int32_t call, int32_t bat
   switch (call) {
     case INFLLM_CALL_BUILD:
       return n < 1 ? 0 : build_workspace_bytes(build_args(cfg, batch, n));
+    case INFLLM_CALL_BUILD_RANGE:
+      return n < 1 ? 0 : build_range_workspace_bytes(build_args(cfg, batch, 0), n);
     case INFLLM_CALL_SCORE:
       if (chunk_len < 1 || n_chunks < 1) return 0;
       return score_workspace_bytes(score_args(cfg, batch, chunk_len, n_chunks));
@@ -182,6 +187,39 @@ infllm_status infllm_build_units(const infllm_config* cfg, int32_t batch, const 
   const size_t need = build_workspace_bytes(a);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return INFLLM_ERR_WORKSPACE;
+  a.q = q;
+  a.q_cap = q_cap;
+  a.k = k;
+  a.kv_cap = kv_cap;
+  a.rep_idx = rep_idx;
+  a.unit_repr = unit_repr;
+  a.ws = workspace;
+  return launched(launch_build(a, (hipStream_t)stream));
+}
+
+infllm_status infllm_build_units_range(const infllm_config* cfg, int32_t batch, const void* q,
+                                       int64_t q_cap, const void* k, int64_t kv_cap,
+                                       int64_t n_ctx, int32_t u_begin, int32_t u_end,
+                                       int32_t pool_units, int32_t* rep_idx, float* unit_repr,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  infllm_status st = check_config(cfg);
+  if (st != INFLLM_OK) return st;
+  if (batch < 1 || n_ctx < 1 || q_cap < n_ctx || kv_cap < n_ctx) return INFLLM_ERR_INVALID_ARG;
+  BuildArgs a = build_args(cfg, batch, n_ctx);
+  if (u_begin < 0 || u_end < u_begin || u_end > a.U || pool_units < u_end)
+    return INFLLM_ERR_INVALID_ARG;
+  const bool tokens = cfg->rep_mode == INFLLM_REP_TOKENS;
+  if (!k || !aligned16(k) || (tokens && (!q || !aligned16(q)))) return INFLLM_ERR_INVALID_ARG;
+  if (u_end > u_begin) {
+    if (!unit_repr || !aligned16(unit_repr)) return INFLLM_ERR_INVALID_ARG;
+    if (tokens && (!rep_idx || !aligned16(rep_idx))) return INFLLM_ERR_INVALID_ARG;
+  }
+  const size_t need = build_range_workspace_bytes(a, u_end - u_begin);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return INFLLM_ERR_WORKSPACE;
+  a.u_begin = u_begin;
+  a.u_end = u_end;
+  a.u_stride = pool_units;
   a.q = q;
   a.q_cap = q_cap;
   a.k = k;

@@ -11,6 +11,7 @@ constexpr int kMaxTopK = 256;
 
 struct BuildArgs {
   int batch, Hq, Hkv, d, B, n_init, W, r_k, rep_mode, U;
+  int u_begin, u_end, u_stride;   // units built, rows of the output pool
   bool bf16;
   const void* q;
   int64_t q_cap;
@@ -55,6 +56,7 @@ struct AttendArgs {
 };
 
 size_t build_workspace_bytes(const BuildArgs& a);
+size_t build_range_workspace_bytes(const BuildArgs& a, int64_t n_units);
 hipError_t launch_build(const BuildArgs& a, hipStream_t st);
 size_t score_workspace_bytes(const ScoreArgs& a);
 hipError_t launch_score(const ScoreArgs& a, hipStream_t st);

@@ -20,9 +20,10 @@ INFLLM_OK, INFLLM_ERR_INVALID_ARG, INFLLM_ERR_UNSUPPORTED, INFLLM_ERR_WORKSPACE,
 INFLLM_F32, INFLLM_BF16 = 0, 1
 INFLLM_REP_TOKENS, INFLLM_REP_MEAN = 0, 1
 INFLLM_CALL_BUILD, INFLLM_CALL_SCORE, INFLLM_CALL_TOPK, INFLLM_CALL_ATTEND = 0, 1, 2, 3
+INFLLM_CALL_BUILD_RANGE = 4
 
 EXPORTED = ("infllm_num_units", "infllm_num_eligible", "infllm_workspace_size",
-            "infllm_build_units", "infllm_score_units", "infllm_topk_units", "infllm_attend",
+            "infllm_build_units", "infllm_build_units_range", "infllm_score_units", "infllm_topk_units", "infllm_attend",
             "infllm_status_string", "infllm_abi_version")
 
 
@@ -60,6 +61,9 @@ def lib() -> ctypes.CDLL:
         L.infllm_build_units.restype = _i32
         L.infllm_build_units.argtypes = [_cfgp, _i32, _vp, _i64, _vp, _i64, _i64, _vp, _vp, _vp,
                                          _sz, _vp]
+        L.infllm_build_units_range.restype = _i32
+        L.infllm_build_units_range.argtypes = [_cfgp, _i32, _vp, _i64, _vp, _i64, _i64, _i32, _i32,
+                                               _i32, _vp, _vp, _vp, _sz, _vp]
         L.infllm_score_units.restype = _i32
         L.infllm_score_units.argtypes = [_cfgp, _i32, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _i32,
                                          _vp, _vp, _sz, _vp]
@@ -175,6 +179,27 @@ def infllm_build_units(cfg, q, k, n_ctx: int, rep_idx, unit_repr, ws=None, strea
     _raise("infllm_build_units", lib().infllm_build_units(
         ctypes.byref(cfg), batch, _ptr(q), q_cap, k.data_ptr(), k.shape[2], n_ctx,
         _ptr(rep_idx), unit_repr.data_ptr(), wp, wb, _stream(stream, k)))
+
+
+def infllm_build_units_range(cfg, q, k, n_ctx: int, u_begin: int, u_end: int, rep_idx, unit_repr,
+                             ws=None, stream=None) -> None:
+    """Rows u_begin .. u_end-1 of a unit pool [batch, H_kv, pool_units, .]."""
+    dt = _dtype_of(cfg)
+    if cfg.rep_mode == INFLLM_REP_TOKENS:
+        _check(q, "q", dt, 4)
+        _check(rep_idx, "rep_idx", torch.int32, 4)
+    _check(k, "k", dt, 4)
+    _check(unit_repr, "unit_repr", torch.float32, 4)
+    batch, pool = k.shape[0], unit_repr.shape[2]
+    if tuple(unit_repr.shape) != (batch, cfg.n_kv_heads, pool, cfg.head_dim):
+        raise ValueError("unit_repr must be [batch, H_kv, pool_units, d]")
+    if rep_idx is not None and tuple(rep_idx.shape) != (batch, cfg.n_kv_heads, pool, cfg.rep_k):
+        raise ValueError("rep_idx must be [batch, H_kv, pool_units, r_k]")
+    q_cap = q.shape[2] if q is not None else 0
+    wp, wb = _ws(ws)
+    _raise("infllm_build_units_range", lib().infllm_build_units_range(
+        ctypes.byref(cfg), batch, _ptr(q), q_cap, k.data_ptr(), k.shape[2], n_ctx, u_begin, u_end,
+        pool, _ptr(rep_idx), unit_repr.data_ptr(), wp, wb, _stream(stream, k)))
 
 
 def infllm_score_units(cfg, q, q_off: int, q_pos: int, chunk_len: int, n_chunks: int, unit_repr,

@@ -12,6 +12,8 @@
  *
  * The four calls mirror that statement:
  *   infllm_build_units  -- representative-token selection per unit
+ *                          (infllm_build_units_range: a range of units, as
+ *                          they leave the window while streaming)
  *   infllm_score_units  -- chunk-query . unit-representation scores
  *   infllm_topk_units   -- top-k_m units per (sequence, KV head, chunk)
  *   infllm_attend       -- exact softmax attention over the working context
@@ -85,7 +87,8 @@ typedef enum {
   INFLLM_CALL_BUILD = 0,
   INFLLM_CALL_SCORE = 1,
   INFLLM_CALL_TOPK = 2,
-  INFLLM_CALL_ATTEND = 3
+  INFLLM_CALL_ATTEND = 3,
+  INFLLM_CALL_BUILD_RANGE = 4
 } infllm_call;
 
 typedef struct {
@@ -112,8 +115,8 @@ INFLLM_API int32_t infllm_num_units(const infllm_config *cfg, int64_t n_ctx);
 INFLLM_API int32_t infllm_num_eligible(const infllm_config *cfg, int64_t t_last, int32_t n_units);
 
 /* Workspace bytes `call` needs for the given sizes (0 if none).  For BUILD
- * pass n = n_ctx; for SCORE/TOPK/ATTEND pass the chunk geometry (n unused
- * for TOPK, which takes n_units in `n`). */
+ * pass n = n_ctx; for BUILD_RANGE n = u_end - u_begin; for SCORE/TOPK/ATTEND
+ * pass the chunk geometry (n unused for TOPK, which takes n_units in `n`). */
 INFLLM_API size_t infllm_workspace_size(const infllm_config *cfg, int32_t call, int32_t batch, int64_t n,
                              int32_t chunk_len, int32_t n_chunks);
 
@@ -143,6 +146,34 @@ INFLLM_API infllm_status infllm_build_units(const infllm_config *cfg, int32_t ba
                                  int64_t q_cap, const void *k, int64_t kv_cap, int64_t n_ctx,
                                  int32_t *rep_idx, float *unit_repr, void *workspace,
                                  size_t workspace_bytes, void *stream);
+
+/*
+ * infllm_build_units_range -- the same representations for units u_begin ..
+ * u_end-1 only: the streaming form, where a unit is added to the memory
+ * when its tokens leave the local window (summary page, "Approach":
+ * distant tokens are stored into memory units).  Scores use the queries
+ * of positions < n_ctx, i.e. the windows are truncated at the current
+ * position; a unit whose last key is at or before n_ctx-1-W (all its keys
+ * have left the window of position n_ctx-1) gets exactly what a build of
+ * any longer context gives it.  Work and workspace
+ * grow with the number of units (plus ceil(W/B)+2 blocks of queries), not
+ * with n_ctx.
+ *
+ *   q, k, n_ctx     as infllm_build_units
+ *   u_begin, u_end  0 <= u_begin <= u_end <= infllm_num_units(n_ctx)
+ *   pool_units      unit capacity (row count) of rep_idx / unit_repr, >= u_end
+ *   rep_idx    out rows u_begin .. u_end-1 of [batch, H_kv, pool_units, r_k]
+ *              (TOKENS; may be NULL for MEAN); other rows untouched
+ *   unit_repr  out rows u_begin .. u_end-1 of [batch, H_kv, pool_units, d]
+ *   workspace  >= infllm_workspace_size(cfg, INFLLM_CALL_BUILD_RANGE, batch,
+ *              u_end - u_begin, 0, 0)
+ */
+INFLLM_API infllm_status infllm_build_units_range(const infllm_config *cfg, int32_t batch,
+                                       const void *q, int64_t q_cap, const void *k,
+                                       int64_t kv_cap, int64_t n_ctx, int32_t u_begin,
+                                       int32_t u_end, int32_t pool_units, int32_t *rep_idx,
+                                       float *unit_repr, void *workspace,
+                                       size_t workspace_bytes, void *stream);
 
 /*
  * infllm_score_units -- relevance of every unit to each query chunk.

@@ -31,7 +31,7 @@ def cfg(**kw):
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 9
+    assert len(names) == 10
     assert set(names) == set(F.EXPORTED)
     L = F.lib()
     for n in names:
@@ -114,6 +114,36 @@ def test_build_argument_validation():
     # MEAN needs no queries, no rep_idx and no workspace
     cm = cfg(rep_mode=F.INFLLM_REP_MEAN)
     assert F.infllm_workspace_size(cm, F.INFLLM_CALL_BUILD, 1, 8192) == 0
+
+
+def test_build_range_validation_and_workspace():
+    c = cfg()
+    L = F.lib()
+    U = F.infllm_num_units(c, 8192)             # 63 units
+    call = lambda **kw: L.infllm_build_units_range(
+        ctypes.byref(c), kw.get("batch", 1), kw.get("q", FAKE), 8192, kw.get("k", FAKE), 8192,
+        kw.get("n_ctx", 8192), kw.get("ub", 10), kw.get("ue", 20), kw.get("pool", 64),
+        kw.get("rep", FAKE), kw.get("repr", FAKE), kw.get("ws", FAKE), kw.get("wsb", 1 << 30),
+        None)
+    assert call(ub=-1) == F.INFLLM_ERR_INVALID_ARG
+    assert call(ub=21) == F.INFLLM_ERR_INVALID_ARG           # u_end < u_begin
+    assert call(ue=U + 1, pool=U + 1) == F.INFLLM_ERR_INVALID_ARG
+    assert call(pool=19) == F.INFLLM_ERR_INVALID_ARG         # pool smaller than u_end
+    assert call(n_ctx=0) == F.INFLLM_ERR_INVALID_ARG
+    assert call(rep=None) == F.INFLLM_ERR_INVALID_ARG
+    assert call(repr=MISALIGNED) == F.INFLLM_ERR_INVALID_ARG
+    assert call(q=None) == F.INFLLM_ERR_INVALID_ARG
+    need = F.infllm_workspace_size(c, F.INFLLM_CALL_BUILD_RANGE, 1, 10)
+    assert need > 0
+    assert call(wsb=need - 1) == F.INFLLM_ERR_WORKSPACE
+    # an empty range succeeds without touching a device
+    assert call(ub=5, ue=5, rep=None, repr=None, ws=None, wsb=0) == F.INFLLM_OK
+    # range workspace grows with the range, not with the context
+    small = F.infllm_workspace_size(c, F.INFLLM_CALL_BUILD_RANGE, 1, 4)
+    assert small < need < F.infllm_workspace_size(c, F.INFLLM_CALL_BUILD, 1, 1 << 20)
+    assert F.infllm_workspace_size(c, F.INFLLM_CALL_BUILD_RANGE, 1, 0) == 0
+    cm = cfg(rep_mode=F.INFLLM_REP_MEAN)
+    assert F.infllm_workspace_size(cm, F.INFLLM_CALL_BUILD_RANGE, 1, 10) == 0
 
 
 def test_score_topk_attend_validation():

@@ -14,6 +14,7 @@ import pytest
 import torch
 
 import bench
+from block_level_kv_amd import infllm as F
 from block_level_kv_amd import synth
 from gpu_helpers import assert_close, check_selection, tolerance
 
@@ -30,21 +31,25 @@ def run(name):
     return w, p
 
 
-def check_build(orc, w, p, samples):
-    """samples: list of (b, h, u_lo, u_hi)."""
+def check_build(orc, w, p, samples, n_ctx=None, rep_idx=None, repr_=None):
+    """samples: list of (b, h, u_lo, u_hi); by default the pipeline's own
+    pool, built at the workload's context."""
     G, B = w.group, w.block
+    n_ctx = w.n_ctx if n_ctx is None else n_ctx
+    rep_idx = p.rep_idx if rep_idx is None else rep_idx
+    repr_ = p.repr if repr_ is None else repr_
     exemptions = 0
     for bi, h, u_lo, u_hi in samples:
-        k = p.inp["k"][bi, h, :w.n_ctx].cpu()
-        repr_g = p.repr[bi, h, u_lo:u_hi].cpu().numpy()
+        k = p.inp["k"][bi, h, :n_ctx].cpu()
+        repr_g = repr_[bi, h, u_lo:u_hi].cpu().numpy()
         if w.rep_mode == "mean":
             repr_o = orc.build_mean(k, B, w.n_init, u_lo, u_hi)
             np.testing.assert_array_equal(repr_g, repr_o.astype(np.float32))
             continue
-        qg = p.inp["q"][bi, h * G:(h + 1) * G, :w.n_ctx].cpu()
-        rep_o, repr_o, ks_o = orc.build_tokens(qg, k, w.n_ctx, B, w.n_init, w.window, w.rep_k,
+        qg = p.inp["q"][bi, h * G:(h + 1) * G, :n_ctx].cpu()
+        rep_o, repr_o, ks_o = orc.build_tokens(qg, k, n_ctx, B, w.n_init, w.window, w.rep_k,
                                                u_lo, u_hi)
-        rep_g = p.rep_idx[bi, h, u_lo:u_hi].cpu().numpy()
+        rep_g = rep_idx[bi, h, u_lo:u_hi].cpu().numpy()
         for i in range(u_hi - u_lo):
             if np.array_equal(rep_g[i], rep_o[i]):
                 np.testing.assert_array_equal(repr_g[i], repr_o[i].astype(np.float32))
@@ -109,6 +114,27 @@ def test_fullsize_llama3_128k_decode(orc):
     k, v = p.inp["k"].cpu(), p.inp["v"].cpu()
     check_outputs(orc, w, qd, k, v, p.out_dec, p.sel_dec,
                   [(s, s, w.n_ctx + s) for s in (0, 1, 128, 255)])
+
+
+def test_fullsize_llama3_128k_range_build(orc):
+    """Streaming unit build at the full size: the last units of the 128K
+    context (windows truncated at the end), and the newest units of a
+    shorter, ragged context, each written into its rows of a pool."""
+    w = synth.WORKLOADS["llama3_8b_128k_decode"]
+    p = bench.Pipeline(w)
+    U = p.U
+    rep = torch.full_like(p.rep_idx, -7)
+    repr_ = torch.full_like(p.repr, float("nan"))
+    ws = F.workspace(p.cfg, F.INFLLM_CALL_BUILD_RANGE, w.batch, 16)
+    F.infllm_build_units_range(p.cfg, p.inp["q"], p.inp["k"], w.n_ctx, U - 16, U, rep, repr_, ws)
+    torch.cuda.synchronize()
+    check_build(orc, w, p, [(0, 0, U - 8, U), (3, 7, U - 16, U - 8)], rep_idx=rep, repr_=repr_)
+    n_mid = 100003
+    Um = F.infllm_num_units(p.cfg, n_mid)
+    F.infllm_build_units_range(p.cfg, p.inp["q"], p.inp["k"], n_mid, Um - 8, Um, rep, repr_, ws)
+    torch.cuda.synchronize()
+    check_build(orc, w, p, [(1, 2, Um - 8, Um)], n_ctx=n_mid, rep_idx=rep, repr_=repr_)
+    assert torch.isnan(repr_[:, :, :Um - 8]).all() and (rep[:, :, :Um - 8] == -7).all()
 
 
 def test_fullsize_llama3_1m_decode_recall(orc):

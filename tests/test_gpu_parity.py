@@ -70,6 +70,101 @@ def test_build_parity(orc, data, name):
     np.testing.assert_array_equal(rg[same], repr_o.astype(np.float32)[same])
 
 
+def check_units(orc, w, inp, n_ctx, u_lo, u_hi, rep_g, repr_g):
+    """GPU rows u_lo .. u_hi-1 (rep_g / repr_g: [b, H_kv, u_hi-u_lo, .]) against
+    the oracle's build of a context of n_ctx tokens, per (batch, KV head)."""
+    G, B = w.group, w.block
+    exemptions = 0
+    for bi in range(w.batch):
+        for h in range(w.n_kv_heads):
+            k = inp["k"][bi, h, :n_ctx]
+            if w.rep_mode == "mean":
+                repr_o = orc.build_mean(k, B, w.n_init, u_lo, u_hi)
+                np.testing.assert_array_equal(repr_g[bi, h], repr_o.astype(np.float32))
+                continue
+            rep_o, repr_o, ks_o = orc.build_tokens(inp["q"][bi, h * G:(h + 1) * G, :n_ctx], k,
+                                                   n_ctx, B, w.n_init, w.window, w.rep_k,
+                                                   u_lo, u_hi)
+            for i in range(u_hi - u_lo):
+                if np.array_equal(rep_g[bi, h, i], rep_o[i]):
+                    np.testing.assert_array_equal(repr_g[bi, h, i], repr_o[i].astype(np.float32))
+                    continue
+                start = (u_lo + i + w.n_init // B) * B
+                by_pos = {start + s: ks_o[i, s] for s in range(B) if np.isfinite(ks_o[i, s])}
+                exemptions += check_selection(rep_g[bi, h, i], rep_o[i], by_pos)
+    assert exemptions <= max(2, w.batch * w.n_kv_heads * (u_hi - u_lo) // 50)
+
+
+def range_pool(cfg, w, pool):
+    """A unit pool of `pool` rows filled with values no build writes."""
+    repr_ = torch.full((w.batch, w.n_kv_heads, pool, w.head_dim), float("nan"), device="cuda")
+    rep = None
+    if w.rep_mode == "tokens":
+        rep = torch.full((w.batch, w.n_kv_heads, pool, w.rep_k), -7, dtype=torch.int32,
+                         device="cuda")
+    return rep, repr_
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_build_range_streaming(orc, data, name):
+    """Units appended to a pool as their keys leave the local window, one
+    range call per step at the context reached so far; the units still in
+    the window at the end are built at the final context.  The pool equals
+    the oracle's build of the final context: a closed unit's windows lie
+    inside every later context."""
+    w, inp, dev = data(name)
+    cfg = cfg_of(w)
+    B = w.block
+    U = F.infllm_num_units(cfg, w.n_ctx)
+    rep, repr_ = range_pool(cfg, w, U + 3)
+    ws = F.workspace(cfg, F.INFLLM_CALL_BUILD_RANGE, w.batch, U, device="cuda")
+    rng = np.random.default_rng(11)
+    done, n, calls = 0, w.n_init + w.window + 1, 0
+    while n < w.n_ctx:
+        closed = done
+        while closed < U and orc.unit_keys(closed, B, w.n_init)[1] <= n - w.window:
+            closed += 1
+        F.infllm_build_units_range(cfg, dev["q"], dev["k"], n, done, closed, rep, repr_, ws)
+        done, calls = closed, calls + 1
+        n += int(rng.integers(1, 3 * B))
+    F.infllm_build_units_range(cfg, dev["q"], dev["k"], w.n_ctx, done, U, rep, repr_, ws)
+    torch.cuda.synchronize()
+    assert calls >= 5 and 0 < done < U
+    rg = repr_.cpu().numpy()
+    assert np.isnan(rg[:, :, U:]).all()
+    repg = None
+    if rep is not None:
+        repg = rep.cpu().numpy()
+        assert (repg[:, :, U:] == -7).all()
+        repg = repg[:, :, :U]
+    check_units(orc, w, inp, w.n_ctx, 0, U, repg, rg[:, :, :U])
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_build_range_truncated(orc, data, name):
+    """A range that ends in units whose windows run past the current
+    position (scores truncated there), written at its rows of a larger pool
+    with every other row untouched; an empty range writes nothing."""
+    w, inp, dev = data(name)
+    cfg = cfg_of(w)
+    n_mid = w.n_ctx - 333
+    Um = F.infllm_num_units(cfg, n_mid)
+    lo = Um // 3
+    rep, repr_ = range_pool(cfg, w, Um + 5)
+    ws = F.workspace(cfg, F.INFLLM_CALL_BUILD_RANGE, w.batch, Um - lo, device="cuda")
+    F.infllm_build_units_range(cfg, dev["q"], dev["k"], n_mid, lo, Um, rep, repr_, ws)
+    F.infllm_build_units_range(cfg, dev["q"], dev["k"], n_mid, 2, 2, rep, repr_, ws)
+    torch.cuda.synchronize()
+    rg = repr_.cpu().numpy()
+    assert np.isnan(rg[:, :, :lo]).all() and np.isnan(rg[:, :, Um:]).all()
+    repg = None
+    if rep is not None:
+        repg = rep.cpu().numpy()
+        assert (repg[:, :, :lo] == -7).all() and (repg[:, :, Um:] == -7).all()
+        repg = repg[:, :, lo:Um]
+    check_units(orc, w, inp, n_mid, lo, Um, repg, rg[:, :, lo:Um])
+
+
 @pytest.mark.parametrize("name", list(CASES))
 def test_score_and_topk_parity(orc, data, name):
     w, inp, dev = data(name)
