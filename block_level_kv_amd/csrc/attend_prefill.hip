@@ -132,7 +132,16 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_prefill(AttendArgs a, Pr
 
   const int q_first = qt * TQ;                          // within the chunk
   const int nq = a.L - q_first < TQ ? a.L - q_first : TQ;
-  const int64_t ta = a.q_pos + (int64_t)ch * a.L + q_first;  // first query position
+  const int64_t base = seq_base(a.pos, a.q_pos, bi);
+  if (a.pos && !seq_pos_ok(base, a.n_pos, a.kv_cap)) {
+    // a sequence whose position does not fit its KV buffer: every split
+    // leaves before any key load or arrival count, split 0 writes NaN rows
+    if (split == 0)
+      nan_rows<bf16_t>((bf16_t*)a.out, a.lse, (int64_t)bi * a.Hq + (int64_t)h * G, G, a.out_cap,
+                       a.out_off + (int64_t)ch * a.L + q_first, nq, kD, tid, kThreads);
+    return;
+  }
+  const int64_t ta = base + (int64_t)ch * a.L + q_first;    // first query position
   const int64_t tb = ta + nq - 1;                            // last valid query position
 
   // the ring: one variable per stage and operand, so that the compiler can

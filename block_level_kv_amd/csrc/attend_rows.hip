@@ -80,7 +80,16 @@ __global__ __launch_bounds__(kRowsThreads) void k_attend_rows(AttendArgs a) {
   const int h = blockIdx.z % a.Hkv, bi = blockIdx.z / a.Hkv;
   const int tid = threadIdx.x, lane = tid % 64, seg = tid % 16, kl = tid / 16;
   const int ch = pos / a.L;
-  const int64_t t = a.q_pos + pos;
+  const int64_t base = seq_base(a.pos, a.q_pos, bi);
+  if (a.pos && !seq_pos_ok(base, a.n_pos, a.kv_cap)) {
+    // a sequence whose position does not fit its KV buffer: every split
+    // leaves before any key load or arrival count, split 0 writes NaN rows
+    if (split == 0)
+      nan_rows<T>((T*)a.out, a.lse, (int64_t)bi * a.Hq + (int64_t)h * G, G, a.out_cap,
+                  a.out_off + pos, 1, D, tid, kRowsThreads);
+    return;
+  }
+  const int64_t t = base + pos;
 
   __shared__ int64_t iv_lo[kMaxIntervals];
   __shared__ int64_t iv_first[kMaxIntervals + 1];  // first key index of each interval

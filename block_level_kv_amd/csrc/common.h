@@ -42,6 +42,40 @@ __host__ __device__ __forceinline__ int64_t eligible_units(int64_t t_last, int64
   return e < U ? e : U;
 }
 
+// Per-sequence positions (variable-length batches).  Positions are kept
+// below 2^31 - 128 so that key indices and tile ends fit 32 bits.
+constexpr int64_t kPosLimit = ((int64_t)1 << 31) - 128;
+
+// Whether a sequence whose first query sits at `base` can hold `n_pos`
+// query positions in a KV buffer of kv_cap rows.
+__host__ __device__ __forceinline__ bool seq_pos_ok(int64_t base, int64_t n_pos, int64_t kv_cap) {
+  return base >= 0 && base <= kv_cap - n_pos && base <= kPosLimit - n_pos;
+}
+
+// First query position of sequence bi: the per-sequence array when there is
+// one (read through the scalar cache, uniform per workgroup), else the
+// call's single position.
+__device__ __forceinline__ int64_t seq_base(const int64_t* pos, int64_t q_pos, int bi) {
+  return pos ? pos[bi] : q_pos;
+}
+
+// Output rows [row0, row0 + n_rows) of query heads [qh0, qh0 + n_heads) set
+// to NaN (and their log-sum-exp, if any): what a sequence with an invalid
+// position receives.  Executed by the n_threads threads of a workgroup.
+template <typename T>
+__device__ __forceinline__ void nan_rows(T* out, float* lse, int64_t qh0, int n_heads,
+                                         int64_t out_cap, int64_t row0, int n_rows, int D,
+                                         int tid, int n_threads) {
+  const float nan = __builtin_nanf("");
+  const int per_head = n_rows * D;
+  for (int i = tid; i < n_heads * per_head; i += n_threads) {
+    const int g = i / per_head, r = (i % per_head) / D, c = i % D;
+    const int64_t row = (qh0 + g) * out_cap + row0 + r;
+    out[row * D + c] = from_f32<T>(nan);
+    if (lse && c == 0) lse[row] = nan;
+  }
+}
+
 // Eight consecutive columns of a row, raw bits, widened to fp64 on use.
 template <typename T> struct Raw8;
 template <> struct Raw8<bf16_t> {

@@ -230,11 +230,15 @@ infllm_status infllm_build_units_range(const infllm_config* cfg, int32_t batch, 
   return launched(launch_build(a, (hipStream_t)stream));
 }
 
-infllm_status infllm_score_units(const infllm_config* cfg, int32_t batch, const void* q,
-                                 int64_t q_cap, int64_t q_off, int64_t q_pos, int32_t chunk_len,
-                                 int32_t n_chunks, const float* unit_repr, int32_t n_units,
-                                 float* scores, void* workspace, size_t workspace_bytes,
-                                 void* stream) {
+}  // extern "C"
+
+// Shared by the single-position and per-sequence-position forms: pos (device,
+// [batch]) replaces q_pos when non-null.
+static infllm_status score_impl(const infllm_config* cfg, int32_t batch, const void* q,
+                                int64_t q_cap, int64_t q_off, int64_t q_pos, const int64_t* pos,
+                                int32_t chunk_len, int32_t n_chunks, const float* unit_repr,
+                                int32_t n_units, float* scores, void* workspace,
+                                size_t workspace_bytes, void* stream) {
   infllm_status st = check_config(cfg);
   if (st != INFLLM_OK) return st;
   if (batch < 1 || chunk_len < 1 || n_chunks < 1 || n_units < 0 || q_off < 0 || q_pos < 0)
@@ -254,9 +258,31 @@ infllm_status infllm_score_units(const infllm_config* cfg, int32_t batch, const 
   a.q_cap = q_cap;
   a.q_off = q_off;
   a.q_pos = q_pos;
+  a.pos = pos;
   a.repr = unit_repr;
   a.scores = scores;
   return launched(launch_score(a, (hipStream_t)stream));
+}
+
+extern "C" {
+
+infllm_status infllm_score_units(const infllm_config* cfg, int32_t batch, const void* q,
+                                 int64_t q_cap, int64_t q_off, int64_t q_pos, int32_t chunk_len,
+                                 int32_t n_chunks, const float* unit_repr, int32_t n_units,
+                                 float* scores, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  return score_impl(cfg, batch, q, q_cap, q_off, q_pos, nullptr, chunk_len, n_chunks, unit_repr,
+                    n_units, scores, workspace, workspace_bytes, stream);
+}
+
+infllm_status infllm_score_units_varlen(const infllm_config* cfg, int32_t batch, const void* q,
+                                        int64_t q_cap, int64_t q_off, const int64_t* pos,
+                                        int32_t chunk_len, int32_t n_chunks,
+                                        const float* unit_repr, int32_t n_units, float* scores,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (!pos || (uintptr_t)pos % 8 != 0) return INFLLM_ERR_INVALID_ARG;
+  return score_impl(cfg, batch, q, q_cap, q_off, 0, pos, chunk_len, n_chunks, unit_repr, n_units,
+                    scores, workspace, workspace_bytes, stream);
 }
 
 infllm_status infllm_topk_units(const infllm_config* cfg, int32_t batch, int32_t n_chunks,
@@ -281,11 +307,17 @@ infllm_status infllm_topk_units(const infllm_config* cfg, int32_t batch, int32_t
   return launched(launch_topk(a, (hipStream_t)stream));
 }
 
-infllm_status infllm_attend(const infllm_config* cfg, int32_t batch, const void* q, int64_t q_cap,
-                            int64_t q_off, int64_t q_pos, int32_t chunk_len, int32_t n_chunks,
-                            const void* k, const void* v, int64_t kv_cap, const int32_t* sel,
-                            void* out, float* lse, int64_t out_cap, int64_t out_off,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+// Shared by the single-position and per-sequence-position forms.  With pos
+// (device, [batch]) the positions are checked in the kernels: a sequence
+// whose position does not fit kv_cap gets NaN rows.
+static infllm_status attend_impl(const infllm_config* cfg, int32_t batch, const void* q,
+                                 int64_t q_cap, int64_t q_off, int64_t q_pos, const int64_t* pos,
+                                 int32_t chunk_len, int32_t n_chunks, const void* k,
+                                 const void* v, int64_t kv_cap, const int32_t* sel, void* out,
+                                 float* lse, int64_t out_cap, int64_t out_off, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
   infllm_status st = check_config(cfg);
   if (st != INFLLM_OK) return st;
   if (batch < 1 || chunk_len < 1 || n_chunks < 1 || q_off < 0 || q_pos < 0 || out_off < 0)
@@ -294,7 +326,7 @@ infllm_status infllm_attend(const infllm_config* cfg, int32_t batch, const void*
   if ((int64_t)batch * cfg->n_kv_heads > 65535) return INFLLM_ERR_UNSUPPORTED;
   if (q_off + n_pos > q_cap || q_pos + n_pos > kv_cap || out_off + n_pos > out_cap)
     return INFLLM_ERR_INVALID_ARG;
-  if (q_pos + n_pos > ((int64_t)1 << 31) - 128) return INFLLM_ERR_UNSUPPORTED;
+  if (q_pos + n_pos > kPosLimit) return INFLLM_ERR_UNSUPPORTED;
   if (!q || !k || !v || !out || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return INFLLM_ERR_INVALID_ARG;
   if (cfg->top_k > 0 && (!sel || !aligned16(sel))) return INFLLM_ERR_INVALID_ARG;
@@ -310,6 +342,7 @@ infllm_status infllm_attend(const infllm_config* cfg, int32_t batch, const void*
   a.q_cap = q_cap;
   a.q_off = q_off;
   a.q_pos = q_pos;
+  a.pos = pos;
   a.k = k;
   a.v = v;
   a.kv_cap = kv_cap;
@@ -326,6 +359,29 @@ infllm_status infllm_attend(const infllm_config* cfg, int32_t batch, const void*
   }
   hipStream_t s = (hipStream_t)stream;
   return launched(mfma ? launch_attend_prefill(a, splits, s) : launch_attend_rows(a, splits, s));
+}
+
+extern "C" {
+
+infllm_status infllm_attend(const infllm_config* cfg, int32_t batch, const void* q, int64_t q_cap,
+                            int64_t q_off, int64_t q_pos, int32_t chunk_len, int32_t n_chunks,
+                            const void* k, const void* v, int64_t kv_cap, const int32_t* sel,
+                            void* out, float* lse, int64_t out_cap, int64_t out_off,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return attend_impl(cfg, batch, q, q_cap, q_off, q_pos, nullptr, chunk_len, n_chunks, k, v,
+                     kv_cap, sel, out, lse, out_cap, out_off, workspace, workspace_bytes, stream);
+}
+
+infllm_status infllm_attend_varlen(const infllm_config* cfg, int32_t batch, const void* q,
+                                   int64_t q_cap, int64_t q_off, const int64_t* pos,
+                                   int32_t chunk_len, int32_t n_chunks, const void* k,
+                                   const void* v, int64_t kv_cap, const int32_t* sel, void* out,
+                                   float* lse, int64_t out_cap, int64_t out_off, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  if (!pos || (uintptr_t)pos % 8 != 0) return INFLLM_ERR_INVALID_ARG;
+  // q_pos = 0 here only checks that kv_cap can hold one sequence's positions
+  return attend_impl(cfg, batch, q, q_cap, q_off, 0, pos, chunk_len, n_chunks, k, v, kv_cap, sel,
+                     out, lse, out_cap, out_off, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

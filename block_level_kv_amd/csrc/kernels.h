@@ -27,6 +27,7 @@ struct ScoreArgs {
   bool bf16;
   const void* q;
   int64_t q_cap, q_off, q_pos;
+  const int64_t* pos;  // device [batch] first query position per sequence, or null (q_pos)
   const float* repr;
   float* scores;
   void* ws;  // fp64 partial query sums of long chunks
@@ -43,6 +44,7 @@ struct AttendArgs {
   bool bf16;
   const void* q;
   int64_t q_cap, q_off, q_pos;
+  const int64_t* pos;  // device [batch] first query position per sequence, or null (q_pos)
   const void* k;
   const void* v;
   int64_t kv_cap;

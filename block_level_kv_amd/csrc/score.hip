@@ -154,7 +154,8 @@ __global__ __launch_bounds__(kScoreThreads) void k_chunk_qsum(
 // Scores of a slice of kUnitsPerWG units.  grid (slices, n_chunks * H_kv, batch).
 template <typename T, int G, int D>
 __global__ __launch_bounds__(kScoreThreads) void k_score_units(
-    const T* __restrict__ q, int64_t q_cap, int64_t q_off, int64_t q_pos, int L, int Hq, int Hkv,
+    const T* __restrict__ q, int64_t q_cap, int64_t q_off, int64_t q_pos,
+    const int64_t* __restrict__ pos, int L, int Hq, int Hkv,
     int B, int n_init, int W, const float* __restrict__ repr, int U, float* __restrict__ scores,
     int n_chunks, const double* __restrict__ parts, int n_parts) {
   using Rows = UnitRows<D, kUnitsPerWG / UnitRows<D, 1>::kPerSlot>;
@@ -209,7 +210,11 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_units(
     __syncthreads();
   }
 
-  const int64_t t_last = q_pos + (int64_t)ch * L + L - 1;
+  // a position out of range leaves no unit eligible (negative) or all of
+  // them (large); the clamp keeps the sum below overflow
+  int64_t base = seq_base(pos, q_pos, bi);
+  base = base < -kPosLimit ? -kPosLimit : (base > kPosLimit ? kPosLimit : base);
+  const int64_t t_last = base + (int64_t)ch * L + L - 1;
   const int64_t e = eligible_units(t_last, U, B, n_init, W);
   const int cg = tid % 64 % (D / 8);
   double qv[8];
@@ -228,7 +233,8 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_units(
 // grid (parts, H_kv, batch * n_chunks).
 template <typename T, int G, int D, int ROWS>
 __global__ __launch_bounds__(kScoreThreads) void k_score_fused(
-    const T* __restrict__ q, int64_t q_cap, int64_t q_off, int64_t q_pos, int L, int Hq, int Hkv,
+    const T* __restrict__ q, int64_t q_cap, int64_t q_off, int64_t q_pos,
+    const int64_t* __restrict__ pos, int L, int Hq, int Hkv,
     int B, int n_init, int W, const float* __restrict__ repr, int U, float* __restrict__ scores,
     int n_chunks, double* __restrict__ parts, int* __restrict__ count) {
   using Rows = UnitRows<D, kBatchUnits / UnitRows<D, 1>::kPerSlot>;
@@ -264,7 +270,11 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_fused(
   const double qs = sum_parts<D>(pp, n_parts, tid % D);
   if (tid < D) qsum[tid] = qs;
   __syncthreads();
-  const int64_t t_last = q_pos + (int64_t)ch * L + L - 1;
+  // a position out of range leaves no unit eligible (negative) or all of
+  // them (large); the clamp keeps the sum below overflow
+  int64_t base = seq_base(pos, q_pos, bi);
+  base = base < -kPosLimit ? -kPosLimit : (base > kPosLimit ? kPosLimit : base);
+  const int64_t t_last = base + (int64_t)ch * L + L - 1;
   const int64_t e = eligible_units(t_last, U, B, n_init, W);
   const int cg = tid % 64 % (D / 8);
   double qv[8];
@@ -298,7 +308,7 @@ static void launch_parts(const ScoreArgs& a, int parts, double* pw, hipStream_t 
   const dim3 grid(parts, a.Hkv, a.batch * a.n_chunks);
   if (score_fused(a))
     k_score_fused<T, G, D, ROWS><<<grid, kScoreThreads, 0, st>>>(
-        (const T*)a.q, a.q_cap, a.q_off, a.q_pos, a.L, a.Hq, a.Hkv, a.B, a.n_init, a.W, a.repr,
+        (const T*)a.q, a.q_cap, a.q_off, a.q_pos, a.pos, a.L, a.Hq, a.Hkv, a.B, a.n_init, a.W, a.repr,
         a.U, a.scores, a.n_chunks, pw, (int*)a.ws);
   else
     k_chunk_qsum<T, G, D, ROWS><<<grid, kScoreThreads, 0, st>>>(
@@ -316,7 +326,7 @@ static hipError_t launch_score_tgd(const ScoreArgs& a, hipStream_t st) {
   }
   dim3 grid((a.U + kUnitsPerWG - 1) / kUnitsPerWG, a.n_chunks * a.Hkv, a.batch);
   k_score_units<T, G, D><<<grid, kScoreThreads, 0, st>>>(
-      (const T*)a.q, a.q_cap, a.q_off, a.q_pos, a.L, a.Hq, a.Hkv, a.B, a.n_init, a.W, a.repr, a.U,
+      (const T*)a.q, a.q_cap, a.q_off, a.q_pos, a.pos, a.L, a.Hq, a.Hkv, a.B, a.n_init, a.W, a.repr, a.U,
       a.scores, a.n_chunks, pw, parts);
   return hipGetLastError();
 }

@@ -23,8 +23,9 @@ INFLLM_CALL_BUILD, INFLLM_CALL_SCORE, INFLLM_CALL_TOPK, INFLLM_CALL_ATTEND = 0, 
 INFLLM_CALL_BUILD_RANGE = 4
 
 EXPORTED = ("infllm_num_units", "infllm_num_eligible", "infllm_workspace_size",
-            "infllm_build_units", "infllm_build_units_range", "infllm_score_units", "infllm_topk_units", "infllm_attend",
-            "infllm_status_string", "infllm_abi_version")
+            "infllm_build_units", "infllm_build_units_range", "infllm_score_units",
+            "infllm_score_units_varlen", "infllm_topk_units", "infllm_attend",
+            "infllm_attend_varlen", "infllm_status_string", "infllm_abi_version")
 
 
 class infllm_config(ctypes.Structure):
@@ -67,6 +68,12 @@ def lib() -> ctypes.CDLL:
         L.infllm_score_units.restype = _i32
         L.infllm_score_units.argtypes = [_cfgp, _i32, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _i32,
                                          _vp, _vp, _sz, _vp]
+        L.infllm_score_units_varlen.restype = _i32
+        L.infllm_score_units_varlen.argtypes = [_cfgp, _i32, _vp, _i64, _i64, _vp, _i32, _i32, _vp,
+                                                _i32, _vp, _vp, _sz, _vp]
+        L.infllm_attend_varlen.restype = _i32
+        L.infllm_attend_varlen.argtypes = [_cfgp, _i32, _vp, _i64, _i64, _vp, _i32, _i32, _vp, _vp,
+                                           _i64, _vp, _vp, _vp, _i64, _i64, _vp, _sz, _vp]
         L.infllm_topk_units.restype = _i32
         L.infllm_topk_units.argtypes = [_cfgp, _i32, _i32, _vp, _i32, _vp, _vp, _sz, _vp]
         L.infllm_attend.restype = _i32
@@ -216,6 +223,28 @@ def infllm_score_units(cfg, q, q_off: int, q_pos: int, chunk_len: int, n_chunks:
         unit_repr.data_ptr(), U, scores.data_ptr(), wp, wb, _stream(stream, q)))
 
 
+def _check_pos(pos, batch):
+    _check(pos, "pos", torch.int64, 1)
+    if pos.shape[0] != batch:
+        raise ValueError("pos must be [batch] int64")
+
+
+def infllm_score_units_varlen(cfg, q, q_off: int, pos, chunk_len: int, n_chunks: int, unit_repr,
+                              scores, ws=None, stream=None) -> None:
+    """pos: device int64 [batch], the position of row q_off per sequence."""
+    _check(q, "q", _dtype_of(cfg), 4)
+    _check(unit_repr, "unit_repr", torch.float32, 4)
+    _check(scores, "scores", torch.float32, 4)
+    batch, U = q.shape[0], unit_repr.shape[2]
+    _check_pos(pos, batch)
+    if tuple(scores.shape) != (batch, cfg.n_kv_heads, n_chunks, U):
+        raise ValueError("scores must be [batch, H_kv, n_chunks, U]")
+    wp, wb = _ws(ws)
+    _raise("infllm_score_units_varlen", lib().infllm_score_units_varlen(
+        ctypes.byref(cfg), batch, q.data_ptr(), q.shape[2], q_off, pos.data_ptr(), chunk_len,
+        n_chunks, unit_repr.data_ptr(), U, scores.data_ptr(), wp, wb, _stream(stream, q)))
+
+
 def infllm_topk_units(cfg, scores, sel, ws=None, stream=None) -> None:
     _check(scores, "scores", torch.float32, 4)
     _check(sel, "sel", torch.int32, 4)
@@ -245,4 +274,26 @@ def infllm_attend(cfg, q, q_off: int, q_pos: int, chunk_len: int, n_chunks: int,
     _raise("infllm_attend", lib().infllm_attend(
         ctypes.byref(cfg), q.shape[0], q.data_ptr(), q.shape[2], q_off, q_pos, chunk_len, n_chunks,
         k.data_ptr(), v.data_ptr(), k.shape[2], _ptr(sel), out.data_ptr(), _ptr(lse),
+        out.shape[2], out_off, wp, wb, _stream(stream, q)))
+
+
+def infllm_attend_varlen(cfg, q, q_off: int, pos, chunk_len: int, n_chunks: int, k, v, sel, out,
+                         lse=None, out_off: int = 0, ws=None, stream=None) -> None:
+    """pos: device int64 [batch], the position of row q_off per sequence."""
+    dt = _dtype_of(cfg)
+    _check(q, "q", dt, 4)
+    _check(k, "k", dt, 4)
+    _check(v, "v", dt, 4)
+    _check(out, "out", dt, 4)
+    _check_pos(pos, q.shape[0])
+    if sel is not None:
+        _check(sel, "sel", torch.int32, 4)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, 3)
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    wp, wb = _ws(ws)
+    _raise("infllm_attend_varlen", lib().infllm_attend_varlen(
+        ctypes.byref(cfg), q.shape[0], q.data_ptr(), q.shape[2], q_off, pos.data_ptr(), chunk_len,
+        n_chunks, k.data_ptr(), v.data_ptr(), k.shape[2], _ptr(sel), out.data_ptr(), _ptr(lse),
         out.shape[2], out_off, wp, wb, _stream(stream, q)))

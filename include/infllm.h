@@ -15,8 +15,10 @@
  *                          (infllm_build_units_range: a range of units, as
  *                          they leave the window while streaming)
  *   infllm_score_units  -- chunk-query . unit-representation scores
+ *                          (infllm_score_units_varlen: a position per sequence)
  *   infllm_topk_units   -- top-k_m units per (sequence, KV head, chunk)
  *   infllm_attend       -- exact softmax attention over the working context
+ *                          (infllm_attend_varlen: a position per sequence)
  *
  * Conventions shared by every call
  * --------------------------------
@@ -205,6 +207,26 @@ INFLLM_API infllm_status infllm_score_units(const infllm_config *cfg, int32_t ba
                                  void *stream);
 
 /*
+ * infllm_score_units_varlen -- infllm_score_units for a batch of sequences
+ * at different positions (a serving batch: one decode step, or one chunk
+ * of prefill, per sequence).  Same arguments, except:
+ *
+ *   pos        device [batch] int64, 8-byte aligned: absolute position of
+ *              row q_off of sequence b (replaces q_pos).  Read on the
+ *              device, so it can be updated there between calls.  A
+ *              negative position leaves no unit eligible; e_c is capped at
+ *              n_units, as in infllm_score_units.
+ *
+ * Row b equals row b of infllm_score_units called with q_pos = pos[b] on
+ * the same batch (bit for bit).  Workspace: INFLLM_CALL_SCORE, same sizes.
+ */
+INFLLM_API infllm_status infllm_score_units_varlen(const infllm_config *cfg, int32_t batch,
+                                        const void *q, int64_t q_cap, int64_t q_off,
+                                        const int64_t *pos, int32_t chunk_len, int32_t n_chunks,
+                                        const float *unit_repr, int32_t n_units, float *scores,
+                                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * infllm_topk_units -- keep the k_m best units per (sequence, KV head,
  * chunk) (InfLLM Guide, "Core Innovation 2", item 2: the top-k highest-
  * scoring units are loaded for exact attention).
@@ -252,6 +274,30 @@ INFLLM_API infllm_status infllm_attend(const infllm_config *cfg, int32_t batch, 
                             const void *k, const void *v, int64_t kv_cap, const int32_t *sel,
                             void *out, float *lse, int64_t out_cap, int64_t out_off,
                             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * infllm_attend_varlen -- infllm_attend for a batch of sequences at
+ * different positions.  Same arguments, except:
+ *
+ *   pos      device [batch] int64, 8-byte aligned: absolute position of
+ *            row q_off of sequence b (replaces q_pos); sequence b attends
+ *            its own K/V rows up to pos[b] + n_chunks*chunk_len - 1.
+ *   kv_cap   must be >= n_chunks*chunk_len.
+ *
+ * The positions are checked on the device: a sequence with pos[b] < 0,
+ * pos[b] + n_chunks*chunk_len > kv_cap or beyond 2^31 - 128 reads nothing
+ * and gets NaN output rows (and NaN lse); the other sequences are
+ * unaffected and the workspace stays valid.  Row b equals row b of
+ * infllm_attend called with q_pos = pos[b] on the same batch (bit for
+ * bit).  Workspace: INFLLM_CALL_ATTEND, same sizes.
+ */
+INFLLM_API infllm_status infllm_attend_varlen(const infllm_config *cfg, int32_t batch,
+                                   const void *q, int64_t q_cap, int64_t q_off,
+                                   const int64_t *pos, int32_t chunk_len, int32_t n_chunks,
+                                   const void *k, const void *v, int64_t kv_cap,
+                                   const int32_t *sel, void *out, float *lse, int64_t out_cap,
+                                   int64_t out_off, void *workspace, size_t workspace_bytes,
+                                   void *stream);
 
 INFLLM_API const char *infllm_status_string(int32_t status);
 INFLLM_API int32_t infllm_abi_version(void);

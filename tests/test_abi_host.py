@@ -31,7 +31,7 @@ def cfg(**kw):
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 10
+    assert len(names) == 12
     assert set(names) == set(F.EXPORTED)
     L = F.lib()
     for n in names:
@@ -144,6 +144,23 @@ def test_build_range_validation_and_workspace():
     assert F.infllm_workspace_size(c, F.INFLLM_CALL_BUILD_RANGE, 1, 0) == 0
     cm = cfg(rep_mode=F.INFLLM_REP_MEAN)
     assert F.infllm_workspace_size(cm, F.INFLLM_CALL_BUILD_RANGE, 1, 10) == 0
+
+
+def test_varlen_validation():
+    c = cfg()
+    L = F.lib()
+    r = ctypes.byref(c)
+    sc = lambda pos: L.infllm_score_units_varlen(r, 2, FAKE, 1000, 0, pos, 1, 1, FAKE, 10, FAKE,
+                                                 FAKE, 1 << 30, None)
+    assert sc(None) == F.INFLLM_ERR_INVALID_ARG
+    assert sc(FAKE + 4) == F.INFLLM_ERR_INVALID_ARG          # not 8-byte aligned
+    at = lambda pos, kv_cap=4096, n_chunks=1: L.infllm_attend_varlen(
+        r, 2, FAKE, 4096, 0, pos, 512, n_chunks, FAKE, FAKE, kv_cap, FAKE, FAKE, None, 4096, 0,
+        FAKE, 1 << 30, None)
+    assert at(None) == F.INFLLM_ERR_INVALID_ARG
+    assert at(FAKE + 4) == F.INFLLM_ERR_INVALID_ARG
+    assert at(FAKE, kv_cap=511) == F.INFLLM_ERR_INVALID_ARG   # no position fits
+    assert at(FAKE, n_chunks=9) == F.INFLLM_ERR_INVALID_ARG   # rows beyond q_cap
 
 
 def test_score_topk_attend_validation():

@@ -472,3 +472,110 @@ def test_score_shared_workspace_repeatable(U_big):
         got = outs[0][:, :, c].double().cpu()
         fin = torch.isfinite(got)
         assert torch.allclose(got[fin], ref[fin].float().double(), rtol=1e-6, atol=1e-6)
+
+
+def _varlen_check(orc, w, inp, dev, cfg, repr_g, q_name, q_off, pos_list, L, n_chunks, n_oracle):
+    """Score, top-k and attend with one position per sequence: each row bit
+    for bit equal to the single-position call at that sequence's position
+    on the same batch, and the attention against the oracle."""
+    b = w.batch
+    pos = torch.tensor(pos_list, dtype=torch.int64, device="cuda")
+    U = repr_g.shape[2]
+    q = dev[q_name]
+    scores = torch.empty((b, w.n_kv_heads, n_chunks, U), dtype=torch.float32, device="cuda")
+    sws = F.workspace(cfg, F.INFLLM_CALL_SCORE, b, 0, L, n_chunks)
+    F.infllm_score_units_varlen(cfg, q, q_off, pos, L, n_chunks, repr_g, scores, sws)
+    sel = gpu_topk(cfg, scores)
+    n = L * n_chunks
+    out = torch.empty((b, w.n_q_heads, n, w.head_dim), dtype=q.dtype, device="cuda")
+    lse = torch.empty((b, w.n_q_heads, n), dtype=torch.float32, device="cuda")
+    aws = F.workspace(cfg, F.INFLLM_CALL_ATTEND, b, 0, L, n_chunks)
+    F.infllm_attend_varlen(cfg, q, q_off, pos, L, n_chunks, dev["k"], dev["v"], sel, out, lse, 0,
+                           aws)
+    torch.cuda.synchronize()
+    sg = sel.cpu().numpy()
+    for bi, t0 in enumerate(pos_list):
+        s1 = gpu_score(cfg, q, q_off, t0, L, n_chunks, repr_g)
+        o1, l1 = gpu_attend(cfg, q, q_off, t0, L, n_chunks, dev["k"], dev["v"], sel)
+        torch.cuda.synchronize()
+        assert torch.equal(scores[bi], s1[bi])
+        assert torch.equal(out[bi], o1[bi]) and torch.equal(lse[bi], l1[bi])
+        for c in range(n_chunks):
+            e = orc.num_eligible(t0 + (c + 1) * L - 1, U, w.block, w.n_init, w.window)
+            assert int(torch.isfinite(scores[bi, :, c]).sum(-1).min()) == e
+        # the oracle on sampled rows of this sequence (first and last of each chunk)
+        rows = sorted({c * L + r for c in range(n_chunks) for r in (0, L - 1)})[:n_oracle]
+        for r in rows:
+            c = r // L
+            o_ref, l_ref = orc.attend_all(inp[q_name][bi:bi + 1, :, q_off + r:q_off + r + 1],
+                                          t0 + r, inp["k"][bi:bi + 1], inp["v"][bi:bi + 1],
+                                          sg[bi:bi + 1, :, c], B=w.block, n_init=w.n_init,
+                                          W=w.window)
+            assert_close(out[bi:bi + 1, :, r:r + 1], o_ref, tolerance(q.dtype, o_ref),
+                         "sequence %d row %d" % (bi, r))
+            assert_close(lse[bi:bi + 1, :, r:r + 1], l_ref, 1e-3, "lse sequence %d row %d" % (bi, r))
+    return pos, sel, out, lse, aws
+
+
+def _nan_rows_and_rest(cfg, w, dev, q_name, q_off, pos_list, L, n_chunks, sel, bad, aws):
+    """A varlen attend where the sequences in `bad` have positions that do not
+    fit the KV buffer: NaN rows there, the others equal to the
+    single-position call, and the shared workspace still valid afterwards."""
+    b = w.batch
+    q = dev[q_name]
+    pos = torch.tensor(pos_list, dtype=torch.int64, device="cuda")
+    n = L * n_chunks
+    out = torch.empty((b, w.n_q_heads, n, w.head_dim), dtype=q.dtype, device="cuda")
+    lse = torch.empty((b, w.n_q_heads, n), dtype=torch.float32, device="cuda")
+    F.infllm_attend_varlen(cfg, q, q_off, pos, L, n_chunks, dev["k"], dev["v"], sel, out, lse, 0,
+                           aws)
+    torch.cuda.synchronize()
+    for bi, t0 in enumerate(pos_list):
+        if bi in bad:
+            assert torch.isnan(out[bi].float()).all() and torch.isnan(lse[bi]).all()
+            continue
+        o1, l1 = gpu_attend(cfg, q, q_off, t0, L, n_chunks, dev["k"], dev["v"], sel)
+        torch.cuda.synchronize()
+        assert torch.equal(out[bi], o1[bi]) and torch.equal(lse[bi], l1[bi])
+
+
+def test_varlen_decode_batch(orc):
+    """One decode step for four sequences at different positions (full
+    context, mid context, before any unit is eligible, ragged), then with
+    two positions that do not fit the KV buffer, then valid again on the
+    same workspace."""
+    w = synth.WORKLOADS["llama3_8b_128k_decode"].replace(n_ctx=6144, batch=4, n_q_heads=8,
+                                                         n_kv_heads=2, decode_steps=4, top_k=8,
+                                                         window=1024)
+    cfg = cfg_of(w)
+    inp = synth.make_inputs(w)
+    dev = {k: v.cuda() for k, v in inp.items() if isinstance(v, torch.Tensor)}
+    _, repr_g = gpu_build(cfg, dev["q"], dev["k"], w.n_ctx)
+    cap = w.n_ctx + w.decode_steps
+    pos_list = [cap - 1, 2000, 700, 4501]
+    pos, sel, out, lse, aws = _varlen_check(orc, w, inp, dev, cfg, repr_g, "q_dec", 1, pos_list,
+                                            1, 1, 1)
+    _nan_rows_and_rest(cfg, w, dev, "q_dec", 1, [cap - 1, -1, cap, 4501], 1, 1, sel, {1, 2}, aws)
+    out2 = torch.empty_like(out)
+    lse2 = torch.empty_like(lse)
+    F.infllm_attend_varlen(cfg, dev["q_dec"], 1, pos, 1, 1, dev["k"], dev["v"], sel, out2, lse2, 0,
+                           aws)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, out) and torch.equal(lse2, lse)
+
+
+def test_varlen_chunked_prefill(orc):
+    """Two 128-query chunks per sequence at different positions (MFMA
+    path): a serving batch where each sequence prefills at its own offset,
+    including the last position that fits the KV buffer; then one position
+    past it."""
+    w = CASES["bf16_g4"].replace(batch=3)
+    cfg = cfg_of(w)
+    inp = synth.make_inputs(w)
+    dev = {k: v.cuda() for k, v in inp.items() if isinstance(v, torch.Tensor) and k != "planted_units"}
+    _, repr_g = gpu_build(cfg, dev["q"], dev["k"], w.n_ctx)
+    L, nc = 128, 2
+    last = w.n_ctx - L * nc
+    pos_list = [last, 1000, 0]
+    _, sel, _, _, aws = _varlen_check(orc, w, inp, dev, cfg, repr_g, "q", 64, pos_list, L, nc, 4)
+    _nan_rows_and_rest(cfg, w, dev, "q", 64, [last + 1, 1000, 0], L, nc, sel, {0}, aws)
