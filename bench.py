@@ -110,7 +110,7 @@ class Pipeline:
             self.sel_enc = self.enc_sel.permute(2, 0, 1, 3).unsqueeze(3)
             self.out_enc = torch.empty_like(self.inp["q"])
         if self.decode:
-            self.dec_score_ws = F.workspace(cfg, F.INFLLM_CALL_SCORE, b, 0, 1, 1, device=dev)
+            self.dec_score_ws = F.workspace(cfg, F.INFLLM_CALL_SELECT, b, 0, 1, 1, device=dev)
             self.dec_attn_ws = F.workspace(cfg, F.INFLLM_CALL_ATTEND, b, 0, 1, 1, device=dev)
             self.sel_dec = torch.empty((w.decode_steps, b, Hkv, 1, w.top_k), dtype=torch.int32,
                                        device=dev)
@@ -136,9 +136,9 @@ class Pipeline:
             self.build(li)
 
     def _select(self, q, q_off, pos, L, sel, score_ws, layer=0):
-        F.infllm_score_units(self.cfg, q, q_off, pos, L, 1, self.layers[layer]["repr"],
-                             self.scores, score_ws)
-        F.infllm_topk_units(self.cfg, self.scores, sel)
+        # scores and top-k in one call (one launch for decode-sized chunks)
+        F.infllm_select_units(self.cfg, q, q_off, pos, L, 1, self.layers[layer]["repr"],
+                              self.scores, sel, ws=score_ws)
 
     def _attend(self, q, q_off, pos, L, sel, out, attn_ws, layer=0):
         ly = self.layers[layer]

@@ -162,6 +162,9 @@ size_t infllm_workspace_size(const infllm_config* cfg, int32_t call, int32_t bat
     case INFLLM_CALL_SCORE:
       if (chunk_len < 1 || n_chunks < 1) return 0;
       return score_workspace_bytes(score_args(cfg, batch, chunk_len, n_chunks));
+    case INFLLM_CALL_SELECT:
+      if (chunk_len < 1 || n_chunks < 1) return 0;
+      return select_workspace_bytes(score_args(cfg, batch, chunk_len, n_chunks));
     case INFLLM_CALL_ATTEND:
       if (chunk_len < 1 || n_chunks < 1) return 0;
       return attend_ws_bytes(attend_args(cfg, batch, chunk_len, n_chunks));
@@ -234,10 +237,11 @@ infllm_status infllm_build_units_range(const infllm_config* cfg, int32_t batch, 
 
 // Shared by the single-position and per-sequence-position forms: pos (device,
 // [batch]) replaces q_pos when non-null.
+// sel non-null: the top-k_m selection is fused into the scoring launch.
 static infllm_status score_impl(const infllm_config* cfg, int32_t batch, const void* q,
                                 int64_t q_cap, int64_t q_off, int64_t q_pos, const int64_t* pos,
                                 int32_t chunk_len, int32_t n_chunks, const float* unit_repr,
-                                int32_t n_units, float* scores, void* workspace,
+                                int32_t n_units, float* scores, int32_t* sel, void* workspace,
                                 size_t workspace_bytes, void* stream) {
   infllm_status st = check_config(cfg);
   if (st != INFLLM_OK) return st;
@@ -250,8 +254,14 @@ static infllm_status score_impl(const infllm_config* cfg, int32_t batch, const v
     return INFLLM_ERR_INVALID_ARG;
   ScoreArgs a = score_args(cfg, batch, chunk_len, n_chunks);
   a.U = n_units;
-  const size_t need = score_workspace_bytes(a);
-  if (n_units > 0 && need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+  if (sel && cfg->top_k > 0) {
+    if (!aligned16(sel)) return INFLLM_ERR_INVALID_ARG;
+    a.k_m = cfg->top_k;
+    a.sel = sel;
+  }
+  const size_t need = a.sel ? select_workspace_bytes(a) : score_workspace_bytes(a);
+  if ((n_units > 0 || a.sel) && need > 0 &&
+      (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return INFLLM_ERR_WORKSPACE;
   a.ws = workspace;
   a.q = q;
@@ -272,7 +282,18 @@ infllm_status infllm_score_units(const infllm_config* cfg, int32_t batch, const 
                                  float* scores, void* workspace, size_t workspace_bytes,
                                  void* stream) {
   return score_impl(cfg, batch, q, q_cap, q_off, q_pos, nullptr, chunk_len, n_chunks, unit_repr,
-                    n_units, scores, workspace, workspace_bytes, stream);
+                    n_units, scores, nullptr, workspace, workspace_bytes, stream);
+}
+
+infllm_status infllm_select_units(const infllm_config* cfg, int32_t batch, const void* q,
+                                  int64_t q_cap, int64_t q_off, int64_t q_pos, const int64_t* pos,
+                                  int32_t chunk_len, int32_t n_chunks, const float* unit_repr,
+                                  int32_t n_units, float* scores, int32_t* sel, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (cfg && cfg->top_k > 0 && !sel) return INFLLM_ERR_INVALID_ARG;
+  if (pos && (uintptr_t)pos % 8 != 0) return INFLLM_ERR_INVALID_ARG;
+  return score_impl(cfg, batch, q, q_cap, q_off, pos ? 0 : q_pos, pos, chunk_len, n_chunks,
+                    unit_repr, n_units, scores, sel, workspace, workspace_bytes, stream);
 }
 
 infllm_status infllm_score_units_varlen(const infllm_config* cfg, int32_t batch, const void* q,
@@ -282,7 +303,7 @@ infllm_status infllm_score_units_varlen(const infllm_config* cfg, int32_t batch,
                                         void* workspace, size_t workspace_bytes, void* stream) {
   if (!pos || (uintptr_t)pos % 8 != 0) return INFLLM_ERR_INVALID_ARG;
   return score_impl(cfg, batch, q, q_cap, q_off, 0, pos, chunk_len, n_chunks, unit_repr, n_units,
-                    scores, workspace, workspace_bytes, stream);
+                    scores, nullptr, workspace, workspace_bytes, stream);
 }
 
 infllm_status infllm_topk_units(const infllm_config* cfg, int32_t batch, int32_t n_chunks,

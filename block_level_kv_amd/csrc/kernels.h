@@ -31,6 +31,8 @@ struct ScoreArgs {
   const float* repr;
   float* scores;
   void* ws;  // fp64 partial query sums of long chunks
+  int k_m;       // fused selection: units kept per row
+  int32_t* sel;  // fused selection output, or null (scores only)
 };
 
 struct TopkArgs {
@@ -61,6 +63,7 @@ size_t build_workspace_bytes(const BuildArgs& a);
 size_t build_range_workspace_bytes(const BuildArgs& a, int64_t n_units);
 hipError_t launch_build(const BuildArgs& a, hipStream_t st);
 size_t score_workspace_bytes(const ScoreArgs& a);
+size_t select_workspace_bytes(const ScoreArgs& a);
 hipError_t launch_score(const ScoreArgs& a, hipStream_t st);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 

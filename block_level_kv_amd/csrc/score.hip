@@ -19,6 +19,7 @@
 // costs one memory round trip.
 #include "common.h"
 #include "kernels.h"
+#include "topk_select.h"
 
 namespace infllm {
 
@@ -31,6 +32,10 @@ constexpr int kDirectRows = 64;      // L*G up to this: sum in the scoring kerne
 constexpr int kFusedMaxUnits = 2048;
 constexpr int kPartBatch = 16;       // partial sums requested together
 constexpr int kBatchUnits = 64;      // units whose rows the fused kernel requests together
+// Fused selection up to this many slices per row: beyond, the arrivals on
+// one row's counter serialize (measured: 128 slices cost more than a
+// separate top-k launch)
+constexpr int kMaxSelSlices = 32;
 
 static int score_rows(const ScoreArgs& a) {
   const int64_t long_parts = (int64_t)a.batch * a.Hkv * a.n_chunks * ((a.L + kRowsLong - 1) / kRowsLong);
@@ -113,7 +118,9 @@ struct UnitRows {
       x[s].load(rb + (int64_t)(u < U ? u : U - 1) * D + cg * 8);
     }
   }
-  // score[u] = qsum . repr[u] (fp64), -inf for u >= e; units in [base, u1)
+  // score[u] = qsum . repr[u] (fp64), -inf for u >= e; units in [base, u1).
+  // DEV: device-scope stores, for a selection by another workgroup.
+  template <bool DEV = false>
   __device__ __forceinline__ void score(const double* qv, int base, int u1, int64_t e,
                                         float* sb) const {
     const int cg = threadIdx.x % 64 % kLpu;
@@ -127,7 +134,11 @@ struct UnitRows {
       t += dpp_f64<INFLLM_DPP_XOR2>(t);
       t += dpp_f64<INFLLM_DPP_HALF_MIRROR>(t);
       if (kLpu == 16) t += dpp_f64<INFLLM_DPP_MIRROR>(t);
-      if (u < u1 && cg == 0) sb[u] = u < e ? (float)t : -INFINITY;
+      if (u < u1 && cg == 0) {
+        const float v = u < e ? (float)t : -INFINITY;
+        if (DEV) st_dev(sb + u, v);
+        else sb[u] = v;
+      }
     }
   }
 };
@@ -152,12 +163,18 @@ __global__ __launch_bounds__(kScoreThreads) void k_chunk_qsum(
 }
 
 // Scores of a slice of kUnitsPerWG units.  grid (slices, n_chunks * H_kv, batch).
-template <typename T, int G, int D>
+// SEL >= 0: the selection is fused -- the scores are published with
+// device-scope stores, and the last slice of a (sequence, KV head, chunk)
+// to arrive (arrival counter in `count`, which it resets) selects that
+// row's top k_m into `sel` with the workgroup search, SEL keys per lane
+// (0: re-read from memory).
+template <typename T, int G, int D, int SEL>
 __global__ __launch_bounds__(kScoreThreads) void k_score_units(
     const T* __restrict__ q, int64_t q_cap, int64_t q_off, int64_t q_pos,
     const int64_t* __restrict__ pos, int L, int Hq, int Hkv,
     int B, int n_init, int W, const float* __restrict__ repr, int U, float* __restrict__ scores,
-    int n_chunks, const double* __restrict__ parts, int n_parts) {
+    int n_chunks, const double* __restrict__ parts, int n_parts, int* __restrict__ count,
+    int k_m, int32_t* __restrict__ sel) {
   using Rows = UnitRows<D, kUnitsPerWG / UnitRows<D, 1>::kPerSlot>;
   const int slice = blockIdx.x;
   const int ch = blockIdx.y % n_chunks, h = blockIdx.y / n_chunks, bi = blockIdx.z;
@@ -212,15 +229,35 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_units(
 
   // a position out of range leaves no unit eligible (negative) or all of
   // them (large); the clamp keeps the sum below overflow
-  int64_t base = seq_base(pos, q_pos, bi);
-  base = base < -kPosLimit ? -kPosLimit : (base > kPosLimit ? kPosLimit : base);
-  const int64_t t_last = base + (int64_t)ch * L + L - 1;
+  int64_t t0 = seq_base(pos, q_pos, bi);
+  t0 = t0 < -kPosLimit ? -kPosLimit : (t0 > kPosLimit ? kPosLimit : t0);
+  const int64_t t_last = t0 + (int64_t)ch * L + L - 1;
   const int64_t e = eligible_units(t_last, U, B, n_init, W);
   const int cg = tid % 64 % (D / 8);
   double qv[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) qv[j] = qsum[cg * 8 + j];
-  rows.score(qv, u0, u1, e, scores + (((int64_t)bi * Hkv + h) * n_chunks + ch) * U);
+  const int64_t prob = ((int64_t)bi * Hkv + h) * n_chunks + ch;
+  float* sb = scores + prob * U;
+  if constexpr (SEL < 0) {
+    rows.score(qv, u0, u1, e, sb);
+  } else {
+    __shared__ TopkShared tsm;
+    __shared__ int last_sh;
+    rows.template score<true>(qv, u0, u1, e, sb);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    if (tid == 0) {
+      const int done = __hip_atomic_fetch_add(&count[prob], 1, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+      last_sh = done == (int)gridDim.x - 1;
+      if (last_sh)   // ready for the next call
+        __hip_atomic_store(&count[prob], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!last_sh) return;
+    block_topk<kScoreThreads / 64, SEL, true>(sb, U, k_m, sel + prob * k_m, tsm);
+  }
 }
 
 // Long chunks with a moderate unit count, in one launch: each workgroup
@@ -272,9 +309,9 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_fused(
   __syncthreads();
   // a position out of range leaves no unit eligible (negative) or all of
   // them (large); the clamp keeps the sum below overflow
-  int64_t base = seq_base(pos, q_pos, bi);
-  base = base < -kPosLimit ? -kPosLimit : (base > kPosLimit ? kPosLimit : base);
-  const int64_t t_last = base + (int64_t)ch * L + L - 1;
+  int64_t t0 = seq_base(pos, q_pos, bi);
+  t0 = t0 < -kPosLimit ? -kPosLimit : (t0 > kPosLimit ? kPosLimit : t0);
+  const int64_t t_last = t0 + (int64_t)ch * L + L - 1;
   const int64_t e = eligible_units(t_last, U, B, n_init, W);
   const int cg = tid % 64 % (D / 8);
   double qv[8];
@@ -303,6 +340,25 @@ size_t score_workspace_bytes(const ScoreArgs& a) {
   return score_counter_bytes(a) + (size_t)parts * a.batch * a.Hkv * a.n_chunks * a.d * sizeof(double);
 }
 
+// Scoring with the fused selection: the counters are needed by every path
+// (the two-launch path for long chunks leaves them unused).
+size_t select_workspace_bytes(const ScoreArgs& a) {
+  const size_t w = score_workspace_bytes(a);
+  return w > 0 ? w : score_counter_bytes(a);
+}
+
+static TopkArgs select_topk_args(const ScoreArgs& a) {
+  TopkArgs t{};
+  t.batch = a.batch;
+  t.Hkv = a.Hkv;
+  t.n_chunks = a.n_chunks;
+  t.U = a.U;
+  t.k_m = a.k_m;
+  t.scores = a.scores;
+  t.sel = a.sel;
+  return t;
+}
+
 template <typename T, int G, int D, int ROWS>
 static void launch_parts(const ScoreArgs& a, int parts, double* pw, hipStream_t st) {
   const dim3 grid(parts, a.Hkv, a.batch * a.n_chunks);
@@ -322,12 +378,28 @@ static hipError_t launch_score_tgd(const ScoreArgs& a, hipStream_t st) {
   if (parts > 0) {
     if (score_rows(a) == kRowsLong) launch_parts<T, G, D, kRowsLong>(a, parts, pw, st);
     else launch_parts<T, G, D, kRowsShort>(a, parts, pw, st);
-    if (score_fused(a)) return hipGetLastError();
+    if (score_fused(a)) {
+      // one workgroup scores each chunk; the selection is a launch of its own
+      if (!a.sel) return hipGetLastError();
+      return launch_topk(select_topk_args(a), st);
+    }
   }
   dim3 grid((a.U + kUnitsPerWG - 1) / kUnitsPerWG, a.n_chunks * a.Hkv, a.batch);
-  k_score_units<T, G, D><<<grid, kScoreThreads, 0, st>>>(
-      (const T*)a.q, a.q_cap, a.q_off, a.q_pos, a.pos, a.L, a.Hq, a.Hkv, a.B, a.n_init, a.W, a.repr, a.U,
-      a.scores, a.n_chunks, pw, parts);
+#define INFLLM_SCORE_UNITS(SEL, CNT)                                                            \
+  k_score_units<T, G, D, SEL><<<grid, kScoreThreads, 0, st>>>(                                 \
+      (const T*)a.q, a.q_cap, a.q_off, a.q_pos, a.pos, a.L, a.Hq, a.Hkv, a.B, a.n_init, a.W,     \
+      a.repr, a.U, a.scores, a.n_chunks, pw, parts, CNT, a.k_m, a.sel)
+  if (!a.sel || grid.x > kMaxSelSlices) {
+    INFLLM_SCORE_UNITS(-1, nullptr);
+    if (a.sel) return launch_topk(select_topk_args(a), st);
+  } else {
+    // keys per lane of the 4-wave search: ceil(U / 256) <= 8
+    static_assert(kMaxSelSlices * kUnitsPerWG <= 8 * kScoreThreads, "keys per lane");
+    int* cnt = (int*)a.ws;
+    if (a.U <= 4 * kScoreThreads) INFLLM_SCORE_UNITS(4, cnt);
+    else INFLLM_SCORE_UNITS(8, cnt);
+  }
+#undef INFLLM_SCORE_UNITS
   return hipGetLastError();
 }
 
@@ -348,7 +420,8 @@ static hipError_t launch_score_t(const ScoreArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_score(const ScoreArgs& a, hipStream_t st) {
-  if (a.U <= 0 || a.n_chunks <= 0) return hipSuccess;
+  if (a.n_chunks <= 0) return hipSuccess;
+  if (a.U <= 0) return a.sel ? launch_topk(select_topk_args(a), st) : hipSuccess;   // all -1
   return a.bf16 ? launch_score_t<bf16_t>(a, st) : launch_score_t<float>(a, st);
 }
 

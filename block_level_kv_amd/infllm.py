@@ -20,11 +20,12 @@ INFLLM_OK, INFLLM_ERR_INVALID_ARG, INFLLM_ERR_UNSUPPORTED, INFLLM_ERR_WORKSPACE,
 INFLLM_F32, INFLLM_BF16 = 0, 1
 INFLLM_REP_TOKENS, INFLLM_REP_MEAN = 0, 1
 INFLLM_CALL_BUILD, INFLLM_CALL_SCORE, INFLLM_CALL_TOPK, INFLLM_CALL_ATTEND = 0, 1, 2, 3
-INFLLM_CALL_BUILD_RANGE = 4
+INFLLM_CALL_BUILD_RANGE, INFLLM_CALL_SELECT = 4, 5
 
 EXPORTED = ("infllm_num_units", "infllm_num_eligible", "infllm_workspace_size",
             "infllm_build_units", "infllm_build_units_range", "infllm_score_units",
-            "infllm_score_units_varlen", "infllm_topk_units", "infllm_attend",
+            "infllm_score_units_varlen", "infllm_select_units", "infllm_topk_units",
+            "infllm_attend",
             "infllm_attend_varlen", "infllm_status_string", "infllm_abi_version")
 
 
@@ -74,6 +75,9 @@ def lib() -> ctypes.CDLL:
         L.infllm_attend_varlen.restype = _i32
         L.infllm_attend_varlen.argtypes = [_cfgp, _i32, _vp, _i64, _i64, _vp, _i32, _i32, _vp, _vp,
                                            _i64, _vp, _vp, _vp, _i64, _i64, _vp, _sz, _vp]
+        L.infllm_select_units.restype = _i32
+        L.infllm_select_units.argtypes = [_cfgp, _i32, _vp, _i64, _i64, _i64, _vp, _i32, _i32, _vp,
+                                          _i32, _vp, _vp, _vp, _sz, _vp]
         L.infllm_topk_units.restype = _i32
         L.infllm_topk_units.argtypes = [_cfgp, _i32, _i32, _vp, _i32, _vp, _vp, _sz, _vp]
         L.infllm_attend.restype = _i32
@@ -243,6 +247,28 @@ def infllm_score_units_varlen(cfg, q, q_off: int, pos, chunk_len: int, n_chunks:
     _raise("infllm_score_units_varlen", lib().infllm_score_units_varlen(
         ctypes.byref(cfg), batch, q.data_ptr(), q.shape[2], q_off, pos.data_ptr(), chunk_len,
         n_chunks, unit_repr.data_ptr(), U, scores.data_ptr(), wp, wb, _stream(stream, q)))
+
+
+def infllm_select_units(cfg, q, q_off: int, q_pos: int, chunk_len: int, n_chunks: int, unit_repr,
+                        scores, sel, pos=None, ws=None, stream=None) -> None:
+    """Scores and top-k in one call; pos (device int64 [batch]) replaces q_pos
+    when given."""
+    _check(q, "q", _dtype_of(cfg), 4)
+    _check(unit_repr, "unit_repr", torch.float32, 4)
+    _check(scores, "scores", torch.float32, 4)
+    _check(sel, "sel", torch.int32, 4)
+    batch, U = q.shape[0], unit_repr.shape[2]
+    if pos is not None:
+        _check_pos(pos, batch)
+    if tuple(scores.shape) != (batch, cfg.n_kv_heads, n_chunks, U):
+        raise ValueError("scores must be [batch, H_kv, n_chunks, U]")
+    if tuple(sel.shape) != (batch, cfg.n_kv_heads, n_chunks, cfg.top_k):
+        raise ValueError("sel must be [batch, H_kv, n_chunks, k_m]")
+    wp, wb = _ws(ws)
+    _raise("infllm_select_units", lib().infllm_select_units(
+        ctypes.byref(cfg), batch, q.data_ptr(), q.shape[2], q_off, q_pos, _ptr(pos), chunk_len,
+        n_chunks, unit_repr.data_ptr(), U, scores.data_ptr(), sel.data_ptr(), wp, wb,
+        _stream(stream, q)))
 
 
 def infllm_topk_units(cfg, scores, sel, ws=None, stream=None) -> None:

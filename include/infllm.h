@@ -17,6 +17,7 @@
  *   infllm_score_units  -- chunk-query . unit-representation scores
  *                          (infllm_score_units_varlen: a position per sequence)
  *   infllm_topk_units   -- top-k_m units per (sequence, KV head, chunk)
+ *                          (infllm_select_units: scores and top-k together)
  *   infllm_attend       -- exact softmax attention over the working context
  *                          (infllm_attend_varlen: a position per sequence)
  *
@@ -90,7 +91,8 @@ typedef enum {
   INFLLM_CALL_SCORE = 1,
   INFLLM_CALL_TOPK = 2,
   INFLLM_CALL_ATTEND = 3,
-  INFLLM_CALL_BUILD_RANGE = 4
+  INFLLM_CALL_BUILD_RANGE = 4,
+  INFLLM_CALL_SELECT = 5
 } infllm_call;
 
 typedef struct {
@@ -225,6 +227,33 @@ INFLLM_API infllm_status infllm_score_units_varlen(const infllm_config *cfg, int
                                         const int64_t *pos, int32_t chunk_len, int32_t n_chunks,
                                         const float *unit_repr, int32_t n_units, float *scores,
                                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * infllm_select_units -- infllm_score_units followed by infllm_topk_units,
+ * in one launch where the chunks are short (decode: the last slice of units
+ * of a (sequence, KV head, chunk) to finish scoring selects that row's
+ * units), in two otherwise.  Results are identical to the two calls.
+ *
+ *   q, q_cap, q_off, chunk_len, n_chunks, unit_repr, n_units
+ *              as infllm_score_units
+ *   q_pos      absolute position of row q_off (used when pos is NULL)
+ *   pos        NULL, or device [batch] int64, 8-byte aligned: a position
+ *              per sequence, as infllm_score_units_varlen
+ *   scores     out [batch, H_kv, n_chunks, n_units] fp32 (also the
+ *              selection's input)
+ *   sel        out [batch, H_kv, n_chunks, k_m] int32, as infllm_topk_units
+ *   workspace  >= infllm_workspace_size(cfg, INFLLM_CALL_SELECT, batch, 0,
+ *              chunk_len, n_chunks): arrival counters (and the scoring
+ *              workspace).  Zero-filled before its first use; every call
+ *              leaves the counters at zero; calls that share a workspace
+ *              must not overlap in time.
+ */
+INFLLM_API infllm_status infllm_select_units(const infllm_config *cfg, int32_t batch, const void *q,
+                                  int64_t q_cap, int64_t q_off, int64_t q_pos,
+                                  const int64_t *pos, int32_t chunk_len, int32_t n_chunks,
+                                  const float *unit_repr, int32_t n_units, float *scores,
+                                  int32_t *sel, void *workspace, size_t workspace_bytes,
+                                  void *stream);
 
 /*
  * infllm_topk_units -- keep the k_m best units per (sequence, KV head,

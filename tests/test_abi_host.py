@@ -31,7 +31,7 @@ def cfg(**kw):
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     assert set(names) == set(F.EXPORTED)
     L = F.lib()
     for n in names:
@@ -161,6 +161,25 @@ def test_varlen_validation():
     assert at(FAKE + 4) == F.INFLLM_ERR_INVALID_ARG
     assert at(FAKE, kv_cap=511) == F.INFLLM_ERR_INVALID_ARG   # no position fits
     assert at(FAKE, n_chunks=9) == F.INFLLM_ERR_INVALID_ARG   # rows beyond q_cap
+
+
+def test_select_validation_and_workspace():
+    c = cfg()
+    L = F.lib()
+    r = ctypes.byref(c)
+    call = lambda **kw: L.infllm_select_units(
+        r, 2, FAKE, 1000, 0, 5000, kw.get("pos", None), 1, 1, FAKE, 1023, FAKE, kw.get("sel", FAKE),
+        kw.get("ws", FAKE), kw.get("wsb", 1 << 30), None)
+    assert call(sel=None) == F.INFLLM_ERR_INVALID_ARG
+    assert call(sel=MISALIGNED) == F.INFLLM_ERR_INVALID_ARG
+    assert call(pos=FAKE + 4) == F.INFLLM_ERR_INVALID_ARG
+    need = F.infllm_workspace_size(c, F.INFLLM_CALL_SELECT, 2, 0, 1, 1)
+    assert need > 0 and F.infllm_workspace_size(c, F.INFLLM_CALL_SCORE, 2, 0, 1, 1) == 0
+    assert call(wsb=need - 1) == F.INFLLM_ERR_WORKSPACE
+    assert call(ws=None, wsb=0) == F.INFLLM_ERR_WORKSPACE
+    # long chunks: the scoring workspace, which already holds the counters
+    assert F.infllm_workspace_size(c, F.INFLLM_CALL_SELECT, 2, 0, 512, 3) == \
+        F.infllm_workspace_size(c, F.INFLLM_CALL_SCORE, 2, 0, 512, 3)
 
 
 def test_score_topk_attend_validation():

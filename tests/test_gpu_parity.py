@@ -579,3 +579,55 @@ def test_varlen_chunked_prefill(orc):
     pos_list = [last, 1000, 0]
     _, sel, _, _, aws = _varlen_check(orc, w, inp, dev, cfg, repr_g, "q", 64, pos_list, L, nc, 4)
     _nan_rows_and_rest(cfg, w, dev, "q", 64, [last + 1, 1000, 0], L, nc, sel, {0}, aws)
+
+
+@pytest.mark.parametrize("U,k_m,L,nc,dup,varlen", [
+    (1023, 32, 1, 1, 0, False),       # 128K decode shape
+    (8191, 32, 1, 1, 0, False),       # 1M decode shape
+    (1023, 32, 1, 1, 7, False),       # exact ties: repeated unit rows
+    (2500, 16, 1, 2, 0, True),        # 10 keys per lane, two chunks, a position per sequence
+    (9000, 8, 1, 1, 5, False),        # keys re-read from memory
+    (3, 32, 1, 1, 0, False),          # fewer units than k_m
+    (0, 4, 1, 1, 0, False),           # no units: all -1
+    (1500, 16, 512, 2, 0, False),     # long chunks, one scoring launch + top-k launch
+    (3000, 16, 512, 2, 3, True),      # long chunks beyond the one-launch limit, fused
+])
+def test_select_units_fused(orc, U, k_m, L, nc, dup, varlen):
+    """infllm_select_units: scores bit-identical to infllm_score_units and
+    selections identical to infllm_topk_units on them (and to the oracle's
+    top-k on the same values), twice in a row on one workspace."""
+    b, Hq, Hkv, d = 2, 8, 2, 128
+    cfg = F.make_config(n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, block=128, n_init=128,
+                        window=512, rep_k=4, top_k=k_m)
+    gen = torch.Generator().manual_seed(U + 7 * k_m + L)
+    q = (torch.randn((b, Hq, L * nc + 3, d), generator=gen) * 0.1).to(torch.bfloat16).cuda()
+    repr_ = torch.randn((b, Hkv, max(U, 1), d), generator=gen)[:, :, :U].contiguous()
+    if dup:
+        repr_ = repr_[:, :, torch.arange(U) % dup].contiguous()
+    repr_ = repr_.cuda()
+    t_last = 128 * (U + 1) + 512 + 77        # every unit eligible at the last chunk
+    pos = None
+    if varlen:
+        pos = torch.tensor([t_last - L * nc, 128 * (U // 2) + 512], dtype=torch.int64).cuda()
+    q_pos = t_last - L * nc
+    scores = torch.empty((b, Hkv, nc, U), dtype=torch.float32, device="cuda")
+    sel = torch.empty((b, Hkv, nc, k_m), dtype=torch.int32, device="cuda")
+    ws = F.workspace(cfg, F.INFLLM_CALL_SELECT, b, 0, L, nc)
+    F.infllm_select_units(cfg, q, 3, q_pos, L, nc, repr_, scores, sel, pos=pos, ws=ws)
+    # reference: the two separate calls
+    ref_s = torch.empty_like(scores)
+    sws = F.workspace(cfg, F.INFLLM_CALL_SCORE, b, 0, L, nc)
+    if pos is None:
+        F.infllm_score_units(cfg, q, 3, q_pos, L, nc, repr_, ref_s, sws)
+    else:
+        F.infllm_score_units_varlen(cfg, q, 3, pos, L, nc, repr_, ref_s, sws)
+    ref_sel = gpu_topk(cfg, ref_s)
+    sel2 = torch.full_like(sel, -5)
+    F.infllm_select_units(cfg, q, 3, q_pos, L, nc, repr_, scores, sel2, pos=pos, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(scores, ref_s)
+    assert torch.equal(sel, ref_sel) and torch.equal(sel2, sel)
+    sg, selg = scores.cpu().double().numpy(), sel.cpu().numpy()
+    for idx in np.ndindex(sg.shape[:3]):
+        e = int(np.isfinite(sg[idx]).sum())
+        assert selg[idx].tolist() == orc.topk(sg[idx], e, k_m).tolist()
