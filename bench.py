@@ -212,6 +212,123 @@ class Pipeline:
         return res
 
 
+class StreamPipeline:
+    """Serving-style decode with a growing unit pool (streaming unit build,
+    variable-length batch).  The sequences of the batch have ragged context
+    lengths (synth.stream_lengths) and decode at their own positions; each
+    decode step is one selection and one attention call over the whole
+    batch with a device array of per-sequence positions.  A unit joins a
+    sequence's pool when its first key leaves that sequence's local window:
+    it is built then (infllm_build_units_range, one call per sequence and
+    layer that gains units) from the queries up to the current position.
+    The pools of the starting contexts are built beforehand, each from its
+    whole context.  Decode steps rotate over `layers` layers as in Pipeline;
+    every layer's pool gains its units at the same step."""
+
+    encode, decode = False, True
+
+    def __init__(self, w: synth.Workload, dev: str = "cuda", layers: int = 1):
+        self.w, self.cfg, self.dev = w, cfg_of(w), dev
+        cfg = self.cfg
+        self.inp = synth.make_inputs(w, device=dev)
+        self.q_all = synth.make_stream_queries(w, self.inp["q"])
+        self.lens = synth.stream_lengths(w)
+        b, Hkv, d, S = w.batch, w.n_kv_heads, w.head_dim, w.decode_steps
+        self.U = F.infllm_num_units(cfg, w.n_cap)              # pool rows
+        self.scores = torch.empty((b, Hkv, 1, self.U), dtype=torch.float32, device=dev)
+        self.sel_dec = torch.empty((S, b, Hkv, 1, w.top_k), dtype=torch.int32, device=dev)
+        self.out_dec = torch.empty_like(self.inp["q_dec"])
+        self.sel_ws = F.workspace(cfg, F.INFLLM_CALL_SELECT, b, 0, 1, 1, device=dev)
+        self.attn_ws = F.workspace(cfg, F.INFLLM_CALL_ATTEND, b, 0, 1, 1, device=dev)
+        self.pos_host = np.array([[self.lens[bi] + s for bi in range(b)] for s in range(S)],
+                                 dtype=np.int64)
+        self.pos = torch.tensor(self.pos_host, dtype=torch.int64, device=dev)   # [S, b]
+        tokens = w.rep_mode == "tokens"
+
+        def pool():
+            return dict(repr=torch.zeros((b, Hkv, self.U, d), dtype=torch.float32, device=dev),
+                        rep_idx=(torch.full((b, Hkv, self.U, w.rep_k), -1, dtype=torch.int32,
+                                            device=dev) if tokens else None))
+        self.layers = [dict(k=self.inp["k"], v=self.inp["v"], **pool())]
+        for li in range(1, layers):
+            k, v = synth.make_layer_kv(w, li, device=dev)
+            self.layers.append(dict(k=k, v=v, **pool()))
+        self.repr = self.layers[0]["repr"]
+
+        def elig(t):
+            return F.infllm_num_eligible(cfg, t, self.U)
+        # units each sequence holds before the first step, and the ranges it
+        # gains at each step (built with the queries up to that position)
+        self.start = [elig(n - 1) for n in self.lens]
+        self.builds = []
+        for s in range(S):
+            todo = []
+            for bi in range(b):
+                t = int(self.pos_host[s, bi])
+                lo, hi = elig(t - 1), elig(t)
+                if hi > lo:
+                    todo.append((bi, lo, hi, t + 1))
+            self.builds.append(todo)
+        self.n_builds = sum(len(x) for x in self.builds)
+        most = max([hi - lo for todo in self.builds for _, lo, hi, _ in todo] + [1])
+        self.range_ws = F.workspace(cfg, F.INFLLM_CALL_BUILD_RANGE, 1, most, device=dev)
+        torch.cuda.synchronize()
+
+    def _build(self, ly, bi, lo, hi, n, ws):
+        sl = slice(bi, bi + 1)
+        F.infllm_build_units_range(self.cfg, self.q_all[sl], ly["k"][sl], n, lo, hi,
+                                   None if ly["rep_idx"] is None else ly["rep_idx"][sl],
+                                   ly["repr"][sl], ws)
+
+    def build_all(self):
+        """The pools of the starting contexts (each sequence's own length)."""
+        ws = F.workspace(self.cfg, F.INFLLM_CALL_BUILD_RANGE, 1, max(self.start + [1]),
+                         device=self.dev)
+        for ly in self.layers:
+            for bi, n in enumerate(self.lens):
+                if self.start[bi] > 0:
+                    self._build(ly, bi, 0, self.start[bi], n, ws)
+
+    @staticmethod
+    def _mark(marks, key):
+        Pipeline._mark(marks, key)
+
+    def step(self, marks=None):
+        """One pass of w.decode_steps steps: the units each step adds and its
+        selection, in step order, then the attentions (selections never
+        depend on attention outputs; a unit added at a later step is not
+        eligible earlier).  Marks 'dec_sel' / 'dec_end' around the attention
+        launches."""
+        w, cfg, q = self.w, self.cfg, self.inp["q_dec"]
+        nl = len(self.layers)
+        for s in range(w.decode_steps):
+            for ly in self.layers:
+                for bi, lo, hi, n in self.builds[s]:
+                    self._build(ly, bi, lo, hi, n, self.range_ws)
+            F.infllm_select_units(cfg, q, s, 0, 1, 1, self.layers[s % nl]["repr"], self.scores,
+                                  self.sel_dec[s], pos=self.pos[s], ws=self.sel_ws)
+        self._mark(marks, "dec_sel")
+        for s in range(w.decode_steps):
+            ly = self.layers[s % nl]
+            F.infllm_attend_varlen(cfg, q, s, self.pos[s], 1, 1, ly["k"], ly["v"], self.sel_dec[s],
+                                   self.out_dec, None, s, self.attn_ws)
+        self._mark(marks, "dec_end")
+
+    def work(self):
+        w = self.w
+        esz = 2 if w.dtype == "bf16" else 4
+        sel = self.sel_dec.cpu().numpy()[:, :, :, 0]
+        tokens = flops = nbytes = 0
+        for s in range(w.decode_steps):
+            for bi in range(w.batch):
+                cnt = attended_counts(w, int(self.pos_host[s, bi]), 1, sel[s, bi:bi + 1])
+                tokens += int(cnt.sum()) // w.n_kv_heads
+                flops += 4 * w.head_dim * w.group * int(cnt.sum())
+                nbytes += int(cnt.sum()) * 2 * w.head_dim * esz
+            nbytes += 2 * w.batch * w.n_q_heads * w.head_dim * esz
+        return {"decode": (tokens, flops, nbytes)}
+
+
 CPU_SAMPLE_SECONDS = 10.0
 
 
@@ -373,6 +490,10 @@ def main():
                          "K/V and unit pools (default 4, so that a step's K/V is not still in "
                          "the 256 MB last-level cache from the step before; 1 for the "
                          "single-layer figure); encoding workloads use one layer")
+    ap.add_argument("--stream", action="store_true",
+                    help="decode workloads: serving form -- ragged sequence lengths, a device "
+                         "position per sequence, units added to the pools as they leave the "
+                         "window (streaming unit build)")
     ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
                     help="after timing, run one plain device copy of MIB MiB (untimed), the "
                          "reference kernel for scaling HBM byte counters")
@@ -386,7 +507,10 @@ def main():
     w = synth.WORKLOADS[args.workload]
     decode_only = w.chunk == 0
     layers = (args.layers or 4) if decode_only else 1
-    pipe = Pipeline(w, layers=layers)
+    if args.stream and not decode_only:
+        print("--stream applies to decode workloads", file=sys.stderr)
+        sys.exit(2)
+    pipe = StreamPipeline(w, layers=layers) if args.stream else Pipeline(w, layers=layers)
     if not pipe.encode:
         pipe.build_all()        # decode-only: the pools are built once, beforehand
     for _ in range(args.warmup):
@@ -434,6 +558,10 @@ def main():
                               span_ms("dec_sel", "dec_end") / w.decode_steps, w.decode_steps,
                               peaks)),
     }
+    if args.stream:
+        line["config"]["stream"] = {"lengths": pipe.lens, "pool_units": pipe.U,
+                                    "unit_build_calls_per_step": pipe.n_builds * len(pipe.layers)}
+        line["roofline"]["traffic"] = None      # counters were taken on the fixed-pool form
     if pipe.decode:
         # one decode step = score + top-k + attention for one token position
         # the decode pass of a step: from the end of its encoding pass

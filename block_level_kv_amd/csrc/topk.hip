@@ -4,9 +4,10 @@
 //
 // Up to 256 units (or up to 2,048 with many problems): one wave per
 // problem, four problems per workgroup, the bit-by-bit search.  Otherwise
-// one workgroup of 16 waves per problem and the radix search (8 bits per
-// pass, LDS histograms); keys in registers up to 16*64*32 units, beyond
-// that re-read every pass.
+// one workgroup of 16 waves per problem and the workgroup search (the keys
+// above a lower bound compacted and searched by one wave; radix passes over
+// all keys past 256 candidates); keys in registers up to 16*64*32 units,
+// beyond that re-read at every use.
 #include "kernels.h"
 #include "topk_select.h"
 
@@ -72,6 +73,7 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   const int wcols = (cols + kBlockWaves - 1) / kBlockWaves;   // columns per wave
   if (wcols <= 2) k_topk_block<2><<<grid, kBlockThreads, 0, st>>>(a.scores, a.U, a.k_m, a.sel);
   else if (wcols <= 8) k_topk_block<8><<<grid, kBlockThreads, 0, st>>>(a.scores, a.U, a.k_m, a.sel);
+  else if (wcols <= 16) k_topk_block<16><<<grid, kBlockThreads, 0, st>>>(a.scores, a.U, a.k_m, a.sel);
   else if (wcols <= 32) k_topk_block<32><<<grid, kBlockThreads, 0, st>>>(a.scores, a.U, a.k_m, a.sel);
   else k_topk_block<0><<<grid, kBlockThreads, 0, st>>>(a.scores, a.U, a.k_m, a.sel);
   return hipGetLastError();

@@ -199,6 +199,29 @@ def make_layer_kv(w: Workload, layer: int, device: str | torch.device = "cpu"):
     return k, v
 
 
+def stream_lengths(w: Workload) -> list[int]:
+    """Context lengths of the sequences of a streaming (serving) run: the
+    workload's context for sequence 0, then ragged shorter ones (each a
+    different distance from a unit boundary)."""
+    return [w.n_ctx - bi * (w.n_ctx // 16 + 37) for bi in range(w.batch)]
+
+
+def make_stream_queries(w: Workload, q: torch.Tensor) -> torch.Tensor:
+    """Queries of every position 0 .. n_cap-1 [b, H_q, n_cap, d]: the
+    context's rows of q, then fresh rows (seeded) for the decode positions,
+    which a streaming unit build reads when a unit leaves the window."""
+    dev = q.device
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed * 1000 + 999)
+    b, Hq, n, d = q.shape
+    out = torch.empty((b, Hq, w.n_cap, d), dtype=q.dtype, device=dev)
+    out[:, :, :n] = q
+    if w.n_cap > n:
+        for bi in range(b):
+            out[bi, :, n:] = _normal((Hq, w.n_cap - n, d), gen, dev, w.scale).to(q.dtype)
+    return out
+
+
 def plant_dominant_block(k: torch.Tensor, block: int, B: int, direction: torch.Tensor,
                          margin: float = 1.5) -> None:
     """Overwrite every key of absolute block `block` (all sequences and heads

@@ -206,7 +206,8 @@ def test_score_and_topk_parity(orc, data, name):
                                         (40, 64, False), (300, 1, True), (2048, 32, True),
                                         (2049, 5, True), (16000, 32, True), (20000, 8, False),
                                         (64, 64, False), (4096, 256, True), (40000, 16, True),
-                                        (1500, 32, True), (600, 8, False)])
+                                        (1500, 32, True), (600, 8, False), (8193, 32, False),
+                                        (12000, 16, True)])
 def test_topk_exact(orc, U, k_m, ties):
     gen = torch.Generator().manual_seed(U * 131 + k_m)
     # 1500 and 600 units: enough problems (2 x 2 x 256) for the one-wave variant
