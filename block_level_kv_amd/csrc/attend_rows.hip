@@ -9,12 +9,14 @@
 //     [0, min(n_init, t+1))                     initial tokens
 //     [first_key(u), min(end(u), t-W+1))        each selected unit u
 //     [max(n_init, t-W+1), t+1)                 local window (t included)
-// so no per-key mask is needed.  The intervals' keys are numbered 0..n-1 and
-// split evenly over gridDim.x workgroups (split-K).  Within a workgroup 16
-// lanes share a key (each holds D/16 columns: one coalesced 16-byte load per
-// lane for bf16, D = 128); the 16 key lanes run independent online softmaxes
-// merged through LDS, and the next group of keys is loaded while the current
-// one is reduced.  Splits publish partial (max, sum, unnormalised output)
+// so no per-key mask is needed.  The work is split over gridDim.x workgroups
+// (split-K): each takes an equal share of the local keys (initial tokens and
+// window, known from t alone, so its first loads go out before the
+// selection is read) and an equal share of the units' keys.  Within a
+// workgroup 16 lanes share a key (each holds D/16 columns: one coalesced
+// 16-byte load per lane for bf16, D = 128); the 16 key lanes run independent
+// online softmaxes merged through LDS, and the next group of keys is loaded
+// while the current one is reduced.  Splits publish partial (max, sum, unnormalised output)
 // rows; the last one to arrive merges them in split order (see common.h for
 // the publication protocol), so one launch produces the output.
 #include <stdlib.h>
@@ -25,7 +27,6 @@
 namespace infllm {
 
 constexpr int kRowsThreads = 256;
-constexpr int kMaxIntervals = kMaxTopK + 2;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -91,8 +92,8 @@ __global__ __launch_bounds__(kRowsThreads) void k_attend_rows(AttendArgs a) {
   }
   const int64_t t = base + pos;
 
-  __shared__ int64_t iv_lo[kMaxIntervals];
-  __shared__ int64_t iv_first[kMaxIntervals + 1];  // first key index of each interval
+  __shared__ int64_t iv_lo[kMaxTopK];               // first key position of unit m
+  __shared__ int64_t iv_first[kMaxTopK + 1];        // first unit-key index of unit m
   __shared__ int wave_tot[kRowsThreads / 64];
   __shared__ int last_sh;
 
@@ -104,24 +105,67 @@ __global__ __launch_bounds__(kRowsThreads) void k_attend_rows(AttendArgs a) {
                  (((int64_t)bi * a.Hq + (int64_t)h * G + g) * a.q_cap + a.q_off + pos) * D +
                  seg * CPT);
 
-  // ---------------------------------------------------------- key intervals
-  // slot 0: initial tokens; slots 1..k_m: units (sel order); slot k_m+1:
-  // window.  Thread m computes unit m's length; a block scan gives offsets.
-  const int niv = a.k_m + 2;
+  // ---------------------------------------------------------- key sets
+  // Local keys (initial tokens, then the window) follow from t alone; the
+  // units' keys need the selection.  Every split takes an equal share of
+  // each: local keys [l_begin, l_stop) of the local numbering first, then
+  // unit keys [u_begin, u_stop) of the units' numbering (sel order, each
+  // unit at most B keys).  Its first local keys are requested before the
+  // selection is read and the unit table formed.
+  const int S = gridDim.x;
+  const int64_t unit_cap = t - a.W + 1;
+  const int64_t init_len = a.n_init < t + 1 ? a.n_init : t + 1;
+  const int64_t win_lo = a.n_init > unit_cap ? a.n_init : unit_cap;
+  const int64_t win_len = t + 1 - win_lo > 0 ? t + 1 - win_lo : 0;
+  const int64_t n_local = init_len + win_len;
+  const int64_t pl = (n_local + S - 1) / S;
+  const int64_t l_begin = (int64_t)split * pl < n_local ? (int64_t)split * pl : n_local;
+  const int64_t l_stop = l_begin + pl < n_local ? l_begin + pl : n_local;
+  const int64_t nl = l_stop - l_begin;
+  const int64_t pu = ((int64_t)a.k_m * a.B + S - 1) / S;
+  const int64_t u_begin = (int64_t)split * pu;
+  int32_t my_unit = -1;                              // sel entry `tid`, requested now
+  if (tid < a.k_m) my_unit = a.sel[(((int64_t)bi * a.Hkv + h) * a.n_chunks + ch) * a.k_m + tid];
+
+  const T* kb = (const T*)a.k + ((int64_t)bi * a.Hkv + h) * a.kv_cap * D + seg * CPT;
+  const T* vb = (const T*)a.v + ((int64_t)bi * a.Hkv + h) * a.kv_cap * D + seg * CPT;
+  // split-local key index i -> position: i < nl local keys, then unit keys
+  // through the table (each lane's indices only grow, so a cursor works)
+  int cur = 0;
+  int64_t n_split = nl;                              // + the unit keys, once known
+  auto key_pos = [&](int64_t i) -> int64_t {
+    if (i < nl) {
+      const int64_t x = l_begin + i;
+      return x < init_len ? x : win_lo + (x - init_len);
+    }
+    const int64_t y = u_begin + (i - nl);
+    while (y >= iv_first[cur + 1]) ++cur;
+    return iv_lo[cur] + (y - iv_first[cur]);
+  };
+  RowRaw<T, CPT> kn[kKeysPerIter], vn[kKeysPerIter];
+  bool okn[kKeysPerIter];
+  auto fetch = [&](int64_t base) {
+#pragma unroll
+    for (int j = 0; j < kKeysPerIter; ++j) {
+      const int64_t idx = base + kl + 16 * j;
+      okn[j] = idx < n_split;
+      const int64_t p = okn[j] ? key_pos(idx) : 0;
+      kn[j].load(kb + p * D);
+      vn[j].load(vb + p * D);
+    }
+  };
+  // the first group of keys, if local only, is in flight during the table
+  const bool early = nl >= 16 * kKeysPerIter;
+  if (early) fetch(0);
+
+  // unit table: thread m computes unit m's length, a block scan the offsets
   {
-    const int64_t unit_cap = t - a.W + 1;
-    const int64_t init_len = a.n_init < t + 1 ? a.n_init : t + 1;
-    const int64_t win_lo = a.n_init > unit_cap ? a.n_init : unit_cap;
-    const int64_t win_len = t + 1 - win_lo > 0 ? t + 1 - win_lo : 0;
     int64_t lo = 0, len = 0;
-    if (tid < a.k_m) {
-      const int32_t u = a.sel[(((int64_t)bi * a.Hkv + h) * a.n_chunks + ch) * a.k_m + tid];
-      if (u >= 0) {
-        lo = unit_first_key(u, a.B, a.n_init);
-        const int64_t hi = ((int64_t)u + a.n_init / a.B + 1) * a.B;
-        len = (hi < unit_cap ? hi : unit_cap) - lo;
-        len = len > 0 ? len : 0;
-      }
+    if (my_unit >= 0) {
+      lo = unit_first_key(my_unit, a.B, a.n_init);
+      const int64_t hi = ((int64_t)my_unit + a.n_init / a.B + 1) * a.B;
+      len = (hi < unit_cap ? hi : unit_cap) - lo;
+      len = len > 0 ? len : 0;
     }
     // inclusive scan of the unit lengths (each <= B)
     int x = (int)len;
@@ -139,25 +183,18 @@ __global__ __launch_bounds__(kRowsThreads) void k_attend_rows(AttendArgs a) {
       all += wave_tot[w2];
     }
     if (tid < a.k_m) {
-      iv_lo[tid + 1] = lo;
-      iv_first[tid + 1] = init_len + before + x - len;
+      iv_lo[tid] = lo;
+      iv_first[tid] = before + x - len;
     }
-    if (tid == 0) {
-      iv_lo[0] = 0;
-      iv_first[0] = 0;
-      iv_lo[niv - 1] = win_lo;
-      iv_first[niv - 1] = init_len + all;
-      iv_first[niv] = init_len + all + win_len;
-    }
+    if (tid == 0) iv_first[a.k_m] = all;
   }
   __syncthreads();
-  const int64_t n_keys = iv_first[niv];
-  const int64_t per = (n_keys + gridDim.x - 1) / gridDim.x;
-  const int64_t k_begin = (int64_t)split * per;
-  const int64_t k_stop = k_begin + per < n_keys ? k_begin + per : n_keys;
+  {
+    const int64_t n_unit = iv_first[a.k_m];
+    const int64_t u_stop = u_begin + pu < n_unit ? u_begin + pu : n_unit;
+    n_split = nl + (u_stop > u_begin ? u_stop - u_begin : 0);
+  }
 
-  const T* kb = (const T*)a.k + ((int64_t)bi * a.Hkv + h) * a.kv_cap * D + seg * CPT;
-  const T* vb = (const T*)a.v + ((int64_t)bi * a.Hkv + h) * a.kv_cap * D + seg * CPT;
   const float qscale = kLog2e / sqrtf((float)D);
   float qv[G][CPT];
 #pragma unroll
@@ -175,26 +212,8 @@ __global__ __launch_bounds__(kRowsThreads) void k_attend_rows(AttendArgs a) {
     for (int c = 0; c < CPT; ++c) acc[g][c] = 0.f;
   }
 
-  // key index -> position; each lane's indices only grow, so a cursor works
-  int cur = 0;
-  auto key_pos = [&](int64_t idx) -> int64_t {
-    while (idx >= iv_first[cur + 1]) ++cur;
-    return iv_lo[cur] + (idx - iv_first[cur]);
-  };
-  RowRaw<T, CPT> kn[kKeysPerIter], vn[kKeysPerIter];
-  bool okn[kKeysPerIter];
-  auto fetch = [&](int64_t base) {
-#pragma unroll
-    for (int j = 0; j < kKeysPerIter; ++j) {
-      const int64_t idx = base + kl + 16 * j;
-      okn[j] = idx < k_stop;
-      const int64_t p = okn[j] ? key_pos(idx) : 0;
-      kn[j].load(kb + p * D);
-      vn[j].load(vb + p * D);
-    }
-  };
-  if (k_begin < k_stop) fetch(k_begin);
-  for (int64_t base = k_begin; base < k_stop; base += 16 * kKeysPerIter) {
+  if (!early) fetch(0);
+  for (int64_t base = 0; base < n_split; base += 16 * kKeysPerIter) {
     RowRaw<T, CPT> kc[kKeysPerIter], vc[kKeysPerIter];
     bool ok[kKeysPerIter];
 #pragma unroll
@@ -203,7 +222,7 @@ __global__ __launch_bounds__(kRowsThreads) void k_attend_rows(AttendArgs a) {
       vc[j] = vn[j];
       ok[j] = okn[j];
     }
-    if (base + 16 * kKeysPerIter < k_stop) fetch(base + 16 * kKeysPerIter);  // in flight
+    if (base + 16 * kKeysPerIter < n_split) fetch(base + 16 * kKeysPerIter);  // in flight
     // logits of the current keys for every head (each key row converted once)
     float s[G][kKeysPerIter];
 #pragma unroll
