@@ -17,6 +17,9 @@ model's layers follow one another, so no step finds its K/V still in the
 Mistral-7B 64K layer (one step = build + 128 encoding chunks + 256 decode
 steps).
 
+Before the W warm-up steps, untimed steps run for --settle seconds (1 by
+default) so that the GPU clocks are in steady state when timing starts.
+
 Prints ONE JSON line.  `value` is attended KV tokens per second over the
 whole step (over sequences and query positions, the number of keys each
 query attends, averaged over KV heads).  `roofline` is for the attention
@@ -490,6 +493,9 @@ def main():
                          "K/V and unit pools (default 4, so that a step's K/V is not still in "
                          "the 256 MB last-level cache from the step before; 1 for the "
                          "single-layer figure); encoding workloads use one layer")
+    ap.add_argument("--settle", type=float, default=1.0, metavar="SECONDS",
+                    help="untimed steps for this long before the warm-up steps, so that the "
+                         "GPU clocks reach steady state (0 to skip)")
     ap.add_argument("--stream", action="store_true",
                     help="decode workloads: serving form -- ragged sequence lengths, a device "
                          "position per sequence, units added to the pools as they leave the "
@@ -513,6 +519,16 @@ def main():
     pipe = StreamPipeline(w, layers=layers) if args.stream else Pipeline(w, layers=layers)
     if not pipe.encode:
         pipe.build_all()        # decode-only: the pools are built once, beforehand
+    # Untimed settling before the warm-up steps: the GPU's clocks ramp up
+    # over the first ~100 ms of sustained work (a 2-step warm-up left the
+    # 32K encoding step ~6% slower than steady state), so steps run until
+    # args.settle seconds have passed.
+    settle_steps = 0
+    t_settle = time.time()
+    while time.time() - t_settle < args.settle:
+        pipe.step()
+        torch.cuda.synchronize()
+        settle_steps += 1
     for _ in range(args.warmup):
         pipe.step()
     torch.cuda.synchronize()
@@ -541,6 +557,7 @@ def main():
         "value": round(tokens / (ms_step * 1e-3), 1),
         "unit": "attended KV tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "settle": {"seconds": args.settle, "steps": settle_steps},
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
