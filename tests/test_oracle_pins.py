@@ -218,6 +218,37 @@ def test_partial_unit_representatives(orc):
     assert sorted(rep_idx2[0].tolist()) == [-1, -1, 30, 31]
 
 
+def test_streaming_build_truncation(orc):
+    """A unit built at a shorter context: its key scores sum only the queries
+    before that context's end (R1 with n_ctx as the current position), so a
+    unit whose last key is at or before n_ctx-1-W (every key's window inside
+    the context) gets exactly its whole-context result, and a unit still in
+    the window differs only through the truncated sums.  Checked against
+    direct sums of q.k over the truncated windows."""
+    G, d, B, n_init, W, r_k = 2, 8, 32, 32, 48, 3
+    n = 400
+    qg, k = rnd((G, n, d), 21), rnd((n, d), 22)
+    rep_f, repr_f, ks_f = orc.build_tokens(qg, k, n, B, n_init, W, r_k)
+    for n_cur in (150, 211, 300):
+        U = orc.num_units(n_cur, B, n_init)
+        rep_c, repr_c, ks_c = orc.build_tokens(qg, k, n_cur, B, n_init, W, r_k, 0, U)
+        for u in range(U):
+            lo, hi = orc.unit_keys(u, B, n_init)
+            # key scores: direct sums over p+1 .. min(p+W, n_cur-1)
+            for p in range(lo, hi):
+                end = min(p + W, n_cur - 1)
+                want = float((qg[:, p + 1:end + 1].double().sum((0, 1)) @ k[p].double()))
+                assert ks_c[u, p - (u + n_init // B) * B] == pytest.approx(want, rel=1e-12,
+                                                                           abs=1e-12)
+            if hi - 1 <= n_cur - 1 - W:
+                assert rep_c[u].tolist() == rep_f[u].tolist()
+                assert np.array_equal(repr_c[u], repr_f[u])
+        # and a range call equals the same rows of the whole-range call
+        lo_u = U // 2
+        rep_r, repr_r, _ = orc.build_tokens(qg, k, n_cur, B, n_init, W, r_k, lo_u, U)
+        assert np.array_equal(rep_r, rep_c[lo_u:]) and np.array_equal(repr_r, repr_c[lo_u:])
+
+
 # --------------------------------------------------------------- unit scores
 def test_chunk_score_bilinear_expansion(orc):
     G, d, B, n_init, W, r_k = 3, 8, 16, 16, 32, 2
