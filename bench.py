@@ -386,9 +386,16 @@ def cpu_baseline(w: synth.Workload, pipe: Pipeline) -> dict:
         sample = "%d of %d decode steps (score, top-k, attention), sequence 0 of %d" % (
             done, w.decode_steps, w.batch)
     dt = time.time() - t_start
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")),
+                       cpu)
+    except OSError:
+        pass
     return {"value": round(tokens / dt, 1), "unit": "attended KV tokens/s",
             "cores": orc.num_threads(), "kind": "oracle", "sample": sample,
-            "seconds": round(dt, 2)}
+            "seconds": round(dt, 2), "cpu": cpu, "host_cpus": os.cpu_count()}
 
 
 def stored_traffic(kernel: str, workload: str):
