@@ -3,12 +3,15 @@
 // "Core Innovation 2", item 2: keep the k highest-scoring units).
 //
 // Scores become order-preserving 32-bit keys (0 for -inf, never kept).  The
-// K-th largest key tau (K = min(k_m, #finite)) is found on the keys' bits:
-// bit by bit for one wave (a candidate is kept when at least K keys reach
-// it; the search stops once exactly K keys reach the candidate), 8 bits per
-// pass with LDS histograms for a workgroup.  Keys above tau are kept, keys
-// equal to tau fill the remaining slots lowest index first (ties go to the
-// lower index).  Integer work on the fp32 scores: exact and deterministic.
+// K-th largest key tau (K = min(k_m, #finite)) is found on the keys' bits,
+// bit by bit by one wave (a candidate is kept when at least K keys reach
+// it; the search stops once exactly K keys reach the candidate).  A
+// workgroup first narrows the keys to those at or above a lower bound on
+// tau and hands them to one wave (block_topk below), or, with too many
+// candidates, searches 8 bits per pass with LDS histograms.  Keys above tau
+// are kept, keys equal to tau fill the remaining slots lowest index first
+// (ties go to the lower index).  Integer work on the fp32 scores: exact and
+// deterministic.
 //
 // Layout: a wave owns a contiguous index range and lane l holds indices
 // base + l + 64*i (one coalesced load per i).  Counts are ballots and
