@@ -41,23 +41,31 @@ __global__ __launch_bounds__(kSumThreads) void k_block_sums(const T* __restrict_
   for (int s2 = 0; s2 < NSUB; ++s2)
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[s2][i] = 0.0;
-  for (int g = 0; g < G; ++g) {
-    const T* qh = q + ((int64_t)bi * Hq + (int64_t)h * G + g) * q_cap * d + cg * 8;
+  // two query heads per batch of loads (16 rows of 16 bytes per thread in
+  // flight); a head past G re-reads the last one and is not added
+  for (int g0 = 0; g0 < G; g0 += 2) {
+    const T* qh0 = q + ((int64_t)bi * Hq + (int64_t)h * G + g0) * q_cap * d + cg * 8;
+    const T* qh1 = g0 + 1 < G ? qh0 + q_cap * d : qh0;
     for (int64_t rb = r0 + ph; rb < r1; rb += 8 * nph) {
-      Raw8<T> raw[8];
+      Raw8<T> raw[2][8];
 #pragma unroll
       for (int y = 0; y < 8; ++y) {
         const int64_t r = rb + (int64_t)y * nph;
-        raw[y].load(qh + (r < r1 ? r : r1 - 1) * d);
+        raw[0][y].load(qh0 + (r < r1 ? r : r1 - 1) * d);
+        raw[1][y].load(qh1 + (r < r1 ? r : r1 - 1) * d);
       }
 #pragma unroll
-      for (int y = 0; y < 8; ++y) {
-        const int64_t r = rb + (int64_t)y * nph;
-        if (r >= r1) break;
-        const int sb = NSUB == 1 ? 0 : (int)((r - r0) / sub_rows);
+      for (int hh = 0; hh < 2; ++hh) {
+        if (g0 + hh >= G) break;
 #pragma unroll
-        for (int s2 = 0; s2 < NSUB; ++s2)
-          if (s2 == sb) raw[y].add(acc[s2]);
+        for (int y = 0; y < 8; ++y) {
+          const int64_t r = rb + (int64_t)y * nph;
+          if (r >= r1) break;
+          const int sb = NSUB == 1 ? 0 : (int)((r - r0) / sub_rows);
+#pragma unroll
+          for (int s2 = 0; s2 < NSUB; ++s2)
+            if (s2 == sb) raw[hh][y].add(acc[s2]);
+        }
       }
     }
   }
@@ -86,21 +94,33 @@ __global__ void k_block_prefix(const double* __restrict__ S, double* __restrict_
   const int h = blockIdx.x, bi = blockIdx.y, c = threadIdx.x;
   const double* s = S + ((int64_t)bi * Hkv + h) * n_blocks * d;
   double* bp = BP + ((int64_t)bi * Hkv + h) * (n_blocks + 1) * d;
+  // batches of kPrefixBatch block sums, the next batch requested before the
+  // current one is added (a dependent chain of one add per block)
+  constexpr int kPrefixBatch = 16;
   double acc = 0.0;
-  int j = 0;
-  for (; j + 8 <= n_blocks; j += 8) {
-    double v[8];
+  double v[kPrefixBatch], w[kPrefixBatch];
+  auto load = [&](double* x, int j0) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) v[t] = s[(int64_t)(j + t) * d + c];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      bp[(int64_t)(j + t) * d + c] = acc;
-      acc += v[t];
+    for (int t = 0; t < kPrefixBatch; ++t) {
+      const int j = j0 + t < n_blocks ? j0 + t : n_blocks - 1;
+      x[t] = s[(int64_t)j * d + c];
     }
-  }
-  for (; j < n_blocks; ++j) {
-    bp[(int64_t)j * d + c] = acc;
-    acc += s[(int64_t)j * d + c];
+  };
+  auto add = [&](const double* x, int j0) {
+#pragma unroll
+    for (int t = 0; t < kPrefixBatch; ++t) {
+      if (j0 + t >= n_blocks) break;
+      bp[(int64_t)(j0 + t) * d + c] = acc;
+      acc += x[t];
+    }
+  };
+  if (n_blocks > 0) load(v, 0);
+  for (int j = 0; j < n_blocks; j += 2 * kPrefixBatch) {
+    if (j + kPrefixBatch < n_blocks) load(w, j + kPrefixBatch);
+    add(v, j);
+    if (j + kPrefixBatch >= n_blocks) break;
+    if (j + 2 * kPrefixBatch < n_blocks) load(v, j + 2 * kPrefixBatch);
+    add(w, j + kPrefixBatch);
   }
   bp[(int64_t)n_blocks * d + c] = acc;
 }
