@@ -179,3 +179,51 @@ def test_fullsize_mistral_64k(orc, name):
                   [(t // w.chunk, t, t) for t in (100, 4300, 40000, 65535)])
     check_outputs(orc, w, qd, k, v, p.out_dec, p.sel_dec,
                   [(s, s, w.n_ctx + s) for s in (0, 200)])
+
+
+def test_fullsize_llama3_128k_serving_form(orc):
+    """The serving form bench.py --stream times, at the 128K decode size:
+    ragged lengths, per-sequence positions, units appended as they leave
+    each sequence's window.  The appended units against the oracle at the
+    context they were built with, the starting pool on samples, and
+    sampled decode steps' selections and outputs per sequence."""
+    w = synth.WORKLOADS["llama3_8b_128k_decode"]
+    p = bench.StreamPipeline(w)
+    p.build_all()
+    p.step()
+    torch.cuda.synchronize()
+    G, B = w.group, w.block
+    appended = [(s, bi, lo, hi, n) for s, todo in enumerate(p.builds) for bi, lo, hi, n in todo]
+    assert len(appended) >= w.batch
+    exemptions = 0
+    k_cpu = {}
+    for s, bi, lo, hi, n in appended[:4] + [(None, 1, p.start[1] - 6, p.start[1], p.lens[1])]:
+        h = (bi * 3 + (lo % 5)) % w.n_kv_heads
+        k = p.inp["k"][bi, h, :n].cpu()
+        qg = p.q_all[bi, h * G:(h + 1) * G, :n].cpu()
+        rep_o, repr_o, ks_o = orc.build_tokens(qg, k, n, B, w.n_init, w.window, w.rep_k, lo, hi)
+        rep_g = p.layers[0]["rep_idx"][bi, h, lo:hi].cpu().numpy()
+        repr_g = p.layers[0]["repr"][bi, h, lo:hi].cpu().numpy()
+        for i in range(hi - lo):
+            if np.array_equal(rep_g[i], rep_o[i]):
+                np.testing.assert_array_equal(repr_g[i], repr_o[i].astype(np.float32))
+                continue
+            start = (lo + i + w.n_init // B) * B
+            by_pos = {start + t: ks_o[i, t] for t in range(B) if np.isfinite(ks_o[i, t])}
+            exemptions += check_selection(rep_g[i], rep_o[i], by_pos)
+    assert exemptions <= 1
+    qd = p.inp["q_dec"].cpu()
+    sel = p.sel_dec.cpu().numpy()[:, :, :, 0]
+    repr_np = p.layers[0]["repr"].cpu().double().numpy()
+    kk, vv = p.inp["k"].cpu(), p.inp["v"].cpu()
+    for s in (0, 200, 255):
+        for bi in (0, w.batch - 1):
+            t = int(p.pos_host[s, bi])
+            e = orc.num_eligible(t, p.U, B, w.n_init, w.window)
+            for h in (0, w.n_kv_heads - 1):
+                so = orc.score_units(qd[bi, h * G:(h + 1) * G, s:s + 1], repr_np[bi, h], e)
+                check_selection(sel[s, bi, h], orc.topk(so, e, w.top_k), so)
+            o_ref, _ = orc.attend_all(qd[bi:bi + 1, :, s:s + 1], t, kk[bi:bi + 1], vv[bi:bi + 1],
+                                      sel[s, bi:bi + 1], B=B, n_init=w.n_init, W=w.window)
+            assert_close(p.out_dec[bi:bi + 1, :, s:s + 1], o_ref,
+                         tolerance(torch.bfloat16, o_ref), "serving step %d sequence %d" % (s, bi))
