@@ -103,6 +103,14 @@ class Pipeline:
                         if w.rep_mode == "tokens" else None)
         self.build_ws = F.workspace(cfg, F.INFLLM_CALL_BUILD, b, w.n_ctx, device=dev)
         self.scores = torch.empty((b, Hkv, 1, self.U), dtype=torch.float32, device=dev)
+        # chunks of whole units take their query sums from the build's block
+        # sums (infllm_build_units_qsum / infllm_score_units_qsum): the
+        # encoding pass reads the queries for them once, in the build
+        self.block_qsum = None
+        if w.chunk > 0 and w.chunk % w.block == 0:
+            nb = (w.n_ctx + w.block - 1) // w.block
+            self.block_qsum = torch.empty((b, Hkv, nb, d), dtype=torch.float64, device=dev)
+            self.build_ws = F.workspace(cfg, F.INFLLM_CALL_BUILD_QSUM, b, w.n_ctx, device=dev)
         if self.encode:
             nc = self.n_chunks = w.n_ctx // w.chunk
             self.enc_scores = torch.empty((b, Hkv, nc, self.U), dtype=torch.float32, device=dev)
@@ -131,8 +139,12 @@ class Pipeline:
 
     def build(self, layer: int = 0):
         ly = self.layers[layer]
-        F.infllm_build_units(self.cfg, self.inp["q"], ly["k"], self.w.n_ctx, ly["rep_idx"],
-                             ly["repr"], self.build_ws)
+        if self.block_qsum is not None and layer == 0:
+            F.infllm_build_units_qsum(self.cfg, self.inp["q"], ly["k"], self.w.n_ctx,
+                                      ly["rep_idx"], ly["repr"], self.block_qsum, self.build_ws)
+        else:
+            F.infllm_build_units(self.cfg, self.inp["q"], ly["k"], self.w.n_ctx, ly["rep_idx"],
+                                 ly["repr"], self.build_ws)
 
     def build_all(self):
         for li in range(len(self.layers)):
@@ -170,8 +182,12 @@ class Pipeline:
             # (chunk c covers queries [c*chunk, (c+1)*chunk), positions equal)
             self.build()
             nc = self.n_chunks
-            F.infllm_score_units(cfg, inp["q"], 0, 0, w.chunk, nc, self.repr, self.enc_scores,
-                                 self.enc_score_ws)
+            if self.block_qsum is not None:
+                F.infllm_score_units_qsum(cfg, self.block_qsum, 0, w.chunk, nc, self.repr,
+                                          self.enc_scores)
+            else:
+                F.infllm_score_units(cfg, inp["q"], 0, 0, w.chunk, nc, self.repr, self.enc_scores,
+                                     self.enc_score_ws)
             F.infllm_topk_units(cfg, self.enc_scores, self.enc_sel)
             self._mark(marks, "enc_sel")
             F.infllm_attend(cfg, inp["q"], 0, 0, w.chunk, nc, inp["k"], inp["v"], self.enc_sel,

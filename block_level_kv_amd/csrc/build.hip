@@ -388,6 +388,11 @@ __global__ void k_mean_repr(const T* __restrict__ k, int64_t kv_cap, int Hkv, in
 // of the prefix enter a score.
 static void build_blocks(const BuildArgs& a, int64_t* jb0, int64_t* nbl) {
   const int64_t nb = (a.n_ctx + a.B - 1) / a.B;
+  if (a.block_qsum) {   // the caller's block sums cover every block of the context
+    *jb0 = 0;
+    *nbl = nb;
+    return;
+  }
   const int64_t j0 = a.n_init / a.B;
   *jb0 = a.u_begin + j0;
   int64_t jb1 = (int64_t)(a.u_end - 1) + j0 + (a.W + a.B - 1) / a.B + 2;
@@ -402,7 +407,7 @@ struct BuildWs {
 static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 static BuildWs build_ws_layout(const BuildArgs& a, int64_t nbl) {
   BuildWs w;
-  w.s = round256((size_t)a.batch * a.Hkv * nbl * a.d * sizeof(double));
+  w.s = a.block_qsum ? 0 : round256((size_t)a.batch * a.Hkv * nbl * a.d * sizeof(double));
   w.bp = round256((size_t)a.batch * a.Hkv * (nbl + 1) * a.d * sizeof(double));
   w.s32 = a.B == 128 ? (size_t)a.batch * a.Hkv * nbl * 4 * a.d * sizeof(double) : 0;
   return w;
@@ -416,6 +421,16 @@ size_t build_workspace_bytes(const BuildArgs& a) {
   return ws_total(build_ws_layout(a, nbl));
 }
 
+// the build that also writes the block query sums (S in the caller's buffer)
+size_t build_qsum_workspace_bytes(const BuildArgs& a) {
+  if (a.rep_mode != 0 || a.U < 1) return 0;
+  BuildArgs b = a;
+  b.block_qsum = reinterpret_cast<double*>(16);   // any non-null: the layout without S
+  int64_t jb0, nbl;
+  build_blocks(b, &jb0, &nbl);
+  return ws_total(build_ws_layout(b, nbl));
+}
+
 size_t build_range_workspace_bytes(const BuildArgs& a, int64_t n_units) {
   if (a.rep_mode != 0 || n_units < 1) return 0;
   return ws_total(build_ws_layout(a, n_units + (a.W + a.B - 1) / a.B + 2));
@@ -426,6 +441,14 @@ static hipError_t launch_build_t(const BuildArgs& a, hipStream_t st) {
   const T* q = (const T*)a.q;
   const T* k = (const T*)a.k;
   const int n_u = a.u_end - a.u_begin;
+  if (a.block_qsum && (a.rep_mode != 0 || n_u <= 0)) {
+    // block query sums of the whole context, for chunk scores; MEAN builds
+    // need nothing else from the queries
+    const int64_t nb_all = (a.n_ctx + a.B - 1) / a.B;
+    k_block_sums<T, 1><<<dim3((unsigned)nb_all, a.Hkv, a.batch), kSumThreads, 0, st>>>(
+        q, a.q_cap, a.Hq, a.Hkv, a.d, a.B, a.n_ctx, 0, (int)nb_all, a.block_qsum, nullptr);
+    if (n_u <= 0) return hipGetLastError();
+  }
   if (n_u <= 0) return hipSuccess;
   if (a.rep_mode != 0) {
     k_mean_repr<T><<<dim3(n_u, a.Hkv, a.batch), a.d, 0, st>>>(k, a.kv_cap, a.Hkv, a.d, a.B,
@@ -436,7 +459,7 @@ static hipError_t launch_build_t(const BuildArgs& a, hipStream_t st) {
   int64_t jb0, nbl;
   build_blocks(a, &jb0, &nbl);
   const BuildWs lay = build_ws_layout(a, nbl);
-  double* S = (double*)a.ws;
+  double* S = a.block_qsum ? a.block_qsum : (double*)a.ws;
   double* BP = (double*)((char*)a.ws + lay.s);
   double* S32 = lay.s32 > 0 ? (double*)((char*)a.ws + lay.s + lay.bp) : nullptr;
   const int nb = (int)nbl;

@@ -157,6 +157,8 @@ size_t infllm_workspace_size(const infllm_config* cfg, int32_t call, int32_t bat
   switch (call) {
     case INFLLM_CALL_BUILD:
       return n < 1 ? 0 : build_workspace_bytes(build_args(cfg, batch, n));
+    case INFLLM_CALL_BUILD_QSUM:
+      return n < 1 ? 0 : build_qsum_workspace_bytes(build_args(cfg, batch, n));
     case INFLLM_CALL_BUILD_RANGE:
       return n < 1 ? 0 : build_range_workspace_bytes(build_args(cfg, batch, 0), n);
     case INFLLM_CALL_SCORE:
@@ -197,6 +199,35 @@ infllm_status infllm_build_units(const infllm_config* cfg, int32_t batch, const 
   a.rep_idx = rep_idx;
   a.unit_repr = unit_repr;
   a.ws = workspace;
+  return launched(launch_build(a, (hipStream_t)stream));
+}
+
+infllm_status infllm_build_units_qsum(const infllm_config* cfg, int32_t batch, const void* q,
+                                      int64_t q_cap, const void* k, int64_t kv_cap, int64_t n_ctx,
+                                      int32_t* rep_idx, float* unit_repr, double* block_qsum,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  infllm_status st = check_config(cfg);
+  if (st != INFLLM_OK) return st;
+  if (batch < 1 || n_ctx < 1 || q_cap < n_ctx || kv_cap < n_ctx) return INFLLM_ERR_INVALID_ARG;
+  const bool tokens = cfg->rep_mode == INFLLM_REP_TOKENS;
+  if (!k || !aligned16(k) || !q || !aligned16(q) || !block_qsum || !aligned16(block_qsum))
+    return INFLLM_ERR_INVALID_ARG;
+  BuildArgs a = build_args(cfg, batch, n_ctx);
+  if (a.U > 0) {
+    if (!unit_repr || !aligned16(unit_repr)) return INFLLM_ERR_INVALID_ARG;
+    if (tokens && (!rep_idx || !aligned16(rep_idx))) return INFLLM_ERR_INVALID_ARG;
+  }
+  const size_t need = build_qsum_workspace_bytes(a);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return INFLLM_ERR_WORKSPACE;
+  a.q = q;
+  a.q_cap = q_cap;
+  a.k = k;
+  a.kv_cap = kv_cap;
+  a.rep_idx = rep_idx;
+  a.unit_repr = unit_repr;
+  a.ws = workspace;
+  a.block_qsum = block_qsum;
   return launched(launch_build(a, (hipStream_t)stream));
 }
 
@@ -283,6 +314,31 @@ infllm_status infllm_score_units(const infllm_config* cfg, int32_t batch, const 
                                  void* stream) {
   return score_impl(cfg, batch, q, q_cap, q_off, q_pos, nullptr, chunk_len, n_chunks, unit_repr,
                     n_units, scores, nullptr, workspace, workspace_bytes, stream);
+}
+
+infllm_status infllm_score_units_qsum(const infllm_config* cfg, int32_t batch,
+                                      const double* block_qsum, int64_t n_blocks, int64_t q_pos,
+                                      int32_t chunk_len, int32_t n_chunks, const float* unit_repr,
+                                      int32_t n_units, float* scores, void* stream) {
+  infllm_status st = check_config(cfg);
+  if (st != INFLLM_OK) return st;
+  if (batch < 1 || chunk_len < 1 || n_chunks < 1 || n_units < 0 || q_pos < 0 || n_blocks < 1)
+    return INFLLM_ERR_INVALID_ARG;
+  // chunks made of whole blocks
+  if (q_pos % cfg->block != 0 || chunk_len % cfg->block != 0) return INFLLM_ERR_INVALID_ARG;
+  if ((q_pos + (int64_t)chunk_len * n_chunks) / cfg->block > n_blocks) return INFLLM_ERR_INVALID_ARG;
+  if ((int64_t)n_chunks * cfg->n_kv_heads > 65535) return INFLLM_ERR_UNSUPPORTED;
+  if (!block_qsum || !aligned16(block_qsum)) return INFLLM_ERR_INVALID_ARG;
+  if (n_units > 0 && (!unit_repr || !scores || !aligned16(unit_repr) || !aligned16(scores)))
+    return INFLLM_ERR_INVALID_ARG;
+  ScoreArgs a = score_args(cfg, batch, chunk_len, n_chunks);
+  a.U = n_units;
+  a.q_pos = q_pos;
+  a.block_qsum = block_qsum;
+  a.n_blocks = n_blocks;
+  a.repr = unit_repr;
+  a.scores = scores;
+  return launched(launch_score(a, (hipStream_t)stream));
 }
 
 infllm_status infllm_select_units(const infllm_config* cfg, int32_t batch, const void* q,

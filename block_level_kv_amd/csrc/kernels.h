@@ -20,6 +20,7 @@ struct BuildArgs {
   int32_t* rep_idx;
   float* unit_repr;
   void* ws;
+  double* block_qsum;  // optional out [batch, H_kv, ceil(n_ctx/B), d]: fp64 block query sums
 };
 
 struct ScoreArgs {
@@ -33,6 +34,8 @@ struct ScoreArgs {
   void* ws;  // fp64 partial query sums of long chunks
   int k_m;       // fused selection: units kept per row
   int32_t* sel;  // fused selection output, or null (scores only)
+  const double* block_qsum;  // chunk sums from block query sums (B-aligned chunks), or null
+  int64_t n_blocks;          // blocks per (sequence, KV head) in block_qsum
 };
 
 struct TopkArgs {
@@ -61,6 +64,7 @@ struct AttendArgs {
 
 size_t build_workspace_bytes(const BuildArgs& a);
 size_t build_range_workspace_bytes(const BuildArgs& a, int64_t n_units);
+size_t build_qsum_workspace_bytes(const BuildArgs& a);
 hipError_t launch_build(const BuildArgs& a, hipStream_t st);
 size_t score_workspace_bytes(const ScoreArgs& a);
 size_t select_workspace_bytes(const ScoreArgs& a);

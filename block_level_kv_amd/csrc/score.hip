@@ -173,7 +173,8 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_units(
     const T* __restrict__ q, int64_t q_cap, int64_t q_off, int64_t q_pos,
     const int64_t* __restrict__ pos, int L, int Hq, int Hkv,
     int B, int n_init, int W, const float* __restrict__ repr, int U, float* __restrict__ scores,
-    int n_chunks, const double* __restrict__ parts, int n_parts, int* __restrict__ count,
+    int n_chunks, const double* __restrict__ parts, int n_parts, int64_t part_stride,
+    int64_t part0, int* __restrict__ count,
     int k_m, int32_t* __restrict__ sel) {
   using Rows = UnitRows<D, kUnitsPerWG / UnitRows<D, 1>::kPerSlot>;
   const int slice = blockIdx.x;
@@ -188,7 +189,10 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_units(
   rows.load(rb, U, u0);              // in flight while the query sum forms
 
   if (n_parts > 0) {
-    const double* pp = parts + (((int64_t)bi * Hkv + h) * n_chunks + ch) * n_parts * D;
+    // partial sums of chunk ch: n_parts rows from row part0 + ch * n_parts
+    // of this (sequence, KV head)'s part_stride rows
+    const double* pp = parts + (((int64_t)bi * Hkv + h) * part_stride + part0 +
+                                (int64_t)ch * n_parts) * D;
     const double t = sum_parts<D>(pp, n_parts, tid % D);
     if (tid < D) qsum[tid] = t;
     __syncthreads();
@@ -373,11 +377,18 @@ static void launch_parts(const ScoreArgs& a, int parts, double* pw, hipStream_t 
 
 template <typename T, int G, int D>
 static hipError_t launch_score_tgd(const ScoreArgs& a, hipStream_t st) {
-  const int parts = score_num_parts(a);
-  double* pw = parts > 0 ? (double*)((char*)a.ws + score_counter_bytes(a)) : nullptr;
-  if (parts > 0) {
-    if (score_rows(a) == kRowsLong) launch_parts<T, G, D, kRowsLong>(a, parts, pw, st);
-    else launch_parts<T, G, D, kRowsShort>(a, parts, pw, st);
+  // chunk sums from block query sums: the chunk's L/B blocks are its parts
+  const bool from_blocks = a.block_qsum != nullptr;
+  const int parts = from_blocks ? a.L / a.B : score_num_parts(a);
+  const double* pw = from_blocks ? a.block_qsum
+                   : parts > 0   ? (const double*)((char*)a.ws + score_counter_bytes(a))
+                                 : nullptr;
+  const int64_t part_stride = from_blocks ? a.n_blocks : (int64_t)a.n_chunks * parts;
+  const int64_t part0 = from_blocks ? a.q_pos / a.B : 0;
+  if (parts > 0 && !from_blocks) {
+    double* pwm = const_cast<double*>(pw);
+    if (score_rows(a) == kRowsLong) launch_parts<T, G, D, kRowsLong>(a, parts, pwm, st);
+    else launch_parts<T, G, D, kRowsShort>(a, parts, pwm, st);
     if (score_fused(a)) {
       // one workgroup scores each chunk; the selection is a launch of its own
       if (!a.sel) return hipGetLastError();
@@ -388,7 +399,7 @@ static hipError_t launch_score_tgd(const ScoreArgs& a, hipStream_t st) {
 #define INFLLM_SCORE_UNITS(SEL, CNT)                                                            \
   k_score_units<T, G, D, SEL><<<grid, kScoreThreads, 0, st>>>(                                 \
       (const T*)a.q, a.q_cap, a.q_off, a.q_pos, a.pos, a.L, a.Hq, a.Hkv, a.B, a.n_init, a.W,     \
-      a.repr, a.U, a.scores, a.n_chunks, pw, parts, CNT, a.k_m, a.sel)
+      a.repr, a.U, a.scores, a.n_chunks, pw, parts, part_stride, part0, CNT, a.k_m, a.sel)
   if (!a.sel || grid.x > kMaxSelSlices) {
     INFLLM_SCORE_UNITS(-1, nullptr);
     if (a.sel) return launch_topk(select_topk_args(a), st);

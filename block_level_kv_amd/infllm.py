@@ -20,10 +20,11 @@ INFLLM_OK, INFLLM_ERR_INVALID_ARG, INFLLM_ERR_UNSUPPORTED, INFLLM_ERR_WORKSPACE,
 INFLLM_F32, INFLLM_BF16 = 0, 1
 INFLLM_REP_TOKENS, INFLLM_REP_MEAN = 0, 1
 INFLLM_CALL_BUILD, INFLLM_CALL_SCORE, INFLLM_CALL_TOPK, INFLLM_CALL_ATTEND = 0, 1, 2, 3
-INFLLM_CALL_BUILD_RANGE, INFLLM_CALL_SELECT = 4, 5
+INFLLM_CALL_BUILD_RANGE, INFLLM_CALL_SELECT, INFLLM_CALL_BUILD_QSUM = 4, 5, 6
 
 EXPORTED = ("infllm_num_units", "infllm_num_eligible", "infllm_workspace_size",
-            "infllm_build_units", "infllm_build_units_range", "infllm_score_units",
+            "infllm_build_units", "infllm_build_units_range", "infllm_build_units_qsum",
+            "infllm_score_units", "infllm_score_units_qsum",
             "infllm_score_units_varlen", "infllm_select_units", "infllm_topk_units",
             "infllm_attend",
             "infllm_attend_varlen", "infllm_status_string", "infllm_abi_version")
@@ -63,6 +64,12 @@ def lib() -> ctypes.CDLL:
         L.infllm_build_units.restype = _i32
         L.infllm_build_units.argtypes = [_cfgp, _i32, _vp, _i64, _vp, _i64, _i64, _vp, _vp, _vp,
                                          _sz, _vp]
+        L.infllm_build_units_qsum.restype = _i32
+        L.infllm_build_units_qsum.argtypes = [_cfgp, _i32, _vp, _i64, _vp, _i64, _i64, _vp, _vp,
+                                              _vp, _vp, _sz, _vp]
+        L.infllm_score_units_qsum.restype = _i32
+        L.infllm_score_units_qsum.argtypes = [_cfgp, _i32, _vp, _i64, _i64, _i32, _i32, _vp, _i32,
+                                              _vp, _vp]
         L.infllm_build_units_range.restype = _i32
         L.infllm_build_units_range.argtypes = [_cfgp, _i32, _vp, _i64, _vp, _i64, _i64, _i32, _i32,
                                                _i32, _vp, _vp, _vp, _sz, _vp]
@@ -190,6 +197,44 @@ def infllm_build_units(cfg, q, k, n_ctx: int, rep_idx, unit_repr, ws=None, strea
     _raise("infllm_build_units", lib().infllm_build_units(
         ctypes.byref(cfg), batch, _ptr(q), q_cap, k.data_ptr(), k.shape[2], n_ctx,
         _ptr(rep_idx), unit_repr.data_ptr(), wp, wb, _stream(stream, k)))
+
+
+def infllm_build_units_qsum(cfg, q, k, n_ctx: int, rep_idx, unit_repr, block_qsum, ws=None,
+                            stream=None) -> None:
+    """infllm_build_units that also writes the fp64 block query sums
+    [batch, H_kv, ceil(n_ctx/B), d]."""
+    dt = _dtype_of(cfg)
+    _check(q, "q", dt, 4)
+    _check(k, "k", dt, 4)
+    _check(unit_repr, "unit_repr", torch.float32, 4)
+    _check(block_qsum, "block_qsum", torch.float64, 4)
+    if cfg.rep_mode == INFLLM_REP_TOKENS:
+        _check(rep_idx, "rep_idx", torch.int32, 4)
+    batch = k.shape[0]
+    U = infllm_num_units(cfg, n_ctx)
+    nb = (n_ctx + cfg.block - 1) // cfg.block
+    if tuple(unit_repr.shape) != (batch, cfg.n_kv_heads, U, cfg.head_dim):
+        raise ValueError("unit_repr must be [batch, H_kv, U=%d, d]" % U)
+    if tuple(block_qsum.shape) != (batch, cfg.n_kv_heads, nb, cfg.head_dim):
+        raise ValueError("block_qsum must be [batch, H_kv, %d, d]" % nb)
+    wp, wb = _ws(ws)
+    _raise("infllm_build_units_qsum", lib().infllm_build_units_qsum(
+        ctypes.byref(cfg), batch, q.data_ptr(), q.shape[2], k.data_ptr(), k.shape[2], n_ctx,
+        _ptr(rep_idx), unit_repr.data_ptr(), block_qsum.data_ptr(), wp, wb, _stream(stream, k)))
+
+
+def infllm_score_units_qsum(cfg, block_qsum, q_pos: int, chunk_len: int, n_chunks: int, unit_repr,
+                            scores, stream=None) -> None:
+    """Chunk scores with the chunk query sums taken from block query sums."""
+    _check(block_qsum, "block_qsum", torch.float64, 4)
+    _check(unit_repr, "unit_repr", torch.float32, 4)
+    _check(scores, "scores", torch.float32, 4)
+    batch, U = block_qsum.shape[0], unit_repr.shape[2]
+    if tuple(scores.shape) != (batch, cfg.n_kv_heads, n_chunks, U):
+        raise ValueError("scores must be [batch, H_kv, n_chunks, U]")
+    _raise("infllm_score_units_qsum", lib().infllm_score_units_qsum(
+        ctypes.byref(cfg), batch, block_qsum.data_ptr(), block_qsum.shape[2], q_pos, chunk_len,
+        n_chunks, unit_repr.data_ptr(), U, scores.data_ptr(), _stream(stream, scores)))
 
 
 def infllm_build_units_range(cfg, q, k, n_ctx: int, u_begin: int, u_end: int, rep_idx, unit_repr,

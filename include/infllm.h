@@ -13,7 +13,9 @@
  * The four calls mirror that statement:
  *   infllm_build_units  -- representative-token selection per unit
  *                          (infllm_build_units_range: a range of units, as
- *                          they leave the window while streaming)
+ *                          they leave the window while streaming;
+ *                          infllm_build_units_qsum: also the block query
+ *                          sums, for infllm_score_units_qsum)
  *   infllm_score_units  -- chunk-query . unit-representation scores
  *                          (infllm_score_units_varlen: a position per sequence)
  *   infllm_topk_units   -- top-k_m units per (sequence, KV head, chunk)
@@ -92,7 +94,8 @@ typedef enum {
   INFLLM_CALL_TOPK = 2,
   INFLLM_CALL_ATTEND = 3,
   INFLLM_CALL_BUILD_RANGE = 4,
-  INFLLM_CALL_SELECT = 5
+  INFLLM_CALL_SELECT = 5,
+  INFLLM_CALL_BUILD_QSUM = 6
 } infllm_call;
 
 typedef struct {
@@ -150,6 +153,28 @@ INFLLM_API infllm_status infllm_build_units(const infllm_config *cfg, int32_t ba
                                  int64_t q_cap, const void *k, int64_t kv_cap, int64_t n_ctx,
                                  int32_t *rep_idx, float *unit_repr, void *workspace,
                                  size_t workspace_bytes, void *stream);
+
+/*
+ * infllm_build_units_qsum -- infllm_build_units that also writes the block
+ * query sums it forms on the way (TOKENS), or forms them (MEAN):
+ *     block_qsum[b][h][j] = sum over rows jB .. min((j+1)B, n_ctx) - 1 and
+ *                           the group's query heads of q       (fp64)
+ * for every block j < ceil(n_ctx / B), including those of the initial
+ * tokens.  A chunk made of whole blocks sums its blocks' entries to get
+ * its query sum (infllm_score_units_qsum), so the encoding pass reads the
+ * queries for its chunk scores once instead of twice.
+ *
+ *   q          required in both modes
+ *   block_qsum out [batch, H_kv, ceil(n_ctx/B), d] fp64, 16-byte aligned
+ *   workspace  >= infllm_workspace_size(cfg, INFLLM_CALL_BUILD_QSUM, batch,
+ *              n_ctx, 0, 0)
+ * Other arguments, outputs and errors as infllm_build_units.
+ */
+INFLLM_API infllm_status infllm_build_units_qsum(const infllm_config *cfg, int32_t batch,
+                                      const void *q, int64_t q_cap, const void *k,
+                                      int64_t kv_cap, int64_t n_ctx, int32_t *rep_idx,
+                                      float *unit_repr, double *block_qsum, void *workspace,
+                                      size_t workspace_bytes, void *stream);
 
 /*
  * infllm_build_units_range -- the same representations for units u_begin ..
@@ -227,6 +252,26 @@ INFLLM_API infllm_status infllm_score_units_varlen(const infllm_config *cfg, int
                                         const int64_t *pos, int32_t chunk_len, int32_t n_chunks,
                                         const float *unit_repr, int32_t n_units, float *scores,
                                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * infllm_score_units_qsum -- infllm_score_units for chunks made of whole
+ * blocks, with the chunk query sums taken from block query sums
+ * (infllm_build_units_qsum) instead of the queries: chunk c's sum is the
+ * sum of the entries of its chunk_len / B blocks, added in block order in
+ * fp64.  The same scores as infllm_score_units up to the fp64 rounding of
+ * the sums' order.
+ *
+ *   block_qsum  [batch, H_kv, n_blocks, d] fp64
+ *   q_pos       position of the first chunk's first query, a multiple of B
+ *   chunk_len   a multiple of B; (q_pos + n_chunks*chunk_len) / B <= n_blocks
+ *   unit_repr, n_units, scores   as infllm_score_units
+ * No workspace.
+ */
+INFLLM_API infllm_status infllm_score_units_qsum(const infllm_config *cfg, int32_t batch,
+                                      const double *block_qsum, int64_t n_blocks, int64_t q_pos,
+                                      int32_t chunk_len, int32_t n_chunks,
+                                      const float *unit_repr, int32_t n_units, float *scores,
+                                      void *stream);
 
 /*
  * infllm_select_units -- infllm_score_units followed by infllm_topk_units,

@@ -31,7 +31,7 @@ def cfg(**kw):
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 15
     assert set(names) == set(F.EXPORTED)
     L = F.lib()
     for n in names:
@@ -180,6 +180,30 @@ def test_select_validation_and_workspace():
     # long chunks: the scoring workspace, which already holds the counters
     assert F.infllm_workspace_size(c, F.INFLLM_CALL_SELECT, 2, 0, 512, 3) == \
         F.infllm_workspace_size(c, F.INFLLM_CALL_SCORE, 2, 0, 512, 3)
+
+
+def test_qsum_validation_and_workspace():
+    c = cfg()
+    L = F.lib()
+    r = ctypes.byref(c)
+    sc = lambda **kw: L.infllm_score_units_qsum(
+        r, 1, kw.get("bq", FAKE), kw.get("nb", 64), kw.get("q_pos", 0), kw.get("L", 512),
+        kw.get("nc", 4), FAKE, 60, FAKE, None)
+    assert sc(q_pos=100) == F.INFLLM_ERR_INVALID_ARG         # not a multiple of B
+    assert sc(L=500) == F.INFLLM_ERR_INVALID_ARG             # chunk not whole blocks
+    assert sc(nc=17) == F.INFLLM_ERR_INVALID_ARG             # past the last block
+    assert sc(bq=None) == F.INFLLM_ERR_INVALID_ARG
+    assert sc(nb=0) == F.INFLLM_ERR_INVALID_ARG
+    bd = lambda **kw: L.infllm_build_units_qsum(
+        r, 1, kw.get("q", FAKE), 8192, FAKE, 8192, 8192, FAKE, FAKE, kw.get("bq", FAKE),
+        FAKE, kw.get("wsb", 1 << 30), None)
+    assert bd(bq=None) == F.INFLLM_ERR_INVALID_ARG
+    assert bd(q=None) == F.INFLLM_ERR_INVALID_ARG
+    need = F.infllm_workspace_size(c, F.INFLLM_CALL_BUILD_QSUM, 1, 8192)
+    assert need > 0
+    assert bd(wsb=need - 1) == F.INFLLM_ERR_WORKSPACE
+    cm = cfg(rep_mode=F.INFLLM_REP_MEAN)
+    assert F.infllm_workspace_size(cm, F.INFLLM_CALL_BUILD_QSUM, 1, 8192) == 0
 
 
 def test_score_topk_attend_validation():

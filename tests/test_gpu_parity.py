@@ -632,3 +632,49 @@ def test_select_units_fused(orc, U, k_m, L, nc, dup, varlen):
     for idx in np.ndindex(sg.shape[:3]):
         e = int(np.isfinite(sg[idx]).sum())
         assert selg[idx].tolist() == orc.topk(sg[idx], e, k_m).tolist()
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_build_qsum_and_block_scores(orc, data, name):
+    """infllm_build_units_qsum: the representations of infllm_build_units (up
+    to near ties of the fp64 key scores) and block query sums equal to fp64
+    sums of the queries; infllm_score_units_qsum: the scores of
+    infllm_score_units for chunks of whole blocks, at an aligned offset."""
+    w, inp, dev = data(name)
+    cfg = cfg_of(w)
+    b, Hkv, G, B, d = w.batch, w.n_kv_heads, w.group, w.block, w.head_dim
+    U = F.infllm_num_units(cfg, w.n_ctx)
+    nb = (w.n_ctx + B - 1) // B
+    repr_ = torch.empty((b, Hkv, U, d), dtype=torch.float32, device="cuda")
+    rep = (torch.empty((b, Hkv, U, w.rep_k), dtype=torch.int32, device="cuda")
+           if w.rep_mode == "tokens" else None)
+    bq = torch.empty((b, Hkv, nb, d), dtype=torch.float64, device="cuda")
+    ws = F.workspace(cfg, F.INFLLM_CALL_BUILD_QSUM, b, w.n_ctx)
+    F.infllm_build_units_qsum(cfg, dev["q"], dev["k"], w.n_ctx, rep, repr_, bq, ws)
+    torch.cuda.synchronize()
+    # block sums against fp64 sums of the queries
+    q64 = inp["q"][:, :, :w.n_ctx].double().reshape(b, Hkv, G, w.n_ctx, d).sum(2)
+    want = torch.zeros((b, Hkv, nb, d), dtype=torch.float64)
+    for j in range(nb):
+        want[:, :, j] = q64[:, :, j * B:min((j + 1) * B, w.n_ctx)].sum(2)
+    np.testing.assert_allclose(bq.cpu().numpy(), want.numpy(), rtol=1e-12, atol=1e-12)
+    # representations against the oracle
+    rep_o, repr_o, ks_o = oracle_build(orc, w, inp)
+    rg = repr_.cpu().numpy()
+    if w.rep_mode == "mean":
+        np.testing.assert_array_equal(rg, repr_o.astype(np.float32))
+    else:
+        ex = check_rep_idx(rep.cpu().numpy(), rep_o, ks_o, B, w.n_init)
+        assert len(ex) <= max(2, rep_o.shape[2] // 50)
+    # chunk scores from the block sums against the ones from the queries
+    L = 2 * B
+    q_pos = B
+    nc = (w.n_ctx - q_pos) // L
+    s_blk = torch.empty((b, Hkv, nc, U), dtype=torch.float32, device="cuda")
+    F.infllm_score_units_qsum(cfg, bq, q_pos, L, nc, repr_, s_blk)
+    s_q = gpu_score(cfg, dev["q"], q_pos, q_pos, L, nc, repr_)
+    torch.cuda.synchronize()
+    a, c = s_blk.cpu().numpy(), s_q.cpu().numpy()
+    assert (np.isfinite(a) == np.isfinite(c)).all()
+    fin = np.isfinite(c)
+    np.testing.assert_allclose(a[fin], c[fin], rtol=1e-6, atol=1e-6 * np.abs(c[fin]).max(initial=1.0))
