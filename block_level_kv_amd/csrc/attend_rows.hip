@@ -19,10 +19,12 @@
 // while the current one is reduced.  Splits publish partial (max, sum, unnormalised output)
 // rows; the last one to arrive merges them in split order (see common.h for
 // the publication protocol), so one launch produces the output.
+#include <stdio.h>
 #include <stdlib.h>
 
 #include "common.h"
 #include "kernels.h"
+#include "score_units.h"
 
 namespace infllm {
 
@@ -74,11 +76,26 @@ template <> struct RowRaw<float, 4> {
 constexpr int kKeysPerIter = 4;  // keys per lane between softmax rescales
 constexpr int kMaxSplits = 64;
 
+// The work of one workgroup: split `split` of the n_splits splits of one
+// (position, KV head, sequence) row.  It attends share l_part of the local
+// keys cut into l_parts equal shares and share u_part of the units' keys
+// cut into u_parts (0 parts: none of them).  `ready` (fused decode step):
+// the row's selection is written in this launch -- wait until ready[row]
+// is set and read it with device-scope loads.
+struct RowsJob {
+  int split, n_splits, pos, h, bi;
+  int l_part, l_parts, u_part, u_parts;
+  const int* ready;
+};
+
+// bounded wait for a selection made in the same launch (polls of a few
+// hundred ns each; the selection takes microseconds)
+constexpr int kSpinLimit = 1 << 18;
+
 template <typename T, int D, int G>
-__global__ __launch_bounds__(kRowsThreads) void k_attend_rows(AttendArgs a) {
+__device__ __forceinline__ void attend_rows_body(const AttendArgs& a, const RowsJob& job) {
   constexpr int CPT = D / 16;
-  const int split = blockIdx.x, pos = blockIdx.y;
-  const int h = blockIdx.z % a.Hkv, bi = blockIdx.z / a.Hkv;
+  const int split = job.split, pos = job.pos, h = job.h, bi = job.bi;
   const int tid = threadIdx.x, lane = tid % 64, seg = tid % 16, kl = tid / 16;
   const int ch = pos / a.L;
   const int64_t base = seq_base(a.pos, a.q_pos, bi);
@@ -112,20 +129,39 @@ __global__ __launch_bounds__(kRowsThreads) void k_attend_rows(AttendArgs a) {
   // unit keys [u_begin, u_stop) of the units' numbering (sel order, each
   // unit at most B keys).  Its first local keys are requested before the
   // selection is read and the unit table formed.
-  const int S = gridDim.x;
   const int64_t unit_cap = t - a.W + 1;
   const int64_t init_len = a.n_init < t + 1 ? a.n_init : t + 1;
   const int64_t win_lo = a.n_init > unit_cap ? a.n_init : unit_cap;
   const int64_t win_len = t + 1 - win_lo > 0 ? t + 1 - win_lo : 0;
   const int64_t n_local = init_len + win_len;
-  const int64_t pl = (n_local + S - 1) / S;
-  const int64_t l_begin = (int64_t)split * pl < n_local ? (int64_t)split * pl : n_local;
+  const int64_t pl = job.l_parts > 0 ? (n_local + job.l_parts - 1) / job.l_parts : 0;
+  const int64_t l_begin = (int64_t)job.l_part * pl < n_local ? (int64_t)job.l_part * pl : n_local;
   const int64_t l_stop = l_begin + pl < n_local ? l_begin + pl : n_local;
   const int64_t nl = l_stop - l_begin;
-  const int64_t pu = ((int64_t)a.k_m * a.B + S - 1) / S;
-  const int64_t u_begin = (int64_t)split * pu;
+  const int64_t pu = job.u_parts > 0 ? ((int64_t)a.k_m * a.B + job.u_parts - 1) / job.u_parts : 0;
+  const int64_t u_begin = (int64_t)job.u_part * pu;
+  const int64_t row_id = ((int64_t)bi * a.Hkv + h) * a.n_pos + pos;
+  __shared__ int ready_sh;
+  bool stale = false;                                // the selection never arrived
+  if (job.ready && job.u_parts > 0) {
+    if (tid == 0) {
+      int ok = 0;
+      for (int it = 0; it < kSpinLimit && !ok; ++it) {
+        ok = __hip_atomic_load(job.ready + row_id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (!ok) __builtin_amdgcn_s_sleep(2);
+      }
+      ready_sh = ok;
+    }
+    __syncthreads();
+    stale = !ready_sh;
+  }
   int32_t my_unit = -1;                              // sel entry `tid`, requested now
-  if (tid < a.k_m) my_unit = a.sel[(((int64_t)bi * a.Hkv + h) * a.n_chunks + ch) * a.k_m + tid];
+  if (tid < a.k_m && job.u_parts > 0 && !stale) {
+    const int32_t* sp = a.sel + (((int64_t)bi * a.Hkv + h) * a.n_chunks + ch) * a.k_m + tid;
+    my_unit = job.ready ? __hip_atomic_load(const_cast<int32_t*>(sp), __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT)
+                        : *sp;
+  }
 
   const T* kb = (const T*)a.k + ((int64_t)bi * a.Hkv + h) * a.kv_cap * D + seg * CPT;
   const T* vb = (const T*)a.v + ((int64_t)bi * a.Hkv + h) * a.kv_cap * D + seg * CPT;
@@ -301,8 +337,13 @@ __global__ __launch_bounds__(kRowsThreads) void k_attend_rows(AttendArgs a) {
     }
   }
 
+  if (stale) {
+#pragma unroll
+    for (int i = 0; i < kOut; ++i) Mv[i] = Lv[i] = Ov[i] = __builtin_nanf("");
+  }
+
   // ---------------------------------------------------------- split-K merge
-  const int splits = gridDim.x;
+  const int splits = job.n_splits;
   const int64_t qh0 = (int64_t)bi * a.Hq + (int64_t)h * G;
   if (splits > 1) {
 #pragma unroll
@@ -320,7 +361,7 @@ __global__ __launch_bounds__(kRowsThreads) void k_attend_rows(AttendArgs a) {
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     if (tid == 0) {
-      int* ctr = a.ws_count + ((int64_t)bi * a.Hkv + h) * a.n_pos + pos;
+      int* ctr = a.ws_count + row_id;
       const int done = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       last_sh = done == splits - 1;
       if (last_sh) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -433,6 +474,14 @@ __global__ __launch_bounds__(kRowsThreads) void k_attend_rows(AttendArgs a) {
   }
 }
 
+template <typename T, int D, int G>
+__global__ __launch_bounds__(kRowsThreads) void k_attend_rows(AttendArgs a) {
+  const int s = blockIdx.x, n = gridDim.x;
+  const RowsJob job{s, n, (int)blockIdx.y, (int)(blockIdx.z % a.Hkv), (int)(blockIdx.z / a.Hkv),
+                    s, n, s, n, nullptr};
+  attend_rows_body<T, D, G>(a, job);
+}
+
 int rows_num_splits(const AttendArgs& a) {
   // enough workgroups to cover the chip several times, >= ~256 keys each
   const int64_t max_keys = (int64_t)a.n_init + (int64_t)a.k_m * a.B + a.W;
@@ -475,6 +524,141 @@ hipError_t launch_attend_rows(const AttendArgs& a, int splits, hipStream_t st) {
                       : launch_rows_td<bf16_t, 64>(a, splits, st);
   return a.d == 128 ? launch_rows_td<float, 128>(a, splits, st)
                     : launch_rows_td<float, 64>(a, splits, st);
+}
+
+// ------------------------------------------------------------ fused decode step
+// Selection and attention of decode positions in one launch.  Workgroups
+// take tickets in the order they start: the first rows * n_slices score a
+// slice of units each (the last slice of a row to arrive selects the row,
+// publishes the selection with device-scope stores and sets the row's ready
+// flag), the next rows * s_local attend a share of the local keys, which
+// need no selection, and the last rows * s_unit attend a share of the
+// selected units' keys once their row is ready.  A workgroup only waits on
+// workgroups with smaller tickets, which have started and never wait, so
+// the waits end; the wait is bounded all the same (a stale selection gives
+// NaN outputs).  The last workgroup to finish clears the tickets and flags.
+template <typename T, int D, int G, int SEL>
+__global__ __launch_bounds__(kRowsThreads) void k_select_attend(ScoreArgs s, AttendArgs a,
+                                                                StepPlan p, int* sync) {
+  static_assert(kRowsThreads == kScoreThreads, "one workgroup size for both roles");
+  __shared__ int tk_sh, last_sh;
+  __shared__ int32_t sel_sm[kMaxTopK];
+  const int tid = threadIdx.x;
+  int* ticket = sync;       // [0] tickets taken, [1] workgroups done
+  int* ready = sync + 2;    // [rows] selection published
+  if (tid == 0) tk_sh = __hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const int tk = tk_sh;
+  const int rows = a.batch * a.Hkv * a.n_pos;
+  const int n_sel = rows * p.n_slices;
+  if (tk < n_sel) {
+    // row = (sequence * H_kv + KV head) * positions + position; one chunk per position
+    const int row = tk / p.n_slices, slice = tk % p.n_slices;
+    const int pos = row % a.n_pos, h = row / a.n_pos % a.Hkv, bi = row / a.n_pos / a.Hkv;
+    if (score_slice<T, G, D, SEL>(slice, p.n_slices, pos, h, bi, (const T*)s.q, s.q_cap, s.q_off,
+                                  s.q_pos, s.pos, 1, s.Hq, s.Hkv, s.B, s.n_init, s.W, s.repr, s.U,
+                                  s.scores, s.n_chunks, nullptr, 0, 0, 0, (int*)s.ws, s.k_m,
+                                  sel_sm)) {
+      __syncthreads();
+      int32_t* dst = s.sel + (int64_t)row * s.k_m;
+      for (int m = tid; m < s.k_m; m += kRowsThreads)
+        __hip_atomic_store(dst + m, sel_sm[m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __syncthreads();
+      if (tid == 0) __hip_atomic_store(ready + row, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  } else {
+    int x = tk - n_sel;
+    const int n_splits = p.s_local + p.s_unit;
+    const bool local = x < rows * p.s_local;
+    if (!local) x -= rows * p.s_local;
+    const int per = local ? p.s_local : p.s_unit;
+    const int row = x / per, part = x % per;
+    const int pos = row % a.n_pos, h = row / a.n_pos % a.Hkv, bi = row / a.n_pos / a.Hkv;
+    const RowsJob job = local ? RowsJob{part, n_splits, pos, h, bi, part, p.s_local, 0, 0, nullptr}
+                              : RowsJob{p.s_local + part, n_splits, pos, h, bi, 0, 0, part,
+                                        p.s_unit, ready};
+    attend_rows_body<T, D, G>(a, job);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const int done = __hip_atomic_fetch_add(ticket + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last_sh = done == (int)gridDim.x - 1;
+  }
+  __syncthreads();
+  if (last_sh) {   // every other workgroup has finished: ready for the next call
+    for (int r = tid; r < rows; r += kRowsThreads)
+      __hip_atomic_store(ready + r, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) {
+      __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(ticket + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+bool select_attend_plan(const ScoreArgs& s, const AttendArgs& a, StepPlan* p) {
+  const int64_t rows = (int64_t)a.batch * a.Hkv * a.n_pos;
+  const int n_slices = (s.U + kUnitsPerWG - 1) / kUnitsPerWG;
+  if (!a.bf16 || a.L != 1 || s.U < 1 || a.k_m < 1 || a.k_m > kMaxTopK || n_slices > kMaxSelSlices)
+    return false;
+  const int G = a.Hq / a.Hkv;
+  if (G * 1 > kDirectRows || (G != 1 && G != 2 && G != 4 && G != 8)) return false;
+  // about `target` attention workgroups, >= ~256 keys each, half on each key set
+  int64_t target = 512;
+  int want_l = 0, want_u = 0;
+  if (const char* e = getenv("INFLLM_STEP_SPLITS")) {   // tuning override "local,unit"
+    if (sscanf(e, "%d,%d", &want_l, &want_u) != 2) want_l = want_u = 0;
+  }
+  const int64_t each = (target / 2 + rows - 1) / rows;
+  int64_t sl = want_l > 0 ? want_l : each, su = want_u > 0 ? want_u : each;
+  const int64_t cap_l = ((int64_t)a.n_init + a.W + 255) / 256;
+  const int64_t cap_u = ((int64_t)a.k_m * a.B + 255) / 256;
+  sl = sl < cap_l ? sl : cap_l;
+  su = su < cap_u ? su : cap_u;
+  sl = sl < 1 ? 1 : sl;
+  su = su < 1 ? 1 : su;
+  if (sl + su > kMaxSplits) return false;
+  if (rows * (n_slices + sl + su) > (int64_t)1 << 30) return false;
+  p->n_slices = n_slices;
+  p->s_local = (int)sl;
+  p->s_unit = (int)su;
+  return true;
+}
+
+int64_t select_attend_sync_ints(const AttendArgs& a) {
+  return 2 + (int64_t)a.batch * a.Hkv * a.n_pos;
+}
+
+template <int D, int G>
+static hipError_t launch_step_dg(const ScoreArgs& s, const AttendArgs& a, const StepPlan& p,
+                                 int* sync, hipStream_t st) {
+  const int64_t rows = (int64_t)a.batch * a.Hkv * a.n_pos;
+  const dim3 grid((unsigned)(rows * (p.n_slices + p.s_local + p.s_unit)));
+  // keys per lane of the 4-wave search: ceil(U / 256) <= 8
+  static_assert(kMaxSelSlices * kUnitsPerWG <= 8 * kScoreThreads, "keys per lane");
+  if (s.U <= 4 * kScoreThreads)
+    k_select_attend<bf16_t, D, G, 4><<<grid, kRowsThreads, 0, st>>>(s, a, p, sync);
+  else
+    k_select_attend<bf16_t, D, G, 8><<<grid, kRowsThreads, 0, st>>>(s, a, p, sync);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_step_d(const ScoreArgs& s, const AttendArgs& a, const StepPlan& p,
+                                int* sync, hipStream_t st) {
+  switch (a.Hq / a.Hkv) {
+    case 1: return launch_step_dg<D, 1>(s, a, p, sync, st);
+    case 2: return launch_step_dg<D, 2>(s, a, p, sync, st);
+    case 4: return launch_step_dg<D, 4>(s, a, p, sync, st);
+    case 8: return launch_step_dg<D, 8>(s, a, p, sync, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_select_attend(const ScoreArgs& s, const AttendArgs& a, const StepPlan& p,
+                                int* sync, hipStream_t st) {
+  if (a.n_pos <= 0) return hipSuccess;
+  return a.d == 128 ? launch_step_d<128>(s, a, p, sync, st) : launch_step_d<64>(s, a, p, sync, st);
 }
 
 }  // namespace infllm

@@ -123,6 +123,43 @@ AttendWs attend_ws_layout(const AttendArgs& a) {
 
 size_t attend_ws_bytes(const AttendArgs& a) { return attend_ws_layout(a).total(); }
 
+// Decode step workspace.  Fused: [tickets and ready flags][selection
+// counters][attention counters, partials of s_local + s_unit splits].
+// Separate calls: [selection workspace][attention workspace].  Sized for
+// the larger of the two.
+struct StepWs {
+  bool fused;
+  StepPlan plan;
+  size_t sync_bytes, sel_bytes;   // fused: sync ints, selection counters
+  AttendWs att;                   // fused attention part
+  size_t sep_sel_bytes;           // separate calls: selection workspace
+  size_t total;
+};
+
+StepWs step_ws_layout(const infllm_config* c, int32_t batch, int32_t n_pos, int32_t n_units) {
+  StepWs w{};
+  ScoreArgs sa = score_args(c, batch, 1, n_pos);
+  sa.U = n_units;
+  sa.k_m = c->top_k;
+  const AttendArgs aa = attend_args(c, batch, 1, n_pos);
+  w.sep_sel_bytes = round256(select_workspace_bytes(sa));
+  const size_t sep = w.sep_sel_bytes + attend_ws_bytes(aa);
+  w.fused = select_attend_plan(sa, aa, &w.plan);
+  size_t fused = 0;
+  if (w.fused) {
+    const size_t rows = (size_t)batch * c->n_kv_heads * n_pos;
+    w.sync_bytes = round256((size_t)select_attend_sync_ints(aa) * sizeof(int));
+    w.sel_bytes = round256(rows * sizeof(int));
+    const size_t prow = (size_t)(w.plan.s_local + w.plan.s_unit) * batch * c->n_q_heads * n_pos;
+    w.att.count_bytes = round256(rows * sizeof(int));
+    w.att.o_bytes = round256(prow * c->head_dim * sizeof(float));
+    w.att.ml_bytes = prow * 2 * sizeof(float);
+    fused = w.sync_bytes + w.sel_bytes + w.att.total();
+  }
+  w.total = sep > fused ? sep : fused;
+  return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -170,6 +207,9 @@ size_t infllm_workspace_size(const infllm_config* cfg, int32_t call, int32_t bat
     case INFLLM_CALL_ATTEND:
       if (chunk_len < 1 || n_chunks < 1) return 0;
       return attend_ws_bytes(attend_args(cfg, batch, chunk_len, n_chunks));
+    case INFLLM_CALL_SELECT_ATTEND:   // n = units, one query per chunk
+      if (chunk_len != 1 || n_chunks < 1 || n < 0 || n > INT32_MAX) return 0;
+      return step_ws_layout(cfg, batch, n_chunks, (int32_t)n).total;
     default:
       return 0;
   }
@@ -273,7 +313,7 @@ static infllm_status score_impl(const infllm_config* cfg, int32_t batch, const v
                                 int64_t q_cap, int64_t q_off, int64_t q_pos, const int64_t* pos,
                                 int32_t chunk_len, int32_t n_chunks, const float* unit_repr,
                                 int32_t n_units, float* scores, int32_t* sel, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+                                size_t workspace_bytes, void* stream, bool dry = false) {
   infllm_status st = check_config(cfg);
   if (st != INFLLM_OK) return st;
   if (batch < 1 || chunk_len < 1 || n_chunks < 1 || n_units < 0 || q_off < 0 || q_pos < 0)
@@ -290,6 +330,7 @@ static infllm_status score_impl(const infllm_config* cfg, int32_t batch, const v
     a.k_m = cfg->top_k;
     a.sel = sel;
   }
+  if (dry) return INFLLM_OK;   // arguments only
   const size_t need = a.sel ? select_workspace_bytes(a) : score_workspace_bytes(a);
   if ((n_units > 0 || a.sel) && need > 0 &&
       (!workspace || workspace_bytes < need || !aligned16(workspace)))
@@ -394,7 +435,7 @@ static infllm_status attend_impl(const infllm_config* cfg, int32_t batch, const 
                                  int32_t chunk_len, int32_t n_chunks, const void* k,
                                  const void* v, int64_t kv_cap, const int32_t* sel, void* out,
                                  float* lse, int64_t out_cap, int64_t out_off, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
+                                 size_t workspace_bytes, void* stream, bool dry = false) {
   infllm_status st = check_config(cfg);
   if (st != INFLLM_OK) return st;
   if (batch < 1 || chunk_len < 1 || n_chunks < 1 || q_off < 0 || q_pos < 0 || out_off < 0)
@@ -412,6 +453,7 @@ static infllm_status attend_impl(const infllm_config* cfg, int32_t batch, const 
   int splits;
   attend_plan(a, &mfma, &splits);
   if (!mfma && n_pos > 65535) return INFLLM_ERR_UNSUPPORTED;   // one grid row per position
+  if (dry) return INFLLM_OK;   // arguments only
   const size_t need = attend_ws_bytes(a);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return INFLLM_ERR_WORKSPACE;
@@ -459,6 +501,68 @@ infllm_status infllm_attend_varlen(const infllm_config* cfg, int32_t batch, cons
   // q_pos = 0 here only checks that kv_cap can hold one sequence's positions
   return attend_impl(cfg, batch, q, q_cap, q_off, 0, pos, chunk_len, n_chunks, k, v, kv_cap, sel,
                      out, lse, out_cap, out_off, workspace, workspace_bytes, stream);
+}
+
+infllm_status infllm_select_attend(const infllm_config* cfg, int32_t batch, const void* q,
+                                   int64_t q_cap, int64_t q_off, int64_t q_pos,
+                                   const int64_t* pos, int32_t n_pos, const float* unit_repr,
+                                   int32_t n_units, const void* k, const void* v, int64_t kv_cap,
+                                   float* scores, int32_t* sel, void* out, float* lse,
+                                   int64_t out_cap, int64_t out_off, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  if (cfg && cfg->top_k > 0 && !sel) return INFLLM_ERR_INVALID_ARG;
+  if (pos && (uintptr_t)pos % 8 != 0) return INFLLM_ERR_INVALID_ARG;
+  const int64_t qp = pos ? 0 : q_pos;
+  // both halves' argument checks, before anything is enqueued
+  infllm_status st = score_impl(cfg, batch, q, q_cap, q_off, qp, pos, 1, n_pos, unit_repr, n_units,
+                                scores, sel, nullptr, 0, stream, true);
+  if (st != INFLLM_OK) return st;
+  st = attend_impl(cfg, batch, q, q_cap, q_off, qp, pos, 1, n_pos, k, v, kv_cap, sel, out, lse,
+                   out_cap, out_off, nullptr, 0, stream, true);
+  if (st != INFLLM_OK) return st;
+  const StepWs w = step_ws_layout(cfg, batch, n_pos, n_units);
+  if (w.total > 0 && (!workspace || workspace_bytes < w.total || !aligned16(workspace)))
+    return INFLLM_ERR_WORKSPACE;
+  char* ws = (char*)workspace;
+  if (!w.fused) {
+    st = score_impl(cfg, batch, q, q_cap, q_off, qp, pos, 1, n_pos, unit_repr, n_units, scores,
+                    sel, ws, w.sep_sel_bytes, stream);
+    if (st != INFLLM_OK) return st;
+    return attend_impl(cfg, batch, q, q_cap, q_off, qp, pos, 1, n_pos, k, v, kv_cap, sel, out,
+                       lse, out_cap, out_off, ws + w.sep_sel_bytes,
+                       workspace_bytes - w.sep_sel_bytes, stream);
+  }
+  ScoreArgs sa = score_args(cfg, batch, 1, n_pos);
+  sa.U = n_units;
+  sa.k_m = cfg->top_k;
+  sa.sel = sel;
+  sa.q = q;
+  sa.q_cap = q_cap;
+  sa.q_off = q_off;
+  sa.q_pos = qp;
+  sa.pos = pos;
+  sa.repr = unit_repr;
+  sa.scores = scores;
+  sa.ws = ws + w.sync_bytes;   // selection counters
+  AttendArgs aa = attend_args(cfg, batch, 1, n_pos);
+  aa.q = q;
+  aa.q_cap = q_cap;
+  aa.q_off = q_off;
+  aa.q_pos = qp;
+  aa.pos = pos;
+  aa.k = k;
+  aa.v = v;
+  aa.kv_cap = kv_cap;
+  aa.sel = sel;
+  aa.out = out;
+  aa.lse = lse;
+  aa.out_cap = out_cap;
+  aa.out_off = out_off;
+  char* att = ws + w.sync_bytes + w.sel_bytes;
+  aa.ws_count = (int*)att;
+  aa.ws_o = (float*)(att + w.att.count_bytes);
+  aa.ws_ml = (float*)(att + w.att.count_bytes + w.att.o_bytes);
+  return launched(launch_select_attend(sa, aa, w.plan, (int*)ws, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -76,6 +76,17 @@ int rows_num_splits(const AttendArgs& a);
 hipError_t launch_attend_rows(const AttendArgs& a, int splits, hipStream_t st);
 int64_t rows_num_counters(const AttendArgs& a);
 
+// fused decode step (bf16): unit scores, selection and attention of single
+// query positions in one launch; false when the shapes need the separate calls
+struct StepPlan {
+  int n_slices;         // scoring slices per row
+  int s_local, s_unit;  // attention splits per row over the local and the unit keys
+};
+bool select_attend_plan(const ScoreArgs& s, const AttendArgs& a, StepPlan* p);
+int64_t select_attend_sync_ints(const AttendArgs& a);   // tickets and ready flags
+hipError_t launch_select_attend(const ScoreArgs& s, const AttendArgs& a, const StepPlan& p,
+                                int* sync, hipStream_t st);
+
 // bf16 MFMA attention tiles for query chunks (head_dim 128)
 bool prefill_supported(const AttendArgs& a);
 int prefill_num_splits(const AttendArgs& a);

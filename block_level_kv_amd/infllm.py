@@ -21,13 +21,14 @@ INFLLM_F32, INFLLM_BF16 = 0, 1
 INFLLM_REP_TOKENS, INFLLM_REP_MEAN = 0, 1
 INFLLM_CALL_BUILD, INFLLM_CALL_SCORE, INFLLM_CALL_TOPK, INFLLM_CALL_ATTEND = 0, 1, 2, 3
 INFLLM_CALL_BUILD_RANGE, INFLLM_CALL_SELECT, INFLLM_CALL_BUILD_QSUM = 4, 5, 6
+INFLLM_CALL_SELECT_ATTEND = 7
 
 EXPORTED = ("infllm_num_units", "infllm_num_eligible", "infllm_workspace_size",
             "infllm_build_units", "infllm_build_units_range", "infllm_build_units_qsum",
             "infllm_score_units", "infllm_score_units_qsum",
             "infllm_score_units_varlen", "infllm_select_units", "infllm_topk_units",
-            "infllm_attend",
-            "infllm_attend_varlen", "infllm_status_string", "infllm_abi_version")
+            "infllm_attend", "infllm_attend_varlen", "infllm_select_attend",
+            "infllm_status_string", "infllm_abi_version")
 
 
 class infllm_config(ctypes.Structure):
@@ -85,6 +86,10 @@ def lib() -> ctypes.CDLL:
         L.infllm_select_units.restype = _i32
         L.infllm_select_units.argtypes = [_cfgp, _i32, _vp, _i64, _i64, _i64, _vp, _i32, _i32, _vp,
                                           _i32, _vp, _vp, _vp, _sz, _vp]
+        L.infllm_select_attend.restype = _i32
+        L.infllm_select_attend.argtypes = [_cfgp, _i32, _vp, _i64, _i64, _i64, _vp, _i32, _vp, _i32,
+                                           _vp, _vp, _i64, _vp, _vp, _vp, _vp, _i64, _i64, _vp,
+                                           _sz, _vp]
         L.infllm_topk_units.restype = _i32
         L.infllm_topk_units.argtypes = [_cfgp, _i32, _i32, _vp, _i32, _vp, _vp, _sz, _vp]
         L.infllm_attend.restype = _i32
@@ -368,3 +373,35 @@ def infllm_attend_varlen(cfg, q, q_off: int, pos, chunk_len: int, n_chunks: int,
         ctypes.byref(cfg), q.shape[0], q.data_ptr(), q.shape[2], q_off, pos.data_ptr(), chunk_len,
         n_chunks, k.data_ptr(), v.data_ptr(), k.shape[2], _ptr(sel), out.data_ptr(), _ptr(lse),
         out.shape[2], out_off, wp, wb, _stream(stream, q)))
+
+
+def infllm_select_attend(cfg, q, q_off: int, q_pos: int, n_pos: int, unit_repr, k, v, scores, sel,
+                         out, lse=None, out_off: int = 0, pos=None, ws=None, stream=None) -> None:
+    """One decode step for n_pos single-query positions: scores, top-k and
+    attention (one launch where the shapes allow); pos (device int64
+    [batch]) replaces q_pos when given."""
+    dt = _dtype_of(cfg)
+    _check(q, "q", dt, 4)
+    _check(k, "k", dt, 4)
+    _check(v, "v", dt, 4)
+    _check(out, "out", dt, 4)
+    _check(unit_repr, "unit_repr", torch.float32, 4)
+    _check(scores, "scores", torch.float32, 4)
+    _check(sel, "sel", torch.int32, 4)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, 3)
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    batch, U = q.shape[0], unit_repr.shape[2]
+    if pos is not None:
+        _check_pos(pos, batch)
+    if tuple(scores.shape) != (batch, cfg.n_kv_heads, n_pos, U):
+        raise ValueError("scores must be [batch, H_kv, n_pos, U]")
+    if tuple(sel.shape) != (batch, cfg.n_kv_heads, n_pos, cfg.top_k):
+        raise ValueError("sel must be [batch, H_kv, n_pos, k_m]")
+    wp, wb = _ws(ws)
+    _raise("infllm_select_attend", lib().infllm_select_attend(
+        ctypes.byref(cfg), batch, q.data_ptr(), q.shape[2], q_off, q_pos, _ptr(pos), n_pos,
+        unit_repr.data_ptr(), U, k.data_ptr(), v.data_ptr(), k.shape[2], scores.data_ptr(),
+        sel.data_ptr(), out.data_ptr(), _ptr(lse), out.shape[2], out_off, wp, wb,
+        _stream(stream, q)))

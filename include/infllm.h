@@ -95,7 +95,8 @@ typedef enum {
   INFLLM_CALL_ATTEND = 3,
   INFLLM_CALL_BUILD_RANGE = 4,
   INFLLM_CALL_SELECT = 5,
-  INFLLM_CALL_BUILD_QSUM = 6
+  INFLLM_CALL_BUILD_QSUM = 6,
+  INFLLM_CALL_SELECT_ATTEND = 7
 } infllm_call;
 
 typedef struct {
@@ -372,6 +373,42 @@ INFLLM_API infllm_status infllm_attend_varlen(const infllm_config *cfg, int32_t 
                                    const int32_t *sel, void *out, float *lse, int64_t out_cap,
                                    int64_t out_off, void *workspace, size_t workspace_bytes,
                                    void *stream);
+
+/*
+ * infllm_select_attend -- one decode step: for each of n_pos consecutive
+ * query positions (each a chunk of one query), score every unit, keep the
+ * top k_m per KV head and attend over the working context (the lookup and
+ * the attention of InfLLM Guide, "Core Innovation 2", items 2-3; SUMMARY,
+ * Approach: each step looks up the relevant units and attends them with
+ * the local window).  The result is that of infllm_select_units (chunk_len
+ * 1, n_chunks n_pos) followed by infllm_attend or infllm_attend_varlen on
+ * its selection: scores and sel are identical; out and lse equal up to fp32
+ * rounding (the attention is split over workgroups differently).
+ *
+ * Where the shapes allow (bf16, at most 2,048 units, k_m >= 1) it is one
+ * launch: the local keys (initial tokens and window) are attended while
+ * the units are scored and selected, and the units' keys as soon as their
+ * row's selection is published.  Otherwise it runs the two calls.
+ *
+ *   q, q_cap, q_off, q_pos, pos, unit_repr, n_units
+ *              as infllm_select_units (pos: as infllm_attend_varlen)
+ *   k, v, kv_cap, out, lse, out_cap, out_off
+ *              as infllm_attend, for n_pos positions
+ *   scores     out [batch, H_kv, n_pos, n_units] fp32
+ *   sel        out [batch, H_kv, n_pos, k_m] int32
+ *   workspace  >= infllm_workspace_size(cfg, INFLLM_CALL_SELECT_ATTEND,
+ *              batch, n_units, 1, n_pos).  Zero-filled before its first
+ *              use; every call leaves it ready for the next; calls that
+ *              share a workspace must not overlap in time.
+ * Errors: as the two calls, checked before anything is enqueued.
+ */
+INFLLM_API infllm_status infllm_select_attend(const infllm_config *cfg, int32_t batch,
+                                   const void *q, int64_t q_cap, int64_t q_off, int64_t q_pos,
+                                   const int64_t *pos, int32_t n_pos, const float *unit_repr,
+                                   int32_t n_units, const void *k, const void *v,
+                                   int64_t kv_cap, float *scores, int32_t *sel, void *out,
+                                   float *lse, int64_t out_cap, int64_t out_off,
+                                   void *workspace, size_t workspace_bytes, void *stream);
 
 INFLLM_API const char *infllm_status_string(int32_t status);
 INFLLM_API int32_t infllm_abi_version(void);

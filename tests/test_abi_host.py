@@ -31,7 +31,7 @@ def cfg(**kw):
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     assert set(names) == set(F.EXPORTED)
     L = F.lib()
     for n in names:
@@ -180,6 +180,37 @@ def test_select_validation_and_workspace():
     # long chunks: the scoring workspace, which already holds the counters
     assert F.infllm_workspace_size(c, F.INFLLM_CALL_SELECT, 2, 0, 512, 3) == \
         F.infllm_workspace_size(c, F.INFLLM_CALL_SCORE, 2, 0, 512, 3)
+
+
+def test_select_attend_validation_and_workspace():
+    c = cfg(top_k=32)
+    L = F.lib()
+    r = ctypes.byref(c)
+    # batch 4 at 128K context: 1,023 units, one position
+    call = lambda **kw: L.infllm_select_attend(
+        r, 4, FAKE, 300, 0, kw.get("q_pos", 131072), kw.get("pos", None), kw.get("n_pos", 1),
+        FAKE, kw.get("U", 1023), FAKE, FAKE, kw.get("kv_cap", 131072 + 256), FAKE,
+        kw.get("sel", FAKE), FAKE, None, 300, 0, kw.get("ws", FAKE), kw.get("wsb", 1 << 30), None)
+    assert call(sel=None) == F.INFLLM_ERR_INVALID_ARG
+    assert call(sel=MISALIGNED) == F.INFLLM_ERR_INVALID_ARG
+    assert call(pos=FAKE + 4) == F.INFLLM_ERR_INVALID_ARG
+    assert call(n_pos=0) == F.INFLLM_ERR_INVALID_ARG
+    assert call(kv_cap=131072) == F.INFLLM_ERR_INVALID_ARG       # position past the K/V rows
+    assert call(U=-1) == F.INFLLM_ERR_INVALID_ARG
+    need = F.infllm_workspace_size(c, F.INFLLM_CALL_SELECT_ATTEND, 4, 1023, 1, 1)
+    # at least what the two separate calls need, one after the other
+    sep = F.infllm_workspace_size(c, F.INFLLM_CALL_SELECT, 4, 0, 1, 1) + \
+        F.infllm_workspace_size(c, F.INFLLM_CALL_ATTEND, 4, 0, 1, 1)
+    assert need >= sep > 0
+    assert call(wsb=need - 1) == F.INFLLM_ERR_WORKSPACE
+    assert call(ws=None, wsb=0) == F.INFLLM_ERR_WORKSPACE
+    assert call(ws=MISALIGNED) == F.INFLLM_ERR_WORKSPACE
+    # one query per chunk only
+    assert F.infllm_workspace_size(c, F.INFLLM_CALL_SELECT_ATTEND, 4, 1023, 2, 1) == 0
+    # past 2,048 units (separate calls) the size still covers both calls
+    big = F.infllm_workspace_size(c, F.INFLLM_CALL_SELECT_ATTEND, 2, 8191, 1, 1)
+    assert big >= F.infllm_workspace_size(c, F.INFLLM_CALL_SELECT, 2, 0, 1, 1) + \
+        F.infllm_workspace_size(c, F.INFLLM_CALL_ATTEND, 2, 0, 1, 1)
 
 
 def test_qsum_validation_and_workspace():
