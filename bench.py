@@ -87,7 +87,8 @@ class Pipeline:
     decode pass (if w.decode_steps > 0) runs single-token steps against the
     pool.  Selections and outputs of the last step are kept for checking."""
 
-    def __init__(self, w: synth.Workload, dev: str = "cuda", layers: int = 1):
+    def __init__(self, w: synth.Workload, dev: str = "cuda", layers: int = 1,
+                 fused_step: bool = True):
         self.w, self.cfg, self.dev = w, cfg_of(w), dev
         t = time.time()
         self.inp = synth.make_inputs(w, device=dev)
@@ -126,6 +127,13 @@ class Pipeline:
             self.sel_dec = torch.empty((w.decode_steps, b, Hkv, 1, w.top_k), dtype=torch.int32,
                                        device=dev)
             self.out_dec = torch.empty_like(self.inp["q_dec"])
+        # a decode step in one launch (infllm_select_attend) where its shapes
+        # allow: bf16, at most 2,048 units (32 scoring slices per row)
+        self.fused = (fused_step and self.decode and w.dtype == "bf16" and 1 <= self.U <= 2048
+                      and w.top_k >= 1)
+        if self.fused:
+            self.dec_step_ws = F.workspace(cfg, F.INFLLM_CALL_SELECT_ATTEND, b, self.U, 1, 1,
+                                           device=dev)
         # Layer 0 is the workload's own K/V; further layers (decode only)
         # have their own K/V, unit pool and selections, over the same queries
         self.layers = [dict(k=self.inp["k"], v=self.inp["v"], repr=self.repr,
@@ -173,9 +181,11 @@ class Pipeline:
         selects units for all of its query chunks (or decode positions) and
         then attends: the encoding pass with one call per kind covering all
         chunks, the decode pass one call per position (each decode step
-        follows the previous one).  With a dict, events are recorded at the
-        phase boundaries: 'enc_sel' / 'enc_end' around the encoding
-        attention launch, 'dec_sel' / 'dec_end' around the decode ones."""
+        follows the previous one); where the fused decode step applies, one
+        infllm_select_attend launch per position does both.  With a dict,
+        events are recorded at the phase boundaries: 'enc_sel' / 'enc_end'
+        around the encoding attention launch, 'dec_sel' / 'dec_end' around
+        the decode attention (or fused step) launches."""
         w, inp, cfg = self.w, self.inp, self.cfg
         if self.encode:
             # the whole encoding pass: every chunk in one call of each kind
@@ -193,7 +203,17 @@ class Pipeline:
             F.infllm_attend(cfg, inp["q"], 0, 0, w.chunk, nc, inp["k"], inp["v"], self.enc_sel,
                             self.out_enc, None, 0, self.enc_attn_ws)
             self._mark(marks, "enc_end")
-        if self.decode:
+        if self.decode and self.fused:
+            # one launch per decode step: scores, selection and attention
+            nl = len(self.layers)
+            self._mark(marks, "dec_sel")
+            for s in range(w.decode_steps):
+                ly = self.layers[s % nl]
+                F.infllm_select_attend(cfg, inp["q_dec"], s, w.n_ctx + s, 1, ly["repr"], ly["k"],
+                                       ly["v"], self.scores, self.sel_dec[s], self.out_dec, None,
+                                       s, ws=self.dec_step_ws)
+            self._mark(marks, "dec_end")
+        elif self.decode:
             # decode step s runs on layer s mod L, as a model's layers follow
             # one another
             nl = len(self.layers)
@@ -227,6 +247,9 @@ class Pipeline:
                 flops += 4 * w.head_dim * w.group * int(cnt.sum())
                 nbytes += int(cnt.sum()) * 2 * w.head_dim * esz      # K and V rows read
                 nbytes += 2 * w.batch * w.n_q_heads * L * w.head_dim * esz  # q in, out
+                if name == "decode" and self.fused:
+                    # the fused launch also reads every unit row and writes its score
+                    nbytes += w.batch * w.n_kv_heads * self.U * (w.head_dim + 1) * 4
             res[name] = (tokens, flops, nbytes)
         return res
 
@@ -259,6 +282,11 @@ class StreamPipeline:
         self.out_dec = torch.empty_like(self.inp["q_dec"])
         self.sel_ws = F.workspace(cfg, F.INFLLM_CALL_SELECT, b, 0, 1, 1, device=dev)
         self.attn_ws = F.workspace(cfg, F.INFLLM_CALL_ATTEND, b, 0, 1, 1, device=dev)
+        # one launch per decode step (infllm_select_attend) where it applies
+        self.fused = w.dtype == "bf16" and 1 <= self.U <= 2048 and w.top_k >= 1
+        if self.fused:
+            self.step_ws = F.workspace(cfg, F.INFLLM_CALL_SELECT_ATTEND, b, self.U, 1, 1,
+                                       device=dev)
         self.pos_host = np.array([[self.lens[bi] + s for bi in range(b)] for s in range(S)],
                                  dtype=np.int64)
         self.pos = torch.tensor(self.pos_host, dtype=torch.int64, device=dev)   # [S, b]
@@ -317,9 +345,25 @@ class StreamPipeline:
         selection, in step order, then the attentions (selections never
         depend on attention outputs; a unit added at a later step is not
         eligible earlier).  Marks 'dec_sel' / 'dec_end' around the attention
-        launches."""
+        launches.  With the fused step: the units of every step, in step
+        order, then one infllm_select_attend launch per step (marked); a
+        unit built ahead of its step is not eligible before it, so the
+        selections are the same."""
         w, cfg, q = self.w, self.cfg, self.inp["q_dec"]
         nl = len(self.layers)
+        if self.fused:
+            for s in range(w.decode_steps):
+                for ly in self.layers:
+                    for bi, lo, hi, n in self.builds[s]:
+                        self._build(ly, bi, lo, hi, n, self.range_ws)
+            self._mark(marks, "dec_sel")
+            for s in range(w.decode_steps):
+                ly = self.layers[s % nl]
+                F.infllm_select_attend(cfg, q, s, 0, 1, ly["repr"], ly["k"], ly["v"], self.scores,
+                                       self.sel_dec[s], self.out_dec, None, s, pos=self.pos[s],
+                                       ws=self.step_ws)
+            self._mark(marks, "dec_end")
+            return
         for s in range(w.decode_steps):
             for ly in self.layers:
                 for bi, lo, hi, n in self.builds[s]:
@@ -345,6 +389,8 @@ class StreamPipeline:
                 flops += 4 * w.head_dim * w.group * int(cnt.sum())
                 nbytes += int(cnt.sum()) * 2 * w.head_dim * esz
             nbytes += 2 * w.batch * w.n_q_heads * w.head_dim * esz
+            if self.fused:   # every pool row read and scored
+                nbytes += w.batch * w.n_kv_heads * self.U * (w.head_dim + 1) * 4
         return {"decode": (tokens, flops, nbytes)}
 
 
@@ -417,7 +463,7 @@ def cpu_baseline(w: synth.Workload, pipe: Pipeline) -> dict:
 def stored_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary
     (profiles/<kernel>_<workload>.md), or None if there is none or the
-    kernel's source has changed since the counters were taken."""
+    kernel's sources have changed since the counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "%s_%s.md" % (kernel, workload))
     if not os.path.exists(path):
@@ -428,8 +474,11 @@ def stored_traffic(kernel: str, workload: str):
             key, val = line[2:].split(":", 1)
             fields[key.strip()] = val.strip()
     try:
-        src = os.path.join(ROOT, fields["kernel_source"])
-        if hashlib.sha256(open(src, "rb").read()).hexdigest() != fields["kernel_source_sha256"]:
+        # one file, or a comma-separated list hashed in order
+        h = hashlib.sha256()
+        for src in fields["kernel_source"].split(","):
+            h.update(open(os.path.join(ROOT, src.strip()), "rb").read())
+        if h.hexdigest() != fields["kernel_source_sha256"]:
             return None
         return int(fields["hbm_bytes_per_launch"])
     except (KeyError, OSError, ValueError):
@@ -467,7 +516,7 @@ def measure_peaks() -> dict:
 
 
 def roofline(w: synth.Workload, phase: str, work, attn_ms: float, n_calls: int,
-             peaks: dict | None = None) -> dict:
+             peaks: dict | None = None, fused: bool = False) -> dict:
     """attn_ms: average duration of one attention launch, in ms."""
     tokens, flops, nbytes = work
     if phase == "encode" and w.dtype == "bf16":
@@ -492,8 +541,11 @@ def roofline(w: synth.Workload, phase: str, work, attn_ms: float, n_calls: int,
         if "measured_peak" in r:
             r["frac_of_measured"] = round(achieved / r["measured_peak"], 4)
     kernel = "k_attend_prefill" if phase == "encode" and w.dtype == "bf16" else "k_attend_rows"
+    call = "infllm_attend"
+    if phase == "decode" and fused:
+        kernel, call = "k_select_attend", "infllm_select_attend"
     r["traffic"] = stored_traffic(kernel, w.name)
-    r["kernel"] = "infllm_attend (%s)" % kernel
+    r["kernel"] = "%s (%s)" % (call, kernel)
     r["avg_launch_us"] = round(attn_ms * 1e3, 2)
     r["launches_per_step"] = n_calls
     r["launch_timing"] = ("HIP events on the launch stream around each timed step's "
@@ -509,6 +561,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="llama3_8b_32k_encode", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate-decode", action="store_true",
+                    help="decode with infllm_select_units + infllm_attend (two launches per "
+                         "step) instead of infllm_select_attend")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip measuring what plain library kernels reach (read, GEMM)")
     ap.add_argument("--layers", type=int, default=None,
@@ -539,7 +594,8 @@ def main():
     if args.stream and not decode_only:
         print("--stream applies to decode workloads", file=sys.stderr)
         sys.exit(2)
-    pipe = StreamPipeline(w, layers=layers) if args.stream else Pipeline(w, layers=layers)
+    pipe = (StreamPipeline(w, layers=layers) if args.stream else
+            Pipeline(w, layers=layers, fused_step=not args.separate_decode))
     if not pipe.encode:
         pipe.build_all()        # decode-only: the pools are built once, beforehand
     # Untimed settling before the warm-up steps: the GPU's clocks ramp up
@@ -596,7 +652,7 @@ def main():
                      if phase == "encode" else
                      roofline(w, "decode", work["decode"],
                               span_ms("dec_sel", "dec_end") / w.decode_steps, w.decode_steps,
-                              peaks)),
+                              peaks, getattr(pipe, "fused", False))),
     }
     if args.stream:
         line["config"]["stream"] = {"lengths": pipe.lens, "pool_units": pipe.U,
@@ -611,7 +667,7 @@ def main():
         if pipe.encode:
             line["decode_roofline"] = roofline(w, "decode", work["decode"],
                                                span_ms("dec_sel", "dec_end") / w.decode_steps,
-                                               w.decode_steps, peaks)
+                                               w.decode_steps, peaks, pipe.fused)
     if args.calibration_copy > 0:
         n = args.calibration_copy << 20
         src = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda")

@@ -19,7 +19,6 @@
 // while the current one is reduced.  Splits publish partial (max, sum, unnormalised output)
 // rows; the last one to arrive merges them in split order (see common.h for
 // the publication protocol), so one launch produces the output.
-#include <stdio.h>
 #include <stdlib.h>
 
 #include "common.h"
@@ -79,9 +78,10 @@ constexpr int kMaxSplits = 64;
 // The work of one workgroup: split `split` of the n_splits splits of one
 // (position, KV head, sequence) row.  It attends share l_part of the local
 // keys cut into l_parts equal shares and share u_part of the units' keys
-// cut into u_parts (0 parts: none of them).  `ready` (fused decode step):
-// the row's selection is written in this launch -- wait until ready[row]
-// is set and read it with device-scope loads.
+// cut into u_parts (0 parts: none of them).  `ready` (fused decode step,
+// every split of the row): the row's selection is written in this launch --
+// splits with unit keys wait until ready[row] is set and read it with
+// device-scope loads, and the split that merges the row clears the flag.
 struct RowsJob {
   int split, n_splits, pos, h, bi;
   int l_part, l_parts, u_part, u_parts;
@@ -364,7 +364,12 @@ __device__ __forceinline__ void attend_rows_body(const AttendArgs& a, const Rows
       int* ctr = a.ws_count + row_id;
       const int done = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       last_sh = done == splits - 1;
-      if (last_sh) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (last_sh) {
+        __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // every split of the row is past its wait: ready for the next call
+        if (job.ready) __hip_atomic_store(const_cast<int*>(job.ready) + row_id, 0,
+                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
     __syncthreads();
     if (!last_sh) return;
@@ -527,35 +532,34 @@ hipError_t launch_attend_rows(const AttendArgs& a, int splits, hipStream_t st) {
 }
 
 // ------------------------------------------------------------ fused decode step
-// Selection and attention of decode positions in one launch.  Workgroups
-// take tickets in the order they start: the first rows * n_slices score a
-// slice of units each (the last slice of a row to arrive selects the row,
-// publishes the selection with device-scope stores and sets the row's ready
-// flag), the next rows * s_local attend a share of the local keys, which
-// need no selection, and the last rows * s_unit attend a share of the
-// selected units' keys once their row is ready.  A workgroup only waits on
-// workgroups with smaller tickets, which have started and never wait, so
-// the waits end; the wait is bounded all the same (a stale selection gives
-// NaN outputs).  The last workgroup to finish clears the tickets and flags.
+// Selection and attention of decode positions in one launch.  A row (one
+// position of one KV head of one sequence) has s_unit unit splits and
+// s_local local splits.  Unit split i first scores units [64i, 64i + 64)
+// of the row (none past the last unit: splits may outnumber the slices)
+// and counts itself in; the last to arrive selects the row, publishes the
+// selection with device-scope stores and sets the row's ready flag; every
+// unit split then waits for the flag and attends its share of the selected
+// units' keys.  A waiting split has itself arrived, so the one it waits on
+// is already running and never waits: the waits end without any
+// assumption on dispatch order (and are bounded all the same: a stale
+// selection gives NaN outputs).  Local splits attend their share of the
+// initial tokens and the window, which need no selection, meanwhile.  The
+// row's merging split clears the flag.
 template <typename T, int D, int G, int SEL>
 __global__ __launch_bounds__(kRowsThreads) void k_select_attend(ScoreArgs s, AttendArgs a,
-                                                                StepPlan p, int* sync) {
+                                                                StepPlan p, int* ready) {
   static_assert(kRowsThreads == kScoreThreads, "one workgroup size for both roles");
-  __shared__ int tk_sh, last_sh;
   __shared__ int32_t sel_sm[kMaxTopK];
   const int tid = threadIdx.x;
-  int* ticket = sync;       // [0] tickets taken, [1] workgroups done
-  int* ready = sync + 2;    // [rows] selection published
-  if (tid == 0) tk_sh = __hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  const int tk = tk_sh;
-  const int rows = a.batch * a.Hkv * a.n_pos;
-  const int n_sel = rows * p.n_slices;
-  if (tk < n_sel) {
-    // row = (sequence * H_kv + KV head) * positions + position; one chunk per position
-    const int row = tk / p.n_slices, slice = tk % p.n_slices;
-    const int pos = row % a.n_pos, h = row / a.n_pos % a.Hkv, bi = row / a.n_pos / a.Hkv;
-    if (score_slice<T, G, D, SEL>(slice, p.n_slices, pos, h, bi, (const T*)s.q, s.q_cap, s.q_off,
+  const int n_unit = a.batch * a.Hkv * a.n_pos * p.s_unit;
+  const bool unit = (int)blockIdx.x < n_unit;
+  const int per = unit ? p.s_unit : p.s_local;
+  const int x = unit ? (int)blockIdx.x : (int)blockIdx.x - n_unit;
+  // row = (sequence * H_kv + KV head) * positions + position; one chunk per position
+  const int row = x / per, part = x % per;
+  const int pos = row % a.n_pos, h = row / a.n_pos % a.Hkv, bi = row / a.n_pos / a.Hkv;
+  if (unit) {
+    if (score_slice<T, G, D, SEL>(part, p.s_unit, pos, h, bi, (const T*)s.q, s.q_cap, s.q_off,
                                   s.q_pos, s.pos, 1, s.Hq, s.Hkv, s.B, s.n_init, s.W, s.repr, s.U,
                                   s.scores, s.n_chunks, nullptr, 0, 0, 0, (int*)s.ws, s.k_m,
                                   sel_sm)) {
@@ -565,36 +569,23 @@ __global__ __launch_bounds__(kRowsThreads) void k_select_attend(ScoreArgs s, Att
         __hip_atomic_store(dst + m, sel_sm[m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       __syncthreads();
-      if (tid == 0) __hip_atomic_store(ready + row, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  } else {
-    int x = tk - n_sel;
-    const int n_splits = p.s_local + p.s_unit;
-    const bool local = x < rows * p.s_local;
-    if (!local) x -= rows * p.s_local;
-    const int per = local ? p.s_local : p.s_unit;
-    const int row = x / per, part = x % per;
-    const int pos = row % a.n_pos, h = row / a.n_pos % a.Hkv, bi = row / a.n_pos / a.Hkv;
-    const RowsJob job = local ? RowsJob{part, n_splits, pos, h, bi, part, p.s_local, 0, 0, nullptr}
-                              : RowsJob{p.s_local + part, n_splits, pos, h, bi, 0, 0, part,
-                                        p.s_unit, ready};
-    attend_rows_body<T, D, G>(a, job);
-  }
-  __syncthreads();
-  if (tid == 0) {
-    const int done = __hip_atomic_fetch_add(ticket + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    last_sh = done == (int)gridDim.x - 1;
-  }
-  __syncthreads();
-  if (last_sh) {   // every other workgroup has finished: ready for the next call
-    for (int r = tid; r < rows; r += kRowsThreads)
-      __hip_atomic_store(ready + r, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (tid == 0) {
-      __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(ticket + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // a row whose position does not fit its KV buffer attends nothing
+      // (every split leaves before waiting), so its flag stays clear
+      const bool valid = !a.pos || seq_pos_ok(seq_base(a.pos, a.q_pos, bi), a.n_pos, a.kv_cap);
+      if (tid == 0 && valid)
+        __hip_atomic_store(ready + row, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
+  const int n_splits = p.s_local + p.s_unit;
+  const RowsJob job = unit ? RowsJob{p.s_local + part, n_splits, pos, h, bi, 0, 0, part,
+                                     p.s_unit, ready}
+                           : RowsJob{part, n_splits, pos, h, bi, part, p.s_local, 0, 0, ready};
+  attend_rows_body<T, D, G>(a, job);
 }
+
+// workgroups of k_select_attend resident at once: 3 per CU (its LDS and
+// registers allow 3) on the 256 CUs
+constexpr int64_t kStepResidentWGs = 3 * 256;
 
 bool select_attend_plan(const ScoreArgs& s, const AttendArgs& a, StepPlan* p) {
   const int64_t rows = (int64_t)a.batch * a.Hkv * a.n_pos;
@@ -602,23 +593,31 @@ bool select_attend_plan(const ScoreArgs& s, const AttendArgs& a, StepPlan* p) {
   if (!a.bf16 || a.L != 1 || s.U < 1 || a.k_m < 1 || a.k_m > kMaxTopK || n_slices > kMaxSelSlices)
     return false;
   const int G = a.Hq / a.Hkv;
-  if (G * 1 > kDirectRows || (G != 1 && G != 2 && G != 4 && G != 8)) return false;
-  // about `target` attention workgroups, >= ~256 keys each, half on each key set
-  int64_t target = 512;
-  int want_l = 0, want_u = 0;
-  if (const char* e = getenv("INFLLM_STEP_SPLITS")) {   // tuning override "local,unit"
-    if (sscanf(e, "%d,%d", &want_l, &want_u) != 2) want_l = want_u = 0;
+  if (G > kDirectRows || (G != 1 && G != 2 && G != 4 && G != 8)) return false;
+  // about 256 workgroups on each key set, >= ~256 keys each; at least one
+  // unit split per scoring slice
+  const int64_t each = (256 + rows - 1) / rows;
+  int64_t sl = each, su = each;
+  if (const char* e = getenv("INFLLM_STEP_LOCAL_SPLITS")) {   // tuning override
+    const int v = atoi(e);
+    if (v >= 1 && v <= kMaxSplits) sl = v;
   }
-  const int64_t each = (target / 2 + rows - 1) / rows;
-  int64_t sl = want_l > 0 ? want_l : each, su = want_u > 0 ? want_u : each;
   const int64_t cap_l = ((int64_t)a.n_init + a.W + 255) / 256;
   const int64_t cap_u = ((int64_t)a.k_m * a.B + 255) / 256;
   sl = sl < cap_l ? sl : cap_l;
-  su = su < cap_u ? su : cap_u;
   sl = sl < 1 ? 1 : sl;
-  su = su < 1 ? 1 : su;
+  su = su < cap_u ? su : cap_u;
+  su = su < kMaxSplits / 2 ? su : kMaxSplits / 2;
+  su = su > n_slices ? su : n_slices;
+  if (sl + su > kMaxSplits) sl = kMaxSplits - su;
+  // the whole launch resident at once where it can be: split counts past
+  // that left a last round of local splits to start late (measured at 128K:
+  // 8 local splits 40.4 us per step, 10 splits 47.8 us)
+  const int64_t fit = kStepResidentWGs / rows - su;
+  if (sl > fit) sl = fit;
+  if (sl < 1) sl = 1;
   if (sl + su > kMaxSplits) return false;
-  if (rows * (n_slices + sl + su) > (int64_t)1 << 30) return false;
+  if (rows * (su + sl) > (int64_t)1 << 30) return false;
   p->n_slices = n_slices;
   p->s_local = (int)sl;
   p->s_unit = (int)su;
@@ -626,39 +625,39 @@ bool select_attend_plan(const ScoreArgs& s, const AttendArgs& a, StepPlan* p) {
 }
 
 int64_t select_attend_sync_ints(const AttendArgs& a) {
-  return 2 + (int64_t)a.batch * a.Hkv * a.n_pos;
+  return (int64_t)a.batch * a.Hkv * a.n_pos;   // ready flags
 }
 
 template <int D, int G>
 static hipError_t launch_step_dg(const ScoreArgs& s, const AttendArgs& a, const StepPlan& p,
-                                 int* sync, hipStream_t st) {
+                                 int* ready, hipStream_t st) {
   const int64_t rows = (int64_t)a.batch * a.Hkv * a.n_pos;
-  const dim3 grid((unsigned)(rows * (p.n_slices + p.s_local + p.s_unit)));
+  const dim3 grid((unsigned)(rows * (p.s_local + p.s_unit)));
   // keys per lane of the 4-wave search: ceil(U / 256) <= 8
   static_assert(kMaxSelSlices * kUnitsPerWG <= 8 * kScoreThreads, "keys per lane");
   if (s.U <= 4 * kScoreThreads)
-    k_select_attend<bf16_t, D, G, 4><<<grid, kRowsThreads, 0, st>>>(s, a, p, sync);
+    k_select_attend<bf16_t, D, G, 4><<<grid, kRowsThreads, 0, st>>>(s, a, p, ready);
   else
-    k_select_attend<bf16_t, D, G, 8><<<grid, kRowsThreads, 0, st>>>(s, a, p, sync);
+    k_select_attend<bf16_t, D, G, 8><<<grid, kRowsThreads, 0, st>>>(s, a, p, ready);
   return hipGetLastError();
 }
 
 template <int D>
 static hipError_t launch_step_d(const ScoreArgs& s, const AttendArgs& a, const StepPlan& p,
-                                int* sync, hipStream_t st) {
+                                int* ready, hipStream_t st) {
   switch (a.Hq / a.Hkv) {
-    case 1: return launch_step_dg<D, 1>(s, a, p, sync, st);
-    case 2: return launch_step_dg<D, 2>(s, a, p, sync, st);
-    case 4: return launch_step_dg<D, 4>(s, a, p, sync, st);
-    case 8: return launch_step_dg<D, 8>(s, a, p, sync, st);
+    case 1: return launch_step_dg<D, 1>(s, a, p, ready, st);
+    case 2: return launch_step_dg<D, 2>(s, a, p, ready, st);
+    case 4: return launch_step_dg<D, 4>(s, a, p, ready, st);
+    case 8: return launch_step_dg<D, 8>(s, a, p, ready, st);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_select_attend(const ScoreArgs& s, const AttendArgs& a, const StepPlan& p,
-                                int* sync, hipStream_t st) {
+                                int* ready, hipStream_t st) {
   if (a.n_pos <= 0) return hipSuccess;
-  return a.d == 128 ? launch_step_d<128>(s, a, p, sync, st) : launch_step_d<64>(s, a, p, sync, st);
+  return a.d == 128 ? launch_step_d<128>(s, a, p, ready, st) : launch_step_d<64>(s, a, p, ready, st);
 }
 
 }  // namespace infllm

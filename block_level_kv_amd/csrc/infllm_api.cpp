@@ -123,14 +123,14 @@ AttendWs attend_ws_layout(const AttendArgs& a) {
 
 size_t attend_ws_bytes(const AttendArgs& a) { return attend_ws_layout(a).total(); }
 
-// Decode step workspace.  Fused: [tickets and ready flags][selection
+// Decode step workspace.  Fused: [ready flags][selection
 // counters][attention counters, partials of s_local + s_unit splits].
 // Separate calls: [selection workspace][attention workspace].  Sized for
 // the larger of the two.
 struct StepWs {
   bool fused;
   StepPlan plan;
-  size_t sync_bytes, sel_bytes;   // fused: sync ints, selection counters
+  size_t sync_bytes, sel_bytes;   // fused: ready flags, selection counters
   AttendWs att;                   // fused attention part
   size_t sep_sel_bytes;           // separate calls: selection workspace
   size_t total;

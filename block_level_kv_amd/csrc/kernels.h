@@ -81,11 +81,12 @@ int64_t rows_num_counters(const AttendArgs& a);
 struct StepPlan {
   int n_slices;         // scoring slices per row
   int s_local, s_unit;  // attention splits per row over the local and the unit keys
+                        // (s_unit >= n_slices; splits past the slices only attend)
 };
 bool select_attend_plan(const ScoreArgs& s, const AttendArgs& a, StepPlan* p);
-int64_t select_attend_sync_ints(const AttendArgs& a);   // tickets and ready flags
+int64_t select_attend_sync_ints(const AttendArgs& a);   // ready flags
 hipError_t launch_select_attend(const ScoreArgs& s, const AttendArgs& a, const StepPlan& p,
-                                int* sync, hipStream_t st);
+                                int* ready, hipStream_t st);
 
 // bf16 MFMA attention tiles for query chunks (head_dim 128)
 bool prefill_supported(const AttendArgs& a);

@@ -117,8 +117,9 @@ SHAPES = [
     (8, 1, 128, 2048, 32, 1, 512, 128, False, "bf16", None),    # 32 slices, 8 keys per lane
     (8, 1, 128, 2049, 32, 1, 512, 128, False, "bf16", None),    # beyond: separate calls
     (4, 2, 128, 30, 40, 1, 512, 128, False, "bf16", None),      # k_m > units
-    (4, 2, 128, 90, 8, 1, 512, 128, False, "bf16", "1,1"),      # one split per key set
-    (4, 2, 128, 90, 8, 2, 512, 128, False, "bf16", "3,7"),      # unequal splits
+    (4, 2, 128, 90, 8, 1, 512, 128, False, "bf16", "1"),        # one local split
+    (4, 2, 128, 90, 8, 2, 512, 128, False, "bf16", "3"),        # three local splits
+    (8, 2, 128, 64, 2, 1, 4096, 128, False, "bf16", "1"),      # a local split merges last
     (2, 1, 64, 40, 4, 1, 512, 64, False, "f32", None),          # fp32: separate calls
 ]
 
@@ -130,7 +131,7 @@ def test_select_attend_shapes(orc, monkeypatch, Hq, Hkv, d, U, k_m, n_pos, W, n_
     eligible, a second sequence (varlen) sits mid-context.  Two calls in a
     row on one workspace."""
     if splits is not None:
-        monkeypatch.setenv("INFLLM_STEP_SPLITS", splits)
+        monkeypatch.setenv("INFLLM_STEP_LOCAL_SPLITS", splits)
     b, B = 2, 128
     dtype = torch.bfloat16 if dt == "bf16" else torch.float32
     cfg = F.make_config(n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, block=B, n_init=n_init,
