@@ -129,7 +129,7 @@ def test_select_attend_shapes(orc, monkeypatch, Hq, Hkv, d, U, k_m, n_pos, W, n_
                               splits):
     """Random unit representations and K/V; the last position sees every unit
     eligible, a second sequence (varlen) sits mid-context.  Two calls in a
-    row on one workspace."""
+    row on one workspace, bit for bit equal."""
     if splits is not None:
         monkeypatch.setenv("INFLLM_STEP_LOCAL_SPLITS", splits)
     b, B = 2, 128
@@ -154,9 +154,14 @@ def test_select_attend_shapes(orc, monkeypatch, Hq, Hkv, d, U, k_m, n_pos, W, n_
         pos = torch.tensor(t_list, dtype=torch.int64).cuda()
     ws = F.workspace(cfg, F.INFLLM_CALL_SELECT_ATTEND, b, U, 1, n_pos)
     ref = separate(cfg, qg, 2, t0, n_pos, rg, kg, vg, pos=pos)
+    first = None
     for _ in range(2):
         got = fused(cfg, qg, 2, t0, n_pos, rg, kg, vg, ws, pos=pos)
         compare(orc, cfg, got, ref, q, 2, t_list, k, v)
+        if first is None:
+            first = got
+        else:   # the same bits on the second call (fixed merge order)
+            assert all(torch.equal(x, y) for x, y in zip(first, got))
 
 
 def test_select_attend_bad_positions(orc):
