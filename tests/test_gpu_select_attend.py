@@ -117,6 +117,7 @@ SHAPES = [
     (8, 1, 128, 2048, 32, 1, 512, 128, False, "bf16", None),    # 32 slices, 8 keys per lane
     (8, 1, 128, 2049, 32, 1, 512, 128, False, "bf16", None),    # beyond: separate calls
     (4, 2, 128, 30, 40, 1, 512, 128, False, "bf16", None),      # k_m > units
+    (4, 2, 128, 600, 256, 1, 512, 128, False, "bf16", None),    # the largest k_m
     (4, 2, 128, 90, 8, 1, 512, 128, False, "bf16", "1"),        # one local split
     (4, 2, 128, 90, 8, 2, 512, 128, False, "bf16", "3"),        # three local splits
     (8, 2, 128, 64, 2, 1, 4096, 128, False, "bf16", "1"),      # a local split merges last
