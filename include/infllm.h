@@ -43,6 +43,11 @@
  *    INFLLM_ERR_UNSUPPORTED / INFLLM_ERR_WORKSPACE) before any device
  *    work is enqueued; a failed launch returns INFLLM_ERR_HIP.  Nothing is
  *    thrown across the ABI.
+ *  Tuning.  The environment variables INFLLM_PREFILL_SPLITS,
+ *    INFLLM_ROWS_WGS and INFLLM_STEP_LOCAL_SPLITS override split counts
+ *    of the chunk attention, the decode attention and the one-launch
+ *    decode step; workspace sizes follow them, so they must not change
+ *    between sizing a workspace and the calls that use it.
  *  Units.  Unit u is absolute block j = u + floor(n_init / block); its keys
  *    are positions [max(j*block, n_init), (j+1)*block).  A context of n_ctx
  *    tokens holds floor(n_ctx/block) - floor(n_init/block) units (blocks
