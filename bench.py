@@ -127,10 +127,10 @@ class Pipeline:
             self.sel_dec = torch.empty((w.decode_steps, b, Hkv, 1, w.top_k), dtype=torch.int32,
                                        device=dev)
             self.out_dec = torch.empty_like(self.inp["q_dec"])
-        # a decode step in one launch (infllm_select_attend) where its shapes
-        # allow: bf16, at most 2,048 units (32 scoring slices per row)
-        self.fused = (fused_step and self.decode and w.dtype == "bf16" and 1 <= self.U <= 2048
-                      and w.top_k >= 1)
+        # a decode step in one launch (infllm_select_attend) where the
+        # library's plan allows it
+        self.fused = bool(fused_step and self.decode
+                          and F.infllm_step_plan(cfg, b, self.U, 1)["fused"])
         if self.fused:
             self.dec_step_ws = F.workspace(cfg, F.INFLLM_CALL_SELECT_ATTEND, b, self.U, 1, 1,
                                            device=dev)
@@ -283,7 +283,7 @@ class StreamPipeline:
         self.sel_ws = F.workspace(cfg, F.INFLLM_CALL_SELECT, b, 0, 1, 1, device=dev)
         self.attn_ws = F.workspace(cfg, F.INFLLM_CALL_ATTEND, b, 0, 1, 1, device=dev)
         # one launch per decode step (infllm_select_attend) where it applies
-        self.fused = w.dtype == "bf16" and 1 <= self.U <= 2048 and w.top_k >= 1
+        self.fused = bool(F.infllm_step_plan(cfg, b, self.U, 1)["fused"])
         if self.fused:
             self.step_ws = F.workspace(cfg, F.INFLLM_CALL_SELECT_ATTEND, b, self.U, 1, 1,
                                        device=dev)

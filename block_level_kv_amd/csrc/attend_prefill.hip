@@ -30,7 +30,6 @@
 // (max, sum, unnormalised output) rows and the last one to finish, found
 // with a per-tile counter in the workspace, merges them and writes the
 // output.  The counters return to zero at the end of every call.
-#include <stdlib.h>
 
 #include "common.h"
 #include "kernels.h"
@@ -167,8 +166,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_prefill(AttendArgs a, Pr
     // this thread's unit: how many of its 64-key tiles hold a usable key
     int64_t jb = 0;
     int cnt = 0, s_first = 0;
+    __shared__ int32_t ids_sm[kMaxTopK];
+    int32_t u = tid < a.k_m ? a.sel[(((int64_t)bi * a.Hkv + h) * a.n_chunks + ch) * a.k_m + tid] : -1;
+    u = drop_repeats(u, tid, a.k_m, ids_sm);   // a repeated id is attended once
     if (tid < a.k_m) {
-      const int32_t u = a.sel[(((int64_t)bi * a.Hkv + h) * a.n_chunks + ch) * a.k_m + tid];
       if (u >= 0) {
         jb = ((int64_t)u + n_init / a.B) * a.B;
         for (int s = 0; s < a.B / kKT; ++s) {
@@ -535,10 +536,7 @@ bool prefill_supported(const AttendArgs& a) {
 }
 
 int prefill_num_splits(const AttendArgs& a) {
-  if (const char* e = getenv("INFLLM_PREFILL_SPLITS")) {  // tuning override
-    const int v = atoi(e);
-    if (v >= 1 && v <= 16) return v;
-  }
+  if (tuning().prefill_splits > 0) return tuning().prefill_splits;   // override
   const int G = a.Hq / a.Hkv;
   const int TQ = kRows / G;
   const int64_t wgs = (int64_t)((a.L + TQ - 1) / TQ) * a.n_chunks * a.Hkv * a.batch;

@@ -1,7 +1,8 @@
-// Working-context attention for one query position per workgroup, on the
-// vector ALUs.  This is the decode path (one query per step, the G query
-// heads of a KV head share every K/V row loaded) and the path for fp32 and
-// head sizes the MFMA kernel does not take.
+// Working-context attention of single query positions on the vector ALUs:
+// the decode path (one query per step; the G query heads of a KV head share
+// every K/V row loaded), the path for fp32 and the head sizes the MFMA
+// kernel does not take, and the decode step in one launch (scores,
+// selection and attention).
 //
 // For a single position t the working context (InfLLM Guide, "Core
 // Innovation 2", item 3; "Core Innovation 1", items 1-2) is a union of
@@ -9,18 +10,11 @@
 //     [0, min(n_init, t+1))                     initial tokens
 //     [first_key(u), min(end(u), t-W+1))        each selected unit u
 //     [max(n_init, t-W+1), t+1)                 local window (t included)
-// so no per-key mask is needed.  The work is split over gridDim.x workgroups
-// (split-K): each takes an equal share of the local keys (initial tokens and
-// window, known from t alone, so its first loads go out before the
-// selection is read) and an equal share of the units' keys.  Within a
-// workgroup 16 lanes share a key (each holds D/16 columns: one coalesced
-// 16-byte load per lane for bf16, D = 128); the 16 key lanes run independent
-// online softmaxes merged through LDS, and the next group of keys is loaded
-// while the current one is reduced.  Splits publish partial (max, sum, unnormalised output)
+// so no per-key mask is needed.  The work of a row is split over several
+// workgroups (split-K), each with a share of the local keys and a share of
+// the units' keys.  They publish partial (max, sum, unnormalised output)
 // rows; the last one to arrive merges them in split order (see common.h for
 // the publication protocol), so one launch produces the output.
-#include <stdlib.h>
-
 #include "common.h"
 #include "kernels.h"
 #include "score_units.h"
@@ -75,191 +69,246 @@ template <> struct RowRaw<float, 4> {
 constexpr int kKeysPerIter = 4;  // keys per lane between softmax rescales
 constexpr int kMaxSplits = 64;
 
-// The work of one workgroup: split `split` of the n_splits splits of one
-// (position, KV head, sequence) row.  It attends share l_part of the local
-// keys cut into l_parts equal shares and share u_part of the units' keys
-// cut into u_parts (0 parts: none of them).  `ready` (fused decode step,
-// every split of the row): the row's selection is written in this launch --
-// splits with unit keys wait until ready[row] is set and read it with
-// device-scope loads, and the split that merges the row clears the flag.
-struct RowsJob {
-  int split, n_splits, pos, h, bi;
-  int l_part, l_parts, u_part, u_parts;
-  const int* ready;
+// Bounded wait for a selection made in the same launch (polls of a few
+// hundred ns each; a selection takes microseconds).  The wait always ends
+// before the bound (see k_select_attend); the bound only turns a broken
+// invariant into NaN rows and a nonzero status word instead of a hang.
+constexpr int kSpinLimit = 1 << 18;
+// The selector's first, bounded spin on the arrival mask before it checks
+// for slices nobody started (normally the row's scorers finish within it).
+constexpr int kPreSpin = 1 << 12;
+
+// LDS of one decode attention workgroup.
+template <int G, int D>
+struct RowsShared {
+  int64_t iv_lo[kMaxTopK];            // first key position of unit m
+  int32_t iv_first[kMaxTopK + 1];     // first unit-key index of unit m (< k_m * B)
+  int32_t ids[kMaxTopK];
+  int wave_tot[kRowsThreads / 64];
+  int flag, last;
+  uint64_t todo;
+  float sm_m[16][G], sm_l[16][G];
+  float sm_o[16][G][D];
+  float sm_M[G], sm_L[G];
 };
 
-// bounded wait for a selection made in the same launch (polls of a few
-// hundred ns each; the selection takes microseconds)
-constexpr int kSpinLimit = 1 << 18;
-
+// The attention of one workgroup over its share of one (position, KV head,
+// sequence) row's working context.  The local keys (initial tokens, then
+// the window; they follow from the position alone) are numbered
+// 0 .. n_local-1 and the workgroup takes [n_local*l_lo/l_den,
+// n_local*l_hi/l_den); the selected units' keys are numbered in selection
+// order (each unit at most B keys) and cut into u_parts equal shares, of
+// which it takes u_part.  Its keys are indexed 0 .. nl-1 (local) and
+// nl .. nl+nu-1 (units) and can be streamed in any order of ranges.
+// Within the workgroup 16 lanes share a key (each holds D/16 columns: one
+// coalesced 16-byte load per lane for bf16, D = 128); the 16 key lanes run
+// independent online softmaxes merged through LDS, and the next group of
+// keys is loaded while the current one is reduced.
 template <typename T, int D, int G>
-__device__ __forceinline__ void attend_rows_body(const AttendArgs& a, const RowsJob& job) {
-  constexpr int CPT = D / 16;
-  const int split = job.split, pos = job.pos, h = job.h, bi = job.bi;
-  const int tid = threadIdx.x, lane = tid % 64, seg = tid % 16, kl = tid / 16;
-  const int ch = pos / a.L;
-  const int64_t base = seq_base(a.pos, a.q_pos, bi);
-  if (a.pos && !seq_pos_ok(base, a.n_pos, a.kv_cap)) {
-    // a sequence whose position does not fit its KV buffer: every split
-    // leaves before any key load or arrival count, split 0 writes NaN rows
-    if (split == 0)
-      nan_rows<T>((T*)a.out, a.lse, (int64_t)bi * a.Hq + (int64_t)h * G, G, a.out_cap,
-                  a.out_off + pos, 1, D, tid, kRowsThreads);
-    return;
-  }
-  const int64_t t = base + pos;
-
-  __shared__ int64_t iv_lo[kMaxTopK];               // first key position of unit m
-  __shared__ int64_t iv_first[kMaxTopK + 1];        // first unit-key index of unit m
-  __shared__ int wave_tot[kRowsThreads / 64];
-  __shared__ int last_sh;
-
-  // query rows first: their loads overlap the interval scan below
+struct RowsAttn {
+  static constexpr int CPT = D / 16;
+  static constexpr int kGroup = 16 * kKeysPerIter;   // keys per iteration
+  const AttendArgs& a;
+  RowsShared<G, D>& sh;
+  int tid, lane, seg, kl, pos, h, bi;
+  bool valid;
+  int64_t t, unit_cap, init_len, win_lo, n_local, l_begin, nl, u_begin, pu, nu;
+  const int32_t* sel_row;
+  const T* kb;   // K and V of the row's KV head (uniform); a lane reads columns seg*CPT ..
+  const T* vb;
+  int cur;
   RowRaw<T, CPT> qraw[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-    qraw[g].load((const T*)a.q +
-                 (((int64_t)bi * a.Hq + (int64_t)h * G + g) * a.q_cap + a.q_off + pos) * D +
-                 seg * CPT);
-
-  // ---------------------------------------------------------- key sets
-  // Local keys (initial tokens, then the window) follow from t alone; the
-  // units' keys need the selection.  Every split takes an equal share of
-  // each: local keys [l_begin, l_stop) of the local numbering first, then
-  // unit keys [u_begin, u_stop) of the units' numbering (sel order, each
-  // unit at most B keys).  Its first local keys are requested before the
-  // selection is read and the unit table formed.
-  const int64_t unit_cap = t - a.W + 1;
-  const int64_t init_len = a.n_init < t + 1 ? a.n_init : t + 1;
-  const int64_t win_lo = a.n_init > unit_cap ? a.n_init : unit_cap;
-  const int64_t win_len = t + 1 - win_lo > 0 ? t + 1 - win_lo : 0;
-  const int64_t n_local = init_len + win_len;
-  const int64_t pl = job.l_parts > 0 ? (n_local + job.l_parts - 1) / job.l_parts : 0;
-  const int64_t l_begin = (int64_t)job.l_part * pl < n_local ? (int64_t)job.l_part * pl : n_local;
-  const int64_t l_stop = l_begin + pl < n_local ? l_begin + pl : n_local;
-  const int64_t nl = l_stop - l_begin;
-  const int64_t pu = job.u_parts > 0 ? ((int64_t)a.k_m * a.B + job.u_parts - 1) / job.u_parts : 0;
-  const int64_t u_begin = (int64_t)job.u_part * pu;
-  const int64_t row_id = ((int64_t)bi * a.Hkv + h) * a.n_pos + pos;
-  __shared__ int ready_sh;
-  bool stale = false;                                // the selection never arrived
-  if (job.ready && job.u_parts > 0) {
-    if (tid == 0) {
-      int ok = 0;
-      for (int it = 0; it < kSpinLimit && !ok; ++it) {
-        ok = __hip_atomic_load(job.ready + row_id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (!ok) __builtin_amdgcn_s_sleep(2);
-      }
-      ready_sh = ok;
-    }
-    __syncthreads();
-    stale = !ready_sh;
-  }
-  int32_t my_unit = -1;                              // sel entry `tid`, requested now
-  if (tid < a.k_m && job.u_parts > 0 && !stale) {
-    const int32_t* sp = a.sel + (((int64_t)bi * a.Hkv + h) * a.n_chunks + ch) * a.k_m + tid;
-    my_unit = job.ready ? __hip_atomic_load(const_cast<int32_t*>(sp), __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT)
-                        : *sp;
-  }
-
-  const T* kb = (const T*)a.k + ((int64_t)bi * a.Hkv + h) * a.kv_cap * D + seg * CPT;
-  const T* vb = (const T*)a.v + ((int64_t)bi * a.Hkv + h) * a.kv_cap * D + seg * CPT;
-  // split-local key index i -> position: i < nl local keys, then unit keys
-  // through the table (each lane's indices only grow, so a cursor works)
-  int cur = 0;
-  int64_t n_split = nl;                              // + the unit keys, once known
-  auto key_pos = [&](int64_t i) -> int64_t {
-    if (i < nl) {
-      const int64_t x = l_begin + i;
-      return x < init_len ? x : win_lo + (x - init_len);
-    }
-    const int64_t y = u_begin + (i - nl);
-    while (y >= iv_first[cur + 1]) ++cur;
-    return iv_lo[cur] + (y - iv_first[cur]);
-  };
+  float qv[G][CPT], m[G], l[G], acc[G][CPT];
   RowRaw<T, CPT> kn[kKeysPerIter], vn[kKeysPerIter];
   bool okn[kKeysPerIter];
-  auto fetch = [&](int64_t base) {
+
+  // A sequence whose position does not fit its KV buffer reads no key and
+  // gets NaN rows; its workgroups still take part in the merge.
+  __device__ __forceinline__ RowsAttn(const AttendArgs& a_, RowsShared<G, D>& sh_, int pos_,
+                                      int h_, int bi_)
+      : a(a_), sh(sh_), pos(pos_), h(h_), bi(bi_) {
+    tid = threadIdx.x;
+    lane = tid % 64;
+    seg = tid % 16;
+    kl = tid / 16;
+    const int64_t base = seq_base(a.pos, a.q_pos, bi);
+    valid = !a.pos || seq_pos_ok(base, a.n_pos, a.kv_cap);
+    t = valid ? base + pos : 0;
+    load_q();   // first: the loads overlap what follows
+    unit_cap = t - a.W + 1;
+    init_len = !valid ? 0 : (a.n_init < t + 1 ? a.n_init : t + 1);
+    win_lo = a.n_init > unit_cap ? a.n_init : unit_cap;
+    const int64_t win_len = valid && t + 1 - win_lo > 0 ? t + 1 - win_lo : 0;
+    n_local = init_len + win_len;
+    const int ch = pos / a.L;
+    sel_row = a.sel ? a.sel + (((int64_t)bi * a.Hkv + h) * a.n_chunks + ch) * a.k_m : nullptr;
+    kb = (const T*)a.k + ((int64_t)bi * a.Hkv + h) * a.kv_cap * D;
+    vb = (const T*)a.v + ((int64_t)bi * a.Hkv + h) * a.kv_cap * D;
+    cur = 0;
+    nu = 0;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      m[g] = -INFINITY;
+      l[g] = 0.f;
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) acc[g][c] = 0.f;
+    }
+  }
+
+  __device__ __forceinline__ void load_q() {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      qraw[g].load((const T*)a.q +
+                   (((int64_t)bi * a.Hq + (int64_t)h * G + g) * a.q_cap + a.q_off + pos) * D +
+                   seg * CPT);
+  }
+
+  // The softmax state to LDS (park) and back with the query rows reloaded
+  // (restore), so that nothing of it stays live in registers across the
+  // work in between.  The 16 lanes of a key lane hold the same m and l.
+  __device__ __forceinline__ void restore() {
+    load_q();
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      m[g] = sh.sm_m[kl][g];
+      l[g] = sh.sm_l[kl][g];
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) acc[g][c] = sh.sm_o[kl][g][seg * CPT + c];
+    }
+    make_qv();
+    __syncthreads();
+  }
+
+  __device__ __forceinline__ void park() {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if (seg == 0) {
+        sh.sm_m[kl][g] = m[g];
+        sh.sm_l[kl][g] = l[g];
+      }
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) sh.sm_o[kl][g][seg * CPT + c] = acc[g][c];
+    }
+    __syncthreads();
+  }
+  __device__ __forceinline__ void shares(int64_t l_lo, int64_t l_hi, int64_t l_den, int u_part,
+                                         int u_parts) {
+    l_begin = n_local * l_lo / l_den;
+    nl = n_local * l_hi / l_den - l_begin;
+    pu = u_parts > 0 ? ((int64_t)a.k_m * a.B + u_parts - 1) / u_parts : 0;
+    u_begin = (int64_t)u_part * pu;
+  }
+
+  // Position of key b0 + li (b0 uniform, li the lane's offset in the
+  // group): keys below nl are local, then unit keys through the table (within
+  // the unit range each lane's indices only grow, so a cursor works).  The
+  // per-lane comparisons are 32-bit.
+  __device__ __forceinline__ static int clamp32(int64_t v) {
+    return v > INT32_MAX ? INT32_MAX : (v < INT32_MIN ? INT32_MIN : (int)v);
+  }
+  // KIND: kMixed, or a range known to hold only local (kLocal) or only unit
+  // (kUnits) keys.
+  static constexpr int kMixed = 0, kLocal = 1, kUnits = 2;
+  template <int KIND>
+  __device__ __forceinline__ int64_t key_pos(int64_t b0, int li) {
+    if (KIND == kLocal || (KIND == kMixed && li < clamp32(nl - b0))) {
+      const int64_t x0 = l_begin + b0;
+      return li < clamp32(init_len - x0) ? x0 + li : x0 + (win_lo - init_len) + li;
+    }
+    const int y = (int)(u_begin + b0 - nl) + li;   // unit-key index, < k_m * B
+    while (y >= sh.iv_first[cur + 1]) ++cur;
+    return sh.iv_lo[cur] + (y - sh.iv_first[cur]);
+  }
+
+  template <int KIND = kMixed>
+  __device__ __forceinline__ void fetch(int64_t b0, int64_t end) {
+    // keys of the group left in the range (uniform), so that the per-lane
+    // index within the group stays 32-bit
+    const int rem = end - b0 < kGroup ? (int)(end - b0) : kGroup;
 #pragma unroll
     for (int j = 0; j < kKeysPerIter; ++j) {
-      const int64_t idx = base + kl + 16 * j;
-      okn[j] = idx < n_split;
-      const int64_t p = okn[j] ? key_pos(idx) : 0;
-      kn[j].load(kb + p * D);
-      vn[j].load(vb + p * D);
+      const int li = kl + 16 * j;
+      okn[j] = li < rem;
+      const int64_t p = okn[j] ? key_pos<KIND>(b0, li) : 0;
+      const int64_t off = p * D + seg * CPT;
+      kn[j].load(kb + off);
+      vn[j].load(vb + off);
     }
-  };
-  // the first group of keys, if local only, is in flight during the table
-  const bool early = nl >= 16 * kKeysPerIter;
-  if (early) fetch(0);
+  }
 
-  // unit table: thread m computes unit m's length, a block scan the offsets
-  {
+  // Unit table of the row's selection (thread m passes entry m; repeated ids
+  // count once): each unit's first key and first unit-key index, by a block
+  // scan of the unit lengths.  Sets nu, this workgroup's unit keys.  Every
+  // thread calls it.
+  __device__ __forceinline__ void build_table(int32_t u) {
+    u = drop_repeats(u, tid, a.k_m, sh.ids);
     int64_t lo = 0, len = 0;
-    if (my_unit >= 0) {
-      lo = unit_first_key(my_unit, a.B, a.n_init);
-      const int64_t hi = ((int64_t)my_unit + a.n_init / a.B + 1) * a.B;
+    if (u >= 0) {
+      lo = unit_first_key(u, a.B, a.n_init);
+      const int64_t hi = ((int64_t)u + a.n_init / a.B + 1) * a.B;
       len = (hi < unit_cap ? hi : unit_cap) - lo;
       len = len > 0 ? len : 0;
     }
-    // inclusive scan of the unit lengths (each <= B)
-    int x = (int)len;
+    int x = (int)len;   // inclusive scan of the unit lengths (each <= B)
 #pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-      const int y = __shfl_up(x, m);
-      if (lane >= m) x += y;
+    for (int mm = 1; mm < 64; mm <<= 1) {
+      const int y = __shfl_up(x, mm);
+      if (lane >= mm) x += y;
     }
-    if (lane == 63) wave_tot[tid / 64] = x;
+    if (lane == 63) sh.wave_tot[tid / 64] = x;
     __syncthreads();
     int before = 0, all = 0;
 #pragma unroll
     for (int w2 = 0; w2 < kRowsThreads / 64; ++w2) {
-      before += w2 < tid / 64 ? wave_tot[w2] : 0;
-      all += wave_tot[w2];
+      before += w2 < tid / 64 ? sh.wave_tot[w2] : 0;
+      all += sh.wave_tot[w2];
     }
     if (tid < a.k_m) {
-      iv_lo[tid] = lo;
-      iv_first[tid] = before + x - len;
+      sh.iv_lo[tid] = lo;
+      sh.iv_first[tid] = before + x - (int)len;
     }
-    if (tid == 0) iv_first[a.k_m] = all;
-  }
-  __syncthreads();
-  {
-    const int64_t n_unit = iv_first[a.k_m];
+    if (tid == 0) sh.iv_first[a.k_m] = all;
+    __syncthreads();
+    const int64_t n_unit = sh.iv_first[a.k_m];
     const int64_t u_stop = u_begin + pu < n_unit ? u_begin + pu : n_unit;
-    n_split = nl + (u_stop > u_begin ? u_stop - u_begin : 0);
+    nu = u_stop > u_begin ? u_stop - u_begin : 0;
+    cur = 0;
   }
 
-  const float qscale = kLog2e / sqrtf((float)D);
-  float qv[G][CPT];
+  __device__ __forceinline__ void make_qv() {
+    const float qscale = kLog2e / sqrtf((float)D);
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    qraw[g].to_f32(qv[g]);
+    for (int g = 0; g < G; ++g) {
+      qraw[g].to_f32(qv[g]);
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) qv[g][c] *= qscale;
-  }
-  float m[G], l[G], acc[G][CPT];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = -INFINITY;
-    l[g] = 0.f;
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) acc[g][c] = 0.f;
-  }
-
-  if (!early) fetch(0);
-  for (int64_t base = 0; base < n_split; base += 16 * kKeysPerIter) {
-    RowRaw<T, CPT> kc[kKeysPerIter], vc[kKeysPerIter];
-    bool ok[kKeysPerIter];
-#pragma unroll
-    for (int j = 0; j < kKeysPerIter; ++j) {
-      kc[j] = kn[j];
-      vc[j] = vn[j];
-      ok[j] = okn[j];
+      for (int c = 0; c < CPT; ++c) qv[g][c] *= qscale;
     }
-    if (base + 16 * kKeysPerIter < n_split) fetch(base + 16 * kKeysPerIter);  // in flight
-    // logits of the current keys for every head (each key row converted once)
+  }
+
+  // Keys [lo, hi), kGroup per iteration, the next group in flight while the
+  // current one is reduced.
+  template <int KIND = kMixed>
+  __device__ __forceinline__ void stream(int64_t lo, int64_t hi, bool in_flight) {
+    if (lo >= hi) return;
+    if (!in_flight) fetch<KIND>(lo, hi);
+    for (int64_t b0 = lo; b0 < hi; b0 += kGroup) {
+      RowRaw<T, CPT> kc[kKeysPerIter], vc[kKeysPerIter];
+      bool ok[kKeysPerIter];
+#pragma unroll
+      for (int j = 0; j < kKeysPerIter; ++j) {
+        kc[j] = kn[j];
+        vc[j] = vn[j];
+        ok[j] = okn[j];
+      }
+      if (b0 + kGroup < hi) fetch<KIND>(b0 + kGroup, hi);  // in flight
+      step(kc, vc, ok);
+    }
+  }
+
+  // One group of keys: logits for every head (each key row converted once),
+  // then the online softmax update; s becomes the weights p.
+  __device__ __forceinline__ void step(const RowRaw<T, CPT>* kc, const RowRaw<T, CPT>* vc,
+                                       const bool* ok) {
     float s[G][kKeysPerIter];
 #pragma unroll
     for (int j = 0; j < kKeysPerIter; ++j) {
@@ -274,7 +323,6 @@ __device__ __forceinline__ void attend_rows_body(const AttendArgs& a, const Rows
         s[g][j] = ok[j] ? r : -INFINITY;
       }
     }
-    // online softmax update per head; s becomes the weights p
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float mx = m[g];
@@ -304,198 +352,211 @@ __device__ __forceinline__ void attend_rows_body(const AttendArgs& a, const Rows
     }
   }
 
-  // ---------------------------------------------------------- merge 16 key lanes
-  __shared__ float sm_m[16][G], sm_l[16][G];
-  __shared__ float sm_o[16][G][D];
+  // Merge of the 16 key lanes, then of the n_splits workgroups of the row
+  // (split-K): each publishes its partial (max, sum, row) with device-scope
+  // stores and counts itself in on merge_count; the last to arrive clears
+  // the counter and the n_reset ints at reset (the fused step's row state),
+  // merges every partial in split order and writes the output.  stale: the
+  // selection never arrived, the row gets NaN.
+  __device__ __forceinline__ void finish(int split, int n_splits, int* merge_count, int* reset,
+                                         int n_reset, bool stale) {
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    if (seg == 0) {
-      sm_m[kl][g] = m[g];
-      sm_l[kl][g] = l[g];
+    for (int g = 0; g < G; ++g) {
+      if (seg == 0) {
+        sh.sm_m[kl][g] = m[g];
+        sh.sm_l[kl][g] = l[g];
+      }
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) sh.sm_o[kl][g][seg * CPT + c] = acc[g][c];
     }
+    __syncthreads();
+    constexpr int kOut = (G * D + kRowsThreads - 1) / kRowsThreads;  // outputs per thread
+    float Mv[kOut], Lv[kOut], Ov[kOut];
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) sm_o[kl][g][seg * CPT + c] = acc[g][c];
-  }
-  __syncthreads();
-  constexpr int kOut = (G * D + kRowsThreads - 1) / kRowsThreads;  // outputs per thread
-  float Mv[kOut], Lv[kOut], Ov[kOut];
-#pragma unroll
-  for (int i = 0; i < kOut; ++i) {
-    const int o = tid + i * kRowsThreads;
-    Mv[i] = -INFINITY;
-    Lv[i] = 0.f;
-    Ov[i] = 0.f;
-    if (o >= G * D) continue;
-    const int g = o / D, col = o % D;
-    for (int r = 0; r < 16; ++r) Mv[i] = fmaxf(Mv[i], sm_m[r][g]);
-    if (Mv[i] != -INFINITY) {
-      for (int r = 0; r < 16; ++r) {
-        const float w = __builtin_amdgcn_exp2f(sm_m[r][g] - Mv[i]);
-        Lv[i] = fmaf(sm_l[r][g], w, Lv[i]);
-        Ov[i] = fmaf(sm_o[r][g][col], w, Ov[i]);
+    for (int i = 0; i < kOut; ++i) {
+      const int o = tid + i * kRowsThreads;
+      Mv[i] = -INFINITY;
+      Lv[i] = 0.f;
+      Ov[i] = 0.f;
+      if (o >= G * D) continue;
+      const int g = o / D, col = o % D;
+      for (int r = 0; r < 16; ++r) Mv[i] = fmaxf(Mv[i], sh.sm_m[r][g]);
+      if (Mv[i] != -INFINITY) {
+        for (int r = 0; r < 16; ++r) {
+          const float w = __builtin_amdgcn_exp2f(sh.sm_m[r][g] - Mv[i]);
+          Lv[i] = fmaf(sh.sm_l[r][g], w, Lv[i]);
+          Ov[i] = fmaf(sh.sm_o[r][g][col], w, Ov[i]);
+        }
       }
     }
-  }
-
-  if (stale) {
+    if (stale) {
 #pragma unroll
-    for (int i = 0; i < kOut; ++i) Mv[i] = Lv[i] = Ov[i] = __builtin_nanf("");
-  }
+      for (int i = 0; i < kOut; ++i) Mv[i] = Lv[i] = Ov[i] = __builtin_nanf("");
+    }
 
-  // ---------------------------------------------------------- split-K merge
-  const int splits = job.n_splits;
-  const int64_t qh0 = (int64_t)bi * a.Hq + (int64_t)h * G;
-  if (splits > 1) {
+    const int splits = n_splits;
+    const int64_t qh0 = (int64_t)bi * a.Hq + (int64_t)h * G;
+    if (splits > 1) {
+#pragma unroll
+      for (int i = 0; i < kOut; ++i) {
+        const int o = tid + i * kRowsThreads;
+        if (o >= G * D) continue;
+        const int g = o / D, col = o % D;
+        const int64_t row = ((int64_t)split * a.batch * a.Hq + qh0 + g) * a.n_pos + pos;
+        st_dev(a.ws_o + row * D + col, Ov[i]);
+        if (col == 0) {
+          st_dev(a.ws_ml + 2 * row, Mv[i]);
+          st_dev(a.ws_ml + 2 * row + 1, Lv[i]);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __syncthreads();
+      if (tid == 0) {
+        const int done =
+            __hip_atomic_fetch_add(merge_count, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sh.last = done == splits - 1;
+      }
+      __syncthreads();
+      if (!sh.last) return;
+      // every workgroup of the row has counted in (and is past everything it
+      // does before that): the row's counters are ready for the next call
+      if (tid == 0) __hip_atomic_store(merge_count, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (tid < n_reset) __hip_atomic_store(reset + tid, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // Merge every split's published rows (this one's included).  Each
+      // thread's (max, sum) pairs and its output columns' first batch of
+      // split values are requested together: one memory round trip when the
+      // splits fit a batch.  The (max, sum) table is padded to kMaxSplits
+      // with (-inf, 0), so the weight pass and the weighted sums run without
+      // per-split branches (padding weights are 0 and padding loads return 0).
+      float* sm_w = &sh.sm_o[0][0][0];               // reuse: [kMaxSplits][G] weights
+      float* sm_sl = sm_w + kMaxSplits * G;          // [kMaxSplits][G] sums
+      constexpr int kMlPer = (kMaxSplits * G + kRowsThreads - 1) / kRowsThreads;
+      constexpr int kBatch = kOut <= 2 ? 32 : (kOut <= 64 ? 64 / kOut : 1);  // splits per batch
+      static_assert(kMaxSplits <= 64 && kMaxSplits % kBatch == 0, "one split per lane of wave 0");
+      const int64_t stride = (int64_t)a.batch * a.Hq * a.n_pos * D;   // between splits
+      float mlm[kMlPer], mll[kMlPer];
+#pragma unroll
+      for (int j = 0; j < kMlPer; ++j) {
+        const int idx = tid + j * kRowsThreads;
+        const int s = idx / G, g = idx % G;
+        const int64_t row = ((int64_t)s * a.batch * a.Hq + qh0 + g) * a.n_pos + pos;
+        mlm[j] = idx < splits * G ? ld_dev(a.ws_ml + 2 * row) : -INFINITY;
+        mll[j] = idx < splits * G ? ld_dev(a.ws_ml + 2 * row + 1) : 0.f;
+      }
+      // Output columns through a buffer resource that ends at the last
+      // split: loads of splits beyond it return 0, so a batch is issued
+      // without branches (byte offsets fit 32 bits: the plans keep the
+      // partial rows below 4 GiB).
+      const __amdgpu_buffer_rsrc_t ro = dev_rsrc(a.ws_o, (uint32_t)(splits * stride * 4));
+      float vbuf[kOut][kBatch];
+      auto load_batch = [&](int s0) {
+#pragma unroll
+        for (int i = 0; i < kOut; ++i) {
+          const int o = tid + i * kRowsThreads;
+          const int g = (o < G * D ? o : 0) / D, col = o % D;
+          const uint32_t off = (uint32_t)(((qh0 + g) * a.n_pos + pos) * D + col);
+#pragma unroll
+          for (int j = 0; j < kBatch; ++j)
+            vbuf[i][j] = ld1_dev(ro, (off + (uint32_t)((s0 + j) * stride)) * 4u);
+        }
+      };
+      load_batch(0);
+#pragma unroll
+      for (int j = 0; j < kMlPer; ++j) {
+        const int idx = tid + j * kRowsThreads;
+        if (idx < kMaxSplits * G) {
+          sm_w[idx] = mlm[j];
+          sm_sl[idx] = mll[j];
+        }
+      }
+      __syncthreads();
+      // wave 0, one split per lane: M = max_s m_s, w_s = 2^(m_s - M),
+      // L = sum_s l_s w_s (fixed reduction tree)
+      if (tid < 64) {
+        float mv[G], lv[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          mv[g] = sm_w[lane * G + g];
+          lv[g] = sm_sl[lane * G + g];
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float M = wave_max_f32(mv[g]);
+          const float w = mv[g] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mv[g] - M);
+          const float Ls = wave_sum_f32(lv[g] * w);
+          sm_w[lane * G + g] = w;
+          if (lane == 0) {
+            sh.sm_M[g] = M;
+            sh.sm_L[g] = Ls;
+          }
+        }
+      }
+      __syncthreads();
+      float Os[kOut];
+#pragma unroll
+      for (int i = 0; i < kOut; ++i) Os[i] = 0.f;
+      for (int s0 = 0; s0 < splits; s0 += kBatch) {
+        if (s0 > 0) load_batch(s0);
+#pragma unroll
+        for (int i = 0; i < kOut; ++i) {
+          const int o = tid + i * kRowsThreads;
+          const int g = (o < G * D ? o : 0) / D;
+#pragma unroll
+          for (int j = 0; j < kBatch; ++j) Os[i] = fmaf(vbuf[i][j], sm_w[(s0 + j) * G + g], Os[i]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kOut; ++i) {
+        const int o = tid + i * kRowsThreads;
+        if (o >= G * D) continue;
+        const int g = o / D;
+        Mv[i] = sh.sm_M[g];
+        Lv[i] = sh.sm_L[g];
+        Ov[i] = Os[i];
+      }
+    }
+    const float nan = __builtin_nanf("");
 #pragma unroll
     for (int i = 0; i < kOut; ++i) {
       const int o = tid + i * kRowsThreads;
       if (o >= G * D) continue;
       const int g = o / D, col = o % D;
-      const int64_t row = ((int64_t)split * a.batch * a.Hq + qh0 + g) * a.n_pos + pos;
-      st_dev(a.ws_o + row * D + col, Ov[i]);
-      if (col == 0) {
-        st_dev(a.ws_ml + 2 * row, Mv[i]);
-        st_dev(a.ws_ml + 2 * row + 1, Lv[i]);
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
-    if (tid == 0) {
-      int* ctr = a.ws_count + row_id;
-      const int done = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      last_sh = done == splits - 1;
-      if (last_sh) {
-        __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        // every split of the row is past its wait: ready for the next call
-        if (job.ready) __hip_atomic_store(const_cast<int*>(job.ready) + row_id, 0,
-                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-    __syncthreads();
-    if (!last_sh) return;
-    // Merge every split's published rows (this one's included).  Each
-    // thread's (max, sum) pairs and its output columns' first batch of split
-    // values are requested together: one memory round trip when the splits
-    // fit a batch.  The (max, sum) table is padded to kMaxSplits with
-    // (-inf, 0), so the weight pass and the weighted sums run without
-    // per-split branches (padding weights are 0 and padding loads return 0).
-    float* sm_w = &sm_o[0][0][0];                  // reuse: [kMaxSplits][G] weights
-    float* sm_sl = sm_w + kMaxSplits * G;          // [kMaxSplits][G] sums
-    constexpr int kMlPer = (kMaxSplits * G + kRowsThreads - 1) / kRowsThreads;
-    constexpr int kBatch = kOut <= 2 ? 32 : (kOut <= 64 ? 64 / kOut : 1);  // splits per batch
-    static_assert(kMaxSplits <= 64 && kMaxSplits % kBatch == 0, "one split per lane of wave 0");
-    const int64_t stride = (int64_t)a.batch * a.Hq * a.n_pos * D;   // between splits
-    float mlm[kMlPer], mll[kMlPer];
-#pragma unroll
-    for (int j = 0; j < kMlPer; ++j) {
-      const int idx = tid + j * kRowsThreads;
-      const int s = idx / G, g = idx % G;
-      const int64_t row = ((int64_t)s * a.batch * a.Hq + qh0 + g) * a.n_pos + pos;
-      mlm[j] = idx < splits * G ? ld_dev(a.ws_ml + 2 * row) : -INFINITY;
-      mll[j] = idx < splits * G ? ld_dev(a.ws_ml + 2 * row + 1) : 0.f;
-    }
-    // Output columns through a buffer resource that ends at the last
-    // split: loads of splits beyond it return 0, so a batch is issued
-    // without branches (the workspace of a split-K launch stays far below
-    // 4 GiB, so byte offsets fit 32 bits).
-    const __amdgpu_buffer_rsrc_t ro = dev_rsrc(a.ws_o, (uint32_t)(splits * stride * 4));
-    float vb[kOut][kBatch];
-    auto load_batch = [&](int s0) {
-#pragma unroll
-      for (int i = 0; i < kOut; ++i) {
-        const int o = tid + i * kRowsThreads;
-        const int g = (o < G * D ? o : 0) / D, col = o % D;
-        const uint32_t base = (uint32_t)(((qh0 + g) * a.n_pos + pos) * D + col);
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j)
-          vb[i][j] = ld1_dev(ro, (base + (uint32_t)((s0 + j) * stride)) * 4u);
-      }
-    };
-    load_batch(0);
-#pragma unroll
-    for (int j = 0; j < kMlPer; ++j) {
-      const int idx = tid + j * kRowsThreads;
-      if (idx < kMaxSplits * G) {
-        sm_w[idx] = mlm[j];
-        sm_sl[idx] = mll[j];
-      }
-    }
-    __syncthreads();
-    // wave 0, one split per lane: M = max_s m_s, w_s = 2^(m_s - M),
-    // L = sum_s l_s w_s (fixed reduction tree)
-    __shared__ float sm_M[G], sm_L[G];
-    if (tid < 64) {
-      float mv[G], lv[G];
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        mv[g] = sm_w[lane * G + g];
-        lv[g] = sm_sl[lane * G + g];
-      }
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float M = wave_max_f32(mv[g]);
-        const float w = mv[g] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mv[g] - M);
-        const float Ls = wave_sum_f32(lv[g] * w);
-        sm_w[lane * G + g] = w;
-        if (lane == 0) {
-          sm_M[g] = M;
-          sm_L[g] = Ls;
-        }
-      }
-    }
-    __syncthreads();
-    float Os[kOut];
-#pragma unroll
-    for (int i = 0; i < kOut; ++i) Os[i] = 0.f;
-    for (int s0 = 0; s0 < splits; s0 += kBatch) {
-      if (s0 > 0) load_batch(s0);
-#pragma unroll
-      for (int i = 0; i < kOut; ++i) {
-        const int o = tid + i * kRowsThreads;
-        const int g = (o < G * D ? o : 0) / D;
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j) Os[i] = fmaf(vb[i][j], sm_w[(s0 + j) * G + g], Os[i]);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < kOut; ++i) {
-      const int o = tid + i * kRowsThreads;
-      if (o >= G * D) continue;
-      const int g = o / D;
-      Mv[i] = sm_M[g];
-      Lv[i] = sm_L[g];
-      Ov[i] = Os[i];
+      const int64_t qh = qh0 + g;
+      T* out = (T*)a.out + (qh * a.out_cap + a.out_off + pos) * D + col;
+      *out = from_f32<T>(valid ? Ov[i] / Lv[i] : nan);
+      if (a.lse && col == 0)
+        a.lse[qh * a.out_cap + a.out_off + pos] = valid ? (Mv[i] + log2f(Lv[i])) * kLn2 : nan;
     }
   }
-#pragma unroll
-  for (int i = 0; i < kOut; ++i) {
-    const int o = tid + i * kRowsThreads;
-    if (o >= G * D) continue;
-    const int g = o / D, col = o % D;
-    const int64_t qh = qh0 + g;
-    T* out = (T*)a.out + (qh * a.out_cap + a.out_off + pos) * D + col;
-    *out = from_f32<T>(Ov[i] / Lv[i]);
-    if (a.lse && col == 0) a.lse[qh * a.out_cap + a.out_off + pos] = (Mv[i] + log2f(Lv[i])) * kLn2;
-  }
-}
+};
 
+// Decode attention (and the fp32 / head-size paths): gridDim.x splits per
+// (position, KV head, sequence) row, each an equal share of the local keys
+// and of the units' keys.  Its first local keys are requested before the
+// selection is read and the unit table formed.
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kRowsThreads) void k_attend_rows(AttendArgs a) {
+  __shared__ RowsShared<G, D> sh;
   const int s = blockIdx.x, n = gridDim.x;
-  const RowsJob job{s, n, (int)blockIdx.y, (int)(blockIdx.z % a.Hkv), (int)(blockIdx.z / a.Hkv),
-                    s, n, s, n, nullptr};
-  attend_rows_body<T, D, G>(a, job);
+  const int pos = blockIdx.y, h = blockIdx.z % a.Hkv, bi = blockIdx.z / a.Hkv;
+  const int64_t row = ((int64_t)bi * a.Hkv + h) * a.n_pos + pos;
+  RowsAttn<T, D, G> r(a, sh, pos, h, bi);
+  r.shares(s, s + 1, n, s, n);
+  int32_t u = -1;   // this thread's sel entry, requested now
+  if (r.valid && threadIdx.x < a.k_m) u = r.sel_row[threadIdx.x];
+  const bool early = r.nl >= RowsAttn<T, D, G>::kGroup;   // first group local only: in flight
+  if (early) r.template fetch<RowsAttn<T, D, G>::kLocal>(0, r.nl);
+  r.build_table(u);
+  r.make_qv();
+  r.stream(0, r.nl + r.nu, early);
+  r.finish(s, n, a.ws_count ? a.ws_count + row : nullptr, nullptr, 0, false);
 }
 
 int rows_num_splits(const AttendArgs& a) {
   // enough workgroups to cover the chip several times, >= ~256 keys each
   const int64_t max_keys = (int64_t)a.n_init + (int64_t)a.k_m * a.B + a.W;
   const int64_t wgs = (int64_t)a.n_pos * a.batch * a.Hkv;
-  int64_t target = 512;
-  if (const char* e = getenv("INFLLM_ROWS_WGS")) {  // tuning override
-    const int v = atoi(e);
-    if (v >= 1 && v <= 65536) target = v;
-  }
+  const int64_t target = tuning().rows_wgs > 0 ? tuning().rows_wgs : 512;
   int64_t s = (target + wgs - 1) / wgs;
   const int64_t cap = (max_keys + 255) / 256;
   if (s > cap) s = cap;
@@ -532,132 +593,369 @@ hipError_t launch_attend_rows(const AttendArgs& a, int splits, hipStream_t st) {
 }
 
 // ------------------------------------------------------------ fused decode step
-// Selection and attention of decode positions in one launch.  A row (one
-// position of one KV head of one sequence) has s_unit unit splits and
-// s_local local splits.  Unit split i first scores units [64i, 64i + 64)
-// of the row (none past the last unit: splits may outnumber the slices)
-// and counts itself in; the last to arrive selects the row, publishes the
-// selection with device-scope stores and sets the row's ready flag; every
-// unit split then waits for the flag and attends its share of the selected
-// units' keys.  A waiting split has itself arrived, so the one it waits on
-// is already running and never waits: the waits end without any
-// assumption on dispatch order (and are bounded all the same: a stale
-// selection gives NaN outputs).  Local splits attend their share of the
-// initial tokens and the window, which need no selection, meanwhile.  The
-// row's merging split clears the flag.
-template <typename T, int D, int G, int SEL>
-__global__ __launch_bounds__(kRowsThreads) void k_select_attend(ScoreArgs s, AttendArgs a,
-                                                                StepPlan p, int* ready) {
-  static_assert(kRowsThreads == kScoreThreads, "one workgroup size for both roles");
-  __shared__ int32_t sel_sm[kMaxTopK];
-  const int tid = threadIdx.x;
-  const int n_unit = a.batch * a.Hkv * a.n_pos * p.s_unit;
-  const bool unit = (int)blockIdx.x < n_unit;
-  const int per = unit ? p.s_unit : p.s_local;
-  const int x = unit ? (int)blockIdx.x : (int)blockIdx.x - n_unit;
-  // row = (sequence * H_kv + KV head) * positions + position; one chunk per position
-  const int row = x / per, part = x % per;
-  const int pos = row % a.n_pos, h = row / a.n_pos % a.Hkv, bi = row / a.n_pos / a.Hkv;
-  if (unit) {
-    if (score_slice<T, G, D, SEL>(part, p.s_unit, pos, h, bi, (const T*)s.q, s.q_cap, s.q_off,
-                                  s.q_pos, s.pos, 1, s.Hq, s.Hkv, s.B, s.n_init, s.W, s.repr, s.U,
-                                  s.scores, s.n_chunks, nullptr, 0, 0, 0, (int*)s.ws, s.k_m,
-                                  sel_sm)) {
-      __syncthreads();
-      int32_t* dst = s.sel + (int64_t)row * s.k_m;
-      for (int m = tid; m < s.k_m; m += kRowsThreads)
-        __hip_atomic_store(dst + m, sel_sm[m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-      __syncthreads();
-      // a row whose position does not fit its KV buffer attends nothing
-      // (every split leaves before waiting), so its flag stays clear
-      const bool valid = !a.pos || seq_pos_ok(seq_base(a.pos, a.q_pos, bi), a.n_pos, a.kv_cap);
-      if (tid == 0 && valid)
-        __hip_atomic_store(ready + row, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-  const int n_splits = p.s_local + p.s_unit;
-  const RowsJob job = unit ? RowsJob{p.s_local + part, n_splits, pos, h, bi, 0, 0, part,
-                                     p.s_unit, ready}
-                           : RowsJob{part, n_splits, pos, h, bi, part, p.s_local, 0, 0, ready};
-  attend_rows_body<T, D, G>(a, job);
+// Scores, selection and attention of decode positions in one launch.  A row
+// (one position of one KV head of one sequence) has p.n_splits workgroups;
+// the first p.s_score of them each score a slice of p.units_per units.
+//
+// A scoring workgroup marks its slice started (a flag), scores it, publishes
+// its candidates -- all of the slice's scores, or its best min(k_m, units)
+// when the row has too many to search at once (the row's top k_m is among
+// the union of every slice's top k_m, ties to the lower index in both) --
+// and sets the slice's bit in the row's arrival mask with an atomic OR.
+// The workgroup whose bit completes the mask selects the row's k_m units
+// from the candidates, publishes them and sets the row's ready flag.
+// Every workgroup of the row (scoring ones after their slice) attends its
+// share of the local keys, which need no selection, then reads the ready
+// flag and attends its share of the selected units' keys.  If the flag is
+// not set yet, it first checks the slices' started flags and scores every
+// slice not started yet itself (publishing the same candidates and setting
+// the same bit, so a slice scored twice is harmless), then waits for it.
+//
+// Why every wait ends: a workgroup waits only after every slice of its row
+// has been started -- by itself, or by workgroups that were running when it
+// looked -- and scoring a slice (and selecting, for the one that completes
+// the mask) never waits on anything, so every bit of the mask gets set and
+// the selection is published.  This holds whatever the dispatch order, the grid size
+// or the number of workgroups resident at once, and needs no atomic at the
+// start of the launch.  All workgroups then publish their partial rows; the
+// last to arrive merges them and clears the row's mask, flags and counter
+// for the next call.
+struct StepRow {
+  uint64_t* mask;      // arrival mask of the slices
+  int* ready;          // the selection is published
+  int* merge;          // merge counter
+  uint8_t* started;    // one byte per slice
+};
+__device__ __forceinline__ StepRow step_row(const StepPtrs& w, int64_t row) {
+  int* base = w.sync + row * kStepSyncInts;
+  return StepRow{(uint64_t*)base, base + 2, base + 3, (uint8_t*)(base + 4)};
 }
 
-// workgroups of k_select_attend resident at once: 3 per CU (its LDS and
-// registers allow 3) on the 256 CUs
-constexpr int64_t kStepResidentWGs = 3 * 256;
+// LDS of the scoring and selection parts of a fused step (one copy per
+// workgroup, shared by both).
+struct StepShared {
+  double qsum[128];
+  float sc[4 * kUnitsPerWG];
+  int32_t pick[kMaxTopK];
+  TopkShared tsm;
+  uint64_t todo;
+  int last;
+};
+
+// The row's selection from its s_score * C published candidates (candidate
+// order is ascending unit order, so positions map to ascending unit ids):
+// entry m for thread m < k_m.  Every thread calls it.
+template <int VPT>
+__device__ __forceinline__ int32_t step_select(const ScoreArgs& s, const StepPlan& p, int row,
+                                               const StepPtrs& w, StepShared& ss) {
+  const int64_t c0 = (int64_t)row * p.s_score * p.cand;
+  __syncthreads();   // the scratch may still be read by an earlier part
+  block_topk<kRowsThreads / 64, VPT, true>(w.cand_s + c0, p.s_score * p.cand, s.k_m, ss.pick,
+                                           ss.tsm);
+  __syncthreads();
+  const int tid = threadIdx.x;
+  const int pp = tid < s.k_m ? ss.pick[tid] : -1;
+  return pp >= 0 ? __hip_atomic_load(w.cand_i + c0 + pp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                 : -1;
+}
+
+// One slice's scores, candidates and arrival bit.  SERIAL: the slice's
+// 64-unit parts are loaded one after another (fewer registers; for the rare
+// scoring of a slice that was not started).
+template <typename T, int G, int D, int NSUB, bool SERIAL>
+__device__ __forceinline__ void step_score(const ScoreArgs& s, const StepPlan& p, int sl, int row,
+                                           int pos, int h, int bi, const StepRow& y,
+                                           const StepPtrs& w, StepShared& ss) {
+  using Rows = UnitRows<D, kUnitsPerWG / UnitRows<D, 1>::kPerSlot>;   // 64 units
+  static_assert(D <= 128 && NSUB <= 4, "StepShared sizes");
+  double* qsum = ss.qsum;
+  float* sc_sm = ss.sc;
+  int32_t* pick_sm = ss.pick;
+  TopkShared& tsm = ss.tsm;
+  const int tid = threadIdx.x;
+  const int U = s.U;
+  const int u0 = sl * p.units_per;
+  const int u1 = u0 + p.units_per < U ? u0 + p.units_per : U;
+  const float* rb = s.repr + ((int64_t)bi * s.Hkv + h) * U * D;
+  constexpr int kHeld = SERIAL ? 1 : NSUB;   // 64-unit parts whose rows are held at once
+  Rows rows[kHeld];
+#pragma unroll
+  for (int j = 0; j < kHeld; ++j) rows[j].load(rb, U, u0 + j * kUnitsPerWG);   // in flight
+  // the group's query sum for this position (fp64, heads in order)
+  if (tid < D) {
+    const T* qb = (const T*)s.q +
+                  (((int64_t)bi * s.Hq + (int64_t)h * G) * s.q_cap + s.q_off + pos) * D + tid;
+    T v[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) v[g] = qb[(int64_t)g * s.q_cap * D];
+    double acc = 0.0;
+#pragma unroll
+    for (int g = 0; g < G; ++g) acc += (double)to_f32(v[g]);
+    qsum[tid] = acc;
+  }
+  __syncthreads();
+  // a position out of range leaves no unit eligible (negative) or all of
+  // them (large); the clamp keeps the sum below overflow
+  int64_t t0 = seq_base(s.pos, s.q_pos, bi);
+  t0 = t0 < -kPosLimit ? -kPosLimit : (t0 > kPosLimit ? kPosLimit : t0);
+  const int64_t e = eligible_units(t0 + pos, U, s.B, s.n_init, s.W);
+  const int cg = tid % 64 % (D / 8);
+  double qv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) qv[j] = qsum[cg * 8 + j];
+  float* sb = s.scores + (int64_t)row * U;
+  if constexpr (SERIAL) {
+    for (int j = 0; j < NSUB; ++j) {
+      if (j > 0) rows[0].load(rb, U, u0 + j * kUnitsPerWG);
+      rows[0].score_lds(qv, u0 + j * kUnitsPerWG, u1, e, sb, sc_sm, u0);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NSUB; ++j) rows[j].score_lds(qv, u0 + j * kUnitsPerWG, u1, e, sb, sc_sm, u0);
+  }
+  __syncthreads();
+  // candidates: the slice's best C units (all of them if it holds at most C)
+  const int n = u1 - u0, C = p.cand;
+  const int64_t slot = ((int64_t)row * p.s_score + sl) * C;
+  if (n > C) {
+    block_topk<kRowsThreads / 64, 1, false>(sc_sm, n, C, pick_sm, tsm);
+    __syncthreads();
+  }
+  for (int m = tid; m < C; m += kRowsThreads) {
+    const int idx = n > C ? pick_sm[m] : (m < n ? m : -1);
+    st_dev(w.cand_s + slot + m, idx >= 0 ? sc_sm[idx] : -INFINITY);
+    __hip_atomic_store(w.cand_i + slot + m, idx >= 0 ? u0 + idx : -1, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  if (tid == 0)
+    __hip_atomic_fetch_or(y.mask, 1ull << sl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Scores every slice of the row not started yet (the check that makes a
+// wait safe), then waits until `done` holds, polling `flag`; returns false
+// (and counts the time-out in the status word) if the bound ran out.
+// Every thread calls it.
+template <typename T, int G, int D, int NSUB, int VPT, typename Done>
+__device__ __forceinline__ bool step_wait(const ScoreArgs& s, const StepPlan& p, int row, int pos,
+                                          int h, int bi, const StepRow& y, const StepPtrs& w,
+                                          StepShared& ss, const Done& done) {
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    const uint64_t mk = __hip_atomic_load(y.mask, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool todo = tid < p.s_score && !((mk >> tid) & 1) &&
+                      __hip_atomic_load(y.started + tid, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT) == 0;
+    const uint64_t b = __ballot(todo);
+    if (tid == 0) ss.todo = b;
+  }
+  __syncthreads();
+  uint64_t todo = ss.todo;
+  while (todo) {
+    const int sl = __builtin_ctzll(todo);
+    todo &= todo - 1;
+    if (tid == 0)
+      __hip_atomic_store(y.started + sl, (uint8_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    step_score<T, G, D, NSUB, true>(s, p, sl, row, pos, h, bi, y, w, ss);
+  }
+  if (tid == 0) {
+    int ok = 0;
+    for (int it = 0; it < kSpinLimit && !ok; ++it) {
+      ok = done();
+      if (!ok) __builtin_amdgcn_s_sleep(2);
+    }
+    if (!ok) __hip_atomic_fetch_add(w.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    ss.last = ok;
+  }
+  __syncthreads();
+  return ss.last;
+}
+
+template <typename T, int D, int G, int NSUB, int VPT>
+__global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(3)))
+void k_select_attend(ScoreArgs s, AttendArgs a, StepPlan p, StepPtrs w) {
+  static_assert(kRowsThreads == kScoreThreads, "one workgroup size for both roles");
+  __shared__ RowsShared<G, D> sh;
+  __shared__ StepShared ss;
+  const int N = p.n_splits, S = p.s_score;
+  // row = (sequence * H_kv + KV head) * positions + position; one chunk per
+  // position.  Workgroup N of a row is its selector.
+  const int row = (int)blockIdx.x / (N + 1), j = (int)blockIdx.x % (N + 1);
+  const int pos = row % a.n_pos, h = row / a.n_pos % a.Hkv, bi = row / a.n_pos / a.Hkv;
+  const StepRow y = step_row(w, row);
+  const int tid = threadIdx.x;
+  const uint64_t full = S == 64 ? ~0ull : (1ull << S) - 1ull;
+  auto mask_full = [&]() {
+    return __hip_atomic_load(y.mask, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == full;
+  };
+  if (j == N) {
+    // the selector: waits for the mask (a bounded spin first, during which
+    // the row's scorers normally finish; then the check that makes the
+    // wait safe), selects and publishes the row's units
+    if (tid == 0) {
+      int ok = 0;
+      for (int it = 0; it < kPreSpin && !ok; ++it) {
+        ok = mask_full();
+        if (!ok) __builtin_amdgcn_s_sleep(2);
+      }
+      ss.last = ok;
+    }
+    __syncthreads();
+    const bool ok = ss.last || step_wait<T, G, D, NSUB, VPT>(s, p, row, pos, h, bi, y, w, ss,
+                                                             mask_full);
+    const int32_t u = ok ? step_select<VPT>(s, p, row, w, ss) : -1;
+    if (tid < s.k_m)
+      __hip_atomic_store(s.sel + (int64_t)row * s.k_m + tid, u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(y.ready, ok ? 1 : -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  if (j < S) {
+    if (tid == 0)
+      __hip_atomic_store(y.started + j, (uint8_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    step_score<T, G, D, NSUB, false>(s, p, j, row, pos, h, bi, y, w, ss);
+  }
+  RowsAttn<T, D, G> r(a, sh, pos, h, bi);
+  const int64_t l_lo = j < S ? (int64_t)j * p.w_score
+                             : (int64_t)S * p.w_score + (int64_t)(j - S) * p.w_unit;
+  r.shares(l_lo, l_lo + (j < S ? p.w_score : p.w_unit),
+           (int64_t)S * p.w_score + (int64_t)(N - S) * p.w_unit, j, N);
+  r.make_qv();
+  // the local keys need no selection
+  r.template stream<RowsAttn<T, D, G>::kLocal>(0, r.nl, false);
+  r.park();
+  if (tid == 0) sh.flag = __hip_atomic_load(y.ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  int rd = sh.flag;
+  if (rd == 0) {
+    // not published yet: make sure every slice is being scored, then wait
+    auto ready = [&]() {
+      return __hip_atomic_load(y.ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+    };
+    rd = step_wait<T, G, D, NSUB, VPT>(s, p, row, pos, h, bi, y, w, ss, ready) ? 1 : -1;
+    if (rd == 1) {
+      if (tid == 0) sh.flag = __hip_atomic_load(y.ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      rd = sh.flag;
+    }
+  }
+  const bool stale = rd != 1;
+  // the row's units, then their keys
+  int32_t u = -1;
+  if (!stale && r.valid && tid < a.k_m)
+    u = __hip_atomic_load(const_cast<int32_t*>(r.sel_row + tid), __ATOMIC_RELAXED,
+                          __HIP_MEMORY_SCOPE_AGENT);
+  r.restore();
+  r.build_table(u);
+  r.template stream<RowsAttn<T, D, G>::kUnits>(r.nl, r.nl + r.nu, false);
+  r.finish(j, N, y.merge, w.sync + (int64_t)row * kStepSyncInts, kStepSyncInts, stale);
+}
+
+// Plan of a fused step.  At most kStepTargetWGs workgroups per launch (3 per
+// CU, so that all of them are resident at once), a selector and n_splits
+// attention workgroups per row.  Scoring workgroups take the fewest units (64 .. 256) that leave
+// at least a sixteenth of a row's workgroups without a slice; every
+// workgroup takes an equal share of the units' keys, and the local keys
+// are shared so that every workgroup moves about the same number of bytes.
+constexpr int64_t kStepTargetWGs = 768;
+constexpr int kStepMaxCand = 8 * kRowsThreads;   // candidates of a row: 8 per lane
+
+int64_t step_rows(const AttendArgs& a) { return (int64_t)a.batch * a.Hkv * a.n_pos; }
 
 bool select_attend_plan(const ScoreArgs& s, const AttendArgs& a, StepPlan* p) {
-  const int64_t rows = (int64_t)a.batch * a.Hkv * a.n_pos;
-  const int n_slices = (s.U + kUnitsPerWG - 1) / kUnitsPerWG;
-  if (!a.bf16 || a.L != 1 || s.U < 1 || a.k_m < 1 || a.k_m > kMaxTopK || n_slices > kMaxSelSlices)
-    return false;
+  if (!a.bf16 || a.L != 1 || s.U < 1 || a.k_m < 1 || a.k_m > kMaxTopK) return false;
   const int G = a.Hq / a.Hkv;
-  if (G > kDirectRows || (G != 1 && G != 2 && G != 4 && G != 8)) return false;
-  // about 256 workgroups on each key set, >= ~256 keys each; at least one
-  // unit split per scoring slice
-  const int64_t each = (256 + rows - 1) / rows;
-  int64_t sl = each, su = each;
-  if (const char* e = getenv("INFLLM_STEP_LOCAL_SPLITS")) {   // tuning override
-    const int v = atoi(e);
-    if (v >= 1 && v <= kMaxSplits) sl = v;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return false;
+  const int64_t rows = step_rows(a);
+  if (rows > ((int64_t)1 << 24)) return false;
+  int64_t n = kStepTargetWGs / rows - 1;   // attention workgroups (the selector is one more)
+  if (tuning().step_splits > 0) n = tuning().step_splits;
+  n = n < 2 ? 2 : (n > kMaxSplits ? kMaxSplits : n);
+  int up = 0;
+  int64_t S = 0;
+  for (int c = kUnitsPerWG; c <= 4 * kUnitsPerWG; c += kUnitsPerWG) {
+    up = c;
+    S = (s.U + c - 1) / c;
+    if (S <= n - (n / 16 > 1 ? n / 16 : 1)) break;
   }
-  const int64_t cap_l = ((int64_t)a.n_init + a.W + 255) / 256;
-  const int64_t cap_u = ((int64_t)a.k_m * a.B + 255) / 256;
-  sl = sl < cap_l ? sl : cap_l;
-  sl = sl < 1 ? 1 : sl;
-  su = su < cap_u ? su : cap_u;
-  su = su < kMaxSplits / 2 ? su : kMaxSplits / 2;
-  su = su > n_slices ? su : n_slices;
-  if (sl + su > kMaxSplits) sl = kMaxSplits - su;
-  // the whole launch resident at once where it can be: split counts past
-  // that left a last round of local splits to start late (measured at 128K:
-  // 8 local splits 40.4 us per step, 10 splits 47.8 us)
-  const int64_t fit = kStepResidentWGs / rows - su;
-  if (sl > fit) sl = fit;
-  if (sl < 1) sl = 1;
-  if (sl + su > kMaxSplits) return false;
-  if (rows * (su + sl) > (int64_t)1 << 30) return false;
-  p->n_slices = n_slices;
-  p->s_local = (int)sl;
-  p->s_unit = (int)su;
+  if (S >= n) n = S + (S / 16 > 1 ? S / 16 : 1);
+  if (n > kMaxSplits) return false;
+  // every score is a candidate when the row has few enough of them.  Rows
+  // with more take the separate calls unless the split count is set by
+  // hand: the first cut of candidates in every slice makes the one launch
+  // slower than the scoring, selection and attention launches there
+  // (measured at 8,191 units: 49.8 against 44.5 us per step).
+  const bool all_scores = S * up <= kStepMaxCand;
+  if (!all_scores && tuning().step_splits == 0) return false;
+  const int C = all_scores ? up : (a.k_m < up ? a.k_m : up);
+  if (S * C > kStepMaxCand) return false;
+  // partial rows are addressed with 32-bit byte offsets in the merge
+  if ((double)n * a.batch * a.Hq * a.n_pos * a.d * 4.0 >= 4294967296.0) return false;
+  // bytes per workgroup: scoring ones move up*(d+1)*4 more, counted twice
+  // (scoring is a latency chain ahead of their local keys, measured to
+  // leave them behind the others at equal bytes)
+  const double esz = 2.0;
+  const double rb = 2.0 * (double)up * (a.d + 1) * 4.0;
+  const double ut = (double)a.k_m * a.B * 2.0 * a.d * esz;
+  const double lt = (double)(a.n_init + a.W) * 2.0 * a.d * esz;
+  const double each = ((double)S * rb + lt + ut) / (double)n;
+  double x = each - ut / (double)n - rb;   // local bytes of a scoring workgroup
+  double y = each - ut / (double)n;        // ... of the others
+  if (x < 0) {
+    x = 0;
+    y = lt / (double)(n - S);
+  }
+  p->n_splits = (int)n;
+  p->s_score = (int)S;
+  p->units_per = up;
+  p->cand = C;
+  p->w_score = (int)(x / 1024.0 + 0.5);
+  p->w_unit = (int)(y / 1024.0 + 0.5);
+  if (p->w_score + p->w_unit == 0) p->w_unit = 1;
   return true;
 }
 
-int64_t select_attend_sync_ints(const AttendArgs& a) {
-  return (int64_t)a.batch * a.Hkv * a.n_pos;   // ready flags
+template <int D, int G, int NSUB>
+static hipError_t launch_step_dgn(const ScoreArgs& s, const AttendArgs& a, const StepPlan& p,
+                                  const StepPtrs& w, hipStream_t st) {
+  const dim3 grid((unsigned)(step_rows(a) * (p.n_splits + 1)));
+  static_assert(kStepMaxCand <= 8 * kRowsThreads, "candidate keys per lane");
+  k_select_attend<bf16_t, D, G, NSUB, 8><<<grid, kRowsThreads, 0, st>>>(s, a, p, w);
+  return hipGetLastError();
 }
 
 template <int D, int G>
 static hipError_t launch_step_dg(const ScoreArgs& s, const AttendArgs& a, const StepPlan& p,
-                                 int* ready, hipStream_t st) {
-  const int64_t rows = (int64_t)a.batch * a.Hkv * a.n_pos;
-  const dim3 grid((unsigned)(rows * (p.s_local + p.s_unit)));
-  // keys per lane of the 4-wave search: ceil(U / 256) <= 8
-  static_assert(kMaxSelSlices * kUnitsPerWG <= 8 * kScoreThreads, "keys per lane");
-  if (s.U <= 4 * kScoreThreads)
-    k_select_attend<bf16_t, D, G, 4><<<grid, kRowsThreads, 0, st>>>(s, a, p, ready);
-  else
-    k_select_attend<bf16_t, D, G, 8><<<grid, kRowsThreads, 0, st>>>(s, a, p, ready);
-  return hipGetLastError();
-}
-
-template <int D>
-static hipError_t launch_step_d(const ScoreArgs& s, const AttendArgs& a, const StepPlan& p,
-                                int* ready, hipStream_t st) {
-  switch (a.Hq / a.Hkv) {
-    case 1: return launch_step_dg<D, 1>(s, a, p, ready, st);
-    case 2: return launch_step_dg<D, 2>(s, a, p, ready, st);
-    case 4: return launch_step_dg<D, 4>(s, a, p, ready, st);
-    case 8: return launch_step_dg<D, 8>(s, a, p, ready, st);
+                                 const StepPtrs& w, hipStream_t st) {
+  switch (p.units_per / kUnitsPerWG) {
+    case 1: return launch_step_dgn<D, G, 1>(s, a, p, w, st);
+    case 2: return launch_step_dgn<D, G, 2>(s, a, p, w, st);
+    case 3: return launch_step_dgn<D, G, 3>(s, a, p, w, st);
+    case 4: return launch_step_dgn<D, G, 4>(s, a, p, w, st);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_select_attend(const ScoreArgs& s, const AttendArgs& a, const StepPlan& p,
-                                int* ready, hipStream_t st) {
+template <int D>
+static hipError_t launch_step_d(const ScoreArgs& s, const AttendArgs& a, const StepPlan& p,
+                                const StepPtrs& w, hipStream_t st) {
+  switch (a.Hq / a.Hkv) {
+    case 1: return launch_step_dg<D, 1>(s, a, p, w, st);
+    case 2: return launch_step_dg<D, 2>(s, a, p, w, st);
+    case 4: return launch_step_dg<D, 4>(s, a, p, w, st);
+    case 8: return launch_step_dg<D, 8>(s, a, p, w, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_select_attend(const ScoreArgs& s, AttendArgs a, const StepPlan& p,
+                                const StepPtrs& w, hipStream_t st) {
   if (a.n_pos <= 0) return hipSuccess;
-  return a.d == 128 ? launch_step_d<128>(s, a, p, ready, st) : launch_step_d<64>(s, a, p, ready, st);
+  a.ws_count = nullptr;   // the merge counts on the rows' sync ints
+  return a.d == 128 ? launch_step_d<128>(s, a, p, w, st) : launch_step_d<64>(s, a, p, w, st);
 }
 
 }  // namespace infllm

@@ -404,7 +404,6 @@ static void build_blocks(const BuildArgs& a, int64_t* jb0, int64_t* nbl) {
 struct BuildWs {
   size_t s, bp, s32;
 };
-static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 static BuildWs build_ws_layout(const BuildArgs& a, int64_t nbl) {
   BuildWs w;
   w.s = a.block_qsum ? 0 : round256((size_t)a.batch * a.Hkv * nbl * a.d * sizeof(double));

@@ -76,6 +76,27 @@ __device__ __forceinline__ void nan_rows(T* out, float* lse, int64_t qh0, int n_
   }
 }
 
+// A selection is a set of units (the working context is a set of keys): an
+// id repeated in one row of a selection counts once.  Every thread of the
+// workgroup calls this (it synchronises); thread m < n passes entry m (u;
+// -1 = empty slot) and gets u back, or -1 if an earlier entry holds the
+// same id.  ids_sm: LDS for n ids.  Ascending ids (what the top-k calls
+// write) are recognised with one comparison per entry; other orders pay a
+// scan of the earlier entries.
+__device__ __forceinline__ int32_t drop_repeats(int32_t u, int m, int n, int32_t* ids_sm) {
+  if (m < n) ids_sm[m] = u;
+  __syncthreads();
+  const bool asc = !(m < n && m > 0 && u >= 0) || (ids_sm[m - 1] >= 0 && ids_sm[m - 1] < u);
+  if (__syncthreads_count(!asc) > 0 && m < n && u >= 0) {
+    for (int j = 0; j < m; ++j)
+      if (ids_sm[j] == u) {
+        u = -1;
+        break;
+      }
+  }
+  return u;
+}
+
 // Eight consecutive columns of a row, raw bits, widened to fp64 on use.
 template <typename T> struct Raw8;
 template <> struct Raw8<bf16_t> {

@@ -4,11 +4,34 @@
 #include "../../include/infllm.h"
 
 #include <hip/hip_runtime.h>
+#include <stdlib.h>
 
 #include "common.h"
 #include "kernels.h"
 
 using namespace infllm;
+
+namespace infllm {
+
+// Read once per process, so that workspace sizes and launch shapes cannot
+// change between sizing a workspace and the calls that use it.
+const Tuning& tuning() {
+  static const Tuning t = [] {
+    auto get = [](const char* name, int lo, int hi) {
+      const char* e = getenv(name);
+      const int v = e ? atoi(e) : 0;
+      return v >= lo && v <= hi ? v : 0;
+    };
+    Tuning x{};
+    x.prefill_splits = get("INFLLM_PREFILL_SPLITS", 1, 16);
+    x.rows_wgs = get("INFLLM_ROWS_WGS", 1, 65536);
+    x.step_splits = get("INFLLM_STEP_SPLITS", 2, 64);
+    return x;
+  }();
+  return t;
+}
+
+}  // namespace infllm
 
 namespace {
 
@@ -98,11 +121,10 @@ void attend_plan(const AttendArgs& a, bool* mfma, int* splits) {
   *splits = *mfma ? prefill_num_splits(a) : rows_num_splits(a);
 }
 
-size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-// Attention workspace: [split-K counters][partial outputs][partial (max, sum)].
+// Attention workspace: [header][split-K counters][partial outputs][partial
+// (max, sum)].
 struct AttendWs {
-  size_t count_bytes, o_bytes, ml_bytes;
+  size_t count_bytes, o_bytes, ml_bytes;   // count_bytes: header + counter region
   size_t total() const { return count_bytes + o_bytes + ml_bytes; }
 };
 
@@ -115,7 +137,7 @@ AttendWs attend_ws_layout(const AttendArgs& a) {
   const size_t rows =
       (size_t)splits * (mfma ? (size_t)prefill_partial_rows(a) : (size_t)a.batch * a.Hq * a.n_pos);
   const int64_t counters = mfma ? prefill_num_counters(a) : rows_num_counters(a);
-  w.count_bytes = round256((size_t)counters * sizeof(int));
+  w.count_bytes = kWsHeaderBytes + ws_counter_region((size_t)counters * sizeof(int));
   w.o_bytes = round256(rows * a.d * sizeof(float));
   w.ml_bytes = rows * 2 * sizeof(float);
   return w;
@@ -123,16 +145,18 @@ AttendWs attend_ws_layout(const AttendArgs& a) {
 
 size_t attend_ws_bytes(const AttendArgs& a) { return attend_ws_layout(a).total(); }
 
-// Decode step workspace.  Fused: [ready flags][selection
-// counters][attention counters, partials of s_local + s_unit splits].
-// Separate calls: [selection workspace][attention workspace].  Sized for
-// the larger of the two.
+// Decode step workspace.  Fused: [header][counter region: per-row sync
+// ints][candidate scores][candidate ids][partial rows of n_splits
+// splits][(max, sum)].  Separate calls: [header][counter region: selection
+// counters, then attention counters][attention partial rows][(max, sum)].
+// Sized for the larger of the two; both keep every counter in the region.
 struct StepWs {
   bool fused;
   StepPlan plan;
-  size_t sync_bytes, sel_bytes;   // fused: ready flags, selection counters
-  AttendWs att;                   // fused attention part
-  size_t sep_sel_bytes;           // separate calls: selection workspace
+  size_t sync_bytes;              // header + counter region (either form)
+  size_t cand_bytes;              // fused: candidate scores, then ids
+  AttendWs att;                   // partial rows and (max, sum) (count_bytes 0)
+  size_t sep_sel_count;           // separate calls: bytes of selection counters
   size_t total;
 };
 
@@ -142,22 +166,58 @@ StepWs step_ws_layout(const infllm_config* c, int32_t batch, int32_t n_pos, int3
   sa.U = n_units;
   sa.k_m = c->top_k;
   const AttendArgs aa = attend_args(c, batch, 1, n_pos);
-  w.sep_sel_bytes = round256(select_workspace_bytes(sa));
-  const size_t sep = w.sep_sel_bytes + attend_ws_bytes(aa);
   w.fused = select_attend_plan(sa, aa, &w.plan);
-  size_t fused = 0;
   if (w.fused) {
-    const size_t rows = (size_t)batch * c->n_kv_heads * n_pos;
-    w.sync_bytes = round256((size_t)select_attend_sync_ints(aa) * sizeof(int));
-    w.sel_bytes = round256(rows * sizeof(int));
-    const size_t prow = (size_t)(w.plan.s_local + w.plan.s_unit) * batch * c->n_q_heads * n_pos;
-    w.att.count_bytes = round256(rows * sizeof(int));
+    const size_t rows = (size_t)step_rows(aa);
+    const size_t cands = rows * w.plan.s_score * w.plan.cand;
+    w.sync_bytes = kWsHeaderBytes + ws_counter_region(rows * kStepSyncInts * sizeof(int));
+    w.cand_bytes = round256(cands * sizeof(float)) + round256(cands * sizeof(int));
+    const size_t prow = (size_t)w.plan.n_splits * batch * c->n_q_heads * n_pos;
     w.att.o_bytes = round256(prow * c->head_dim * sizeof(float));
     w.att.ml_bytes = prow * 2 * sizeof(float);
-    fused = w.sync_bytes + w.sel_bytes + w.att.total();
+  } else {
+    w.sep_sel_count = round256((size_t)batch * c->n_kv_heads * n_pos * sizeof(int));
+    const AttendWs at = attend_ws_layout(aa);
+    const size_t at_count = at.count_bytes > 0 ? (size_t)rows_num_counters(aa) * sizeof(int) : 0;
+    w.sync_bytes = kWsHeaderBytes + ws_counter_region(w.sep_sel_count + at_count);
+    w.att.o_bytes = at.o_bytes;
+    w.att.ml_bytes = at.ml_bytes;
   }
-  w.total = sep > fused ? sep : fused;
+  w.att.count_bytes = 0;
+  w.total = w.sync_bytes + w.cand_bytes + w.att.total();
   return w;
+}
+
+// Counter region [begin, end) of a call's workspace (begin = end = 0 when
+// it has none).
+void counter_region(const infllm_config* cfg, int32_t call, int32_t batch, int64_t n,
+                    int32_t chunk_len, int32_t n_chunks, size_t* begin, size_t* end) {
+  *begin = *end = 0;
+  size_t region = 0;
+  switch (call) {
+    case INFLLM_CALL_SCORE:
+    case INFLLM_CALL_SELECT: {
+      ScoreArgs a = score_args(cfg, batch, chunk_len, n_chunks);
+      if (call == INFLLM_CALL_SCORE && score_workspace_bytes(a) == 0) return;
+      region = ws_counter_region((size_t)batch * cfg->n_kv_heads * n_chunks * sizeof(int));
+      break;
+    }
+    case INFLLM_CALL_ATTEND: {
+      const AttendWs w = attend_ws_layout(attend_args(cfg, batch, chunk_len, n_chunks));
+      if (w.count_bytes == 0) return;
+      region = w.count_bytes - kWsHeaderBytes;
+      break;
+    }
+    case INFLLM_CALL_SELECT_ATTEND: {
+      const StepWs w = step_ws_layout(cfg, batch, n_chunks, (int32_t)n);
+      region = w.sync_bytes - kWsHeaderBytes;
+      break;
+    }
+    default:
+      return;
+  }
+  *begin = kWsHeaderBytes;
+  *end = kWsHeaderBytes + region;
 }
 
 }  // namespace
@@ -453,6 +513,8 @@ static infllm_status attend_impl(const infllm_config* cfg, int32_t batch, const 
   int splits;
   attend_plan(a, &mfma, &splits);
   if (!mfma && n_pos > 65535) return INFLLM_ERR_UNSUPPORTED;   // one grid row per position
+  // the merge addresses partial rows with 32-bit byte offsets
+  if (attend_ws_layout(a).o_bytes >= ((size_t)1 << 32)) return INFLLM_ERR_UNSUPPORTED;
   if (dry) return INFLLM_OK;   // arguments only
   const size_t need = attend_ws_bytes(a);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
@@ -472,12 +534,70 @@ static infllm_status attend_impl(const infllm_config* cfg, int32_t batch, const 
   a.out_off = out_off;
   if (need > 0) {
     const AttendWs lay = attend_ws_layout(a);
-    a.ws_count = (int*)workspace;
+    a.ws_count = (int*)((char*)workspace + kWsHeaderBytes);
     a.ws_o = (float*)((char*)workspace + lay.count_bytes);
     a.ws_ml = (float*)((char*)workspace + lay.count_bytes + lay.o_bytes);
   }
   hipStream_t s = (hipStream_t)stream;
   return launched(mfma ? launch_attend_prefill(a, splits, s) : launch_attend_rows(a, splits, s));
+}
+
+// One decode step on a workspace laid out by step_ws_layout (arguments
+// already validated): the fused launch, or the selection and attention
+// launches with both sets of counters in the workspace's counter region.
+static infllm_status step_launch(const infllm_config* cfg, int32_t batch, const void* q,
+                                 int64_t q_cap, int64_t q_off, int64_t qp, const int64_t* pos,
+                                 int32_t n_pos, const float* unit_repr, int32_t n_units,
+                                 const void* k, const void* v, int64_t kv_cap, float* scores,
+                                 int32_t* sel, void* out, float* lse, int64_t out_cap,
+                                 int64_t out_off, const StepWs& w, char* ws, hipStream_t st) {
+  ScoreArgs sa = score_args(cfg, batch, 1, n_pos);
+  sa.U = n_units;
+  sa.q = q;
+  sa.q_cap = q_cap;
+  sa.q_off = q_off;
+  sa.q_pos = qp;
+  sa.pos = pos;
+  sa.repr = unit_repr;
+  sa.scores = scores;
+  if (cfg->top_k > 0) {
+    sa.k_m = cfg->top_k;
+    sa.sel = sel;
+  }
+  sa.ws = ws;   // header; counters from kWsHeaderBytes
+  AttendArgs aa = attend_args(cfg, batch, 1, n_pos);
+  aa.q = q;
+  aa.q_cap = q_cap;
+  aa.q_off = q_off;
+  aa.q_pos = qp;
+  aa.pos = pos;
+  aa.k = k;
+  aa.v = v;
+  aa.kv_cap = kv_cap;
+  aa.sel = cfg->top_k > 0 ? sel : nullptr;
+  aa.out = out;
+  aa.lse = lse;
+  aa.out_cap = out_cap;
+  aa.out_off = out_off;
+  char* data = ws + w.sync_bytes;
+  aa.ws_o = (float*)(data + w.cand_bytes);
+  aa.ws_ml = (float*)(data + w.cand_bytes + w.att.o_bytes);
+  if (!w.fused) {
+    bool mfma;
+    int splits;
+    attend_plan(aa, &mfma, &splits);
+    aa.ws_count = splits > 1 ? (int*)(ws + kWsHeaderBytes + w.sep_sel_count) : nullptr;
+    const infllm_status s1 = launched(launch_score(sa, st));
+    if (s1 != INFLLM_OK) return s1;
+    return launched(launch_attend_rows(aa, splits, st));
+  }
+  StepPtrs p{};
+  p.status = (int*)ws;
+  p.sync = (int*)(ws + kWsHeaderBytes);
+  const size_t cands = (size_t)step_rows(aa) * w.plan.s_score * w.plan.cand;
+  p.cand_s = (float*)data;
+  p.cand_i = (int*)(data + round256(cands * sizeof(float)));
+  return launched(launch_select_attend(sa, aa, w.plan, p, st));
 }
 
 extern "C" {
@@ -521,48 +641,55 @@ infllm_status infllm_select_attend(const infllm_config* cfg, int32_t batch, cons
                    out_cap, out_off, nullptr, 0, stream, true);
   if (st != INFLLM_OK) return st;
   const StepWs w = step_ws_layout(cfg, batch, n_pos, n_units);
-  if (w.total > 0 && (!workspace || workspace_bytes < w.total || !aligned16(workspace)))
+  if (!workspace || workspace_bytes < w.total || !aligned16(workspace))
     return INFLLM_ERR_WORKSPACE;
-  char* ws = (char*)workspace;
-  if (!w.fused) {
-    st = score_impl(cfg, batch, q, q_cap, q_off, qp, pos, 1, n_pos, unit_repr, n_units, scores,
-                    sel, ws, w.sep_sel_bytes, stream);
-    if (st != INFLLM_OK) return st;
-    return attend_impl(cfg, batch, q, q_cap, q_off, qp, pos, 1, n_pos, k, v, kv_cap, sel, out,
-                       lse, out_cap, out_off, ws + w.sep_sel_bytes,
-                       workspace_bytes - w.sep_sel_bytes, stream);
-  }
-  ScoreArgs sa = score_args(cfg, batch, 1, n_pos);
-  sa.U = n_units;
-  sa.k_m = cfg->top_k;
-  sa.sel = sel;
-  sa.q = q;
-  sa.q_cap = q_cap;
-  sa.q_off = q_off;
-  sa.q_pos = qp;
-  sa.pos = pos;
-  sa.repr = unit_repr;
-  sa.scores = scores;
-  sa.ws = ws + w.sync_bytes;   // selection counters
-  AttendArgs aa = attend_args(cfg, batch, 1, n_pos);
-  aa.q = q;
-  aa.q_cap = q_cap;
-  aa.q_off = q_off;
-  aa.q_pos = qp;
-  aa.pos = pos;
-  aa.k = k;
-  aa.v = v;
-  aa.kv_cap = kv_cap;
-  aa.sel = sel;
-  aa.out = out;
-  aa.lse = lse;
-  aa.out_cap = out_cap;
-  aa.out_off = out_off;
-  char* att = ws + w.sync_bytes + w.sel_bytes;
-  aa.ws_count = (int*)att;
-  aa.ws_o = (float*)(att + w.att.count_bytes);
-  aa.ws_ml = (float*)(att + w.att.count_bytes + w.att.o_bytes);
-  return launched(launch_select_attend(sa, aa, w.plan, (int*)ws, (hipStream_t)stream));
+  return step_launch(cfg, batch, q, q_cap, q_off, qp, pos, n_pos, unit_repr, n_units, k, v, kv_cap,
+                     scores, sel, out, lse, out_cap, out_off, w, (char*)workspace,
+                     (hipStream_t)stream);
+}
+
+int32_t infllm_workspace_layout(const infllm_config* cfg, int32_t call, int32_t batch, int64_t n,
+                                int32_t chunk_len, int32_t n_chunks, size_t* counters_begin,
+                                size_t* counters_end, size_t* total) {
+  if (!counters_begin || !counters_end || !total) return INFLLM_ERR_INVALID_ARG;
+  *counters_begin = *counters_end = *total = 0;
+  if (check_config(cfg) != INFLLM_OK || batch < 1) return INFLLM_ERR_INVALID_ARG;
+  *total = infllm_workspace_size(cfg, call, batch, n, chunk_len, n_chunks);
+  if (*total > 0) counter_region(cfg, call, batch, n, chunk_len, n_chunks, counters_begin, counters_end);
+  return INFLLM_OK;
+}
+
+int32_t infllm_step_plan(const infllm_config* cfg, int32_t batch, int32_t n_units, int32_t n_pos,
+                         int32_t* plan) {
+  if (!plan) return INFLLM_ERR_INVALID_ARG;
+  for (int i = 0; i < 7; ++i) plan[i] = 0;
+  if (check_config(cfg) != INFLLM_OK || batch < 1 || n_units < 0 || n_pos < 1)
+    return INFLLM_ERR_INVALID_ARG;
+  const StepWs w = step_ws_layout(cfg, batch, n_pos, n_units);
+  if (!w.fused) return INFLLM_OK;
+  plan[0] = 1;
+  plan[1] = w.plan.n_splits;
+  plan[2] = w.plan.s_score;
+  plan[3] = w.plan.units_per;
+  plan[4] = w.plan.cand;
+  plan[5] = w.plan.w_score;
+  plan[6] = w.plan.w_unit;
+  return INFLLM_OK;
+}
+
+int32_t infllm_workspace_status(const void* workspace, size_t workspace_bytes, int32_t* timeouts,
+                                void* stream) {
+  if (!timeouts) return INFLLM_ERR_INVALID_ARG;
+  *timeouts = 0;
+  if (!workspace || workspace_bytes < kWsHeaderBytes || !aligned16(workspace))
+    return INFLLM_ERR_INVALID_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  if (hipStreamSynchronize(st) != hipSuccess) return INFLLM_ERR_HIP;
+  int32_t v = 0;
+  if (hipMemcpy(&v, workspace, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess)
+    return INFLLM_ERR_HIP;
+  *timeouts = v;
+  return INFLLM_OK;
 }
 
 }  // extern "C"

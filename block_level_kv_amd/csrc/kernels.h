@@ -9,6 +9,29 @@ namespace infllm {
 
 constexpr int kMaxTopK = 256;
 
+// Every workspace that holds counters starts with a header (word 0: waits
+// that timed out, the rest reserved) and a counter region of at least
+// kWsCounterBytes, then the call's data (partial sums, partial rows).  Every
+// call leaves its counters at zero, and counters of every call kind and
+// shape lie in the region's first bytes, so a zero-filled workspace can be
+// reused by calls of other kinds and shapes as long as their counters fit
+// the fixed-size region.
+constexpr size_t kWsHeaderBytes = 256;
+constexpr size_t kWsCounterBytes = 65536;
+inline size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+inline size_t ws_counter_region(size_t counter_bytes) {
+  const size_t r = round256(counter_bytes);
+  return r > kWsCounterBytes ? r : kWsCounterBytes;
+}
+
+// Tuning overrides (split counts), read from the environment once per
+// process: INFLLM_PREFILL_SPLITS, INFLLM_ROWS_WGS, INFLLM_STEP_SPLITS.
+// Zero: the built-in choice.
+struct Tuning {
+  int prefill_splits, rows_wgs, step_splits;
+};
+const Tuning& tuning();
+
 struct BuildArgs {
   int batch, Hq, Hkv, d, B, n_init, W, r_k, rep_mode, U;
   int u_begin, u_end, u_stride;   // units built, rows of the output pool
@@ -77,16 +100,33 @@ hipError_t launch_attend_rows(const AttendArgs& a, int splits, hipStream_t st);
 int64_t rows_num_counters(const AttendArgs& a);
 
 // fused decode step (bf16): unit scores, selection and attention of single
-// query positions in one launch; false when the shapes need the separate calls
+// query positions in one launch; false when the shapes need the separate calls.
+// Every row (position x KV head x sequence) has n_splits workgroups; the
+// first s_score of them score a slice of units_per units each.  Every
+// workgroup attends an equal share of the selected units' keys and a share
+// of the local keys (initial tokens and window) weighted w_score (scoring
+// workgroups) or w_unit (the others).
 struct StepPlan {
-  int n_slices;         // scoring slices per row
-  int s_local, s_unit;  // attention splits per row over the local and the unit keys
-                        // (s_unit >= n_slices; splits past the slices only attend)
+  int n_splits;            // workgroups per row (<= 64)
+  int s_score;             // scoring workgroups per row
+  int units_per;           // units per scoring workgroup: 64, 128, 192 or 256
+  int cand;                // candidates each scoring workgroup publishes
+  int w_score, w_unit;     // local-key weights of a scoring / another workgroup
 };
 bool select_attend_plan(const ScoreArgs& s, const AttendArgs& a, StepPlan* p);
-int64_t select_attend_sync_ints(const AttendArgs& a);   // ready flags
-hipError_t launch_select_attend(const ScoreArgs& s, const AttendArgs& a, const StepPlan& p,
-                                int* ready, hipStream_t st);
+int64_t step_rows(const AttendArgs& a);                  // rows of one call
+constexpr int kStepSyncInts = 20;   // per row: arrival mask (2), unused, merge, started bytes (16)
+// Row state, candidates and partials of one call: sync [rows][kStepSyncInts]
+// in the workspace's counter region, then candidate scores and ids, partial
+// rows and (max, sum) pairs.
+struct StepPtrs {
+  int* sync;
+  float* cand_s;
+  int* cand_i;
+  int* status;   // workspace word 0: waits that timed out
+};
+hipError_t launch_select_attend(const ScoreArgs& s, AttendArgs a, const StepPlan& p,
+                                const StepPtrs& w, hipStream_t st);
 
 // bf16 MFMA attention tiles for query chunks (head_dim 128)
 bool prefill_supported(const AttendArgs& a);

@@ -179,12 +179,14 @@ static bool score_fused(const ScoreArgs& a) {
   return score_num_parts(a) > 0 && a.U <= kFusedMaxUnits;
 }
 
+// header and counter region (arrival counters at the region's start)
 static size_t score_counter_bytes(const ScoreArgs& a) {
-  return ((size_t)a.batch * a.Hkv * a.n_chunks * sizeof(int) + 255) & ~(size_t)255;
+  return kWsHeaderBytes + ws_counter_region((size_t)a.batch * a.Hkv * a.n_chunks * sizeof(int));
 }
+static int* score_counters(const ScoreArgs& a) { return (int*)((char*)a.ws + kWsHeaderBytes); }
 
-// [arrival counters, 256-byte aligned][fp64 partial query sums]; sized for
-// either path (the unit count is not known here)
+// [header][arrival counters][fp64 partial query sums]; sized for either
+// path (the unit count is not known here)
 size_t score_workspace_bytes(const ScoreArgs& a) {
   const int parts = score_num_parts(a);
   if (parts == 0) return 0;
@@ -216,7 +218,7 @@ static void launch_parts(const ScoreArgs& a, int parts, double* pw, hipStream_t 
   if (score_fused(a))
     k_score_fused<T, G, D, ROWS><<<grid, kScoreThreads, 0, st>>>(
         (const T*)a.q, a.q_cap, a.q_off, a.q_pos, a.pos, a.L, a.Hq, a.Hkv, a.B, a.n_init, a.W, a.repr,
-        a.U, a.scores, a.n_chunks, pw, (int*)a.ws);
+        a.U, a.scores, a.n_chunks, pw, score_counters(a));
   else
     k_chunk_qsum<T, G, D, ROWS><<<grid, kScoreThreads, 0, st>>>(
         (const T*)a.q, a.q_cap, a.q_off, a.L, a.Hq, a.Hkv, a.n_chunks, pw);
@@ -253,7 +255,7 @@ static hipError_t launch_score_tgd(const ScoreArgs& a, hipStream_t st) {
   } else {
     // keys per lane of the 4-wave search: ceil(U / 256) <= 8
     static_assert(kMaxSelSlices * kUnitsPerWG <= 8 * kScoreThreads, "keys per lane");
-    int* cnt = (int*)a.ws;
+    int* cnt = score_counters(a);
     if (a.U <= 4 * kScoreThreads) INFLLM_SCORE_UNITS(4, cnt);
     else INFLLM_SCORE_UNITS(8, cnt);
   }

@@ -74,6 +74,27 @@ struct UnitRows {
       }
     }
   }
+  // The same scores, written to sb[u] and to lds[u - lds0].
+  __device__ __forceinline__ void score_lds(const double* qv, int base, int u1, int64_t e,
+                                            float* sb, float* lds, int lds0) const {
+    const int cg = threadIdx.x % 64 % kLpu;
+#pragma unroll
+    for (int s = 0; s < kSlots; ++s) {
+      const int u = unit(base, s);
+      double t = 0.0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) t = fma(x[s].get(j), qv[j], t);
+      t += dpp_f64<INFLLM_DPP_XOR1>(t);
+      t += dpp_f64<INFLLM_DPP_XOR2>(t);
+      t += dpp_f64<INFLLM_DPP_HALF_MIRROR>(t);
+      if (kLpu == 16) t += dpp_f64<INFLLM_DPP_MIRROR>(t);
+      if (u < u1 && cg == 0) {
+        const float v = u < e ? (float)t : -INFINITY;
+        sb[u] = v;
+        lds[u - lds0] = v;
+      }
+    }
+  }
 };
 
 // Scores of slice `slice` (of n_slices, kUnitsPerWG units each) for chunk ch

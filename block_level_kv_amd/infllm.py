@@ -28,6 +28,7 @@ EXPORTED = ("infllm_num_units", "infllm_num_eligible", "infllm_workspace_size",
             "infllm_score_units", "infllm_score_units_qsum",
             "infllm_score_units_varlen", "infllm_select_units", "infllm_topk_units",
             "infllm_attend", "infllm_attend_varlen", "infllm_select_attend",
+            "infllm_workspace_layout", "infllm_workspace_status", "infllm_step_plan",
             "infllm_status_string", "infllm_abi_version")
 
 
@@ -95,6 +96,14 @@ def lib() -> ctypes.CDLL:
         L.infllm_attend.restype = _i32
         L.infllm_attend.argtypes = [_cfgp, _i32, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _i64,
                                     _vp, _vp, _vp, _i64, _i64, _vp, _sz, _vp]
+        L.infllm_workspace_layout.restype = _i32
+        L.infllm_workspace_layout.argtypes = [_cfgp, _i32, _i32, _i64, _i32, _i32,
+                                              ctypes.POINTER(_sz), ctypes.POINTER(_sz),
+                                              ctypes.POINTER(_sz)]
+        L.infllm_step_plan.restype = _i32
+        L.infllm_step_plan.argtypes = [_cfgp, _i32, _i32, _i32, ctypes.POINTER(_i32)]
+        L.infllm_workspace_status.restype = _i32
+        L.infllm_workspace_status.argtypes = [_vp, _sz, ctypes.POINTER(_i32), _vp]
         L.infllm_status_string.restype = ctypes.c_char_p
         L.infllm_status_string.argtypes = [_i32]
         L.infllm_abi_version.restype = _i32
@@ -170,6 +179,33 @@ def infllm_num_eligible(cfg: infllm_config, t_last: int, n_units: int) -> int:
 def infllm_workspace_size(cfg: infllm_config, call: int, batch: int, n: int = 0,
                           chunk_len: int = 0, n_chunks: int = 0) -> int:
     return int(lib().infllm_workspace_size(ctypes.byref(cfg), call, batch, n, chunk_len, n_chunks))
+
+
+def infllm_workspace_layout(cfg: infllm_config, call: int, batch: int, n: int = 0,
+                            chunk_len: int = 0, n_chunks: int = 0) -> tuple[int, int, int]:
+    """(counters_begin, counters_end, total) bytes of a call's workspace."""
+    b, e, t = _sz(0), _sz(0), _sz(0)
+    _raise("infllm_workspace_layout", lib().infllm_workspace_layout(
+        ctypes.byref(cfg), call, batch, n, chunk_len, n_chunks, ctypes.byref(b), ctypes.byref(e),
+        ctypes.byref(t)))
+    return b.value, e.value, t.value
+
+
+def infllm_step_plan(cfg: infllm_config, batch: int, n_units: int, n_pos: int = 1) -> dict:
+    """How infllm_select_attend runs a step: one launch or the two calls, and
+    the one launch's shape."""
+    p = (_i32 * 7)()
+    _raise("infllm_step_plan", lib().infllm_step_plan(ctypes.byref(cfg), batch, n_units, n_pos, p))
+    keys = ("fused", "n_splits", "s_score", "units_per", "cand", "w_score", "w_unit")
+    return {k: int(v) for k, v in zip(keys, p)}
+
+
+def infllm_workspace_status(ws: torch.Tensor, stream=None) -> int:
+    """Waits of the one-launch decode step that hit their bound (synchronises)."""
+    n = _i32(0)
+    _raise("infllm_workspace_status", lib().infllm_workspace_status(
+        ws.data_ptr(), ws.numel() * ws.element_size(), ctypes.byref(n), _stream(stream, ws)))
+    return n.value
 
 
 def workspace(cfg: infllm_config, call: int, batch: int, n: int = 0, chunk_len: int = 0,

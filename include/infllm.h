@@ -43,11 +43,26 @@
  *    INFLLM_ERR_UNSUPPORTED / INFLLM_ERR_WORKSPACE) before any device
  *    work is enqueued; a failed launch returns INFLLM_ERR_HIP.  Nothing is
  *    thrown across the ABI.
+ *  Workspaces.  A workspace that carries counters (score calls with long
+ *    chunks, the selection, split attention, the decode step) starts with
+ *    a 256-byte header -- its first int32 counts waits of the decode step
+ *    that timed out (infllm_workspace_status) -- followed by a counter
+ *    region of at least 64 KiB, then the call's data (partial sums and
+ *    rows).  It must be zero-filled before its first use; every call
+ *    leaves its counters at zero again.  Since every call kind keeps its
+ *    counters in that region, one zero-filled workspace may serve calls of
+ *    other kinds and shapes (if large enough) as long as each call's
+ *    counters fit the first 64 KiB of the region (infllm_workspace_layout
+ *    reports a call's region; e.g. a decode step needs 16 bytes per
+ *    (sequence, KV head, position)).  A call whose counters need more
+ *    binds the workspace to its own shape: zero-fill it again before
+ *    other calls use it.  Calls that share a workspace must not overlap
+ *    in time.
  *  Tuning.  The environment variables INFLLM_PREFILL_SPLITS,
- *    INFLLM_ROWS_WGS and INFLLM_STEP_LOCAL_SPLITS override split counts
- *    of the chunk attention, the decode attention and the one-launch
- *    decode step; workspace sizes follow them, so they must not change
- *    between sizing a workspace and the calls that use it.
+ *    INFLLM_ROWS_WGS and INFLLM_STEP_SPLITS override split counts of the
+ *    chunk attention, the decode attention and the one-launch decode step
+ *    (workgroups per row).  They are read once per process, at the first
+ *    call that needs them; workspace sizes follow them.
  *  Units.  Unit u is absolute block j = u + floor(n_init / block); its keys
  *    are positions [max(j*block, n_init), (j+1)*block).  A context of n_ctx
  *    tokens holds floor(n_ctx/block) - floor(n_init/block) units (blocks
@@ -339,7 +354,9 @@ INFLLM_API infllm_status infllm_topk_units(const infllm_config *cfg, int32_t bat
  *            (q_pos + n_chunks*chunk_len <= kv_cap)
  *   sel      [batch, H_kv, n_chunks, k_m] int32 unit ids (-1 = empty slot),
  *            e.g. from infllm_topk_units; ids must be < the number of units
- *            the K/V context holds (not checked on the device)
+ *            the K/V context holds (not checked on the device).  A row is
+ *            a set: an id repeated in it is attended once, like the
+ *            working context's membership test above.
  *   out      out [batch, H_q, out_cap, d], rows out_off .. out_off +
  *            n_chunks*chunk_len - 1, cfg->dtype
  *   lse      optional out [batch, H_q, out_cap] fp32 natural-log
@@ -390,10 +407,19 @@ INFLLM_API infllm_status infllm_attend_varlen(const infllm_config *cfg, int32_t 
  * its selection: scores and sel are identical; out and lse equal up to fp32
  * rounding (the attention is split over workgroups differently).
  *
- * Where the shapes allow (bf16, at most 2,048 units, k_m >= 1) it is one
- * launch: the local keys (initial tokens and window) are attended while
- * the units are scored and selected, and the units' keys as soon as their
- * row's selection is published.  Otherwise it runs the two calls.
+ * Where the shapes allow (bf16, k_m >= 1, and a row's scores few enough
+ * to be searched at once: up to 2,048 units) it is one launch: in each
+ * (sequence, KV head, position) row some workgroups score a slice of units
+ * each and publish the scores, a selector workgroup selects the row's units
+ * from them and publishes the selection, and every attention workgroup
+ * attends its share of the local keys (initial tokens and window), then of
+ * the selected units' keys.  A workgroup waits for a selection only after
+ * checking that every slice of its row has been started, scoring the ones
+ * that have not itself, so the waits end whatever the dispatch order or
+ * residency.  Otherwise it runs the two calls.  With INFLLM_STEP_SPLITS
+ * set, rows of up to 64 x 256 units also take the one launch: each slice
+ * then publishes only its best k_m scores (the row's top k_m is among
+ * them).  infllm_step_plan reports which form a call takes.
  *
  *   q, q_cap, q_off, q_pos, pos, unit_repr, n_units
  *              as infllm_select_units (pos: as infllm_attend_varlen)
@@ -414,6 +440,41 @@ INFLLM_API infllm_status infllm_select_attend(const infllm_config *cfg, int32_t 
                                    int64_t kv_cap, float *scores, int32_t *sel, void *out,
                                    float *lse, int64_t out_cap, int64_t out_off,
                                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * infllm_workspace_layout -- where a call keeps its counters: bytes
+ * [*counters_begin, *counters_end) of its workspace (both 0 if it has
+ * none), and *total = infllm_workspace_size of the same arguments.  Host
+ * only.  Returns INFLLM_OK, or INFLLM_ERR_INVALID_ARG (outputs zeroed).
+ */
+INFLLM_API int32_t infllm_workspace_layout(const infllm_config *cfg, int32_t call, int32_t batch,
+                                           int64_t n, int32_t chunk_len, int32_t n_chunks,
+                                           size_t *counters_begin, size_t *counters_end,
+                                           size_t *total);
+
+/*
+ * infllm_step_plan -- how infllm_select_attend runs a step of the given
+ * sizes (host only).  plan[0..6] = {one launch (1) or the two calls (0),
+ * workgroups per row, scoring workgroups per row, units each scores,
+ * candidates each publishes, local-key weight of a scoring workgroup, of a
+ * unit workgroup}; all 0 for the two calls.  Returns INFLLM_OK or
+ * INFLLM_ERR_INVALID_ARG.
+ */
+INFLLM_API int32_t infllm_step_plan(const infllm_config *cfg, int32_t batch, int32_t n_units,
+                                    int32_t n_pos, int32_t *plan);
+
+/*
+ * infllm_workspace_status -- synchronises `stream`, then reads the header
+ * word of a workspace used by infllm_select_attend: the number of waits for
+ * a row's selection that hit their bound since the workspace was zero-
+ * filled (rows concerned got NaN outputs).  Every wait ends on its own
+ * (see infllm_select_attend), so a nonzero count means the workspace was
+ * not zero-filled or was shared by calls that overlapped in time.  The
+ * only call that synchronises.  Returns INFLLM_OK, INFLLM_ERR_INVALID_ARG
+ * or INFLLM_ERR_HIP.
+ */
+INFLLM_API int32_t infllm_workspace_status(const void *workspace, size_t workspace_bytes,
+                                           int32_t *timeouts, void *stream);
 
 INFLLM_API const char *infllm_status_string(int32_t status);
 INFLLM_API int32_t infllm_abi_version(void);

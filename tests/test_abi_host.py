@@ -31,7 +31,7 @@ def cfg(**kw):
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 19
     assert set(names) == set(F.EXPORTED)
     L = F.lib()
     for n in names:
@@ -198,19 +198,77 @@ def test_select_attend_validation_and_workspace():
     assert call(kv_cap=131072) == F.INFLLM_ERR_INVALID_ARG       # position past the K/V rows
     assert call(U=-1) == F.INFLLM_ERR_INVALID_ARG
     need = F.infllm_workspace_size(c, F.INFLLM_CALL_SELECT_ATTEND, 4, 1023, 1, 1)
-    # at least what the two separate calls need, one after the other
-    sep = F.infllm_workspace_size(c, F.INFLLM_CALL_SELECT, 4, 0, 1, 1) + \
-        F.infllm_workspace_size(c, F.INFLLM_CALL_ATTEND, 4, 0, 1, 1)
-    assert need >= sep > 0
+    assert need > 0
     assert call(wsb=need - 1) == F.INFLLM_ERR_WORKSPACE
     assert call(ws=None, wsb=0) == F.INFLLM_ERR_WORKSPACE
     assert call(ws=MISALIGNED) == F.INFLLM_ERR_WORKSPACE
     # one query per chunk only
     assert F.infllm_workspace_size(c, F.INFLLM_CALL_SELECT_ATTEND, 4, 1023, 2, 1) == 0
-    # past 2,048 units (separate calls) the size still covers both calls
-    big = F.infllm_workspace_size(c, F.INFLLM_CALL_SELECT_ATTEND, 2, 8191, 1, 1)
-    assert big >= F.infllm_workspace_size(c, F.INFLLM_CALL_SELECT, 2, 0, 1, 1) + \
-        F.infllm_workspace_size(c, F.INFLLM_CALL_ATTEND, 2, 0, 1, 1)
+
+
+# (batch, KV heads, G, units, k_m, positions)
+STEP_SHAPES = [(4, 8, 4, 1023, 32, 1), (2, 8, 4, 8191, 32, 1), (1, 8, 4, 511, 32, 1),
+               (8, 8, 4, 8191, 32, 1), (8, 8, 4, 1023, 32, 16), (4, 8, 8, 1023, 32, 64),
+               (1, 2, 4, 18, 4, 1), (1, 8, 4, 2047, 256, 1), (1, 8, 4, 4095, 256, 1),
+               (2, 1, 8, 16384, 32, 1), (2, 1, 8, 16385, 32, 1), (1, 1, 1, 1, 1, 1),
+               (64, 8, 4, 1023, 32, 1), (1, 8, 4, 1023, 300, 1)]
+
+
+@pytest.mark.parametrize("b,Hkv,G,U,k_m,n_pos", STEP_SHAPES)
+def test_step_plan(b, Hkv, G, U, k_m, n_pos):
+    """The one-launch decode step's plan: scoring workgroups cover the units
+    exactly once, at least one attention workgroup per row has no slice, at
+    most 64 attention workgroups per row (plus the selector), every score
+    of a row is a candidate (rows with more take the two calls unless the
+    split count is set by hand), and the workspace holds the row state, the
+    candidates and every split's partial rows.  Large batches and many
+    positions stay in one launch even when the grid exceeds what the chip
+    holds at once (the waits do not depend on residency)."""
+    c = cfg(n_q_heads=G * Hkv, n_kv_heads=Hkv, top_k=k_m)
+    if k_m > 256:
+        assert F.infllm_workspace_size(c, F.INFLLM_CALL_SELECT_ATTEND, b, U, 1, n_pos) == 0
+        return
+    p = F.infllm_step_plan(c, b, U, n_pos)
+    total = F.infllm_workspace_size(c, F.INFLLM_CALL_SELECT_ATTEND, b, U, 1, n_pos)
+    c0, c1, t = F.infllm_workspace_layout(c, F.INFLLM_CALL_SELECT_ATTEND, b, U, 1, n_pos)
+    rows = b * Hkv * n_pos
+    assert t == total > 0 and c0 == 256 and c1 - c0 >= 65536 and total >= c1
+    if not p["fused"]:
+        # more scores in a row than one search takes at the coarsest slices
+        assert -(-U // 256) * 256 > 2048 or U > 2048
+        return
+    N, S, up, C = p["n_splits"], p["s_score"], p["units_per"], p["cand"]
+    assert 2 <= N <= 64 and 1 <= S < N
+    assert up in (64, 128, 192, 256) and (S - 1) * up < U <= S * up
+    assert C == up and S * C <= 2048
+    assert p["w_score"] >= 0 and p["w_unit"] >= 0 and p["w_score"] + p["w_unit"] >= 1
+    assert c1 - c0 >= 80 * rows
+    d, Hq = 128, G * Hkv
+    assert total >= c1 + rows * S * C * 8 + N * b * Hq * n_pos * (d * 4 + 8)
+
+
+def test_workspace_counter_regions():
+    """Every call kind keeps its counters in [256, 256 + region) with a
+    region of at least 64 KiB, and its data after it: a zero-filled
+    workspace may serve calls of other kinds and shapes whose counters fit
+    64 KiB without a counter landing on another call's data."""
+    c = cfg()
+    cases = [(F.INFLLM_CALL_SCORE, 1, 0, 512, 64), (F.INFLLM_CALL_SELECT, 4, 0, 1, 1),
+             (F.INFLLM_CALL_SELECT, 1, 0, 512, 64), (F.INFLLM_CALL_ATTEND, 4, 0, 1, 1),
+             (F.INFLLM_CALL_ATTEND, 1, 0, 1, 4), (F.INFLLM_CALL_ATTEND, 1, 0, 512, 1),
+             (F.INFLLM_CALL_SELECT_ATTEND, 4, 1023, 1, 1),
+             (F.INFLLM_CALL_SELECT_ATTEND, 2, 8191, 1, 1),
+             (F.INFLLM_CALL_SELECT_ATTEND, 8, 4095, 1, 8)]
+    for call, b, n, L, nc in cases:
+        c0, c1, total = F.infllm_workspace_layout(c, call, b, n, L, nc)
+        assert total == F.infllm_workspace_size(c, call, b, n, L, nc)
+        assert total > 0 and c0 == 256 and c1 - c0 == 65536 and total >= c1, (call, b, n, L, nc)
+    # a step whose counters need more than 64 KiB: its own, larger region
+    c0, c1, total = F.infllm_workspace_layout(c, F.INFLLM_CALL_SELECT_ATTEND, 8, 1023, 1, 256)
+    assert c0 == 256 and c1 - c0 >= 16 * 8 * 8 * 256 > 65536
+    # calls without counters
+    assert F.infllm_workspace_layout(c, F.INFLLM_CALL_SCORE, 4, 0, 1, 1) == (0, 0, 0)
+    assert F.infllm_workspace_layout(c, F.INFLLM_CALL_BUILD, 1, 8192)[:2] == (0, 0)
 
 
 def test_qsum_validation_and_workspace():

@@ -272,6 +272,14 @@ def test_attend_edge_cases(orc, data, name):
              ("ragged", cfg_of(w), None, w.window + w.n_init - 20, 37),
              ("early", cfg_of(w), None, 0, 1),
              ("late_single", cfg_of(w), None, w.n_ctx - 1, 1)]
+    # (e) repeated ids, out of order, with empty slots in between: a row of
+    # sel is a set (the oracle's membership test), each unit attended once
+    for label, t0, L in (("repeated_chunk", w.n_ctx - 64, 64), ("repeated_single", w.n_ctx - 1, 1)):
+        e = orc.num_eligible(t0 + L - 1, U, w.block, w.n_init, w.window)
+        a, b_, c_ = 0, e // 2, e - 1
+        row = np.array([c_, a, c_, -1, a, b_, b_, -1], np.int32)
+        cases.append((label, cfg_of(w, top_k=8),
+                      np.broadcast_to(row, (w.batch, w.n_kv_heads, 1, 8)).copy(), t0, L))
     _, repr_o, _ = oracle_build(orc, w, inp)
     for label, cfg, sel, t0, L in cases:
         if sel is None:
@@ -383,10 +391,10 @@ PREFILL_VARIANTS = [
 
 
 @pytest.mark.parametrize("G,n_init,W,chunk,n_ctx,top_k,Hkv", PREFILL_VARIANTS)
-@pytest.mark.parametrize("splits", ["auto", "1", "3"])
-def test_prefill_mfma_variants(orc, monkeypatch, G, n_init, W, chunk, n_ctx, top_k, Hkv, splits):
-    if splits != "auto":
-        monkeypatch.setenv("INFLLM_PREFILL_SPLITS", splits)
+@pytest.mark.parametrize("per_call", ["all", "one"])
+def test_prefill_mfma_variants(orc, G, n_init, W, chunk, n_ctx, top_k, Hkv, per_call):
+    """All chunks in one call, or one chunk per call (few workgroups: the
+    tile lists are split over workgroups and merged in the kernel)."""
     w = LL.replace(n_ctx=n_ctx, n_q_heads=Hkv * G, n_kv_heads=Hkv, window=W, n_init=n_init,
                    top_k=top_k, chunk=chunk, seed=G * 1000 + n_init + Hkv)
     cfg = cfg_of(w)
@@ -396,10 +404,22 @@ def test_prefill_mfma_variants(orc, monkeypatch, G, n_init, W, chunk, n_ctx, top
     n_chunks = n_ctx // chunk
     sels = np.stack([_oracle_selection(orc, w, inp, c * chunk, chunk, repr_o)
                      for c in range(n_chunks)], axis=2)
-    out, lse = gpu_attend(cfg, dev["q"], 0, 0, chunk, n_chunks, dev["k"], dev["v"],
-                          torch.from_numpy(sels).cuda())
+    checked = sorted({0, 1, n_chunks // 2, n_chunks - 1})
+    sel_g = torch.from_numpy(sels).cuda()
+    if per_call == "all":
+        out, lse = gpu_attend(cfg, dev["q"], 0, 0, chunk, n_chunks, dev["k"], dev["v"], sel_g)
+    else:
+        out = torch.zeros((w.batch, w.n_q_heads, n_ctx, w.head_dim), dtype=torch.bfloat16,
+                          device="cuda")
+        lse = torch.zeros((w.batch, w.n_q_heads, n_ctx), dtype=torch.float32, device="cuda")
+        for c in checked:
+            t0 = c * chunk
+            oc, lc = gpu_attend(cfg, dev["q"], t0, t0, chunk, 1, dev["k"], dev["v"],
+                                sel_g[:, :, c:c + 1].contiguous())
+            out[:, :, t0:t0 + chunk] = oc[:, :, :chunk]
+            lse[:, :, t0:t0 + chunk] = lc[:, :, :chunk]
     torch.cuda.synchronize()
-    for c in sorted({0, 1, n_chunks // 2, n_chunks - 1}):
+    for c in checked:
         t0 = c * chunk
         o_ref, l_ref = orc.attend_all(inp["q"][:, :, t0:t0 + chunk], t0, inp["k"], inp["v"],
                                       sels[:, :, c], B=w.block, n_init=n_init, W=W)
@@ -434,7 +454,10 @@ def test_prefill_deterministic_and_sequential_equals_batched(orc):
     assert torch.equal(out, o1)
     if ws is not None:
         n_counters = -(-w.chunk // (128 // w.group)) * n_chunks * w.n_kv_heads * w.batch
-        assert int(ws[:4 * n_counters].view(torch.int32).abs().sum()) == 0
+        c0, c1, _ = F.infllm_workspace_layout(cfg, F.INFLLM_CALL_ATTEND, w.batch, 0, w.chunk,
+                                              n_chunks)
+        assert c1 - c0 >= 4 * n_counters
+        assert int(ws[c0:c1].view(torch.int32).abs().sum()) == 0
     c = n_chunks - 2
     oc, lc = gpu_attend(cfg, dev["q"], c * w.chunk, c * w.chunk, w.chunk, 1, dev["k"], dev["v"],
                         sel[:, :, c:c + 1].contiguous())
@@ -464,7 +487,9 @@ def test_score_shared_workspace_repeatable(U_big):
     torch.cuda.synchronize()
     assert all(torch.equal(outs[0], o) for o in outs[1:])
     n_prob = w.batch * w.n_kv_heads * n_chunks
-    assert int(ws[:4 * n_prob].view(torch.int32).abs().sum().item()) == 0
+    c0, c1, _ = F.infllm_workspace_layout(cfg, F.INFLLM_CALL_SCORE, w.batch, 0, w.chunk, n_chunks)
+    assert c1 - c0 >= 4 * n_prob
+    assert int(ws[c0:c1].view(torch.int32).abs().sum().item()) == 0
     # against a float64 evaluation of the definition
     qs = inp["q"].double().view(w.batch, w.n_kv_heads, w.group, -1, w.head_dim)
     for c in range(n_chunks):

@@ -107,37 +107,54 @@ def test_decode_steps_one_workspace(orc):
                 check_selection(sg[bi, h, 0], orc.topk(so, e, w.top_k), so)
 
 
-# (Hq, Hkv, d, U, k_m, n_pos, W, n_init, varlen, dtype, splits)
+ANY_PLAN = "any"   # a plan whose shape the test does not fix
+
+
+# (Hq, Hkv, d, U, k_m, n_pos, W, n_init, varlen, dtype, plan): plan is the
+# one-launch shape infllm_step_plan must report, (workgroups per row,
+# scoring workgroups, units each), or None for the two separate calls
 SHAPES = [
-    (8, 2, 128, 47, 8, 1, 1024, 128, False, "bf16", None),      # one slice per row
-    (4, 4, 128, 300, 16, 2, 512, 128, False, "bf16", None),     # G = 1, two positions
-    (8, 4, 64, 200, 6, 3, 384, 100, False, "bf16", None),       # G = 2, d = 64, sinks not B-aligned
-    (16, 2, 128, 100, 4, 1, 512, 128, True, "bf16", None),      # G = 8, a position per sequence
-    (8, 2, 128, 1024, 32, 1, 1024, 128, False, "bf16", None),   # 4 keys per lane of the search
-    (8, 1, 128, 2048, 32, 1, 512, 128, False, "bf16", None),    # 32 slices, 8 keys per lane
-    (8, 1, 128, 2049, 32, 1, 512, 128, False, "bf16", None),    # beyond: separate calls
-    (4, 2, 128, 30, 40, 1, 512, 128, False, "bf16", None),      # k_m > units
-    (4, 2, 128, 600, 256, 1, 512, 128, False, "bf16", None),    # the largest k_m
-    (4, 2, 128, 90, 8, 1, 512, 128, False, "bf16", "1"),        # one local split
-    (4, 2, 128, 90, 8, 2, 512, 128, False, "bf16", "3"),        # three local splits
-    (8, 2, 128, 64, 2, 1, 4096, 128, False, "bf16", "1"),      # a local split merges last
-    (2, 1, 64, 40, 4, 1, 512, 64, False, "f32", None),          # fp32: separate calls
+    (8, 2, 128, 47, 8, 1, 1024, 128, False, "bf16", (64, 1, 64)),      # one scorer per row
+    (4, 4, 128, 300, 16, 2, 512, 128, False, "bf16", (47, 5, 64)),     # G = 1, two positions
+    (8, 4, 64, 200, 6, 3, 384, 100, False, "bf16", (31, 4, 64)),       # G = 2, d = 64, sinks not B-aligned
+    (16, 2, 128, 100, 4, 1, 512, 128, True, "bf16", (64, 2, 64)),      # G = 8, a position per sequence
+    (8, 2, 128, 1024, 32, 1, 1024, 128, False, "bf16", (64, 16, 64)),  # 512 candidates per row
+    (8, 1, 128, 2048, 32, 1, 512, 128, False, "bf16", (64, 32, 64)),   # 32 scorers
+    (8, 2, 128, 1500, 32, 8, 512, 128, False, "bf16", (23, 12, 128)),  # 128 units per scorer
+    (8, 2, 128, 1500, 32, 16, 512, 128, False, "bf16", (11, 8, 192)),  # 192 units per scorer
+    (4, 2, 128, 4000, 32, 1, 512, 128, False, "bf16", None),  # more scores than one search: two calls
+    (4, 2, 128, 300, 8, 16, 512, 128, False, "bf16", (11, 5, 64)),     # few workgroups per row
+    (4, 2, 128, 30, 40, 1, 512, 128, False, "bf16", (64, 1, 64)),      # k_m > units
+    (4, 2, 128, 600, 256, 1, 512, 128, False, "bf16", (64, 10, 64)),   # the largest k_m
+    (8, 2, 128, 64, 2, 1, 4096, 128, False, "bf16", (64, 1, 64)),      # nearly all keys local
+    (32, 8, 128, 300, 8, 32, 512, 128, False, "bf16", (3, 2, 256)),    # 1,536 workgroups: twice what fits at once
+    (4, 2, 128, 4095, 256, 1, 512, 128, False, "bf16", None),          # 4,096 candidates: separate calls
+    (2, 1, 64, 40, 4, 1, 512, 64, False, "f32", None),                 # fp32: separate calls
 ]
 
 
-@pytest.mark.parametrize("Hq,Hkv,d,U,k_m,n_pos,W,n_init,varlen,dt,splits", SHAPES)
-def test_select_attend_shapes(orc, monkeypatch, Hq, Hkv, d, U, k_m, n_pos, W, n_init, varlen, dt,
-                              splits):
+@pytest.mark.parametrize("Hq,Hkv,d,U,k_m,n_pos,W,n_init,varlen,dt,plan", SHAPES)
+def test_select_attend_shapes(orc, Hq, Hkv, d, U, k_m, n_pos, W, n_init, varlen, dt, plan):
+    run_shape(orc, Hq, Hkv, d, U, k_m, n_pos, W, n_init, varlen, dt, plan)
+
+
+def run_shape(orc, Hq, Hkv, d, U, k_m, n_pos, W, n_init, varlen, dt, plan, cut=False):
     """Random unit representations and K/V; the last position sees every unit
     eligible, a second sequence (varlen) sits mid-context.  Two calls in a
-    row on one workspace, bit for bit equal."""
-    if splits is not None:
-        monkeypatch.setenv("INFLLM_STEP_LOCAL_SPLITS", splits)
+    row on one workspace, bit for bit equal; no wait hits its bound.  cut:
+    the plan must have every slice publish fewer candidates than units."""
     b, B = 2, 128
     dtype = torch.bfloat16 if dt == "bf16" else torch.float32
     cfg = F.make_config(n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, block=B, n_init=n_init,
                         window=W, rep_k=4, top_k=k_m,
                         dtype=F.INFLLM_BF16 if dt == "bf16" else F.INFLLM_F32)
+    got_plan = F.infllm_step_plan(cfg, b, U, n_pos)
+    if plan is None:
+        assert got_plan["fused"] == 0
+    elif plan is not ANY_PLAN:
+        assert (got_plan["n_splits"], got_plan["s_score"], got_plan["units_per"]) == plan
+    if cut:
+        assert got_plan["fused"] == 1 and got_plan["cand"] < got_plan["units_per"], got_plan
     gen = torch.Generator().manual_seed(U * 31 + k_m + n_pos)
     n_units_ctx = U + n_init // B                       # blocks before the window
     t0 = n_units_ctx * B + W + 17                       # every unit eligible
@@ -163,6 +180,36 @@ def test_select_attend_shapes(orc, monkeypatch, Hq, Hkv, d, U, k_m, n_pos, W, n_
             first = got
         else:   # the same bits on the second call (fixed merge order)
             assert all(torch.equal(x, y) for x, y in zip(first, got))
+    assert F.infllm_workspace_status(ws) == 0
+
+
+# one launch for rows with more scores than one search takes (as at the
+# 1M-token context): each slice publishes only its best k_m.  The library
+# takes this form only with the split count set by hand, read once per
+# process, so it runs in a child process.
+CUT_SHAPES = [
+    (4, 2, 128, 4000, 32, 1, 512, 128, False, "bf16"),    # best 32 of 128 per slice
+    (8, 1, 128, 8191, 32, 1, 512, 128, True, "bf16"),     # 8,191 units: best 32 of 256 per slice
+]
+
+
+def test_select_attend_candidate_cut():
+    import os
+    import subprocess
+    import sys
+    here = os.path.dirname(os.path.abspath(__file__))
+    code = ("import sys\n"
+            "sys.path[:0] = [%r, %r]\n"
+            "from oracle import oracle as orc\n"
+            "import test_gpu_select_attend as t\n"
+            "for sh in t.CUT_SHAPES:\n"
+            "    print('shape', sh, flush=True)\n"
+            "    t.run_shape(orc, *sh, plan=t.ANY_PLAN, cut=True)\n"
+            "print('ok', flush=True)\n") % (here, os.path.dirname(here))
+    env = dict(os.environ, INFLLM_STEP_SPLITS="48")
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout + r.stderr
 
 
 def test_select_attend_bad_positions(orc):
