@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -33,7 +35,34 @@ const Tuning& tuning() {
 
 }  // namespace infllm
 
+// Scratch memory of infllm_select_attend_static: the workspace of one decode
+// step, for callers that cannot allocate.  Each GPU holds its own copy until
+// the process ends; device globals start zero-filled, and every call leaves
+// the counters in it at zero.  Host code never passes the array's name to a
+// kernel (on the host it only names the symbol): the device address comes
+// from hipGetSymbolAddress, once per device.
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch array's device address on the current device.
+infllm_status static_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return INFLLM_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return INFLLM_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return INFLLM_OK;
+}
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -542,6 +571,15 @@ static infllm_status attend_impl(const infllm_config* cfg, int32_t batch, const 
   return launched(mfma ? launch_attend_prefill(a, splits, s) : launch_attend_rows(a, splits, s));
 }
 
+// Both halves' argument checks of a decode step, before anything is
+// enqueued, and the step's workspace layout.
+static infllm_status step_check(const infllm_config* cfg, int32_t batch, const void* q,
+                                int64_t q_cap, int64_t q_off, int64_t q_pos, const int64_t* pos,
+                                int32_t n_pos, const float* unit_repr, int32_t n_units,
+                                const void* k, const void* v, int64_t kv_cap, float* scores,
+                                int32_t* sel, void* out, float* lse, int64_t out_cap,
+                                int64_t out_off, void* stream, StepWs* w);
+
 // One decode step on a workspace laid out by step_ws_layout (arguments
 // already validated): the fused launch, or the selection and attention
 // launches with both sets of counters in the workspace's counter region.
@@ -600,6 +638,25 @@ static infllm_status step_launch(const infllm_config* cfg, int32_t batch, const 
   return launched(launch_select_attend(sa, aa, w.plan, p, st));
 }
 
+static infllm_status step_check(const infllm_config* cfg, int32_t batch, const void* q,
+                                int64_t q_cap, int64_t q_off, int64_t q_pos, const int64_t* pos,
+                                int32_t n_pos, const float* unit_repr, int32_t n_units,
+                                const void* k, const void* v, int64_t kv_cap, float* scores,
+                                int32_t* sel, void* out, float* lse, int64_t out_cap,
+                                int64_t out_off, void* stream, StepWs* w) {
+  if (cfg && cfg->top_k > 0 && !sel) return INFLLM_ERR_INVALID_ARG;
+  if (pos && (uintptr_t)pos % 8 != 0) return INFLLM_ERR_INVALID_ARG;
+  const int64_t qp = pos ? 0 : q_pos;
+  infllm_status st = score_impl(cfg, batch, q, q_cap, q_off, qp, pos, 1, n_pos, unit_repr, n_units,
+                                scores, sel, nullptr, 0, stream, true);
+  if (st != INFLLM_OK) return st;
+  st = attend_impl(cfg, batch, q, q_cap, q_off, qp, pos, 1, n_pos, k, v, kv_cap, sel, out, lse,
+                   out_cap, out_off, nullptr, 0, stream, true);
+  if (st != INFLLM_OK) return st;
+  *w = step_ws_layout(cfg, batch, n_pos, n_units);
+  return INFLLM_OK;
+}
+
 extern "C" {
 
 infllm_status infllm_attend(const infllm_config* cfg, int32_t batch, const void* q, int64_t q_cap,
@@ -630,21 +687,37 @@ infllm_status infllm_select_attend(const infllm_config* cfg, int32_t batch, cons
                                    float* scores, int32_t* sel, void* out, float* lse,
                                    int64_t out_cap, int64_t out_off, void* workspace,
                                    size_t workspace_bytes, void* stream) {
-  if (cfg && cfg->top_k > 0 && !sel) return INFLLM_ERR_INVALID_ARG;
-  if (pos && (uintptr_t)pos % 8 != 0) return INFLLM_ERR_INVALID_ARG;
-  const int64_t qp = pos ? 0 : q_pos;
-  // both halves' argument checks, before anything is enqueued
-  infllm_status st = score_impl(cfg, batch, q, q_cap, q_off, qp, pos, 1, n_pos, unit_repr, n_units,
-                                scores, sel, nullptr, 0, stream, true);
+  StepWs w;
+  infllm_status st = step_check(cfg, batch, q, q_cap, q_off, q_pos, pos, n_pos, unit_repr, n_units,
+                                k, v, kv_cap, scores, sel, out, lse, out_cap, out_off, stream, &w);
   if (st != INFLLM_OK) return st;
-  st = attend_impl(cfg, batch, q, q_cap, q_off, qp, pos, 1, n_pos, k, v, kv_cap, sel, out, lse,
-                   out_cap, out_off, nullptr, 0, stream, true);
-  if (st != INFLLM_OK) return st;
-  const StepWs w = step_ws_layout(cfg, batch, n_pos, n_units);
   if (!workspace || workspace_bytes < w.total || !aligned16(workspace))
     return INFLLM_ERR_WORKSPACE;
-  return step_launch(cfg, batch, q, q_cap, q_off, qp, pos, n_pos, unit_repr, n_units, k, v, kv_cap,
-                     scores, sel, out, lse, out_cap, out_off, w, (char*)workspace,
+  return step_launch(cfg, batch, q, q_cap, q_off, pos ? 0 : q_pos, pos, n_pos, unit_repr, n_units,
+                     k, v, kv_cap, scores, sel, out, lse, out_cap, out_off, w, (char*)workspace,
+                     (hipStream_t)stream);
+}
+
+infllm_status infllm_select_attend_static(const infllm_config* cfg, int32_t batch, const void* q,
+                                          int64_t q_cap, int64_t q_off, int64_t q_pos,
+                                          const int64_t* pos, int32_t n_pos,
+                                          const float* unit_repr, int32_t n_units, const void* k,
+                                          const void* v, int64_t kv_cap, float* scores,
+                                          int32_t* sel, void* out, float* lse, int64_t out_cap,
+                                          int64_t out_off, void* stream) {
+  StepWs w;
+  infllm_status st = step_check(cfg, batch, q, q_cap, q_off, q_pos, pos, n_pos, unit_repr, n_units,
+                                k, v, kv_cap, scores, sel, out, lse, out_cap, out_off, stream, &w);
+  if (st != INFLLM_OK) return st;
+  // the step must fit the scratch array, with its counters inside the
+  // fixed-size counter region (so that calls of any shape can follow)
+  if (w.total > kStaticScratchBytes || w.sync_bytes > kWsHeaderBytes + kWsCounterBytes)
+    return INFLLM_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = static_scratch(&ws);
+  if (st != INFLLM_OK) return st;
+  return step_launch(cfg, batch, q, q_cap, q_off, pos ? 0 : q_pos, pos, n_pos, unit_repr, n_units,
+                     k, v, kv_cap, scores, sel, out, lse, out_cap, out_off, w, (char*)ws,
                      (hipStream_t)stream);
 }
 

@@ -28,6 +28,7 @@ EXPORTED = ("infllm_num_units", "infllm_num_eligible", "infllm_workspace_size",
             "infllm_score_units", "infllm_score_units_qsum",
             "infllm_score_units_varlen", "infllm_select_units", "infllm_topk_units",
             "infllm_attend", "infllm_attend_varlen", "infllm_select_attend",
+            "infllm_select_attend_static",
             "infllm_workspace_layout", "infllm_workspace_status", "infllm_step_plan",
             "infllm_status_string", "infllm_abi_version")
 
@@ -91,6 +92,10 @@ def lib() -> ctypes.CDLL:
         L.infllm_select_attend.argtypes = [_cfgp, _i32, _vp, _i64, _i64, _i64, _vp, _i32, _vp, _i32,
                                            _vp, _vp, _i64, _vp, _vp, _vp, _vp, _i64, _i64, _vp,
                                            _sz, _vp]
+        L.infllm_select_attend_static.restype = _i32
+        L.infllm_select_attend_static.argtypes = [_cfgp, _i32, _vp, _i64, _i64, _i64, _vp, _i32, _vp,
+                                                  _i32, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _i64,
+                                                  _i64, _vp]
         L.infllm_topk_units.restype = _i32
         L.infllm_topk_units.argtypes = [_cfgp, _i32, _i32, _vp, _i32, _vp, _vp, _sz, _vp]
         L.infllm_attend.restype = _i32
@@ -441,3 +446,33 @@ def infllm_select_attend(cfg, q, q_off: int, q_pos: int, n_pos: int, unit_repr, 
         unit_repr.data_ptr(), U, k.data_ptr(), v.data_ptr(), k.shape[2], scores.data_ptr(),
         sel.data_ptr(), out.data_ptr(), _ptr(lse), out.shape[2], out_off, wp, wb,
         _stream(stream, q)))
+
+
+def infllm_select_attend_static(cfg, q, q_off: int, q_pos: int, n_pos: int, unit_repr, k, v, scores,
+                                sel, out, lse=None, out_off: int = 0, pos=None,
+                                stream=None) -> None:
+    """infllm_select_attend on the library's own scratch memory (no workspace:
+    nothing is allocated)."""
+    dt = _dtype_of(cfg)
+    _check(q, "q", dt, 4)
+    _check(k, "k", dt, 4)
+    _check(v, "v", dt, 4)
+    _check(out, "out", dt, 4)
+    _check(unit_repr, "unit_repr", torch.float32, 4)
+    _check(scores, "scores", torch.float32, 4)
+    _check(sel, "sel", torch.int32, 4)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, 3)
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    batch, U = q.shape[0], unit_repr.shape[2]
+    if pos is not None:
+        _check_pos(pos, batch)
+    if tuple(scores.shape) != (batch, cfg.n_kv_heads, n_pos, U):
+        raise ValueError("scores must be [batch, H_kv, n_pos, U]")
+    if tuple(sel.shape) != (batch, cfg.n_kv_heads, n_pos, cfg.top_k):
+        raise ValueError("sel must be [batch, H_kv, n_pos, k_m]")
+    _raise("infllm_select_attend_static", lib().infllm_select_attend_static(
+        ctypes.byref(cfg), batch, q.data_ptr(), q.shape[2], q_off, q_pos, _ptr(pos), n_pos,
+        unit_repr.data_ptr(), U, k.data_ptr(), v.data_ptr(), k.shape[2], scores.data_ptr(),
+        sel.data_ptr(), out.data_ptr(), _ptr(lse), out.shape[2], out_off, _stream(stream, q)))

@@ -442,6 +442,33 @@ INFLLM_API infllm_status infllm_select_attend(const infllm_config *cfg, int32_t 
                                    void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * infllm_select_attend_static -- infllm_select_attend without a workspace
+ * argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  It
+ * allocates nothing: the step's workspace is a scratch array of 16 MiB
+ * inside the library, one per GPU (each GPU that runs it holds the array
+ * until the process ends; the current device's copy is used, its address
+ * taken once per device), zero-filled at load and left with its counters
+ * at zero by every call.
+ *
+ * Arguments, results and errors as infllm_select_attend, except:
+ * INFLLM_ERR_WORKSPACE when the step needs more than the 16 MiB
+ * (infllm_workspace_size(cfg, INFLLM_CALL_SELECT_ATTEND, batch, n_units,
+ * 1, n_pos)) or more than the 64 KiB counter region (16 bytes per
+ * (sequence, KV head, position) in the separate-call form, 80 in the
+ * one-launch form); INFLLM_ERR_HIP when the array's address cannot be
+ * obtained.  Every call on a GPU shares that GPU's array: calls that
+ * overlap in time on one GPU (other streams, other threads) race and give
+ * wrong results.  The status word of infllm_workspace_status is not
+ * readable for it.
+ */
+INFLLM_API infllm_status infllm_select_attend_static(
+    const infllm_config *cfg, int32_t batch, const void *q, int64_t q_cap, int64_t q_off,
+    int64_t q_pos, const int64_t *pos, int32_t n_pos, const float *unit_repr, int32_t n_units,
+    const void *k, const void *v, int64_t kv_cap, float *scores, int32_t *sel, void *out,
+    float *lse, int64_t out_cap, int64_t out_off, void *stream);
+
+/*
  * infllm_workspace_layout -- where a call keeps its counters: bytes
  * [*counters_begin, *counters_end) of its workspace (both 0 if it has
  * none), and *total = infllm_workspace_size of the same arguments.  Host

@@ -31,7 +31,7 @@ def cfg(**kw):
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 19
+    assert len(names) == 20
     assert set(names) == set(F.EXPORTED)
     L = F.lib()
     for n in names:
@@ -336,3 +336,24 @@ def test_attend_workspace_sizing():
     st = L.infllm_attend(ctypes.byref(c), 4, FAKE, 1, 0, 131072, 1, 1, FAKE, FAKE, 131328, FAKE,
                          FAKE, None, 1, 0, FAKE, ws_dec - 1, None)
     assert st == F.INFLLM_ERR_WORKSPACE
+
+
+def test_static_scratch_limits():
+    """infllm_select_attend_static refuses, before any device call, a step
+    whose workspace exceeds the library's 16 MiB scratch array or whose
+    counters exceed the fixed 64 KiB counter region, and validates its
+    arguments like infllm_select_attend."""
+    c = cfg(top_k=32)
+    L = F.lib()
+    r = ctypes.byref(c)
+
+    def call(batch, n_pos, U=1023, sel=FAKE):
+        return L.infllm_select_attend_static(r, batch, FAKE, 1 << 20, 0, 131072, None, n_pos, FAKE,
+                                             U, FAKE, FAKE, 131072 + 4096, FAKE, sel, FAKE, None,
+                                             1 << 20, 0, None)
+    # 64 x 8 x 64 rows: counters beyond the region (and partials beyond 16 MiB)
+    big = F.infllm_workspace_layout(c, F.INFLLM_CALL_SELECT_ATTEND, 64, 1023, 1, 64)
+    assert big[1] - big[0] > 65536 or big[2] > (16 << 20)
+    assert call(64, 64) == F.INFLLM_ERR_WORKSPACE
+    assert call(4, 1, sel=None) == F.INFLLM_ERR_INVALID_ARG
+    assert call(0, 1) == F.INFLLM_ERR_INVALID_ARG
