@@ -2,20 +2,24 @@
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
-Default workload: a Llama-3-8B-shaped layer (32 query / 8 KV heads, head_dim
-128, bf16), 32,768-token context, chunked encoding in 512-query chunks
-processed one after another: one step = build the unit pool over the context
-(representative tokens, r_k = 4), then for every chunk score every unit and
-keep the top 16 per KV head, then for every chunk attend over 128 initial
-tokens + 16 units + a 4,096-token window.  Selection never depends on
-attention outputs, so each of the three stages covers all 64 chunks in one
-call.  Other workloads (--workload): the 128K and 1M decode
-layers (unit pools built once beforehand; one step = 256 consecutive
-single-token decode steps, rotating over 4 layers' K/V and unit pools as a
-model's layers follow one another, so no step finds its K/V still in the
-256 MB last-level cache; --layers 1 gives the single-layer figure) and the
-Mistral-7B 64K layer (one step = build + 128 encoding chunks + 256 decode
-steps).
+Headline workload: a Llama-3-8B-shaped layer (32 query / 8 KV heads,
+head_dim 128, bf16), 32,768-token context, chunked encoding in 512-query
+chunks: one step = build the unit pool over the context (representative
+tokens, r_k = 4), then for every chunk score every unit and keep the top 16
+per KV head, then for every chunk attend over 128 initial tokens + 16 units
++ a 4,096-token window.  Selection never depends on attention outputs, so
+each of the three stages covers all 64 chunks in one call; the record also
+times the same pass chunk by chunk (one call of each kind per chunk).
+
+Without --workload the same line then carries a sub-record ("workloads")
+for every other workload: the 128K and 1M decode layers (unit pools built
+once beforehand; one step = 256 consecutive single-token decode steps,
+rotating over 4 layers' K/V and unit pools as a model's layers follow one
+another, so no step finds its K/V still in the 256 MB last-level cache;
+--layers 1 gives the single-layer figure), the Mistral-7B 64K layer with
+representative tokens and with mean-of-keys units (one step = build + 128
+encoding chunks + 256 decode steps) and the tiny fp32 layer.  --workload
+NAME measures one workload only.
 
 Before the W warm-up steps, untimed steps run for --settle seconds (1 by
 default) so that the GPU clocks are in steady state when timing starts.
@@ -25,10 +29,12 @@ whole step (over sequences and query positions, the number of keys each
 query attends, averaged over KV heads).  `roofline` is for the attention
 kernel of the dominant pass (chunked encoding if the workload has one):
 algorithmic work per launch -- MFMA flops 4*d*H_q*sum|A(t)| for chunks, or
-the K/V rows, queries and outputs it must move for decode -- divided by its
-average launch time: HIP events on the launch stream, inside the timed
-region, around each step's attention launches.  `cpu_baseline` is the fp64 oracle on a bounded sample of
-the same work on the host cores.
+the K/V rows, queries, outputs (and unit rows, for the one-launch decode
+step) it must move for decode -- divided by its average launch time: HIP
+events on the launch stream, inside the timed region, around each step's
+attention launches; `frac_from_profile` is the same work over the kernel's
+average in the committed rocprofv3 trace.  `cpu_baseline` is the fp64
+oracle on a bounded sample of the same work on the host cores.
 """
 from __future__ import annotations
 
@@ -121,6 +127,11 @@ class Pipeline:
             # per-chunk view [chunk, b, H_kv, 1, k_m]
             self.sel_enc = self.enc_sel.permute(2, 0, 1, 3).unsqueeze(3)
             self.out_enc = torch.empty_like(self.inp["q"])
+            # the chunk-by-chunk form's buffers (one chunk per call)
+            self.seq_scores = torch.empty((b, Hkv, 1, self.U), dtype=torch.float32, device=dev)
+            self.seq_sel = torch.empty((b, Hkv, 1, w.top_k), dtype=torch.int32, device=dev)
+            self.seq_score_ws = F.workspace(cfg, F.INFLLM_CALL_SCORE, b, 0, w.chunk, 1, device=dev)
+            self.seq_attn_ws = F.workspace(cfg, F.INFLLM_CALL_ATTEND, b, 0, w.chunk, 1, device=dev)
         if self.decode:
             self.dec_score_ws = F.workspace(cfg, F.INFLLM_CALL_SELECT, b, 0, 1, 1, device=dev)
             self.dec_attn_ws = F.workspace(cfg, F.INFLLM_CALL_ATTEND, b, 0, 1, 1, device=dev)
@@ -225,6 +236,24 @@ class Pipeline:
                 self._attend(inp["q_dec"], s, w.n_ctx + s, 1, self.sel_dec[s], self.out_dec,
                              self.dec_attn_ws, s % nl)
             self._mark(marks, "dec_end")
+
+    def step_sequential(self):
+        """The encoding pass with one call of each kind per chunk, chunk after
+        chunk (the chunk-by-chunk form of the same work: the results are
+        identical to step()'s)."""
+        w, inp, cfg = self.w, self.inp, self.cfg
+        self.build()
+        for c in range(self.n_chunks):
+            t0 = c * w.chunk
+            if self.block_qsum is not None:
+                F.infllm_score_units_qsum(cfg, self.block_qsum, t0, w.chunk, 1, self.repr,
+                                          self.seq_scores)
+            else:
+                F.infllm_score_units(cfg, inp["q"], t0, t0, w.chunk, 1, self.repr, self.seq_scores,
+                                     self.seq_score_ws)
+            F.infllm_topk_units(cfg, self.seq_scores, self.seq_sel)
+            F.infllm_attend(cfg, inp["q"], t0, t0, w.chunk, 1, inp["k"], inp["v"], self.seq_sel,
+                            self.out_enc, None, t0, self.seq_attn_ws)
 
     def work(self):
         """Per pass: (attended KV tokens, attention flops, attention bytes)."""
@@ -397,7 +426,7 @@ class StreamPipeline:
 CPU_SAMPLE_SECONDS = 10.0
 
 
-def cpu_baseline(w: synth.Workload, pipe: Pipeline) -> dict:
+def cpu_baseline(w: synth.Workload, pipe: Pipeline, seconds: float = CPU_SAMPLE_SECONDS) -> dict:
     """The oracle on a bounded sample of the same work, about
     CPU_SAMPLE_SECONDS long: for chunked encoding, whole chunks (score, top-k,
     attention, sequence 0) from the last backwards, each with its share of
@@ -416,7 +445,7 @@ def cpu_baseline(w: synth.Workload, pipe: Pipeline) -> dict:
         U = orc.num_units(w.n_ctx, B, n_init)
         share = max(1, math.ceil(U / n_chunks))          # units per chunk of the build
         done = 0
-        while done < n_chunks and time.time() - t_start < CPU_SAMPLE_SECONDS:
+        while done < n_chunks and time.time() - t_start < seconds:
             u0 = min(done * share, max(U - share, 0))
             for h in range(w.n_kv_heads):
                 if w.rep_mode == "mean":
@@ -437,7 +466,7 @@ def cpu_baseline(w: synth.Workload, pipe: Pipeline) -> dict:
     else:
         qd0 = pipe.inp["q_dec"][:1].cpu()
         done = 0
-        while done < w.decode_steps and time.time() - t_start < CPU_SAMPLE_SECONDS:
+        while done < w.decode_steps and time.time() - t_start < seconds:
             s = done
             t = w.n_ctx + s
             qd = qd0[:, :, s:s + 1]
@@ -481,6 +510,30 @@ def stored_traffic(kernel: str, workload: str):
         if h.hexdigest() != fields["kernel_source_sha256"]:
             return None
         return int(fields["hbm_bytes_per_launch"])
+    except (KeyError, OSError, ValueError):
+        return None
+
+
+def stored_profile_us(kernel: str, workload: str):
+    """Average duration (us) of the kernel in the committed rocprofv3 kernel
+    trace summary (profiles/<kernel>_<workload>.md: field avg_launch_us), or
+    None if there is none or the kernel's sources have changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "%s_%s.md" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if line.startswith("- ") and ":" in line:
+            key, val = line[2:].split(":", 1)
+            fields[key.strip()] = val.strip()
+    try:
+        h = hashlib.sha256()
+        for src in fields["kernel_source"].split(","):
+            h.update(open(os.path.join(ROOT, src.strip()), "rb").read())
+        if h.hexdigest() != fields["kernel_source_sha256"]:
+            return None
+        return float(fields["avg_launch_us"])
     except (KeyError, OSError, ValueError):
         return None
 
@@ -547,6 +600,12 @@ def roofline(w: synth.Workload, phase: str, work, attn_ms: float, n_calls: int,
     r["traffic"] = stored_traffic(kernel, w.name)
     r["kernel"] = "%s (%s)" % (call, kernel)
     r["avg_launch_us"] = round(attn_ms * 1e3, 2)
+    # the same work over the kernel's average duration in the committed
+    # rocprofv3 trace (another run, on another box): what the profile gives
+    prof_us = stored_profile_us(kernel, w.name)
+    r["profile_avg_launch_us"] = prof_us
+    r["frac_from_profile"] = (round(r["frac"] * attn_ms * 1e3 / prof_us, 4)
+                              if prof_us else None)
     r["launches_per_step"] = n_calls
     r["launch_timing"] = ("HIP events on the launch stream around each timed step's "
                           "attention launches (back to back), divided by their count; "
@@ -554,46 +613,17 @@ def roofline(w: synth.Workload, phase: str, work, attn_ms: float, n_calls: int,
     return r
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="llama3_8b_32k_encode", choices=sorted(synth.WORKLOADS))
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--separate-decode", action="store_true",
-                    help="decode with infllm_select_units + infllm_attend (two launches per "
-                         "step) instead of infllm_select_attend")
-    ap.add_argument("--no-peaks", action="store_true",
-                    help="skip measuring what plain library kernels reach (read, GEMM)")
-    ap.add_argument("--layers", type=int, default=None,
-                    help="decode workloads: rotate the decode steps over this many layers' "
-                         "K/V and unit pools (default 4, so that a step's K/V is not still in "
-                         "the 256 MB last-level cache from the step before; 1 for the "
-                         "single-layer figure); encoding workloads use one layer")
-    ap.add_argument("--settle", type=float, default=1.0, metavar="SECONDS",
-                    help="untimed steps for this long before the warm-up steps, so that the "
-                         "GPU clocks reach steady state (0 to skip)")
-    ap.add_argument("--stream", action="store_true",
-                    help="decode workloads: serving form -- ragged sequence lengths, a device "
-                         "position per sequence, units added to the pools as they leave the "
-                         "window (streaming unit build)")
-    ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
-                    help="after timing, run one plain device copy of MIB MiB (untimed), the "
-                         "reference kernel for scaling HBM byte counters")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: the path runs on a single MI355X with the whole unit "
-              "pool resident; runs on %d GPUs are not part of this benchmark" % args.gpus,
-              file=sys.stderr)
-        sys.exit(2)
-    torch.cuda.set_device(0)
-    w = synth.WORKLOADS[args.workload]
+# Every workload of the scope, in the order the default run measures them;
+# the first is the headline (the chunked encoding of a Llama-3-8B layer).
+ALL_WORKLOADS = ["llama3_8b_32k_encode", "llama3_8b_128k_decode", "llama3_8b_1m_decode",
+                 "mistral_7b_64k_tokens", "mistral_7b_64k_mean", "tiny_f32"]
+
+
+def measure(w: synth.Workload, args, peaks, cpu_seconds: float) -> dict:
+    """One workload: settle, warm up, time args.steps steps; the record (the
+    bench line's fields for this workload)."""
     decode_only = w.chunk == 0
     layers = (args.layers or 4) if decode_only else 1
-    if args.stream and not decode_only:
-        print("--stream applies to decode workloads", file=sys.stderr)
-        sys.exit(2)
     pipe = (StreamPipeline(w, layers=layers) if args.stream else
             Pipeline(w, layers=layers, fused_step=not args.separate_decode))
     if not pipe.encode:
@@ -628,19 +658,16 @@ def main():
         return float(np.mean([x.elapsed_time(y) for x, y in zip(marks[a], marks[b])]))
 
     work = pipe.work()
-    peaks = None if args.no_peaks else measure_peaks()
     tokens = sum(v[0] for v in work.values())
     phase = "encode" if pipe.encode else "decode"
-    line = {
+    rec = {
         "metric": "attended KV tokens/s (InfLLM attention step, Llama-3-8B layer)",
         "value": round(tokens / (ms_step * 1e-3), 1),
         "unit": "attended KV tokens/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "steps": args.steps, "warmup": args.warmup,
         "settle": {"seconds": args.settle, "steps": settle_steps},
         "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
-        "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "n_ctx": w.n_ctx,
                    "heads": "%dq/%dkv" % (w.n_q_heads, w.n_kv_heads), "head_dim": w.head_dim,
                    "chunk": w.chunk, "decode_steps": w.decode_steps, "block": w.block,
@@ -655,19 +682,50 @@ def main():
                               peaks, getattr(pipe, "fused", False))),
     }
     if args.stream:
-        line["config"]["stream"] = {"lengths": pipe.lens, "pool_units": pipe.U,
-                                    "unit_build_calls_per_step": pipe.n_builds * len(pipe.layers)}
-        line["roofline"]["traffic"] = None      # counters were taken on the fixed-pool form
+        rec["config"]["stream"] = {"lengths": pipe.lens, "pool_units": pipe.U,
+                                   "unit_build_calls_per_step": pipe.n_builds * len(pipe.layers)}
+        rec["roofline"]["traffic"] = None      # counters were taken on the fixed-pool form
     if pipe.decode:
-        # one decode step = score + top-k + attention for one token position
+        # one decode step = score + top-k + attention for one token position;
         # the decode pass of a step: from the end of its encoding pass
         ms_decode = span_ms("enc_end", "dec_end") if pipe.encode else ms_step
-        line["ms_per_decode_step"] = round(ms_decode / w.decode_steps, 5)
-        line["decode_tokens_per_s"] = round(work["decode"][0] / (ms_decode * 1e-3), 1)
+        rec["ms_per_decode_step"] = round(ms_decode / w.decode_steps, 5)
+        rec["decode_tokens_per_s"] = round(work["decode"][0] / (ms_decode * 1e-3), 1)
+        rec["decode_form"] = ("one launch per step (infllm_select_attend)"
+                              if getattr(pipe, "fused", False) else
+                              "selection and attention launches per step")
+        # the whole step against HBM: every byte the step must move (K/V rows
+        # attended, queries and outputs, every unit row scored) over the
+        # step's own time
+        step_bytes = work["decode"][2] / w.decode_steps
+        if not getattr(pipe, "fused", False):
+            step_bytes += w.batch * w.n_kv_heads * pipe.U * (w.head_dim + 1) * 4
+        gbs = step_bytes / (ms_decode / w.decode_steps * 1e-3) / 1e9
+        rec["decode_step_hbm"] = {"bytes": int(step_bytes), "GB_s": round(gbs, 1),
+                                  "frac": round(gbs / PEAK_HBM_GBS, 4), "peak": PEAK_HBM_GBS}
         if pipe.encode:
-            line["decode_roofline"] = roofline(w, "decode", work["decode"],
-                                               span_ms("dec_sel", "dec_end") / w.decode_steps,
-                                               w.decode_steps, peaks, pipe.fused)
+            rec["decode_roofline"] = roofline(w, "decode", work["decode"],
+                                              span_ms("dec_sel", "dec_end") / w.decode_steps,
+                                              w.decode_steps, peaks, pipe.fused)
+    if pipe.encode and not args.stream:
+        # the same encoding pass chunk by chunk (one call of each kind per
+        # chunk), as the pages process a context
+        n_seq = max(1, min(args.steps, 5))
+        pipe.step_sequential()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n_seq):
+            pipe.step_sequential()
+        e1.record()
+        torch.cuda.synchronize()
+        ms_seq = e0.elapsed_time(e1) / n_seq
+        enc_ms = ms_step - (span_ms("enc_end", "dec_end") if pipe.decode else 0.0)
+        rec["sequential_encode"] = {
+            "form": "build, then score + top-k + attention per chunk, %d chunks one after another"
+                    % pipe.n_chunks,
+            "ms_per_pass": round(ms_seq, 4), "batched_ms_per_pass": round(enc_ms, 4),
+            "tokens_per_s": round(work["encode"][0] / (ms_seq * 1e-3), 1)}
     if args.calibration_copy > 0:
         n = args.calibration_copy << 20
         src = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda")
@@ -675,9 +733,73 @@ def main():
         torch.cuda.synchronize()
         dst.copy_(src)                       # reads n bytes, writes n bytes
         torch.cuda.synchronize()
-        line["calibration_copy_bytes"] = n
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, pipe)
+        rec["calibration_copy_bytes"] = n
+    if cpu_seconds > 0:
+        rec["cpu_baseline"] = cpu_baseline(w, pipe, cpu_seconds)
+    del pipe
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default=None, choices=sorted(synth.WORKLOADS),
+                    help="measure this workload only (default: the 32K encoding headline, then "
+                         "every other workload as a sub-record of the same line)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate-decode", action="store_true",
+                    help="decode with infllm_select_units + infllm_attend (two launches per "
+                         "step) instead of infllm_select_attend")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip measuring what plain library kernels reach (read, GEMM)")
+    ap.add_argument("--layers", type=int, default=None,
+                    help="decode workloads: rotate the decode steps over this many layers' "
+                         "K/V and unit pools (default 4, so that a step's K/V is not still in "
+                         "the 256 MB last-level cache from the step before; 1 for the "
+                         "single-layer figure); encoding workloads use one layer")
+    ap.add_argument("--settle", type=float, default=1.0, metavar="SECONDS",
+                    help="untimed steps for this long before the warm-up steps, so that the "
+                         "GPU clocks reach steady state (0 to skip)")
+    ap.add_argument("--stream", action="store_true",
+                    help="decode workloads: serving form -- ragged sequence lengths, a device "
+                         "position per sequence, units added to the pools as they leave the "
+                         "window (streaming unit build)")
+    ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
+                    help="after timing, run one plain device copy of MIB MiB (untimed), the "
+                         "reference kernel for scaling HBM byte counters")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the path runs on a single MI355X with the whole unit "
+              "pool resident; runs on %d GPUs are not part of this benchmark" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    names = [args.workload] if args.workload else ALL_WORKLOADS
+    if args.stream and any(synth.WORKLOADS[n].chunk > 0 for n in names):
+        print("--stream applies to decode workloads (name one with --workload)", file=sys.stderr)
+        sys.exit(2)
+    peaks = None if args.no_peaks else measure_peaks()
+    cpu = 0.0 if args.no_cpu_baseline else CPU_SAMPLE_SECONDS
+    head = measure(synth.WORKLOADS[names[0]], args, peaks, cpu)
+    line = {"metric": head.pop("metric"), "value": head.pop("value"), "unit": head.pop("unit"),
+            "n_gpus": 1}
+    line.update({k: head[k] for k in ("steps", "warmup", "settle", "ms_per_step")})
+    line.update({"higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+                 "dtype": head["dtype"], "data": "synthetic"})
+    for k, v in head.items():
+        if k not in line:
+            line[k] = v
+    if len(names) > 1:
+        # the other workloads of the scope, each measured the same way (a
+        # shorter oracle sample each)
+        line["workloads"] = {}
+        for n in names[1:]:
+            print("measuring %s" % n, file=sys.stderr, flush=True)
+            line["workloads"][n] = measure(synth.WORKLOADS[n], args, peaks, cpu / 2)
     print(json.dumps(line), flush=True)
 
 
