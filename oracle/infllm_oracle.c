@@ -295,14 +295,52 @@ int64_t orc_working_context(int64_t t, const int32_t *sel, int32_t k_m,
   return n;
 }
 
+/* Rotary position embedding ([GUIDE] "Operational Checklist", RoPE item:
+ * the native base theta is kept): the pairs (c, c + d/2) of x are rotated
+ * by the angle pos * theta^(-2c/d), c = 0 .. d/2 - 1 (rotate-half pairing).
+ * A negative pos undoes the rotation at -pos. */
+static void rope_rotate(double *x, int32_t d, double theta, double pos) {
+  const int32_t h = d / 2;
+  for (int32_t c = 0; c < h; ++c) {
+    const double a = pos * pow(theta, -2.0 * (double)c / (double)d);
+    const double cs = cos(a), sn = sin(a);
+    const double x0 = x[c], x1 = x[c + h];
+    x[c] = x0 * cs - x1 * sn;
+    x[c + h] = x1 * cs + x0 * sn;
+  }
+}
+
+/* Position of token p inside the working context of the chunk whose first
+ * query sits at t0 ([GUIDE] "Operational Checklist": local relative
+ * positional offsets within memory units keep positions in the pretrained
+ * range).  Reading: positions by place in the working context -- the
+ * initial tokens keep 0 .. n_init-1; the unit in slot m of the selection
+ * occupies n_init + m*B + (offset of p in its block); the local tokens from
+ * lo = max(n_init, t0 - W + 1) on (the first query's window and every later
+ * position of the chunk, queries included) follow at n_init + k_m*B + (p -
+ * lo).  Returns -1 for a token in none of these. */
+int64_t orc_context_pos(int64_t p, int64_t t0, const int32_t *sel, int32_t k_m, int32_t B,
+                        int32_t n_init, int32_t W) {
+  const int64_t lo = maxi64(n_init, t0 - W + 1);
+  if (p < n_init) return p;
+  if (p >= lo) return n_init + (int64_t)k_m * B + (p - lo);
+  const int64_t u = p / B - n_init / B;
+  for (int32_t m = 0; m < k_m; ++m)
+    if (sel[m] >= 0 && (int64_t)sel[m] == u) return n_init + (int64_t)m * B + (p - (p / B) * B);
+  return -1;
+}
+
 /* Exact softmax attention of queries at positions t0 .. t0+L-1 (rows 0..L-1
  * of each of the G query-head arrays) over their working contexts, with
  * logits q.k/sqrt(d) ([GUIDE] listing: scaled dot-product attention).
- * out [G, L, d]; lse [G, L] = log sum_p exp(q.k_p/sqrt(d)) (may be NULL).  */
+ * out [G, L, d]; lse [G, L] = log sum_p exp(q.k_p/sqrt(d)) (may be NULL).
+ * rope_theta > 0: q and k hold vectors rotated at their absolute positions
+ * (rope_rotate); each is rotated back from its absolute position and then
+ * to its working-context position (orc_context_pos) before the product. */
 void orc_attend(const void *q, int64_t q_head_stride, int32_t G, int64_t t0,
                 int64_t L, const void *k, const void *v, int32_t d, int32_t dt,
                 const int32_t *sel, int32_t k_m, int32_t B, int32_t n_init,
-                int32_t W, double *out, double *lse) {
+                int32_t W, double rope_theta, double *out, double *lse) {
   const double scale = 1.0 / sqrt((double)d);
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t i = 0; i < L; ++i) {
@@ -311,13 +349,25 @@ void orc_attend(const void *q, int64_t q_head_stride, int32_t G, int64_t t0,
     int64_t *pos = (int64_t *)malloc(sizeof(int64_t) * (n > 0 ? n : 1));
     double *logit = (double *)malloc(sizeof(double) * (n > 0 ? n : 1));
     orc_working_context(t, sel, k_m, B, n_init, W, pos);
+    double *qv = (double *)malloc(sizeof(double) * d);
+    double *kv = (double *)malloc(sizeof(double) * d);
     for (int32_t g = 0; g < G; ++g) {
       const int64_t qrow = (int64_t)g * q_head_stride + i * d;
+      for (int32_t c = 0; c < d; ++c) qv[c] = ld(q, qrow + c, dt);
+      if (rope_theta > 0.0) {
+        rope_rotate(qv, d, rope_theta, -(double)t);
+        rope_rotate(qv, d, rope_theta, (double)orc_context_pos(t, t0, sel, k_m, B, n_init, W));
+      }
       double m = -INFINITY;
       for (int64_t a = 0; a < n; ++a) {
+        for (int32_t c = 0; c < d; ++c) kv[c] = ld(k, pos[a] * d + c, dt);
+        if (rope_theta > 0.0) {
+          rope_rotate(kv, d, rope_theta, -(double)pos[a]);
+          rope_rotate(kv, d, rope_theta,
+                      (double)orc_context_pos(pos[a], t0, sel, k_m, B, n_init, W));
+        }
         double dot = 0.0;
-        for (int32_t c = 0; c < d; ++c)
-          dot += ld(q, qrow + c, dt) * ld(k, pos[a] * d + c, dt);
+        for (int32_t c = 0; c < d; ++c) dot += qv[c] * kv[c];
         logit[a] = dot * scale;
         if (logit[a] > m) m = logit[a];
       }
@@ -331,6 +381,8 @@ void orc_attend(const void *q, int64_t q_head_stride, int32_t G, int64_t t0,
       }
       if (lse) lse[(int64_t)g * L + i] = m + log(denom);
     }
+    free(qv);
+    free(kv);
     free(pos);
     free(logit);
   }

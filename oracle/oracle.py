@@ -68,7 +68,9 @@ def lib():
         L.orc_working_context.restype = _i64
         L.orc_working_context.argtypes = [_i64, _vp, _i32, _i32, _i32, _i32, _vp]
         L.orc_attend.argtypes = [_vp, _i64, _i32, _i64, _i64, _vp, _vp, _i32, _i32, _vp,
-                                 _i32, _i32, _i32, _i32, _vp, _vp]
+                                 _i32, _i32, _i32, _i32, _f64, _vp, _vp]
+        L.orc_context_pos.restype = _i64
+        L.orc_context_pos.argtypes = [_i64, _i64, _vp, _i32, _i32, _i32, _i32]
         _LIB = L
     return _LIB
 
@@ -183,8 +185,10 @@ def working_context(t: int, sel, B: int, n_init: int, W: int) -> np.ndarray:
     return out[:n]
 
 
-def attend(qg, t0: int, k, v, sel, B: int, n_init: int, W: int):
-    """Queries rows 0..L-1 of qg sit at positions t0..t0+L-1.
+def attend(qg, t0: int, k, v, sel, B: int, n_init: int, W: int, rope_theta: float = 0.0):
+    """Queries rows 0..L-1 of qg sit at positions t0..t0+L-1.  rope_theta > 0:
+    q and k are rotated at their absolute positions and the attention re-
+    indexes them to working-context positions.
     -> out f64 [G, L, d], lse f64 [G, L]."""
     qg, k, v = _host(qg), _host(k), _host(v)
     G, L, d = qg.shape
@@ -193,8 +197,14 @@ def attend(qg, t0: int, k, v, sel, B: int, n_init: int, W: int):
     lse = np.zeros((G, L), np.float64)
     if L > 0:
         lib().orc_attend(_p(qg), L * d, G, t0, L, _p(k), _p(v), d, _dt(k), _p(s), s.shape[0],
-                         B, n_init, W, _p(out), _p(lse))
+                         B, n_init, W, float(rope_theta), _p(out), _p(lse))
     return out, lse
+
+
+def context_pos(p: int, t0: int, sel, B: int, n_init: int, W: int) -> int:
+    """Working-context position of token p for the chunk starting at t0."""
+    s = _i32arr(sel)
+    return int(lib().orc_context_pos(p, t0, _p(s), s.shape[0], B, n_init, W))
 
 
 # --------------------------------------------------------------------------
@@ -239,7 +249,8 @@ def select_all(q_chunk, t0: int, repr_, *, B: int, n_init: int, W: int, k_m: int
     return scores, sel, e
 
 
-def attend_all(q_chunk, t0: int, k, v, sel, *, B: int, n_init: int, W: int):
+def attend_all(q_chunk, t0: int, k, v, sel, *, B: int, n_init: int, W: int,
+               rope_theta: float = 0.0):
     """q_chunk [b,H_q,L,d] at positions t0.., k/v [b,H_kv,n,d], sel [b,H_kv,k_m]
     -> out f64 [b,H_q,L,d], lse f64 [b,H_q,L]."""
     b, Hq, L, d = q_chunk.shape
@@ -250,6 +261,6 @@ def attend_all(q_chunk, t0: int, k, v, sel, *, B: int, n_init: int, W: int):
     for bi in range(b):
         for h in range(Hkv):
             o, l = attend(q_chunk[bi, h * G:(h + 1) * G], t0, k[bi, h], v[bi, h], sel[bi, h],
-                          B, n_init, W)
+                          B, n_init, W, rope_theta)
             out[bi, h * G:(h + 1) * G], lse[bi, h * G:(h + 1) * G] = o, l
     return out, lse

@@ -41,6 +41,19 @@ MUTANTS = [
     ("topk_keeps_one_less", "int64_t n_keep = mini64(k_m, e);\n  int64_t kept",
      "int64_t n_keep = mini64(k_m - 1, e);\n  int64_t kept"),
     ("lse_without_max", "lse[(int64_t)g * L + i] = m + log(denom);", "lse[(int64_t)g * L + i] = log(denom);"),
+    ("rope_frequency_halved", "pow(theta, -2.0 * (double)c / (double)d)",
+     "pow(theta, -1.0 * (double)c / (double)d)"),
+    ("rope_sin_sign", "x[c] = x0 * cs - x1 * sn;", "x[c] = x0 * cs + x1 * sn;"),
+    ("rope_interleaved_pairs", "const double x0 = x[c], x1 = x[c + h];\n    x[c] = x0 * cs - x1 * sn;\n    x[c + h] = x1 * cs + x0 * sn;",
+     "const double x0 = x[2 * c % d], x1 = x[(2 * c + 1) % d];\n    x[2 * c % d] = x0 * cs - x1 * sn;\n    x[(2 * c + 1) % d] = x1 * cs + x0 * sn;"),
+    ("context_lo_one_early", "const int64_t lo = maxi64(n_init, t0 - W + 1);",
+     "const int64_t lo = maxi64(n_init, t0 - W);"),
+    ("unit_position_ignores_slot", "return n_init + (int64_t)m * B + (p - (p / B) * B);",
+     "return n_init + (p - (p / B) * B);"),
+    ("local_after_units_missing", "if (p >= lo) return n_init + (int64_t)k_m * B + (p - lo);",
+     "if (p >= lo) return n_init + (p - lo);"),
+    ("query_kept_absolute", "rope_rotate(qv, d, rope_theta, (double)orc_context_pos(t, t0, sel, k_m, B, n_init, W));",
+     "rope_rotate(qv, d, rope_theta, (double)t);"),
 ]
 
 
@@ -57,6 +70,7 @@ def test_pins_kill_mutant(tmp_path, name, old, new):
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         os.path.join(ROOT, "tests", "test_oracle_pins.py"),
                         os.path.join(ROOT, "tests", "test_oracle_workloads.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_rope.py"),
                         "-k", "not reduced"],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, "mutant %s survived the pins:\n%s" % (name, r.stdout[-2000:])
