@@ -30,9 +30,20 @@
 // (max, sum, unnormalised output) rows and the last one to finish, found
 // with a per-tile counter in the workspace, merges them and writes the
 // output.  The counters return to zero at the end of every call.
+//
+// RoPE (rope.h): window tiles need nothing; each initial-token or unit tile
+// has one shift, and the wave that loaded a tile's rows turns them by it in
+// LDS after its loads land and before the barrier that hands the tile to
+// the other waves (lanes pos and pos ^ 8 of a 16-lane row hold the two
+// halves of every rotary pair); the turned keys are rounded to bf16.  The
+// tile's cosines and sines are computed two tiles ahead into one of two LDS
+// tables, so the ring keeps one barrier per tile.  Unit keys at or past the
+// chunk's first local place keep their own position; queries before n_init
+// are turned once, when loaded.
 
 #include "common.h"
 #include "kernels.h"
+#include "rope.h"
 
 namespace infllm {
 
@@ -60,6 +71,8 @@ __device__ __forceinline__ float max3(float a, float b, float c) {
 // s_waitcnt vmcnt(4 (kStages - 2)) lgkmcnt(0): the loads of the next tile
 // have landed and no LDS read of this wave is still in flight
 constexpr int kWaitRing = 0x0078;
+// s_waitcnt lgkmcnt(0) alone (vmcnt and expcnt at their maxima)
+constexpr int kWaitLgkm0 = 0xC07F;
 static_assert(kStages == 4, "kWaitRing encodes 4 loads x 2 tiles in flight");
 
 __device__ __forceinline__ int swap_bits23(int m) {
@@ -108,7 +121,16 @@ __device__ __forceinline__ void tile_window(int type, int64_t p0, int64_t t, int
   *hi = (int)(h < -1 ? -1 : (h > kKT ? kKT : h));
 }
 
-template <int G>
+// bf16 pair <-> two floats; packing rounds to nearest even
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ uint32_t bf_pack(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+template <int G, bool ROPE>
 __global__ __launch_bounds__(kThreads, 2) void k_attend_prefill(AttendArgs a, PrefillGeom geo) {
   constexpr int TQ = kRows / G;  // queries per workgroup
   const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
@@ -152,6 +174,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_prefill(AttendArgs a, Pr
   __shared__ int tiles[kMaxTiles];
   __shared__ int n_tiles_sh;
   __shared__ int last_sh;
+  // RoPE: each tile's shift (0: none), the frequencies, and two tables of
+  // cos / sin (the tile after next is computed while one is in use)
+  __shared__ int tile_turn[ROPE ? kMaxTiles : 1];
+  __shared__ double turns_sm[ROPE ? kD / 2 : 1];
+  __shared__ __attribute__((aligned(16))) float turn_cs[ROPE ? 2 : 1][2][kD / 2];
+  // chunk start -> first local place; shift of the initial tokens
+  const int64_t lo_ctx = rope_local_start(base + (int64_t)ch * a.L, a.n_init, a.W);
+  const int e_sink = (int)(a.n_init + (int64_t)a.k_m * a.B - lo_ctx);
 
   // ---------------------------------------------------------- tile list
   // [initial-token tiles][unit tiles, in sel order][window-band tiles];
@@ -198,22 +228,30 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_prefill(AttendArgs a, Pr
       all += wave_tot[w2];
     }
     const int off = n_init_tiles + before + x - cnt;
+    // slot tid: E_m = (k_m - m) B + jB - lo
+    const int e_unit = (int)((int64_t)(a.k_m - tid) * a.B + jb - lo_ctx);
     for (int i = 0; i < cnt; ++i) {
       const int64_t p0 = jb + (int64_t)(s_first + i) * kKT;
       const bool fast = p0 >= n_init && p0 + kKT - 1 <= ta - W;
       tiles[off + i] = (int)p0 | kTileUnit | (fast ? 0 : kTileMask);
+      if constexpr (ROPE) tile_turn[off + i] = e_unit;
     }
     for (int i = tid; i < n_init_tiles; i += kThreads) {
       const int64_t p0 = (int64_t)i * kKT;
       const bool fast = p0 + kKT - 1 < n_init && p0 + kKT - 1 <= ta;
       tiles[i] = (int)p0 | kTileInit | (fast ? 0 : kTileMask);
+      if constexpr (ROPE) tile_turn[i] = e_sink;
     }
     for (int i = tid; i < n_win_tiles; i += kThreads) {
       const int64_t p0 = w0 + (int64_t)i * kKT;
       const bool fast = p0 >= n_init && p0 > tb - W && p0 + kKT - 1 <= ta;
       tiles[n_init_tiles + all + i] = (int)p0 | kTileWin | (fast ? 0 : kTileMask);
+      if constexpr (ROPE) tile_turn[n_init_tiles + all + i] = 0;
     }
     if (tid == 0) n_tiles_sh = n_init_tiles + all + n_win_tiles;
+    if constexpr (ROPE) {
+      if (tid < kD / 2) turns_sm[tid] = rope_turns(a.rope_theta, kD, tid);
+    }
   }
   __syncthreads();
   const int n_tiles = n_tiles_sh;
@@ -233,6 +271,29 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_prefill(AttendArgs a, Pr
     const bf16_t* qp = Q + (qh * a.q_cap + q_row) * kD + half * 8;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qreg[ks] = *(const bf16x8*)(qp + ks * 16);
+  }
+  if constexpr (ROPE) {
+    // a query before n_init sees initial tokens only, which are turned by
+    // -E_s: turn it by -E_s too.  qreg[ks] holds columns 8 (2 ks + half) ..
+    // +7, so the pairs (c, c + 64) are qreg[ks] and qreg[ks + 4], ks < 4.
+    if (row_ok && t_row < a.n_init && e_sink != 0) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int c0 = 8 * (2 * ks + half);
+        u32x4 wl = __builtin_bit_cast(u32x4, qreg[ks]), wh = __builtin_bit_cast(u32x4, qreg[ks + 4]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float c2[2], s2[2];
+          rope_cs(e_sink, turns_sm[c0 + 2 * i], &c2[0], &s2[0]);
+          rope_cs(e_sink, turns_sm[c0 + 2 * i + 1], &c2[1], &s2[1]);
+          const float l0 = bf_lo(wl[i]), l1 = bf_hi(wl[i]), h0 = bf_lo(wh[i]), h1 = bf_hi(wh[i]);
+          wl[i] = bf_pack(rope_turn(l0, h0, c2[0], s2[0], true), rope_turn(l1, h1, c2[1], s2[1], true));
+          wh[i] = bf_pack(rope_turn(h0, l0, c2[0], s2[0], false), rope_turn(h1, l1, c2[1], s2[1], false));
+        }
+        qreg[ks] = __builtin_bit_cast(bf16x8, wl);
+        qreg[ks + 4] = __builtin_bit_cast(bf16x8, wh);
+      }
+    }
   }
 
   // ---------------------------------------------------------- staging
@@ -288,9 +349,62 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_prefill(AttendArgs a, Pr
   // __syncthreads' fence would also wait for the loads of tiles i+2 and
   // i+3.  The empty asm statements keep the compiler from moving LDS
   // accesses across it.
-  auto ring_barrier = [&]() {
+  //
+  // RoPE: cos / sin of tile j's shift into table j % 2, frequency 8 w + l
+  // by lane l < 8 of wave w.  Table j % 2 was last read while tile j - 2 was
+  // turned, before the barrier that preceded tile j - 2's math.
+  auto turn_table = [&](int j) {
+    if (j >= nt) return;
+    const int E = tile_turn[tile_begin + j];
+    if (E == 0 || lane >= 8) return;
+    const int f = 8 * wave + lane;
+    rope_cs(E, turns_sm[f], &turn_cs[j & 1][0][f], &turn_cs[j & 1][1][f]);
+  };
+  // RoPE: turn this wave's rows of tile j (landed in kbuf) by its shift.
+  // Lane l holds position l % 16 of row r = 4 grp + l / 16, i.e. chunk c =
+  // (l % 16) ^ (r % 16) (the same for both of its rows); chunk c ^ 8, the
+  // other half of its pairs, sits in lane l ^ 8.
+  auto turn_tile = [&](int j, bf16_t* kbuf) {
+    if (j >= nt) return;
+    const int E = tile_turn[tile_begin + j];
+    if (E == 0) return;
+    const int desc = tiles[tile_begin + j];
+    const int64_t p0 = desc & ~7;
+    const bool unit = (desc & 3) == kTileUnit;
+    const int c = (lane % 16) ^ ((4 * wave + lane / 16) & 15);
+    const bool low = c < 8;
+    const f32x4* ct = (const f32x4*)&turn_cs[j & 1][0][8 * (c & 7)];
+    const f32x4* st = (const f32x4*)&turn_cs[j & 1][1][8 * (c & 7)];
+    const f32x4 c0 = ct[0], c1 = ct[1], s0 = st[0], s1 = st[1];
+    const float cs[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+    const float sn[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int grp = wave + kWaves * jj;
+      const int r = 4 * grp + lane / 16;
+      u32x4* at = (u32x4*)(kbuf + grp * 4 * kD) + lane;   // row r, position lane % 16
+      u32x4 w = *at, pw;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pw[i] = __builtin_amdgcn_mov_dpp(w[i], INFLLM_DPP_ROR8, 0xF, 0xF, true);
+      // unit keys past the chunk's first local place sit at their own place
+      if (!(unit && p0 + r >= lo_ctx)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          w[i] = bf_pack(rope_turn(bf_lo(w[i]), bf_lo(pw[i]), cs[2 * i], sn[2 * i], low),
+                         rope_turn(bf_hi(w[i]), bf_hi(pw[i]), cs[2 * i + 1], sn[2 * i + 1], low));
+        *at = w;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  };
+  // tile j landed in kbuf: turn it (RoPE), then the barrier
+  auto ring_barrier = [&](int j, bf16_t* kbuf) {
     __builtin_amdgcn_s_waitcnt(kWaitRing);
     asm volatile("" ::: "memory");
+    if constexpr (ROPE) {
+      turn_tile(j, kbuf);
+      asm volatile("" ::: "memory");
+    }
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
@@ -300,7 +414,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_prefill(AttendArgs a, Pr
     load_tile(tl[1 < nt ? 1 : nt - 1], lds_k1, lds_v1);
     load_tile(tl[2 < nt ? 2 : nt - 1], lds_k2, lds_v2);
   }
-  ring_barrier();   // tile 0 landed
+  if constexpr (ROPE) {
+    turn_table(0);
+    turn_table(1);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  }
+  ring_barrier(0, lds_k0);   // tile 0 landed
 
   // One tile: issue the loads of tile i+3, then the math on tile i.  The
   // ring buffers are separate variables and the loop below is unrolled over
@@ -311,6 +433,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_prefill(AttendArgs a, Pr
                        bf16_t* vn, int i) {
     const int desc = tl[i];
     load_tile(tl[i + kStages - 1 < nt ? i + kStages - 1 : nt - 1], kn, vn);
+    if constexpr (ROPE) turn_table(i + 2);
 
     // S^T = K Q^T for 64 keys x 32 rows: two 32-key sub-tiles
     f32x16 s0 = f32x16{}, s1 = f32x16{};
@@ -404,16 +527,16 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_prefill(AttendArgs a, Pr
     const int* tl = tiles + tile_begin;
     for (int i = 0; i < nt; i += kStages) {
       tile_step(tl, lds_k0, lds_v0, lds_k3, lds_v3, i);
-      ring_barrier();
+      ring_barrier(i + 1, lds_k1);
       if (i + 1 >= nt) break;
       tile_step(tl, lds_k1, lds_v1, lds_k0, lds_v0, i + 1);
-      ring_barrier();
+      ring_barrier(i + 2, lds_k2);
       if (i + 2 >= nt) break;
       tile_step(tl, lds_k2, lds_v2, lds_k1, lds_v1, i + 2);
-      ring_barrier();
+      ring_barrier(i + 3, lds_k3);
       if (i + 3 >= nt) break;
       tile_step(tl, lds_k3, lds_v3, lds_k2, lds_v2, i + 3);
-      ring_barrier();
+      ring_barrier(i + 4, lds_k0);
     }
   }
   // the repeat loads past the end must land before the workgroup's LDS can
@@ -553,8 +676,8 @@ int64_t prefill_num_counters(const AttendArgs& a) {
   return (int64_t)((a.L + TQ - 1) / TQ) * a.n_chunks * a.Hkv * a.batch;
 }
 
-template <int G>
-static void launch_g(const AttendArgs& a, int splits, hipStream_t st) {
+template <int G, bool ROPE>
+static void launch_gr(const AttendArgs& a, int splits, hipStream_t st) {
   constexpr int TQ = kRows / G;
   PrefillGeom geo;
   geo.TQ = TQ;
@@ -564,7 +687,13 @@ static void launch_g(const AttendArgs& a, int splits, hipStream_t st) {
   const int groups = a.Hkv * a.batch;
   geo.n_items = geo.n_qtiles * a.n_chunks * groups;
   geo.xcd_groups = groups % kXcds == 0;
-  k_attend_prefill<G><<<dim3(geo.per_group * groups), kThreads, 0, st>>>(a, geo);
+  k_attend_prefill<G, ROPE><<<dim3(geo.per_group * groups), kThreads, 0, st>>>(a, geo);
+}
+
+template <int G>
+static void launch_g(const AttendArgs& a, int splits, hipStream_t st) {
+  if (a.rope_theta > 0.0) launch_gr<G, true>(a, splits, st);
+  else launch_gr<G, false>(a, splits, st);
 }
 
 hipError_t launch_attend_prefill(const AttendArgs& a, int splits, hipStream_t st) {

@@ -17,6 +17,7 @@
 // the publication protocol), so one launch produces the output.
 #include "common.h"
 #include "kernels.h"
+#include "rope.h"
 #include "score_units.h"
 
 namespace infllm {
@@ -75,17 +76,21 @@ constexpr int kMaxSplits = 64;
 // invariant into NaN rows and a nonzero status word instead of a hang.
 constexpr int kSpinLimit = 1 << 18;
 // The selector's first, bounded spin on the arrival mask before it checks
-// for slices nobody started (normally the row's scorers finish within it).
+// for slices nobody started (normally the row's scorers finish within it),
+// and an attention workgroup's on the selector's flag before it selects
+// the row itself (INFLLM_STEP_PRESPIN overrides the latter).
 constexpr int kPreSpin = 1 << 12;
 
 // LDS of one decode attention workgroup.
-template <int G, int D>
+template <int G, int D, bool ROPE = false>
 struct RowsShared {
   int64_t iv_lo[kMaxTopK];            // first key position of unit m
   int32_t iv_first[kMaxTopK + 1];     // first unit-key index of unit m (< k_m * B)
   int32_t ids[kMaxTopK];
+  int32_t iv_turn[ROPE ? kMaxTopK : 1];   // RoPE: shift E_m of unit m (rope.h)
+  double turns[ROPE ? D / 2 : 1];         // RoPE: frequencies, turns per position
   int wave_tot[kRowsThreads / 64];
-  int flag, last;
+  int flag, last, all_in;
   uint64_t todo;
   float sm_m[16][G], sm_l[16][G];
   float sm_o[16][G][D];
@@ -104,12 +109,16 @@ struct RowsShared {
 // coalesced 16-byte load per lane for bf16, D = 128); the 16 key lanes run
 // independent online softmaxes merged through LDS, and the next group of
 // keys is loaded while the current one is reduced.
-template <typename T, int D, int G>
+// ROPE: every key is turned by the shift of its place in the working
+// context (rope.h) as it is converted: lanes seg and seg ^ 8 hold the two
+// halves of each rotary pair, the cosines and sines of the last shift stay
+// in registers until a key of another shift comes.
+template <typename T, int D, int G, bool ROPE = false>
 struct RowsAttn {
   static constexpr int CPT = D / 16;
   static constexpr int kGroup = 16 * kKeysPerIter;   // keys per iteration
   const AttendArgs& a;
-  RowsShared<G, D>& sh;
+  RowsShared<G, D, ROPE>& sh;
   int tid, lane, seg, kl, pos, h, bi;
   bool valid;
   int64_t t, unit_cap, init_len, win_lo, n_local, l_begin, nl, u_begin, pu, nu;
@@ -121,10 +130,16 @@ struct RowsAttn {
   float qv[G][CPT], m[G], l[G], acc[G][CPT];
   RowRaw<T, CPT> kn[kKeysPerIter], vn[kKeysPerIter];
   bool okn[kKeysPerIter];
+  // RoPE: first local place lo, shift of the initial tokens, shift of each
+  // key in flight, and the shift whose cos / sin (sign folded in) are held
+  int64_t lo_ctx;
+  int e_sink, e_have;
+  int en[kKeysPerIter];
+  float rc[CPT], rs[CPT];
 
   // A sequence whose position does not fit its KV buffer reads no key and
   // gets NaN rows; its workgroups still take part in the merge.
-  __device__ __forceinline__ RowsAttn(const AttendArgs& a_, RowsShared<G, D>& sh_, int pos_,
+  __device__ __forceinline__ RowsAttn(const AttendArgs& a_, RowsShared<G, D, ROPE>& sh_, int pos_,
                                       int h_, int bi_)
       : a(a_), sh(sh_), pos(pos_), h(h_), bi(bi_) {
     tid = threadIdx.x;
@@ -146,6 +161,14 @@ struct RowsAttn {
     vb = (const T*)a.v + ((int64_t)bi * a.Hkv + h) * a.kv_cap * D;
     cur = 0;
     nu = 0;
+    if constexpr (ROPE) {
+      // chunk start t0 -> first local place; published by build_table's barrier
+      const int64_t t0 = valid ? base + (int64_t)(pos / a.L) * a.L : 0;
+      lo_ctx = rope_local_start(t0, a.n_init, a.W);
+      e_sink = (int)(a.n_init + (int64_t)a.k_m * a.B - lo_ctx);
+      e_have = 0;   // 0 is never turned: nothing held yet
+      if (tid < D / 2) sh.turns[tid] = rope_turns(a.rope_theta, D, tid);
+    }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       m[g] = -INFINITY;
@@ -233,6 +256,8 @@ struct RowsAttn {
       const int64_t off = p * D + seg * CPT;
       kn[j].load(kb + off);
       vn[j].load(vb + off);
+      if constexpr (ROPE)   // only unit keys lie in [n_init, lo): cur is theirs
+        en[j] = !okn[j] || p >= lo_ctx ? 0 : (p < a.n_init ? e_sink : sh.iv_turn[cur]);
     }
   }
 
@@ -266,6 +291,9 @@ struct RowsAttn {
     if (tid < a.k_m) {
       sh.iv_lo[tid] = lo;
       sh.iv_first[tid] = before + x - (int)len;
+      if constexpr (ROPE)   // slot tid: E_m = (k_m - m) B + jB - lo
+        sh.iv_turn[tid] = u < 0 ? 0 : (int)((int64_t)(a.k_m - tid) * a.B +
+                                            ((int64_t)u + a.n_init / a.B) * a.B - lo_ctx);
     }
     if (tid == 0) sh.iv_first[a.k_m] = all;
     __syncthreads();
@@ -275,11 +303,38 @@ struct RowsAttn {
     cur = 0;
   }
 
+  // cos / sin of shift E at this lane's columns, sign of its half folded in
+  __device__ __forceinline__ void hold_turn(int E) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      rope_cs(E, sh.turns[(seg & 7) * CPT + i], &rc[i], &rs[i]);
+      if (seg >= 8) rs[i] = -rs[i];
+    }
+    e_have = E;
+  }
+  // x (this lane's CPT columns of one vector) turned by -E; both lanes of
+  // every pair take the same branch (same key, or the row's query)
+  __device__ __forceinline__ void turn(float* x, int E) {
+    if (E == 0) return;
+    if (E != e_have) hold_turn(E);
+    float px[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) px[i] = dpp_f32<INFLLM_DPP_ROR8>(x[i]);
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) x[i] = fmaf(px[i], rs[i], x[i] * rc[i]);
+  }
+
+  // A query before n_init sees initial tokens only; they are turned by
+  // -E_s, so it is turned by -E_s too (every lane of the workgroup holds
+  // the same position: a uniform branch).
   __device__ __forceinline__ void make_qv() {
     const float qscale = kLog2e / sqrtf((float)D);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       qraw[g].to_f32(qv[g]);
+      if constexpr (ROPE) {
+        if (valid && t < a.n_init) turn(qv[g], e_sink);
+      }
 #pragma unroll
       for (int c = 0; c < CPT; ++c) qv[g][c] *= qscale;
     }
@@ -294,26 +349,29 @@ struct RowsAttn {
     for (int64_t b0 = lo; b0 < hi; b0 += kGroup) {
       RowRaw<T, CPT> kc[kKeysPerIter], vc[kKeysPerIter];
       bool ok[kKeysPerIter];
+      int ec[kKeysPerIter];
 #pragma unroll
       for (int j = 0; j < kKeysPerIter; ++j) {
         kc[j] = kn[j];
         vc[j] = vn[j];
         ok[j] = okn[j];
+        if constexpr (ROPE) ec[j] = en[j];
       }
       if (b0 + kGroup < hi) fetch<KIND>(b0 + kGroup, hi);  // in flight
-      step(kc, vc, ok);
+      step(kc, vc, ok, ec);
     }
   }
 
   // One group of keys: logits for every head (each key row converted once),
   // then the online softmax update; s becomes the weights p.
   __device__ __forceinline__ void step(const RowRaw<T, CPT>* kc, const RowRaw<T, CPT>* vc,
-                                       const bool* ok) {
+                                       const bool* ok, const int* ec) {
     float s[G][kKeysPerIter];
 #pragma unroll
     for (int j = 0; j < kKeysPerIter; ++j) {
       float kf[CPT];
       kc[j].to_f32(kf);
+      if constexpr (ROPE) turn(kf, ec[j]);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         float d0 = 0.f;
@@ -354,12 +412,14 @@ struct RowsAttn {
 
   // Merge of the 16 key lanes, then of the n_splits workgroups of the row
   // (split-K): each publishes its partial (max, sum, row) with device-scope
-  // stores and counts itself in on merge_count; the last to arrive clears
-  // the counter and the n_reset ints at reset (the fused step's row state),
-  // merges every partial in split order and writes the output.  stale: the
+  // stores and counts itself in on merge_count (adding 1); the last of them
+  // merges every partial in split order and writes the output.  `others`
+  // more workgroups of the row count in with 1 << 16 and merge nothing;
+  // whichever arrival completes the count clears the counter and the
+  // n_reset ints at reset (the fused step's row state).  stale: the
   // selection never arrived, the row gets NaN.
-  __device__ __forceinline__ void finish(int split, int n_splits, int* merge_count, int* reset,
-                                         int n_reset, bool stale) {
+  __device__ __forceinline__ void finish(int split, int n_splits, int* merge_count, int others,
+                                         int* reset, int n_reset, bool stale) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       if (seg == 0) {
@@ -414,14 +474,18 @@ struct RowsAttn {
       if (tid == 0) {
         const int done =
             __hip_atomic_fetch_add(merge_count, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        sh.last = done == splits - 1;
+        sh.last = (done & 0xFFFF) == splits - 1;
+        sh.all_in = done + 1 == ((others << 16) | splits);
       }
       __syncthreads();
+      if (sh.all_in) {
+        // every workgroup of the row has counted in (and is past everything
+        // it does before that): the row's counters are ready for the next call
+        if (tid == 0) __hip_atomic_store(merge_count, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid < n_reset)
+          __hip_atomic_store(reset + tid, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
       if (!sh.last) return;
-      // every workgroup of the row has counted in (and is past everything it
-      // does before that): the row's counters are ready for the next call
-      if (tid == 0) __hip_atomic_store(merge_count, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (tid < n_reset) __hip_atomic_store(reset + tid, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       // Merge every split's published rows (this one's included).  Each
       // thread's (max, sum) pairs and its output columns' first batch of
       // split values are requested together: one memory round trip when the
@@ -534,22 +598,23 @@ struct RowsAttn {
 // (position, KV head, sequence) row, each an equal share of the local keys
 // and of the units' keys.  Its first local keys are requested before the
 // selection is read and the unit table formed.
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool ROPE>
 __global__ __launch_bounds__(kRowsThreads) void k_attend_rows(AttendArgs a) {
-  __shared__ RowsShared<G, D> sh;
+  using Attn = RowsAttn<T, D, G, ROPE>;
+  __shared__ RowsShared<G, D, ROPE> sh;
   const int s = blockIdx.x, n = gridDim.x;
   const int pos = blockIdx.y, h = blockIdx.z % a.Hkv, bi = blockIdx.z / a.Hkv;
   const int64_t row = ((int64_t)bi * a.Hkv + h) * a.n_pos + pos;
-  RowsAttn<T, D, G> r(a, sh, pos, h, bi);
+  Attn r(a, sh, pos, h, bi);
   r.shares(s, s + 1, n, s, n);
   int32_t u = -1;   // this thread's sel entry, requested now
   if (r.valid && threadIdx.x < a.k_m) u = r.sel_row[threadIdx.x];
-  const bool early = r.nl >= RowsAttn<T, D, G>::kGroup;   // first group local only: in flight
-  if (early) r.template fetch<RowsAttn<T, D, G>::kLocal>(0, r.nl);
+  const bool early = r.nl >= Attn::kGroup;   // first group local only: in flight
+  if (early) r.template fetch<Attn::kLocal>(0, r.nl);
   r.build_table(u);
   r.make_qv();
   r.stream(0, r.nl + r.nu, early);
-  r.finish(s, n, a.ws_count ? a.ws_count + row : nullptr, nullptr, 0, false);
+  r.finish(s, n, a.ws_count ? a.ws_count + row : nullptr, 0, nullptr, 0, false);
 }
 
 int rows_num_splits(const AttendArgs& a) {
@@ -568,7 +633,11 @@ int64_t rows_num_counters(const AttendArgs& a) { return (int64_t)a.n_pos * a.bat
 
 template <typename T, int D, int G>
 static hipError_t launch_rows_tdg(const AttendArgs& a, int splits, hipStream_t st) {
-  k_attend_rows<T, D, G><<<dim3(splits, a.n_pos, a.batch * a.Hkv), kRowsThreads, 0, st>>>(a);
+  const dim3 grid(splits, a.n_pos, a.batch * a.Hkv);
+  if (a.rope_theta > 0.0)
+    k_attend_rows<T, D, G, true><<<grid, kRowsThreads, 0, st>>>(a);
+  else
+    k_attend_rows<T, D, G, false><<<grid, kRowsThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -602,24 +671,27 @@ hipError_t launch_attend_rows(const AttendArgs& a, int splits, hipStream_t st) {
 // when the row has too many to search at once (the row's top k_m is among
 // the union of every slice's top k_m, ties to the lower index in both) --
 // and sets the slice's bit in the row's arrival mask with an atomic OR.
-// The workgroup whose bit completes the mask selects the row's k_m units
-// from the candidates, publishes them and sets the row's ready flag.
-// Every workgroup of the row (scoring ones after their slice) attends its
-// share of the local keys, which need no selection, then reads the ready
-// flag and attends its share of the selected units' keys.  If the flag is
-// not set yet, it first checks the slices' started flags and scores every
-// slice not started yet itself (publishing the same candidates and setting
-// the same bit, so a slice scored twice is harmless), then waits for it.
+// One more workgroup per row, the selector, waits for the full mask,
+// selects the row's k_m units from the candidates, publishes them and sets
+// the row's ready flag.  Every other workgroup of the row (scoring ones
+// after their slice) attends its share of the local keys, which need no
+// selection, then reads the ready flag and attends its share of the
+// selected units' keys.
 //
-// Why every wait ends: a workgroup waits only after every slice of its row
-// has been started -- by itself, or by workgroups that were running when it
-// looked -- and scoring a slice (and selecting, for the one that completes
-// the mask) never waits on anything, so every bit of the mask gets set and
-// the selection is published.  This holds whatever the dispatch order, the grid size
-// or the number of workgroups resident at once, and needs no atomic at the
-// start of the launch.  All workgroups then publish their partial rows; the
-// last to arrive merges them and clears the row's mask, flags and counter
-// for the next call.
+// Why every wait ends, whatever the dispatch order, the grid size or the
+// number of workgroups resident at once: no workgroup waits on one that
+// may not be running.  Before waiting for the mask (the selector, or an
+// attention workgroup whose flag is not set yet) a workgroup checks the
+// slices' started flags and scores every slice not started itself
+// (publishing the same candidates and setting the same bit, so a slice
+// scored twice is harmless); scoring never waits, so the mask fills.  An
+// attention workgroup then spins a bounded time for the selector's flag;
+// if it has not come, it selects the row itself: the same candidates and
+// the same search give the same units, so every copy it or the selector
+// stores is the same.  All attention workgroups publish their partial rows
+// and the last of them merges; the selector counts in on the same counter
+// (with a separate field), and the last arrival of all clears the row's
+// mask, flags and counter for the next call.
 struct StepRow {
   uint64_t* mask;      // arrival mask of the slices
   int* ready;          // the selection is published
@@ -776,6 +848,7 @@ template <typename T, int D, int G, int NSUB, int VPT>
 __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(3)))
 void k_select_attend(ScoreArgs s, AttendArgs a, StepPlan p, StepPtrs w) {
   static_assert(kRowsThreads == kScoreThreads, "one workgroup size for both roles");
+  using Attn = RowsAttn<T, D, G>;
   __shared__ RowsShared<G, D> sh;
   __shared__ StepShared ss;
   const int N = p.n_splits, S = p.s_score;
@@ -804,13 +877,31 @@ void k_select_attend(ScoreArgs s, AttendArgs a, StepPlan p, StepPtrs w) {
     __syncthreads();
     const bool ok = ss.last || step_wait<T, G, D, NSUB, VPT>(s, p, row, pos, h, bi, y, w, ss,
                                                              mask_full);
-    const int32_t u = ok ? step_select<VPT>(s, p, row, w, ss) : -1;
-    if (tid < s.k_m)
-      __hip_atomic_store(s.sel + (int64_t)row * s.k_m + tid, u, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+    if (ok) {
+      const int32_t u = step_select<VPT>(s, p, row, w, ss);
+      if (tid < s.k_m)
+        __hip_atomic_store(s.sel + (int64_t)row * s.k_m + tid, u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
-    if (tid == 0) __hip_atomic_store(y.ready, ok ? 1 : -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) {
+      if (ok) {
+        __hip_atomic_store(y.ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {   // a time-out marks the row unless an attention workgroup selected it
+        int zero = 0;
+        __hip_atomic_compare_exchange_strong(y.ready, &zero, -1, __ATOMIC_RELAXED,
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // the flag lands before the count
+      const int done =
+          __hip_atomic_fetch_add(y.merge, 1 << 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      sh.all_in = done + (1 << 16) == ((1 << 16) | N);
+    }
+    __syncthreads();
+    if (sh.all_in && tid < kStepSyncInts)   // the last of the row: clear its state
+      __hip_atomic_store(w.sync + (int64_t)row * kStepSyncInts + tid, 0, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
   if (j < S) {
@@ -818,40 +909,63 @@ void k_select_attend(ScoreArgs s, AttendArgs a, StepPlan p, StepPtrs w) {
       __hip_atomic_store(y.started + j, (uint8_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     step_score<T, G, D, NSUB, false>(s, p, j, row, pos, h, bi, y, w, ss);
   }
-  RowsAttn<T, D, G> r(a, sh, pos, h, bi);
+  Attn r(a, sh, pos, h, bi);
   const int64_t l_lo = j < S ? (int64_t)j * p.w_score
                              : (int64_t)S * p.w_score + (int64_t)(j - S) * p.w_unit;
   r.shares(l_lo, l_lo + (j < S ? p.w_score : p.w_unit),
            (int64_t)S * p.w_score + (int64_t)(N - S) * p.w_unit, j, N);
   r.make_qv();
   // the local keys need no selection
-  r.template stream<RowsAttn<T, D, G>::kLocal>(0, r.nl, false);
+  r.template stream<Attn::kLocal>(0, r.nl, false);
   r.park();
   if (tid == 0) sh.flag = __hip_atomic_load(y.ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   int rd = sh.flag;
+  int32_t u = -1;
+  bool own = false;   // u holds this workgroup's own selection
   if (rd == 0) {
-    // not published yet: make sure every slice is being scored, then wait
-    auto ready = [&]() {
-      return __hip_atomic_load(y.ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
-    };
-    rd = step_wait<T, G, D, NSUB, VPT>(s, p, row, pos, h, bi, y, w, ss, ready) ? 1 : -1;
-    if (rd == 1) {
-      if (tid == 0) sh.flag = __hip_atomic_load(y.ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // not published yet: every slice started, then the full mask (neither
+    // wait depends on a workgroup that may not be running), then a bounded
+    // spin for the selector's flag, and the selection here if it has not come
+    if (step_wait<T, G, D, NSUB, VPT>(s, p, row, pos, h, bi, y, w, ss, mask_full)) {
+      if (tid == 0) {
+        int f = 0;
+        for (int it = 0; it < p.pre_spin && f == 0; ++it) {
+          f = __hip_atomic_load(y.ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (f == 0) __builtin_amdgcn_s_sleep(2);
+        }
+        sh.flag = f;
+      }
       __syncthreads();
       rd = sh.flag;
+      if (rd == 0) {
+        u = step_select<VPT>(s, p, row, w, ss);
+        if (tid < s.k_m)
+          __hip_atomic_store(s.sel + (int64_t)row * s.k_m + tid, u, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        __syncthreads();
+        if (tid == 0) {
+          __hip_atomic_store(y.ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_fetch_add(w.status + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        rd = 1;
+        own = true;
+      }
+    } else {
+      rd = -1;
     }
   }
   const bool stale = rd != 1;
   // the row's units, then their keys
-  int32_t u = -1;
-  if (!stale && r.valid && tid < a.k_m)
+  if (stale || !r.valid) u = -1;
+  else if (!own && tid < a.k_m)
     u = __hip_atomic_load(const_cast<int32_t*>(r.sel_row + tid), __ATOMIC_RELAXED,
                           __HIP_MEMORY_SCOPE_AGENT);
   r.restore();
   r.build_table(u);
-  r.template stream<RowsAttn<T, D, G>::kUnits>(r.nl, r.nl + r.nu, false);
-  r.finish(j, N, y.merge, w.sync + (int64_t)row * kStepSyncInts, kStepSyncInts, stale);
+  r.template stream<Attn::kUnits>(r.nl, r.nl + r.nu, false);
+  r.finish(j, N, y.merge, 1, w.sync + (int64_t)row * kStepSyncInts, kStepSyncInts, stale);
 }
 
 // Plan of a fused step.  At most kStepTargetWGs workgroups per launch (3 per
@@ -867,6 +981,10 @@ int64_t step_rows(const AttendArgs& a) { return (int64_t)a.batch * a.Hkv * a.n_p
 
 bool select_attend_plan(const ScoreArgs& s, const AttendArgs& a, StepPlan* p) {
   if (!a.bf16 || a.L != 1 || s.U < 1 || a.k_m < 1 || a.k_m > kMaxTopK) return false;
+  // re-positioned keys take the attention launch: turning them here needs
+  // ~40 more VGPRs than the three resident workgroups per CU leave (with
+  // the spills, 96 against 53 us per step at 128K in two launches)
+  if (a.rope_theta > 0.0) return false;
   const int G = a.Hq / a.Hkv;
   if (G != 1 && G != 2 && G != 4 && G != 8) return false;
   const int64_t rows = step_rows(a);
@@ -915,6 +1033,7 @@ bool select_attend_plan(const ScoreArgs& s, const AttendArgs& a, StepPlan* p) {
   p->w_score = (int)(x / 1024.0 + 0.5);
   p->w_unit = (int)(y / 1024.0 + 0.5);
   if (p->w_score + p->w_unit == 0) p->w_unit = 1;
+  p->pre_spin = tuning().step_prespin >= 0 ? tuning().step_prespin : kPreSpin;
   return true;
 }
 

@@ -28,6 +28,8 @@ const Tuning& tuning() {
     x.prefill_splits = get("INFLLM_PREFILL_SPLITS", 1, 16);
     x.rows_wgs = get("INFLLM_ROWS_WGS", 1, 65536);
     x.step_splits = get("INFLLM_STEP_SPLITS", 2, 64);
+    const char* e = getenv("INFLLM_STEP_PRESPIN");
+    x.step_prespin = e && atoi(e) >= 0 && atoi(e) <= (1 << 20) ? atoi(e) : -1;
     return x;
   }();
   return t;
@@ -75,6 +77,9 @@ infllm_status check_config(const infllm_config* c) {
   if (c->rep_mode != INFLLM_REP_TOKENS && c->rep_mode != INFLLM_REP_MEAN)
     return INFLLM_ERR_INVALID_ARG;
   if (c->dtype != INFLLM_F32 && c->dtype != INFLLM_BF16) return INFLLM_ERR_INVALID_ARG;
+  // 0 (off) or a finite positive base; NaN fails both tests
+  if (!(c->rope_theta == 0.0 || (c->rope_theta > 0.0 && c->rope_theta < 1e300)))
+    return INFLLM_ERR_INVALID_ARG;
   if (c->rep_mode == INFLLM_REP_TOKENS && (c->rep_k < 1 || c->rep_k > c->block))
     return INFLLM_ERR_INVALID_ARG;
   const int G = c->n_q_heads / c->n_kv_heads;
@@ -141,6 +146,7 @@ AttendArgs attend_args(const infllm_config* c, int32_t batch, int32_t chunk_len,
   a.n_chunks = n_chunks;
   a.n_pos = chunk_len * n_chunks;
   a.bf16 = c->dtype == INFLLM_BF16;
+  a.rope_theta = c->rope_theta;
   return a;
 }
 

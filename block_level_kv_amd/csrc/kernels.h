@@ -29,6 +29,7 @@ inline size_t ws_counter_region(size_t counter_bytes) {
 // Zero: the built-in choice.
 struct Tuning {
   int prefill_splits, rows_wgs, step_splits;
+  int step_prespin;   // -1: the default bound
 };
 const Tuning& tuning();
 
@@ -70,6 +71,7 @@ struct TopkArgs {
 struct AttendArgs {
   int batch, Hq, Hkv, d, B, n_init, W, k_m, L, n_chunks, n_pos;
   bool bf16;
+  double rope_theta;   // 0: logits of q and k as given; > 0: re-positioned (rope.h)
   const void* q;
   int64_t q_cap, q_off, q_pos;
   const int64_t* pos;  // device [batch] first query position per sequence, or null (q_pos)
@@ -112,10 +114,13 @@ struct StepPlan {
   int units_per;           // units per scoring workgroup: 64, 128, 192 or 256
   int cand;                // candidates each scoring workgroup publishes
   int w_score, w_unit;     // local-key weights of a scoring / another workgroup
+  int pre_spin;            // polls of an attention workgroup for the selector's flag
 };
 bool select_attend_plan(const ScoreArgs& s, const AttendArgs& a, StepPlan* p);
 int64_t step_rows(const AttendArgs& a);                  // rows of one call
-constexpr int kStepSyncInts = 20;   // per row: arrival mask (2), unused, merge, started bytes (16)
+// per row: arrival mask (2), ready flag, exit counter (attention
+// workgroups in the low 16 bits, the selector above), started bytes (16)
+constexpr int kStepSyncInts = 20;
 // Row state, candidates and partials of one call: sync [rows][kStepSyncInts]
 // in the workspace's counter region, then candidate scores and ids, partial
 // rows and (max, sum) pairs.

@@ -33,12 +33,16 @@ EXPORTED = ("infllm_num_units", "infllm_num_eligible", "infllm_workspace_size",
             "infllm_status_string", "infllm_abi_version")
 
 
+ABI_VERSION = 2   # INFLLM_ABI_VERSION of include/infllm.h
+
+
 class infllm_config(ctypes.Structure):
     _fields_ = [("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("block", ctypes.c_int32),
                 ("n_init", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("rep_k", ctypes.c_int32), ("top_k", ctypes.c_int32),
-                ("rep_mode", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("rep_mode", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("rope_theta", ctypes.c_double)]
 
 
 class InfllmError(RuntimeError):
@@ -112,6 +116,10 @@ def lib() -> ctypes.CDLL:
         L.infllm_status_string.restype = ctypes.c_char_p
         L.infllm_status_string.argtypes = [_i32]
         L.infllm_abi_version.restype = _i32
+        if L.infllm_abi_version() != ABI_VERSION:   # infllm_config layout changed
+            raise RuntimeError("libinfllm.so has ABI version %d, this binding needs %d "
+                               "(rebuild: python -m block_level_kv_amd.build)"
+                               % (L.infllm_abi_version(), ABI_VERSION))
         _LIB = L
     return _LIB
 
@@ -122,9 +130,9 @@ def status_string(status: int) -> str:
 
 def make_config(*, n_q_heads: int, n_kv_heads: int, head_dim: int, block: int, n_init: int,
                 window: int, rep_k: int, top_k: int, rep_mode: int = INFLLM_REP_TOKENS,
-                dtype: int = INFLLM_BF16) -> infllm_config:
+                dtype: int = INFLLM_BF16, rope_theta: float = 0.0) -> infllm_config:
     return infllm_config(n_q_heads, n_kv_heads, head_dim, block, n_init, window, rep_k, top_k,
-                         rep_mode, dtype)
+                         rep_mode, dtype, rope_theta)
 
 
 # ------------------------------------------------------------------ helpers

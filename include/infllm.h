@@ -46,7 +46,9 @@
  *  Workspaces.  A workspace that carries counters (score calls with long
  *    chunks, the selection, split attention, the decode step) starts with
  *    a 256-byte header -- its first int32 counts waits of the decode step
- *    that timed out (infllm_workspace_status) -- followed by a counter
+ *    that timed out (infllm_workspace_status), its second the rows of the
+ *    one-launch step that an attention workgroup selected itself (a
+ *    diagnostic; both only grow) -- followed by a counter
  *    region of at least 64 KiB, then the call's data (partial sums and
  *    rows).  It must be zero-filled before its first use; every call
  *    leaves its counters at zero again.  Since every call kind keeps its
@@ -61,8 +63,11 @@
  *  Tuning.  The environment variables INFLLM_PREFILL_SPLITS,
  *    INFLLM_ROWS_WGS and INFLLM_STEP_SPLITS override split counts of the
  *    chunk attention, the decode attention and the one-launch decode step
- *    (workgroups per row).  They are read once per process, at the first
- *    call that needs them; workspace sizes follow them.
+ *    (workgroups per row); INFLLM_STEP_PRESPIN (0 .. 2^20) the polls of
+ *    the one-launch step's attention workgroups for the row's selection
+ *    before they select it themselves (same result, more work).  They are
+ *    read once per process, at the first call that needs them; workspace
+ *    sizes follow them.
  *  Units.  Unit u is absolute block j = u + floor(n_init / block); its keys
  *    are positions [max(j*block, n_init), (j+1)*block).  A context of n_ctx
  *    tokens holds floor(n_ctx/block) - floor(n_init/block) units (blocks
@@ -85,7 +90,7 @@
 extern "C" {
 #endif
 
-#define INFLLM_ABI_VERSION 1
+#define INFLLM_ABI_VERSION 2
 
 #if defined(__GNUC__) || defined(__clang__)
 #define INFLLM_API __attribute__((visibility("default")))
@@ -130,7 +135,27 @@ typedef struct {
   int32_t top_k;      /* units retrieved per chunk k_m, 0..256              */
   int32_t rep_mode;   /* infllm_rep_mode                                    */
   int32_t dtype;      /* infllm_dtype of Q, K, V and the attention output  */
+  double rope_theta;  /* 0: attention takes q and k as they are.  > 0: RoPE
+                       * base theta; q and k hold vectors rotated at their
+                       * absolute positions (rotate-half pairs (c, c + d/2)
+                       * turned by p * theta^(-2c/d)), and the attention
+                       * calls re-position every token to its place in the
+                       * working context (below).  Build and scoring calls
+                       * take q and k as they are either way.              */
 } infllm_config;
+
+/* Positions inside the working context (rope_theta > 0; InfLLM Guide,
+ * "Operational Checklist", RoPE item: the native base is kept and memory
+ * units take local relative offsets).  For the chunk whose first query is
+ * at t0, with lo = max(n_init, t0 - W + 1):
+ *   initial token p < n_init              sits at p
+ *   key p of the unit in sel slot m       sits at n_init + m*B + (p mod B)
+ *   token p >= lo (window keys, queries)  sits at n_init + k_m*B + (p - lo)
+ * A key in both a selected unit and [lo, t0 + chunk_len) takes the last
+ * rule; a repeated id takes its first slot.  Each attended logit is that of
+ * q and k turned from their absolute positions to these ones (fp64 angle
+ * reduction, fp32 rotation; the bf16 MFMA path rounds the turned keys of
+ * initial and unit tokens to bf16). */
 
 /* Units held by a context of n_ctx tokens: floor(n_ctx/B) - floor(n_init/B),
  * or 0.  Returns -1 for an invalid config. */
@@ -407,16 +432,17 @@ INFLLM_API infllm_status infllm_attend_varlen(const infllm_config *cfg, int32_t 
  * its selection: scores and sel are identical; out and lse equal up to fp32
  * rounding (the attention is split over workgroups differently).
  *
- * Where the shapes allow (bf16, k_m >= 1, and a row's scores few enough
- * to be searched at once: up to 2,048 units) it is one launch: in each
+ * Where the shapes allow (bf16, rope_theta 0, k_m >= 1, and a row's scores
+ * few enough to be searched at once: up to 2,048 units) it is one launch: in each
  * (sequence, KV head, position) row some workgroups score a slice of units
  * each and publish the scores, a selector workgroup selects the row's units
  * from them and publishes the selection, and every attention workgroup
  * attends its share of the local keys (initial tokens and window), then of
- * the selected units' keys.  A workgroup waits for a selection only after
- * checking that every slice of its row has been started, scoring the ones
- * that have not itself, so the waits end whatever the dispatch order or
- * residency.  Otherwise it runs the two calls.  With INFLLM_STEP_SPLITS
+ * the selected units' keys.  A workgroup waits for the row's scores only
+ * after checking that every slice of its row has been started, scoring the
+ * ones that have not itself, and for the selector only a bounded time
+ * before selecting the row itself (the same units), so the waits end
+ * whatever the dispatch order or residency.  Otherwise it runs the two calls.  With INFLLM_STEP_SPLITS
  * set, rows of up to 64 x 256 units also take the one launch: each slice
  * then publishes only its best k_m scores (the row's top k_m is among
  * them).  infllm_step_plan reports which form a call takes.

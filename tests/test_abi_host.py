@@ -36,7 +36,7 @@ def test_library_exports_every_declared_function():
     L = F.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.infllm_abi_version() == 1
+    assert L.infllm_abi_version() == 2
 
 
 def test_status_strings():

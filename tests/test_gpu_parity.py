@@ -29,6 +29,10 @@ CASES = {
     # bf16, G=2, d=64
     "bf16_g2_d64": LL.replace(n_ctx=2304, n_q_heads=4, n_kv_heads=2, head_dim=64, window=256,
                               top_k=3, chunk=128, scale=0.125),
+    # bf16, G=4, entries of std 1: logits of order 1, so the softmax weights
+    # (not only which keys are attended) are checked on the MFMA path
+    "bf16_g4_unit": LL.replace(n_ctx=2560, n_q_heads=8, n_kv_heads=2, window=384, top_k=4,
+                               chunk=256, scale=1.0),
 }
 
 

@@ -181,6 +181,7 @@ def run_shape(orc, Hq, Hkv, d, U, k_m, n_pos, W, n_init, varlen, dt, plan, cut=F
         else:   # the same bits on the second call (fixed merge order)
             assert all(torch.equal(x, y) for x, y in zip(first, got))
     assert F.infllm_workspace_status(ws) == 0
+    return ws
 
 
 # one launch for rows with more scores than one search takes (as at the
@@ -210,6 +211,43 @@ def test_select_attend_candidate_cut():
     r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
                        timeout=300)
     assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout + r.stderr
+
+
+# The attention workgroups' bounded spin for the selector set to zero: every
+# one that finds its row's selection unpublished selects the row itself
+# (the path that keeps the step independent of the selector being
+# dispatched); the selector may then arrive last and clear the row.  Read
+# once per process, so it runs in a child process.
+SELF_SELECT_SHAPES = [
+    (8, 2, 128, 1024, 32, 1, 1024, 128, False, "bf16"),   # 16 scorers, 512 candidates
+    (16, 2, 128, 100, 4, 1, 512, 128, True, "bf16"),      # G = 8, a position per sequence
+    (4, 2, 128, 600, 256, 1, 512, 128, False, "bf16"),    # the largest k_m
+    (32, 8, 128, 300, 8, 32, 512, 128, False, "bf16"),    # 1,536 workgroups
+    (8, 4, 64, 200, 6, 3, 384, 100, False, "bf16"),       # d = 64, sinks not B-aligned
+]
+
+
+def test_select_attend_self_selection():
+    import os
+    import subprocess
+    import sys
+    here = os.path.dirname(os.path.abspath(__file__))
+    code = ("import sys\n"
+            "sys.path[:0] = [%r, %r]\n"
+            "from oracle import oracle as orc\n"
+            "import test_gpu_select_attend as t\n"
+            "for sh in t.SELF_SELECT_SHAPES:\n"
+            "    print('shape', sh, flush=True)\n"
+            "    ws = t.run_shape(orc, *sh, plan=t.ANY_PLAN)\n"
+            "    print('self-selected rows', int(ws[4:8].view(t.torch.int32)[0]), flush=True)\n"
+            "print('ok', flush=True)\n") % (here, os.path.dirname(here))
+    env = dict(os.environ, INFLLM_STEP_PRESPIN="0")
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout + r.stderr
+    # the path ran: some rows were selected by attention workgroups
+    n_self = [int(x.split()[-1]) for x in r.stdout.splitlines() if x.startswith("self-selected")]
+    assert len(n_self) == len(SELF_SELECT_SHAPES) and sum(n_self) > 0, r.stdout
 
 
 def test_select_attend_bad_positions(orc):
