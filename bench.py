@@ -619,6 +619,90 @@ ALL_WORKLOADS = ["llama3_8b_32k_encode", "llama3_8b_128k_decode", "llama3_8b_1m_
                  "mistral_7b_64k_tokens", "mistral_7b_64k_mean", "tiny_f32"]
 
 
+def offload_decode(pipe: Pipeline, slots: int, steps: int) -> dict:
+    """The decode pass with the context's K/V in pinned host memory (the
+    GPU holding only the initial tokens, a ring of the window and a cache of
+    `slots` units per (sequence, KV head)): per step the selection, the
+    fetch (misses copied in by the GPU over the host link) and the
+    attention over the cache; layer 0, a fresh (empty) cache, the first
+    `steps` decode positions.  The last step's output is checked bit for
+    bit against the resident attention."""
+    w, cfg, inp = pipe.w, pipe.cfg, pipe.inp
+    k, v = pipe.layers[0]["k"], pipe.layers[0]["v"]
+    b, Hkv, d, B = w.batch, w.n_kv_heads, w.head_dim, w.block
+    t = time.time()
+    k_host = torch.empty(k.shape, dtype=k.dtype, pin_memory=True)
+    v_host = torch.empty(v.shape, dtype=v.dtype, pin_memory=True)
+    k_host.copy_(k)
+    v_host.copy_(v)
+    pin_s = time.time() - t
+    n_init, W = w.n_init, w.window
+    t_last = w.n_ctx + steps - 1
+    local_cap = n_init + W + steps + 64
+    R = local_cap - n_init
+    kl = torch.zeros((b, Hkv, local_cap, d), dtype=k.dtype, device="cuda")
+    vl = torch.zeros_like(kl)
+    kl[:, :, :n_init] = k[:, :, :n_init]
+    vl[:, :, :n_init] = v[:, :, :n_init]
+    pp = torch.arange(max(n_init, t_last - R + 1), t_last + 1, device="cuda")
+    rows = n_init + (pp - n_init) % R
+    kl[:, :, rows] = k[:, :, pp]
+    vl[:, :, rows] = v[:, :, pp]
+    cache_k = torch.empty((b, Hkv, slots, B, d), dtype=k.dtype, device="cuda")
+    cache_v = torch.empty_like(cache_k)
+    ws = F.workspace(cfg, F.INFLLM_CALL_ATTEND, b, 0, 1, 1)
+    out = torch.empty_like(inp["q_dec"])
+    sel = pipe.sel_dec
+
+    def run(state, n, fetch_only=False):
+        for s in range(n):
+            F.infllm_cache_fetch(cfg, sel[s], pipe.U, s + 1, k_host, v_host, cache_k, cache_v,
+                                 state)
+            if not fetch_only:
+                F.infllm_attend_cached(cfg, inp["q_dec"], s, w.n_ctx + s, 1, kl, vl, k.shape[2],
+                                       sel[s], pipe.U, cache_k, cache_v, state, out, None, s,
+                                       ws=ws)
+
+    for s in range(steps):
+        pipe._select(inp["q_dec"], s, w.n_ctx + s, 1, sel[s], pipe.dec_score_ws, 0)
+    run(F.cache_state(cfg, b, pipe.U, slots), 2)            # warm-up
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    state = F.cache_state(cfg, b, pipe.U, slots)
+    e[0].record()
+    for s in range(steps):
+        pipe._select(inp["q_dec"], s, w.n_ctx + s, 1, sel[s], pipe.dec_score_ws, 0)
+    run(state, steps)
+    e[1].record()
+    torch.cuda.synchronize()
+    hits, misses = F.infllm_cache_stats(state)
+    e[2].record()
+    run(F.cache_state(cfg, b, pipe.U, slots), steps, fetch_only=True)
+    e[3].record()
+    torch.cuda.synchronize()
+    o_res = torch.empty_like(out)
+    F.infllm_attend(cfg, inp["q_dec"], steps - 1, w.n_ctx + steps - 1, 1, 1, k, v,
+                    sel[steps - 1], o_res, None, steps - 1, pipe.dec_attn_ws)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(out[:, :, steps - 1], o_res[:, :, steps - 1]))
+    ms = e[0].elapsed_time(e[1]) / steps
+    fetch_ms = e[2].elapsed_time(e[3]) / steps
+    unit_bytes = 2 * B * d * k.element_size()           # K and V of one unit
+    host_bytes = misses * unit_bytes / steps
+    return {"form": "K/V in pinned host memory; per step select, fetch (GPU loads over the "
+                    "host link) and attention over the unit cache; fresh cache, layer 0",
+            "slots": slots, "steps": steps, "ms_per_decode_step": round(ms, 4),
+            "hit_ratio": round(hits / max(1, hits + misses), 4),
+            "misses_per_step": round(misses / steps, 2),
+            "host_bytes_per_step": int(host_bytes),
+            "fetch_ms_per_step": round(fetch_ms, 4),
+            "host_link_GB_s": round(host_bytes / (fetch_ms * 1e-3) / 1e9, 2),
+            "gpu_resident_bytes": int((kl.numel() + vl.numel() + cache_k.numel() * 2)
+                                      * k.element_size()),
+            "pin_seconds": round(pin_s, 2),
+            "last_step_equals_resident": same}
+
+
 def measure(w: synth.Workload, args, peaks, cpu_seconds: float) -> dict:
     """One workload: settle, warm up, time args.steps steps; the record (the
     bench line's fields for this workload)."""
@@ -707,6 +791,10 @@ def measure(w: synth.Workload, args, peaks, cpu_seconds: float) -> dict:
             rec["decode_roofline"] = roofline(w, "decode", work["decode"],
                                               span_ms("dec_sel", "dec_end") / w.decode_steps,
                                               w.decode_steps, peaks, pipe.fused)
+    if (pipe.decode and not pipe.encode and not args.stream and args.offload_slots > 0
+            and w.n_ctx >= (1 << 20)):
+        rec["offload"] = offload_decode(pipe, args.offload_slots,
+                                        min(args.offload_steps, w.decode_steps))
     if pipe.encode and not args.stream:
         # the same encoding pass chunk by chunk (one call of each kind per
         # chunk), as the pages process a context
@@ -768,6 +856,12 @@ def main():
                     help="decode workloads: serving form -- ragged sequence lengths, a device "
                          "position per sequence, units added to the pools as they leave the "
                          "window (streaming unit build)")
+    ap.add_argument("--offload-slots", type=int, default=64,
+                    help="1M-token decode: also run the decode pass with the K/V in pinned host "
+                         "memory and a GPU cache of this many units per (sequence, KV head) "
+                         "(0 to skip)")
+    ap.add_argument("--offload-steps", type=int, default=16,
+                    help="decode steps of that pass (each miss moves a unit over the host link)")
     ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
                     help="after timing, run one plain device copy of MIB MiB (untimed), the "
                          "reference kernel for scaling HBM byte counters")

@@ -17,7 +17,7 @@ LIB = os.path.join(HERE, "libinfllm.so")
 ROOT = os.path.dirname(HERE)
 
 SOURCES = ["infllm_api.cpp", "build.hip", "score.hip", "topk.hip", "attend_rows.hip",
-           "attend_prefill.hip"]
+           "attend_prefill.hip", "unit_cache.hip"]
 
 ARCH = "gfx950"
 

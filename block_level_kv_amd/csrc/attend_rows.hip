@@ -113,7 +113,10 @@ struct RowsShared {
 // context (rope.h) as it is converted: lanes seg and seg ^ 8 hold the two
 // halves of each rotary pair, the cosines and sines of the last shift stay
 // in registers until a key of another shift comes.
-template <typename T, int D, int G, bool ROPE = false>
+// CACHED: the local keys come from a buffer of the initial tokens and a
+// ring of the later positions, the units' keys from their slots in a unit
+// cache (the unit table holds slab rows instead of positions).
+template <typename T, int D, int G, bool ROPE = false, bool CACHED = false>
 struct RowsAttn {
   static constexpr int CPT = D / 16;
   static constexpr int kGroup = 16 * kKeysPerIter;   // keys per iteration
@@ -125,6 +128,9 @@ struct RowsAttn {
   const int32_t* sel_row;
   const T* kb;   // K and V of the row's KV head (uniform); a lane reads columns seg*CPT ..
   const T* vb;
+  const T* cb;   // CACHED: the row's cache slabs
+  const T* cvb;
+  int64_t ring_off, ring_len;   // CACHED: window position p sits at row p + ring_off (wrapped)
   int cur;
   RowRaw<T, CPT> qraw[G];
   float qv[G][CPT], m[G], l[G], acc[G][CPT];
@@ -157,8 +163,16 @@ struct RowsAttn {
     n_local = init_len + win_len;
     const int ch = pos / a.L;
     sel_row = a.sel ? a.sel + (((int64_t)bi * a.Hkv + h) * a.n_chunks + ch) * a.k_m : nullptr;
-    kb = (const T*)a.k + ((int64_t)bi * a.Hkv + h) * a.kv_cap * D;
-    vb = (const T*)a.v + ((int64_t)bi * a.Hkv + h) * a.kv_cap * D;
+    const int64_t stride = CACHED ? a.local_cap : a.kv_cap;
+    kb = (const T*)a.k + ((int64_t)bi * a.Hkv + h) * stride * D;
+    vb = (const T*)a.v + ((int64_t)bi * a.Hkv + h) * stride * D;
+    if constexpr (CACHED) {
+      const int64_t slab = ((int64_t)bi * a.Hkv + h) * a.n_slots * a.B * D;
+      cb = (const T*)a.ck + slab;
+      cvb = (const T*)a.cv + slab;
+      ring_len = a.local_cap - a.n_init;
+      ring_off = a.n_init + (win_lo - a.n_init) % ring_len - win_lo;
+    }
     cur = 0;
     nu = 0;
     if constexpr (ROPE) {
@@ -253,9 +267,22 @@ struct RowsAttn {
       const int li = kl + 16 * j;
       okn[j] = li < rem;
       const int64_t p = okn[j] ? key_pos<KIND>(b0, li) : 0;
-      const int64_t off = p * D + seg * CPT;
-      kn[j].load(kb + off);
-      vn[j].load(vb + off);
+      if constexpr (CACHED) {
+        // unit keys: p is a slab row; local ones: the ring row of position p
+        const bool unit = KIND == kUnits || (KIND == kMixed && li >= clamp32(nl - b0));
+        int64_t r = p;
+        if (!unit && p >= a.n_init) {
+          r = p + ring_off;
+          if (r >= a.local_cap) r -= ring_len;
+        }
+        const int64_t off = r * D + seg * CPT;
+        kn[j].load((unit ? cb : kb) + off);
+        vn[j].load((unit ? cvb : vb) + off);
+      } else {
+        const int64_t off = p * D + seg * CPT;
+        kn[j].load(kb + off);
+        vn[j].load(vb + off);
+      }
       if constexpr (ROPE)   // only unit keys lie in [n_init, lo): cur is theirs
         en[j] = !okn[j] || p >= lo_ctx ? 0 : (p < a.n_init ? e_sink : sh.iv_turn[cur]);
     }
@@ -264,15 +291,26 @@ struct RowsAttn {
   // Unit table of the row's selection (thread m passes entry m; repeated ids
   // count once): each unit's first key and first unit-key index, by a block
   // scan of the unit lengths.  Sets nu, this workgroup's unit keys.  Every
-  // thread calls it.
-  __device__ __forceinline__ void build_table(int32_t u) {
+  // thread calls it.  CACHED: the first key's slab row instead of its
+  // position; returns true if a unit with keys to attend is not cached.
+  __device__ __forceinline__ bool build_table(int32_t u) {
     u = drop_repeats(u, tid, a.k_m, sh.ids);
     int64_t lo = 0, len = 0;
+    bool absent = false;
     if (u >= 0) {
       lo = unit_first_key(u, a.B, a.n_init);
       const int64_t hi = ((int64_t)u + a.n_init / a.B + 1) * a.B;
       len = (hi < unit_cap ? hi : unit_cap) - lo;
       len = len > 0 ? len : 0;
+      if constexpr (CACHED) {
+        const int s = u < a.n_units ? a.c_slot[((int64_t)bi * a.Hkv + h) * a.n_units + u] - 1 : -1;
+        if (s < 0) {
+          absent = len > 0;
+          len = 0;
+        } else {
+          lo = (int64_t)s * a.B + (lo - hi + a.B);   // row of the first key in slot s
+        }
+      }
     }
     int x = (int)len;   // inclusive scan of the unit lengths (each <= B)
 #pragma unroll
@@ -301,6 +339,8 @@ struct RowsAttn {
     const int64_t u_stop = u_begin + pu < n_unit ? u_begin + pu : n_unit;
     nu = u_stop > u_begin ? u_stop - u_begin : 0;
     cur = 0;
+    if constexpr (CACHED) return __syncthreads_or(absent);
+    return false;
   }
 
   // cos / sin of shift E at this lane's columns, sign of its half folded in
@@ -598,9 +638,9 @@ struct RowsAttn {
 // (position, KV head, sequence) row, each an equal share of the local keys
 // and of the units' keys.  Its first local keys are requested before the
 // selection is read and the unit table formed.
-template <typename T, int D, int G, bool ROPE>
+template <typename T, int D, int G, bool ROPE, bool CACHED = false>
 __global__ __launch_bounds__(kRowsThreads) void k_attend_rows(AttendArgs a) {
-  using Attn = RowsAttn<T, D, G, ROPE>;
+  using Attn = RowsAttn<T, D, G, ROPE, CACHED>;
   __shared__ RowsShared<G, D, ROPE> sh;
   const int s = blockIdx.x, n = gridDim.x;
   const int pos = blockIdx.y, h = blockIdx.z % a.Hkv, bi = blockIdx.z / a.Hkv;
@@ -611,10 +651,10 @@ __global__ __launch_bounds__(kRowsThreads) void k_attend_rows(AttendArgs a) {
   if (r.valid && threadIdx.x < a.k_m) u = r.sel_row[threadIdx.x];
   const bool early = r.nl >= Attn::kGroup;   // first group local only: in flight
   if (early) r.template fetch<Attn::kLocal>(0, r.nl);
-  r.build_table(u);
+  const bool absent = r.build_table(u);
   r.make_qv();
   r.stream(0, r.nl + r.nu, early);
-  r.finish(s, n, a.ws_count ? a.ws_count + row : nullptr, 0, nullptr, 0, false);
+  r.finish(s, n, a.ws_count ? a.ws_count + row : nullptr, 0, nullptr, 0, absent);
 }
 
 int rows_num_splits(const AttendArgs& a) {
@@ -650,6 +690,28 @@ static hipError_t launch_rows_td(const AttendArgs& a, int splits, hipStream_t st
     case 8: return launch_rows_tdg<T, D, 8>(a, splits, st);
   }
   return hipErrorInvalidValue;
+}
+
+template <typename T, int D>
+static hipError_t launch_cached_td(const AttendArgs& a, int splits, hipStream_t st) {
+  const dim3 grid(splits, a.n_pos, a.batch * a.Hkv);
+  switch (a.Hq / a.Hkv) {
+    case 1: k_attend_rows<T, D, 1, false, true><<<grid, kRowsThreads, 0, st>>>(a); break;
+    case 2: k_attend_rows<T, D, 2, false, true><<<grid, kRowsThreads, 0, st>>>(a); break;
+    case 4: k_attend_rows<T, D, 4, false, true><<<grid, kRowsThreads, 0, st>>>(a); break;
+    case 8: k_attend_rows<T, D, 8, false, true><<<grid, kRowsThreads, 0, st>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attend_rows_cached(const AttendArgs& a, int splits, hipStream_t st) {
+  if (a.n_pos <= 0) return hipSuccess;
+  if (a.bf16)
+    return a.d == 128 ? launch_cached_td<bf16_t, 128>(a, splits, st)
+                      : launch_cached_td<bf16_t, 64>(a, splits, st);
+  return a.d == 128 ? launch_cached_td<float, 128>(a, splits, st)
+                    : launch_cached_td<float, 64>(a, splits, st);
 }
 
 hipError_t launch_attend_rows(const AttendArgs& a, int splits, hipStream_t st) {

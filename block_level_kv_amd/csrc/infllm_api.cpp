@@ -772,3 +772,155 @@ int32_t infllm_workspace_status(const void* workspace, size_t workspace_bytes, i
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------------ unit cache
+namespace {
+
+// Host memory the kernels may read at the same address: pinned (registered
+// with the runtime) and mapped into the GPU's address space as is.  Pageable
+// memory would fault on the device, so it is refused here.
+bool device_readable_host(const void* p) {
+  hipPointerAttribute_t at{};
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();   // clear the error this query leaves
+    return false;
+  }
+  return at.type == hipMemoryTypeHost && at.devicePointer == p;
+}
+
+infllm_status cache_shape_check(const infllm_config* cfg, int32_t batch, int32_t n_units,
+                                int32_t n_slots) {
+  const infllm_status st = check_config(cfg);
+  if (st != INFLLM_OK) return st;
+  if (batch < 1 || n_units < 1 || n_slots < 1) return INFLLM_ERR_INVALID_ARG;
+  if (n_units > kCacheMaxUnits || n_slots > kCacheMaxSlots) return INFLLM_ERR_UNSUPPORTED;
+  if ((int64_t)batch * cfg->n_kv_heads > ((int64_t)1 << 31) - 1) return INFLLM_ERR_UNSUPPORTED;
+  return INFLLM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t infllm_cache_state_size(const infllm_config* cfg, int32_t batch, int32_t n_units,
+                               int32_t n_slots) {
+  if (cache_shape_check(cfg, batch, n_units, n_slots) != INFLLM_OK) return 0;
+  return cache_state_bytes((int64_t)batch * cfg->n_kv_heads, n_units, n_slots);
+}
+
+infllm_status infllm_cache_fetch(const infllm_config* cfg, int32_t batch, int32_t n_pos,
+                                 const int32_t* sel, int32_t n_units, int64_t step,
+                                 const void* k_host, const void* v_host, int64_t host_cap,
+                                 void* cache_k, void* cache_v, int32_t n_slots, void* state,
+                                 void* stream) {
+  infllm_status st = cache_shape_check(cfg, batch, n_units, n_slots);
+  if (st != INFLLM_OK) return st;
+  if (n_pos < 1 || step < 1) return INFLLM_ERR_INVALID_ARG;
+  if ((int64_t)n_pos * cfg->top_k > n_slots) return INFLLM_ERR_INVALID_ARG;   // union must fit
+  // every unit's block lies in the host pool
+  if (host_cap < ((int64_t)n_units + cfg->n_init / cfg->block) * cfg->block)
+    return INFLLM_ERR_INVALID_ARG;
+  if (!k_host || !v_host || !cache_k || !cache_v || !state || !aligned16(k_host) ||
+      !aligned16(v_host) || !aligned16(cache_k) || !aligned16(cache_v) || !aligned16(state))
+    return INFLLM_ERR_INVALID_ARG;
+  if (cfg->top_k == 0) return INFLLM_OK;   // nothing selected
+  if (!sel || !aligned16(sel)) return INFLLM_ERR_INVALID_ARG;
+  if (!device_readable_host(k_host) || !device_readable_host(v_host)) return INFLLM_ERR_INVALID_ARG;
+  const int64_t rows = (int64_t)batch * cfg->n_kv_heads;
+  const CacheTables t = cache_tables(state, rows, n_units, n_slots);
+  CacheArgs a{};
+  a.batch = batch;
+  a.Hkv = cfg->n_kv_heads;
+  a.d = cfg->head_dim;
+  a.B = cfg->block;
+  a.n_init = cfg->n_init;
+  a.k_m = cfg->top_k;
+  a.n_pos = n_pos;
+  a.n_units = n_units;
+  a.n_slots = n_slots;
+  a.elem = cfg->dtype == INFLLM_BF16 ? 2 : 4;
+  a.sel = sel;
+  a.step = step;
+  a.k_host = k_host;
+  a.v_host = v_host;
+  a.host_cap = host_cap;
+  a.ck = cache_k;
+  a.cv = cache_v;
+  a.stats = t.stats;
+  a.slot_of = t.slot_of;
+  a.unit_of = t.unit_of;
+  a.stamp = t.stamp;
+  return launched(launch_cache_fetch(a, (hipStream_t)stream));
+}
+
+infllm_status infllm_attend_cached(const infllm_config* cfg, int32_t batch, const void* q,
+                                   int64_t q_cap, int64_t q_off, int64_t q_pos,
+                                   const int64_t* pos, int32_t n_pos, const void* k_local,
+                                   const void* v_local, int64_t local_cap, int64_t ctx_cap,
+                                   const int32_t* sel, int32_t n_units, const void* cache_k,
+                                   const void* cache_v, int32_t n_slots, const void* state,
+                                   void* out, float* lse, int64_t out_cap, int64_t out_off,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  infllm_status st = cache_shape_check(cfg, batch, n_units, n_slots);
+  if (st != INFLLM_OK) return st;
+  if (cfg->rope_theta != 0.0) return INFLLM_ERR_UNSUPPORTED;
+  if (n_pos < 1 || q_off < 0 || q_pos < 0 || out_off < 0) return INFLLM_ERR_INVALID_ARG;
+  if ((int64_t)batch * cfg->n_kv_heads > 65535 || n_pos > 65535) return INFLLM_ERR_UNSUPPORTED;
+  if (q_off + n_pos > q_cap || out_off + n_pos > out_cap) return INFLLM_ERR_INVALID_ARG;
+  if (!pos && q_pos + n_pos > ctx_cap) return INFLLM_ERR_INVALID_ARG;
+  if (ctx_cap > kPosLimit) return INFLLM_ERR_UNSUPPORTED;
+  // the ring holds every window of the call: W + n_pos - 1 positions
+  if (local_cap <= cfg->n_init || local_cap - cfg->n_init < (int64_t)cfg->window + n_pos - 1)
+    return INFLLM_ERR_INVALID_ARG;
+  if (!q || !k_local || !v_local || !out || !state || !cache_k || !cache_v || !aligned16(q) ||
+      !aligned16(k_local) || !aligned16(v_local) || !aligned16(out) || !aligned16(state) ||
+      !aligned16(cache_k) || !aligned16(cache_v))
+    return INFLLM_ERR_INVALID_ARG;
+  if (pos && ((uintptr_t)pos & 7u)) return INFLLM_ERR_INVALID_ARG;
+  if (cfg->top_k > 0 && (!sel || !aligned16(sel))) return INFLLM_ERR_INVALID_ARG;
+  AttendArgs a = attend_args(cfg, batch, 1, n_pos);
+  int splits = rows_num_splits(a);
+  if (attend_ws_layout(a).o_bytes >= ((size_t)1 << 32)) return INFLLM_ERR_UNSUPPORTED;
+  const size_t need = attend_ws_bytes(a);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return INFLLM_ERR_WORKSPACE;
+  a.q = q;
+  a.q_cap = q_cap;
+  a.q_off = q_off;
+  a.q_pos = q_pos;
+  a.pos = pos;
+  a.k = k_local;
+  a.v = v_local;
+  a.kv_cap = ctx_cap;
+  a.local_cap = local_cap;
+  a.sel = cfg->top_k > 0 ? sel : nullptr;
+  a.out = out;
+  a.lse = lse;
+  a.out_cap = out_cap;
+  a.out_off = out_off;
+  a.ck = cache_k;
+  a.cv = cache_v;
+  a.c_slot = cache_tables(const_cast<void*>(state), (int64_t)batch * cfg->n_kv_heads, n_units,
+                          n_slots).slot_of;
+  a.n_units = n_units;
+  a.n_slots = n_slots;
+  if (need > 0) {
+    const AttendWs lay = attend_ws_layout(a);
+    a.ws_count = (int*)((char*)workspace + kWsHeaderBytes);
+    a.ws_o = (float*)((char*)workspace + lay.count_bytes);
+    a.ws_ml = (float*)((char*)workspace + lay.count_bytes + lay.o_bytes);
+  }
+  return launched(launch_attend_rows_cached(a, splits, (hipStream_t)stream));
+}
+
+int32_t infllm_cache_stats(const void* state, int64_t* hits, int64_t* misses, void* stream) {
+  if (!state || !hits || !misses || !aligned16(state)) return INFLLM_ERR_INVALID_ARG;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return INFLLM_ERR_HIP;
+  int64_t v[2] = {0, 0};
+  if (hipMemcpy(v, state, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return INFLLM_ERR_HIP;
+  *hits = v[0];
+  *misses = v[1];
+  return INFLLM_OK;
+}
+
+}  // extern "C"

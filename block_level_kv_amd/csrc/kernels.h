@@ -85,7 +85,46 @@ struct AttendArgs {
   float* ws_o;   // split-K partial outputs
   float* ws_ml;  // split-K partial (max, sum) pairs
   int* ws_count; // split-K arrival counters (zero between calls)
+  // unit cache (decode attention only): k, v hold the initial tokens and a
+  // ring of the later ones (local_cap rows per (sequence, KV head): row p
+  // for p < n_init, n_init + (p - n_init) mod (local_cap - n_init) after),
+  // kv_cap is the context's capacity; units' keys come from the slabs
+  const void* ck;           // [b, H_kv, n_slots, B, d]
+  const void* cv;
+  const int32_t* c_slot;    // [b, H_kv, n_units]: slot + 1, 0 = not cached
+  int n_units, n_slots;
+  int64_t local_cap;
 };
+
+// Unit cache: tables in a caller-owned, zero-filled state buffer
+// [header: hits, misses (int64)][slot_of int32 rows x U][unit_of int32
+// rows x C][stamp int64 rows x C], each part 256-byte aligned.
+constexpr int kCacheMaxSlots = 1024;
+constexpr int kCacheMaxUnits = 65536;
+constexpr size_t kCacheHeaderBytes = 256;
+struct CacheTables {
+  int64_t* stats;
+  int32_t* slot_of;
+  int32_t* unit_of;
+  int64_t* stamp;
+};
+size_t cache_state_bytes(int64_t rows, int n_units, int n_slots);
+CacheTables cache_tables(void* state, int64_t rows, int n_units, int n_slots);
+struct CacheArgs {
+  int batch, Hkv, d, B, n_init, k_m, n_pos, n_units, n_slots, elem;
+  const int32_t* sel;       // [b, H_kv, n_pos, k_m]
+  int64_t step;
+  const void* k_host;       // [b, H_kv, host_cap, d], device-accessible host memory
+  const void* v_host;
+  int64_t host_cap;
+  void* ck;                 // [b, H_kv, n_slots, B, d]
+  void* cv;
+  int64_t* stats;
+  int32_t* slot_of;
+  int32_t* unit_of;
+  int64_t* stamp;
+};
+hipError_t launch_cache_fetch(const CacheArgs& a, hipStream_t st);
 
 size_t build_workspace_bytes(const BuildArgs& a);
 size_t build_range_workspace_bytes(const BuildArgs& a, int64_t n_units);
@@ -99,6 +138,8 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 // vector-ALU attention, one query position per workgroup
 int rows_num_splits(const AttendArgs& a);
 hipError_t launch_attend_rows(const AttendArgs& a, int splits, hipStream_t st);
+// the same over a unit cache (a.ck set)
+hipError_t launch_attend_rows_cached(const AttendArgs& a, int splits, hipStream_t st);
 int64_t rows_num_counters(const AttendArgs& a);
 
 // fused decode step (bf16): unit scores, selection and attention of single

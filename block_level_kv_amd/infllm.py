@@ -30,7 +30,8 @@ EXPORTED = ("infllm_num_units", "infllm_num_eligible", "infllm_workspace_size",
             "infllm_attend", "infllm_attend_varlen", "infllm_select_attend",
             "infllm_select_attend_static",
             "infllm_workspace_layout", "infllm_workspace_status", "infllm_step_plan",
-            "infllm_status_string", "infllm_abi_version")
+            "infllm_cache_state_size", "infllm_cache_fetch", "infllm_attend_cached",
+            "infllm_cache_stats", "infllm_status_string", "infllm_abi_version")
 
 
 ABI_VERSION = 2   # INFLLM_ABI_VERSION of include/infllm.h
@@ -89,6 +90,17 @@ def lib() -> ctypes.CDLL:
         L.infllm_attend_varlen.restype = _i32
         L.infllm_attend_varlen.argtypes = [_cfgp, _i32, _vp, _i64, _i64, _vp, _i32, _i32, _vp, _vp,
                                            _i64, _vp, _vp, _vp, _i64, _i64, _vp, _sz, _vp]
+        L.infllm_cache_state_size.restype = _sz
+        L.infllm_cache_state_size.argtypes = [_cfgp, _i32, _i32, _i32]
+        L.infllm_cache_fetch.restype = _i32
+        L.infllm_cache_fetch.argtypes = [_cfgp, _i32, _i32, _vp, _i32, _i64, _vp, _vp, _i64, _vp,
+                                         _vp, _i32, _vp, _vp]
+        L.infllm_attend_cached.restype = _i32
+        L.infllm_attend_cached.argtypes = [_cfgp, _i32, _vp, _i64, _i64, _i64, _vp, _i32, _vp, _vp,
+                                           _i64, _i64, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp,
+                                           _i64, _i64, _vp, _sz, _vp]
+        L.infllm_cache_stats.restype = _i32
+        L.infllm_cache_stats.argtypes = [_vp, ctypes.POINTER(_i64), ctypes.POINTER(_i64), _vp]
         L.infllm_select_units.restype = _i32
         L.infllm_select_units.argtypes = [_cfgp, _i32, _vp, _i64, _i64, _i64, _vp, _i32, _i32, _vp,
                                           _i32, _vp, _vp, _vp, _sz, _vp]
@@ -484,3 +496,77 @@ def infllm_select_attend_static(cfg, q, q_off: int, q_pos: int, n_pos: int, unit
         ctypes.byref(cfg), batch, q.data_ptr(), q.shape[2], q_off, q_pos, _ptr(pos), n_pos,
         unit_repr.data_ptr(), U, k.data_ptr(), v.data_ptr(), k.shape[2], scores.data_ptr(),
         sel.data_ptr(), out.data_ptr(), _ptr(lse), out.shape[2], out_off, _stream(stream, q)))
+
+
+# ------------------------------------------------------------------ unit cache
+def infllm_cache_state_size(cfg: infllm_config, batch: int, n_units: int, n_slots: int) -> int:
+    return int(lib().infllm_cache_state_size(ctypes.byref(cfg), batch, n_units, n_slots))
+
+
+def cache_state(cfg: infllm_config, batch: int, n_units: int, n_slots: int,
+                device="cuda") -> torch.Tensor:
+    """A zero-filled (empty) unit cache state."""
+    size = infllm_cache_state_size(cfg, batch, n_units, n_slots)
+    if size == 0:
+        raise ValueError("invalid unit cache shape")
+    return torch.zeros(size, dtype=torch.uint8, device=device)
+
+
+def _check_host(t: torch.Tensor, name: str, dtype: torch.dtype) -> None:
+    if not isinstance(t, torch.Tensor) or t.is_cuda or t.dtype != dtype or t.dim() != 4 \
+            or not t.is_contiguous() or not t.is_pinned():
+        raise ValueError("%s must be a contiguous 4D %s tensor in pinned host memory" %
+                         (name, dtype))
+
+
+def infllm_cache_fetch(cfg, sel, n_units: int, step: int, k_host, v_host, cache_k, cache_v, state,
+                       stream=None) -> None:
+    """sel [b, H_kv, n_pos, k_m] (device); k_host / v_host [b, H_kv, host_cap, d] pinned;
+    cache_k / cache_v [b, H_kv, n_slots, B, d] (device)."""
+    dt = _dtype_of(cfg)
+    _check(sel, "sel", torch.int32, 4)
+    _check_host(k_host, "k_host", dt)
+    _check_host(v_host, "v_host", dt)
+    _check(cache_k, "cache_k", dt, 5)
+    _check(cache_v, "cache_v", dt, 5)
+    if k_host.shape != v_host.shape or cache_k.shape != cache_v.shape:
+        raise ValueError("K and V buffers must have the same shapes")
+    b, _, n_pos, _ = sel.shape
+    _raise("infllm_cache_fetch", lib().infllm_cache_fetch(
+        ctypes.byref(cfg), b, n_pos, sel.data_ptr(), n_units, step, k_host.data_ptr(),
+        v_host.data_ptr(), k_host.shape[2], cache_k.data_ptr(), cache_v.data_ptr(),
+        cache_k.shape[2], state.data_ptr(), _stream(stream, sel)))
+
+
+def infllm_attend_cached(cfg, q, q_off: int, q_pos: int, n_pos: int, k_local, v_local,
+                         ctx_cap: int, sel, n_units: int, cache_k, cache_v, state, out, lse=None,
+                         out_off: int = 0, pos=None, ws=None, stream=None) -> None:
+    """Decode attention (n_pos single positions) with units' keys from the cache;
+    k_local / v_local [b, H_kv, local_cap, d]: initial tokens, then a ring."""
+    dt = _dtype_of(cfg)
+    _check(q, "q", dt, 4)
+    _check(k_local, "k_local", dt, 4)
+    _check(v_local, "v_local", dt, 4)
+    _check(out, "out", dt, 4)
+    _check(cache_k, "cache_k", dt, 5)
+    _check(cache_v, "cache_v", dt, 5)
+    if sel is not None:
+        _check(sel, "sel", torch.int32, 4)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, 3)
+    if pos is not None:
+        _check_pos(pos, q.shape[0])
+    wp, wb = _ws(ws)
+    _raise("infllm_attend_cached", lib().infllm_attend_cached(
+        ctypes.byref(cfg), q.shape[0], q.data_ptr(), q.shape[2], q_off, q_pos, _ptr(pos), n_pos,
+        k_local.data_ptr(), v_local.data_ptr(), k_local.shape[2], ctx_cap, _ptr(sel), n_units,
+        cache_k.data_ptr(), cache_v.data_ptr(), cache_k.shape[2], state.data_ptr(),
+        out.data_ptr(), _ptr(lse), out.shape[2], out_off, wp, wb, _stream(stream, q)))
+
+
+def infllm_cache_stats(state: torch.Tensor, stream=None) -> tuple[int, int]:
+    """(hits, misses) since the state was zero-filled (synchronises)."""
+    h, m = _i64(0), _i64(0)
+    _raise("infllm_cache_stats", lib().infllm_cache_stats(
+        state.data_ptr(), ctypes.byref(h), ctypes.byref(m), _stream(stream, state)))
+    return int(h.value), int(m.value)

@@ -529,6 +529,93 @@ INFLLM_API int32_t infllm_step_plan(const infllm_config *cfg, int32_t batch, int
 INFLLM_API int32_t infllm_workspace_status(const void *workspace, size_t workspace_bytes,
                                            int32_t *timeouts, void *stream);
 
+/*
+ * Unit cache -- every unit's K/V in host memory, a pool of n_slots hot
+ * units per (sequence, KV head) in GPU memory, for contexts whose K/V do
+ * not fit the GPU (InfLLM Guide, "Core Innovation 3": a least-recently-used
+ * GPU pool of hot units over host-resident units; the representatives stay
+ * on the GPU for scoring).  A decode step is then infllm_select_units,
+ * infllm_cache_fetch and infllm_attend_cached on one stream; fetch and
+ * attention take the same sel.
+ *
+ * Cache state: a caller-owned device buffer of infllm_cache_state_size
+ * bytes, zero-filled before first use (zero = empty cache): a 256-byte
+ * header (int64 hits, int64 misses: totals since zero-filled), then per
+ * (sequence, KV head) the slot of each unit, the unit of each slot and the
+ * step that last used each slot.  Returns 0 for an invalid shape.
+ * Limits: n_units <= 65,536, n_slots <= 1,024.
+ */
+INFLLM_API size_t infllm_cache_state_size(const infllm_config *cfg, int32_t batch,
+                                          int32_t n_units, int32_t n_slots);
+
+/*
+ * infllm_cache_fetch -- makes every unit of sel resident, per (sequence,
+ * KV head), without a host round trip: one workgroup per (sequence, KV
+ * head) reads sel on the device, updates the tables, and copies each
+ * missed unit's block (B rows of K and of V) from host memory into its
+ * slot with the GPU's own loads over the host link.  Policy: the selected
+ * units already cached are hits (last use = step); the others, ascending by
+ * unit id, take the slots no selected unit holds, least recently used first
+ * (empty slots first, lower slot first among equals), evicting their units.
+ *
+ *   sel       device [batch, H_kv, n_pos, k_m] int32 unit ids (-1 = empty;
+ *             ids outside [0, n_units) and repeats are ignored); the union
+ *             of a (sequence, KV head)'s n_pos rows must fit: n_pos * k_m
+ *             <= n_slots (checked)
+ *   step      >= 1, larger than every step passed before on this state (not
+ *             checked; equal steps protect the earlier call's units too)
+ *   k_host,   pinned host memory the GPU reads at the same address
+ *   v_host    (hipHostMalloc; other memory: INFLLM_ERR_INVALID_ARG),
+ *             [batch, H_kv, host_cap, d], row p = position p; must hold
+ *             every unit's block: host_cap >= (n_units + n_init/B) * B
+ *   cache_k,  device [batch, H_kv, n_slots, B, d], cfg->dtype: slot c holds
+ *   cache_v   the block of unit_of[c] (rows below n_init of unit 0 unused)
+ *   state     the cache state (above)
+ * Calls on one state must not overlap in time.
+ */
+INFLLM_API infllm_status infllm_cache_fetch(const infllm_config *cfg, int32_t batch,
+                                            int32_t n_pos, const int32_t *sel, int32_t n_units,
+                                            int64_t step, const void *k_host, const void *v_host,
+                                            int64_t host_cap, void *cache_k, void *cache_v,
+                                            int32_t n_slots, void *state, void *stream);
+
+/*
+ * infllm_attend_cached -- infllm_attend of n_pos single positions (chunks
+ * of one, as in decoding) whose units' keys come from the unit cache.  The
+ * result is bit for bit that of infllm_attend (chunk_len 1, n_chunks n_pos)
+ * over the full K/V.
+ *
+ *   q, q_cap, q_off, q_pos, pos, sel, out, lse, out_cap, out_off
+ *             as infllm_attend / infllm_attend_varlen
+ *   k_local,  device [batch, H_kv, local_cap, d]: the initial tokens at rows
+ *   v_local   0 .. n_init-1, position p >= n_init at row n_init + (p -
+ *             n_init) mod (local_cap - n_init); local_cap - n_init >= W +
+ *             n_pos - 1, so that every window of the call is held
+ *   ctx_cap   context capacity: positions are checked against it as
+ *             infllm_attend checks them against kv_cap
+ *   cache_k, cache_v, n_slots, state, n_units
+ *             the unit cache after infllm_cache_fetch of the same sel; a
+ *             selected unit with keys to attend that is not cached gives its
+ *             row NaN outputs
+ *   workspace as infllm_attend with chunk_len 1, n_chunks n_pos
+ * rope_theta must be 0 (INFLLM_ERR_UNSUPPORTED otherwise).
+ */
+INFLLM_API infllm_status infllm_attend_cached(
+    const infllm_config *cfg, int32_t batch, const void *q, int64_t q_cap, int64_t q_off,
+    int64_t q_pos, const int64_t *pos, int32_t n_pos, const void *k_local, const void *v_local,
+    int64_t local_cap, int64_t ctx_cap, const int32_t *sel, int32_t n_units,
+    const void *cache_k, const void *cache_v, int32_t n_slots, const void *state, void *out,
+    float *lse, int64_t out_cap, int64_t out_off, void *workspace, size_t workspace_bytes,
+    void *stream);
+
+/*
+ * infllm_cache_stats -- synchronises `stream`, then reads the hit and miss
+ * totals of a cache state.  Returns INFLLM_OK, INFLLM_ERR_INVALID_ARG or
+ * INFLLM_ERR_HIP.
+ */
+INFLLM_API int32_t infllm_cache_stats(const void *state, int64_t *hits, int64_t *misses,
+                                      void *stream);
+
 INFLLM_API const char *infllm_status_string(int32_t status);
 INFLLM_API int32_t infllm_abi_version(void);
 

@@ -31,7 +31,7 @@ def cfg(**kw):
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 20
+    assert len(names) == 24
     assert set(names) == set(F.EXPORTED)
     L = F.lib()
     for n in names:
@@ -357,3 +357,62 @@ def test_static_scratch_limits():
     assert call(64, 64) == F.INFLLM_ERR_WORKSPACE
     assert call(4, 1, sel=None) == F.INFLLM_ERR_INVALID_ARG
     assert call(0, 1) == F.INFLLM_ERR_INVALID_ARG
+
+
+# ------------------------------------------------------------------ unit cache
+def test_cache_state_size():
+    c = cfg()
+    # header 256 B; slot_of rows x U int32, unit_of rows x C int32, stamp rows x C int64,
+    # each rounded up to 256 B
+    def want(rows, U, C):
+        r = lambda x: (x + 255) // 256 * 256
+        return 256 + r(rows * U * 4) + r(rows * C * 4) + r(rows * C * 8)
+    assert F.infllm_cache_state_size(c, 2, 8191, 64) == want(16, 8191, 64)
+    assert F.infllm_cache_state_size(c, 1, 1, 1) == want(8, 1, 1)
+    assert F.infllm_cache_state_size(c, 0, 10, 10) == 0
+    assert F.infllm_cache_state_size(c, 1, 0, 10) == 0
+    assert F.infllm_cache_state_size(c, 1, 65537, 10) == 0      # above the unit limit
+    assert F.infllm_cache_state_size(c, 1, 100, 1025) == 0      # above the slot limit
+
+
+def test_cache_fetch_host_checks():
+    """Rejections before anything is enqueued (fake, aligned device pointers)."""
+    L = F.lib()
+    P = 1 << 20       # a 16-byte aligned stand-in address; never dereferenced
+    c = cfg(top_k=32)
+    U, C = 1000, 64
+    host_cap = (U + 1) * 128
+
+    def fetch(cfg_=c, n_pos=1, U_=U, step=1, host_cap_=host_cap, C_=C, sel=P, kh=P, state=P):
+        return L.infllm_cache_fetch(ctypes.byref(cfg_), 2, n_pos, sel, U_, step, kh, P, host_cap_,
+                                    P, P, C_, state, None)
+    assert fetch(n_pos=3) == F.INFLLM_ERR_INVALID_ARG        # 3 x 32 selections > 64 slots
+    assert fetch(step=0) == F.INFLLM_ERR_INVALID_ARG
+    assert fetch(host_cap_=host_cap - 1) == F.INFLLM_ERR_INVALID_ARG
+    assert fetch(kh=None) == F.INFLLM_ERR_INVALID_ARG
+    assert fetch(kh=P + 8) == F.INFLLM_ERR_INVALID_ARG        # misaligned
+    assert fetch(state=None) == F.INFLLM_ERR_INVALID_ARG
+    assert fetch(sel=None) == F.INFLLM_ERR_INVALID_ARG
+    assert fetch(U_=70000, host_cap_=(70001) * 128) == F.INFLLM_ERR_UNSUPPORTED
+    assert fetch(C_=2000, n_pos=1) == F.INFLLM_ERR_UNSUPPORTED
+    # k_m = 0: nothing to fetch, nothing enqueued
+    assert fetch(cfg_=cfg(top_k=0), sel=None) == F.INFLLM_OK
+
+
+def test_attend_cached_host_checks():
+    L = F.lib()
+    P = 1 << 20
+    c = cfg()
+    W, n_init = 4096, 128
+
+    def att(cfg_=c, n_pos=1, local_cap=n_init + W, ctx_cap=10000, q_pos=5000, ws_bytes=1 << 30,
+            state=P):
+        return L.infllm_attend_cached(ctypes.byref(cfg_), 1, P, n_pos, 0, q_pos, None, n_pos, P,
+                                      P, local_cap, ctx_cap, P, 100, P, P, 64, state, P, None,
+                                      n_pos, 0, P, ws_bytes, None)
+    assert att(local_cap=n_init + W - 1) == F.INFLLM_ERR_INVALID_ARG     # ring too short
+    assert att(n_pos=4, local_cap=n_init + W + 2) == F.INFLLM_ERR_INVALID_ARG
+    assert att(cfg_=cfg(rope_theta=10000.0)) == F.INFLLM_ERR_UNSUPPORTED
+    assert att(q_pos=9999, n_pos=2, local_cap=n_init + W + 1) == F.INFLLM_ERR_INVALID_ARG
+    assert att(state=None) == F.INFLLM_ERR_INVALID_ARG
+    assert att(ws_bytes=0) == F.INFLLM_ERR_WORKSPACE
