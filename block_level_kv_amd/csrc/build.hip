@@ -141,6 +141,57 @@ constexpr int kRepWaves = 4;
 constexpr int kPass1Batch = 8;
 constexpr int kPass2Batch = 8;
 
+// The unit's r_k best keys from score[0 .. nk) (score desc, position asc),
+// written ascending to rep_idx (-1 past the unit's keys), and their sum in
+// ascending position order to unit_repr.  Every thread calls it; score is
+// complete (a barrier before).
+template <typename T>
+__device__ __forceinline__ void rep_finish(const double* score, int* picked, int nk, int r_k,
+                                           int64_t lo, const T* kb, int d, int64_t out_row,
+                                           int32_t* __restrict__ rep_idx,
+                                           float* __restrict__ unit_repr) {
+  const int c = threadIdx.x;
+  // rank each key: #keys ahead of it in (score desc, position asc)
+  for (int a = c; a < nk; a += blockDim.x) {
+    const double sa = score[a];
+    int rank = 0;
+    for (int b2 = 0; b2 < nk; ++b2) {
+      const double sb = score[b2];
+      rank += (sb > sa) || (sb == sa && b2 < a);
+    }
+    picked[a] = rank < r_k;
+  }
+  __syncthreads();
+  int32_t* ri = rep_idx + out_row * r_k;
+  __shared__ int chosen[kMaxBlock];     // kept key offsets, ascending
+  for (int a = c; a < nk; a += blockDim.x) {
+    if (picked[a]) {
+      int at = 0;
+      for (int b2 = 0; b2 < a; ++b2) at += picked[b2];
+      ri[at] = (int32_t)(lo + a);
+      chosen[at] = a;
+    }
+  }
+  for (int s = nk + c; s < r_k; s += blockDim.x) ri[s] = -1;  // fewer keys than r_k
+  __syncthreads();
+  // the representation: kept keys summed in ascending position, their rows
+  // requested together
+  const int n_kept = nk < r_k ? nk : r_k;
+  if (c < d) {
+    double acc = 0.0;
+    for (int a0 = 0; a0 < n_kept; a0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int y = 0; y < 8; ++y)
+        v[y] = to_f32(kb[(lo + chosen[a0 + y < n_kept ? a0 + y : n_kept - 1]) * d + c]);
+#pragma unroll
+      for (int y = 0; y < 8; ++y)
+        if (a0 + y < n_kept) acc += (double)v[y];
+    }
+    unit_repr[out_row * d + c] = (float)acc;
+  }
+}
+
 template <typename T, int HPL>
 __global__ __launch_bounds__(64 * kRepWaves) void k_rep_select(
     const T* __restrict__ q, int64_t q_cap, const T* __restrict__ k, int64_t kv_cap, int Hq,
@@ -150,7 +201,6 @@ __global__ __launch_bounds__(64 * kRepWaves) void k_rep_select(
   const int u = u_begin + (int)blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
   const int G = Hq / Hkv;
   const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
-  const int c = tid;   // column owner in the final phases (c < d)
   const int64_t j = u + n_init / B;
   const int64_t lo = unit_first_key(u, B, n_init), hi = (j + 1) * B;
   const int nk = (int)(hi - lo);
@@ -320,45 +370,276 @@ __global__ __launch_bounds__(64 * kRepWaves) void k_rep_select(
   }
   __syncthreads();
 
-  // rank each key: #keys ahead of it in (score desc, position asc)
-  for (int a = c; a < nk; a += blockDim.x) {
-    const double sa = score[a];
-    int rank = 0;
-    for (int b2 = 0; b2 < nk; ++b2) {
-      const double sb = score[b2];
-      rank += (sb > sa) || (sb == sa && b2 < a);
-    }
-    picked[a] = rank < r_k;
+  rep_finish(score, picked, nk, r_k, lo, kb, d,
+             ((int64_t)bi * Hkv + h) * u_stride + u, rep_idx, unit_repr);
+}
+
+// Single-pass build.  One workgroup per block j of [j_first, j_last]: the
+// blocks of units u_begin .. u_end-1 and, past them, every block their
+// windows reach (helpers).  Workgroup x takes block j_last - x, so the
+// blocks after a unit's are normally taken first.  Each workgroup
+//   A. sums its block's rows over the group's query heads (fp64), wave w
+//      the w-th quarter, and publishes the sums of its first 1, 2, 3 and 4
+//      quarters (device-scope stores drained, then a flag);
+//   B. (unit blocks) gives each wave the window sum of its first key p0,
+//      w = sum_{i=p0+1}^{e} q_i with e = min(p0 + W, n_ctx - 1).  A unit of
+//      whole quarters with W a multiple of B and e inside the context takes
+//      the rest of its own block from the quarter sums in LDS, the blocks in
+//      between from their published sums (loaded by the whole workgroup at
+//      once) and the head of e's block from its published quarter prefix,
+//      plus rows p0 and e; otherwise the rows are summed here.  A sum not
+//      published after a bounded spin is also summed from the rows here, so
+//      no workgroup waits on one that is not running;
+//   C. walks its keys: s_p = k_p . w_p, then w_{p+1} = w_p - q_{p+1} +
+//      q_{p+1+W} (the second term while p + 1 + W stays in the context);
+//   D. keeps the unit's r_k best keys and their sum.
+// The last workgroup of each (sequence, KV head) to count in clears its
+// flags and counter.  Queries are read about once (rows p + W are the rows
+// the block of that position's owner read shortly before).
+constexpr int kWalkSpin = 1 << 10;
+
+struct WalkArgs {
+  const void* q;
+  int64_t q_cap;
+  const void* k;
+  int64_t kv_cap, n_ctx, j_first;
+  int Hq, Hkv, d, B, n_init, W, r_k;
+  int u_begin, u_end, u_stride, nbl;
+  double* S;       // [rows][nbl][4][d] published sums of quarters 0..q-1, q = 1..4
+  int* flag;       // [rows][nbl]
+  int* count;      // [rows]
+  int32_t* rep_idx;
+  float* unit_repr;
+};
+
+__device__ __forceinline__ double ld_dev_f64(const double* p) {
+  return __hip_atomic_load(const_cast<double*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <typename T, int HPL>
+__global__ __launch_bounds__(64 * kRepWaves) void k_rep_walk(WalkArgs a) {
+  const int lb = a.nbl - 1 - (int)blockIdx.x;   // local block index, last first
+  const int h = blockIdx.y, bi = blockIdx.z;
+  const int64_t j = a.j_first + lb;
+  const int64_t row = (int64_t)bi * a.Hkv + h;
+  const int G = a.Hq / a.Hkv, d = a.d, B = a.B;
+  const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
+  const int cgs = d / 8, cg = lane % cgs, slot = lane / cgs, hs = 64 / cgs;
+  const int64_t last = a.n_ctx - 1;
+  __shared__ double part[kRepWaves][64][8];   // per-lane quarter sums
+  __shared__ double mid[2][128];              // sums of the blocks in between (halves)
+  __shared__ double score[kMaxBlock];
+  __shared__ int picked[kMaxBlock];
+  __shared__ int all_in;
+
+  const T* qh[HPL];
+  bool hv[HPL];
+#pragma unroll
+  for (int x = 0; x < HPL; ++x) {
+    const int g = slot + hs * x;
+    hv[x] = g < G;
+    qh[x] = (const T*)a.q + ((int64_t)bi * a.Hq + (int64_t)h * G + (hv[x] ? g : 0)) * a.q_cap * d +
+            cg * 8;
   }
-  __syncthreads();
-  const int64_t out_row = ((int64_t)bi * Hkv + h) * u_stride + u;
-  int32_t* ri = rep_idx + out_row * r_k;
-  __shared__ int chosen[kMaxBlock];     // kept key offsets, ascending
-  for (int a = c; a < nk; a += blockDim.x) {
-    if (picked[a]) {
-      int at = 0;
-      for (int b2 = 0; b2 < a; ++b2) at += picked[b2];
-      ri[at] = (int32_t)(lo + a);
-      chosen[at] = a;
-    }
-  }
-  for (int s = nk + c; s < r_k; s += blockDim.x) ri[s] = -1;  // fewer keys than r_k
-  __syncthreads();
-  // the representation: kept keys summed in ascending position, their rows
-  // requested together
-  const int n_kept = nk < r_k ? nk : r_k;
-  if (c < d) {
-    double acc = 0.0;
-    for (int a0 = 0; a0 < n_kept; a0 += 8) {
-      float v[8];
+  // rows r0 .. r1 (inclusive) of this lane's heads added to acc, eight rows
+  // requested before any is added; step: row stride
+  auto add_rows = [&](int64_t r0, int64_t r1, int64_t step, double* acc) {
+    for (int64_t i0 = r0; i0 <= r1; i0 += 8 * step) {
+      Raw8<T> r[8][HPL];
+#pragma unroll
+      for (int y = 0; y < 8; ++y) {
+        const int64_t rr = i0 + y * step <= r1 ? i0 + y * step : r1;
+#pragma unroll
+        for (int x = 0; x < HPL; ++x) r[y][x].load(qh[x] + rr * d);
+      }
 #pragma unroll
       for (int y = 0; y < 8; ++y)
-        v[y] = to_f32(kb[(lo + chosen[a0 + y < n_kept ? a0 + y : n_kept - 1]) * d + c]);
 #pragma unroll
-      for (int y = 0; y < 8; ++y)
-        if (a0 + y < n_kept) acc += (double)v[y];
+        for (int x = 0; x < HPL; ++x)
+          if (hv[x] && i0 + y * step <= r1) r[y][x].add(acc);
     }
-    unit_repr[out_row * d + c] = (float)acc;
+  };
+
+  // ---- A: this block's quarter sums over the group's heads, published
+  const int64_t b0 = j * B, b1 = (b0 + B < a.n_ctx ? b0 + B : a.n_ctx) - 1;
+  const int qn = B / kRepWaves;                 // rows per quarter
+  double* pub = a.S + (row * a.nbl + lb) * kRepWaves * d;
+  {
+    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    const int64_t q0 = b0 + (int64_t)wave * qn, q1 = q0 + qn - 1 < b1 ? q0 + qn - 1 : b1;
+    add_rows(q0, q1, 1, acc);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) part[wave][lane][i] = acc[i];
+    __syncthreads();
+    if (tid < d) {
+      double t = 0.0;
+      for (int w2 = 0; w2 < kRepWaves; ++w2) {
+        for (int sl = 0; sl < hs; ++sl) t += part[w2][sl * cgs + tid / 8][tid % 8];
+        __hip_atomic_store(pub + w2 * d + tid, t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    if (tid == 0)
+      __hip_atomic_store(a.flag + row * a.nbl + lb, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  const int64_t j0 = a.n_init / B;
+  if (j >= a.u_begin + j0 && j < a.u_end + j0) {
+    const int u = (int)(j - j0);
+    const int64_t lo = unit_first_key(u, B, a.n_init), hi = (j + 1) * B;
+    const int nk = (int)(hi - lo);
+    const int per = (nk + kRepWaves - 1) / kRepWaves;
+    const int k0 = wave * per < nk ? wave * per : nk;
+    const int k1 = k0 + per < nk ? k0 + per : nk;
+    const T* kb = (const T*)a.k + row * a.kv_cap * d;
+    // a unit of whole quarters with W >= B whose first keys' windows end past
+    // its block: the published sums serve.  Wave w's first key p0 = b0 + w qn
+    // has its window end e_w = min(p0 + W, last) in block je_w (je_0 <=
+    // je_w <= je_0 + 1)
+    const bool whole = lo == b0 && nk == B && per == qn && B % kRepWaves == 0 && a.W >= B &&
+                       (b0 + a.W < last ? b0 + a.W : last) > b1;
+    const int64_t e_first = b0 + a.W < last ? b0 + a.W : last;
+    const int64_t e_lastw = b0 + (int64_t)(kRepWaves - 1) * qn + a.W < last
+                                ? b0 + (int64_t)(kRepWaves - 1) * qn + a.W : last;
+    const int64_t jm = e_first / B, jx = e_lastw / B;   // je_0, je_3
+    bool pub_ok = false;
+    if (whole) {
+      // flags of blocks j+1 .. jx: a bounded spin, then the rows instead
+      const int n_need = (int)(jx - j);
+      int f = 1;
+      const int* fl = a.flag + row * a.nbl + (j + 1 - a.j_first);
+      if (tid < n_need) f = __hip_atomic_load(fl + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      bool miss = __syncthreads_or(f == 0);
+      for (int it = 0; it < kWalkSpin && miss; ++it) {
+        __builtin_amdgcn_s_sleep(2);
+        if (tid < n_need && f == 0)
+          f = __hip_atomic_load(fl + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        miss = __syncthreads_or(f == 0);
+      }
+      pub_ok = !miss && n_need <= (int)blockDim.x;
+      if (pub_ok) {
+        // full sums of blocks j+1 .. jm-1, blockDim/d threads a column,
+        // every load in flight together
+        const int n_mid = (int)(jm - j - 1);
+        const int c = tid % d, part_i = tid / d, nh = blockDim.x / d;   // 2 (d 128) or 4
+        double t = 0.0;
+        if (n_mid > 0) {
+          const double* base = a.S + (row * a.nbl + (j + 1 - a.j_first)) * kRepWaves * d;
+          const __amdgpu_buffer_rsrc_t r =
+              dev_rsrc(base, (uint32_t)((int64_t)n_mid * kRepWaves * d * 8));
+          for (int m0 = part_i; m0 < n_mid; m0 += 8 * nh) {
+            double v[8];
+#pragma unroll
+            for (int y = 0; y < 8; ++y)
+              v[y] = ld1_dev_f64(
+                  r, (uint32_t)((((m0 + y * nh) * kRepWaves + kRepWaves - 1) * d + c) * 8));
+#pragma unroll
+            for (int y = 0; y < 8; ++y) t += m0 + y * nh < n_mid ? v[y] : 0.0;
+          }
+        }
+        if (part_i < 2) mid[part_i][c] = t;
+        __syncthreads();
+        if (part_i >= 2) mid[part_i & 1][c] += t;   // d = 64: fold parts 2, 3 in
+        __syncthreads();
+      }
+    }
+    if (k0 < k1) {
+      // ---- B: the window sum of the wave's first key
+      const int64_t p0 = lo + k0;
+      const int64_t e0 = p0 + a.W < last ? p0 + a.W : last;
+      double w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (pub_ok) {
+        const int64_t je = e0 / B, off = e0 - je * B;
+        const int qf = (int)((off + 1) / qn);         // whole quarters of je's block up to e0
+        // rest of this block: this quarter and the later ones, minus row p0
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          double t = 0.0;
+          for (int w2 = wave; w2 < kRepWaves; ++w2) t += part[w2][lane][i];
+          w[i] = t;
+        }
+        Raw8<T> rp[HPL];
+#pragma unroll
+        for (int x = 0; x < HPL; ++x) rp[x].load(qh[x] + p0 * d);
+        if (slot == 0) {
+          // blocks j+1 .. jm-1, block jm when je = jm + 1, then je's first qf quarters
+          const double* pm = a.S + (row * a.nbl + (jm - a.j_first)) * kRepWaves * d + cg * 8;
+          const double* pj = a.S + (row * a.nbl + (je - a.j_first)) * kRepWaves * d + cg * 8;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            double v = mid[0][cg * 8 + i] + mid[1][cg * 8 + i];
+            if (je > jm) v += ld_dev_f64(pm + (kRepWaves - 1) * d + i);
+            if (qf > 0) v += ld_dev_f64(pj + (qf - 1) * d + i);
+            w[i] += v;
+          }
+        }
+#pragma unroll
+        for (int x = 0; x < HPL; ++x)
+          if (hv[x]) rp[x].sub(w);
+        add_rows(je * B + (int64_t)qf * qn, e0, 1, w);   // fewer than qn rows
+      } else {
+        add_rows(p0 + 1, e0 < b1 ? e0 : b1, 1, w);            // rest of this block
+        if (e0 > b1) {
+          const int64_t jb = e0 / B;
+          for (int64_t mm = j + 1; mm < jb; ++mm) add_rows(mm * B, mm * B + B - 1, 1, w);
+          add_rows(jb * B, e0, 1, w);                          // head of e's block
+        }
+      }
+      // ---- C: the walk, a batch's rows requested before any is used
+      for (int o0 = k0; o0 < k1; o0 += kPass2Batch) {
+        Raw8<T> rl[kPass2Batch][HPL], ru[kPass2Batch][HPL], rk[kPass2Batch];
+#pragma unroll
+        for (int y = 0; y < kPass2Batch; ++y) {
+          const int64_t p = lo + (o0 + y < k1 ? o0 + y : k1 - 1);
+          const int64_t pl = p + 1 < last ? p + 1 : last;
+          const int64_t pe = p + 1 + a.W < last ? p + 1 + a.W : last;
+#pragma unroll
+          for (int x = 0; x < HPL; ++x) {
+            rl[y][x].load(qh[x] + pl * d);
+            ru[y][x].load(qh[x] + pe * d);
+          }
+          rk[y].load(kb + p * d + cg * 8);
+        }
+        double t[kPass2Batch];
+#pragma unroll
+        for (int y = 0; y < kPass2Batch; ++y) {
+          const int64_t p = lo + o0 + y;
+          t[y] = 0.0;
+          if (o0 + y >= k1) continue;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) t[y] = fma(rk[y].get(i), w[i], t[y]);
+          // w_p -> w_{p+1}
+#pragma unroll
+          for (int x = 0; x < HPL; ++x) {
+            if (!hv[x]) continue;
+            if (p + 1 <= last) rl[y][x].sub(w);
+            if (p + 1 + a.W <= last) ru[y][x].add(w);
+          }
+        }
+#pragma unroll
+        for (int y = 0; y < kPass2Batch; ++y) {
+          const double tt = wave_sum_f64_dpp(t[y]);
+          if (lane == 0 && o0 + y < k1) score[o0 + y] = tt;
+        }
+      }
+    }
+    __syncthreads();
+    rep_finish(score, picked, nk, a.r_k, lo, kb, d, row * a.u_stride + u, a.rep_idx,
+               a.unit_repr);
+  }
+  // ---- the last workgroup of this (sequence, KV head) clears its flags
+  __syncthreads();
+  if (tid == 0) {
+    const int done = __hip_atomic_fetch_add(a.count + row, 1, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+    all_in = done == a.nbl - 1;
+  }
+  __syncthreads();
+  if (all_in) {
+    for (int i = tid; i < a.nbl; i += blockDim.x)
+      __hip_atomic_store(a.flag + row * a.nbl + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_store(a.count + row, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -413,11 +694,41 @@ static BuildWs build_ws_layout(const BuildArgs& a, int64_t nbl) {
 }
 static size_t ws_total(const BuildWs& w) { return w.s + w.bp + w.s32; }
 
+// Single-pass build: blocks j_first .. j_last, the last one any of the
+// range's windows reaches.
+static void walk_blocks(const BuildArgs& a, int64_t* j_first, int64_t* nbl) {
+  const int64_t j0 = a.n_init / a.B;
+  *j_first = a.u_begin + j0;
+  const int64_t last = a.n_ctx - 1;
+  int64_t e = ((int64_t)a.u_end + j0) * a.B - 1 + a.W;   // window end of the last key
+  e = e < last ? e : last;
+  *nbl = e / a.B - *j_first + 1;
+}
+// [header][counter region: flags rows x nbl, counters rows][quarter-prefix
+// sums rows x nbl x 4 x d]
+struct WalkWs {
+  size_t counters, sums;
+};
+static WalkWs walk_ws_layout(const BuildArgs& a, int64_t nbl) {
+  const size_t rows = (size_t)a.batch * a.Hkv;
+  WalkWs w;
+  w.counters = kWsHeaderBytes + ws_counter_region(rows * (nbl + 1) * sizeof(int));
+  w.sums = round256(rows * nbl * kRepWaves * a.d * sizeof(double));
+  return w;
+}
+size_t walk_counter_bytes(const BuildArgs& a, int64_t nbl) {
+  return ws_counter_region((size_t)a.batch * a.Hkv * (nbl + 1) * sizeof(int));
+}
+// the most blocks a range of n_units units reaches (its windows' end past its
+// last block, plus the block of that end)
+static int64_t walk_blocks_bound(const BuildArgs& a, int64_t n_units) {
+  return n_units + (a.W + a.B - 1) / a.B + 1;
+}
+
 size_t build_workspace_bytes(const BuildArgs& a) {
   if (a.rep_mode != 0 || a.u_end <= a.u_begin) return 0;
-  int64_t jb0, nbl;
-  build_blocks(a, &jb0, &nbl);
-  return ws_total(build_ws_layout(a, nbl));
+  const WalkWs w = walk_ws_layout(a, walk_blocks_bound(a, a.u_end - a.u_begin));
+  return w.counters + w.sums;
 }
 
 // the build that also writes the block query sums (S in the caller's buffer)
@@ -432,7 +743,14 @@ size_t build_qsum_workspace_bytes(const BuildArgs& a) {
 
 size_t build_range_workspace_bytes(const BuildArgs& a, int64_t n_units) {
   if (a.rep_mode != 0 || n_units < 1) return 0;
-  return ws_total(build_ws_layout(a, n_units + (a.W + a.B - 1) / a.B + 2));
+  const WalkWs w = walk_ws_layout(a, walk_blocks_bound(a, n_units));
+  return w.counters + w.sums;
+}
+
+// Counter region of a build's workspace (0: none).
+size_t build_counter_region(const BuildArgs& a, int64_t n_units) {
+  if (a.rep_mode != 0 || n_units < 1) return 0;
+  return walk_counter_bytes(a, walk_blocks_bound(a, n_units));
 }
 
 template <typename T>
@@ -455,6 +773,45 @@ static hipError_t launch_build_t(const BuildArgs& a, hipStream_t st) {
                                                               a.unit_repr);
     return hipGetLastError();
   }
+  const int hs = 64 / (a.d / 8), G = a.Hq / a.Hkv;
+  if (!a.block_qsum) {
+    // the single-pass build; its workspace laid out for at most the range's
+    // bound of blocks, so that ranges of one size share a layout
+    WalkArgs w{};
+    int64_t nbl;
+    walk_blocks(a, &w.j_first, &nbl);
+    const WalkWs lay = walk_ws_layout(a, walk_blocks_bound(a, n_u));
+    const size_t rows = (size_t)a.batch * a.Hkv;
+    w.q = q;
+    w.q_cap = a.q_cap;
+    w.k = k;
+    w.kv_cap = a.kv_cap;
+    w.n_ctx = a.n_ctx;
+    w.Hq = a.Hq;
+    w.Hkv = a.Hkv;
+    w.d = a.d;
+    w.B = a.B;
+    w.n_init = a.n_init;
+    w.W = a.W;
+    w.r_k = a.r_k;
+    w.u_begin = a.u_begin;
+    w.u_end = a.u_end;
+    w.u_stride = a.u_stride;
+    w.nbl = (int)nbl;
+    w.flag = (int*)((char*)a.ws + kWsHeaderBytes);
+    w.count = w.flag + rows * nbl;
+    w.S = (double*)((char*)a.ws + lay.counters);
+    w.rep_idx = a.rep_idx;
+    w.unit_repr = a.unit_repr;
+    const dim3 wgrid((unsigned)nbl, a.Hkv, a.batch);
+    if (G <= hs)
+      k_rep_walk<T, 1><<<wgrid, 64 * kRepWaves, 0, st>>>(w);
+    else if (G <= 2 * hs)
+      k_rep_walk<T, 2><<<wgrid, 64 * kRepWaves, 0, st>>>(w);
+    else
+      return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
   int64_t jb0, nbl;
   build_blocks(a, &jb0, &nbl);
   const BuildWs lay = build_ws_layout(a, nbl);
@@ -471,7 +828,6 @@ static hipError_t launch_build_t(const BuildArgs& a, hipStream_t st) {
                                                       jb0, nb, S, nullptr);
   k_block_prefix<<<dim3(a.Hkv, a.batch), a.d, 0, st>>>(S, BP, a.Hkv, a.d, nb);
   // heads per lane: 64 / (d / 8) head slots per wave
-  const int hs = 64 / (a.d / 8), G = a.Hq / a.Hkv;
   const dim3 grid(n_u, a.Hkv, a.batch);
   if (G <= hs)
     k_rep_select<T, 1><<<grid, 64 * kRepWaves, 0, st>>>(

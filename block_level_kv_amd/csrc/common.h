@@ -109,6 +109,13 @@ template <> struct Raw8<bf16_t> {
       acc[2 * i + 1] += (double)__uint_as_float(w[i] & 0xffff0000u);
     }
   }
+  __device__ __forceinline__ void sub(double* acc) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] -= (double)__uint_as_float(w[i] << 16);
+      acc[2 * i + 1] -= (double)__uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
   __device__ __forceinline__ double get(int i) const {
     return (double)__uint_as_float(i & 1 ? w[i / 2] & 0xffff0000u : w[i / 2] << 16);
   }
@@ -122,6 +129,10 @@ template <> struct Raw8<float> {
   __device__ __forceinline__ void add(double* acc) const {
     acc[0] += x.x; acc[1] += x.y; acc[2] += x.z; acc[3] += x.w;
     acc[4] += y.x; acc[5] += y.y; acc[6] += y.z; acc[7] += y.w;
+  }
+  __device__ __forceinline__ void sub(double* acc) const {
+    acc[0] -= x.x; acc[1] -= x.y; acc[2] -= x.z; acc[3] -= x.w;
+    acc[4] -= y.x; acc[5] -= y.y; acc[6] -= y.z; acc[7] -= y.w;
   }
   __device__ __forceinline__ double get(int i) const {
     const float v[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};

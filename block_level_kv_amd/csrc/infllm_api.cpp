@@ -230,6 +230,17 @@ void counter_region(const infllm_config* cfg, int32_t call, int32_t batch, int64
   *begin = *end = 0;
   size_t region = 0;
   switch (call) {
+    case INFLLM_CALL_BUILD: {
+      const BuildArgs a = build_args(cfg, batch, n);
+      region = build_counter_region(a, a.u_end - a.u_begin);
+      if (region == 0) return;
+      break;
+    }
+    case INFLLM_CALL_BUILD_RANGE: {
+      region = build_counter_region(build_args(cfg, batch, 0), n);
+      if (region == 0) return;
+      break;
+    }
     case INFLLM_CALL_SCORE:
     case INFLLM_CALL_SELECT: {
       ScoreArgs a = score_args(cfg, batch, chunk_len, n_chunks);

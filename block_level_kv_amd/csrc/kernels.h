@@ -128,6 +128,7 @@ hipError_t launch_cache_fetch(const CacheArgs& a, hipStream_t st);
 
 size_t build_workspace_bytes(const BuildArgs& a);
 size_t build_range_workspace_bytes(const BuildArgs& a, int64_t n_units);
+size_t build_counter_region(const BuildArgs& a, int64_t n_units);   // bytes after the header
 size_t build_qsum_workspace_bytes(const BuildArgs& a);
 hipError_t launch_build(const BuildArgs& a, hipStream_t st);
 size_t score_workspace_bytes(const ScoreArgs& a);

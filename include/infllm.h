@@ -193,7 +193,14 @@ INFLLM_API size_t infllm_workspace_size(const infllm_config *cfg, int32_t call, 
  *   rep_idx    out [batch, H_kv, U, r_k] int32 absolute positions, -1 pads
  *              (TOKENS; may be NULL for MEAN)
  *   unit_repr  out [batch, H_kv, U, d] fp32, U = infllm_num_units(n_ctx)
- *   workspace  >= infllm_workspace_size(cfg, INFLLM_CALL_BUILD, batch, n_ctx, 0, 0)
+ *   workspace  >= infllm_workspace_size(cfg, INFLLM_CALL_BUILD, batch, n_ctx, 0, 0),
+ *              zero-filled before its first use (TOKENS: it carries flags of
+ *              published block sums, which every call leaves at zero)
+ * TOKENS runs as one launch that reads the queries about once: one
+ * workgroup per block, from the last block back, publishes its block's
+ * query sum; each unit's window sums take the published sums of the blocks
+ * after it (or sum them itself when one is not published yet: nothing
+ * waits).
  */
 INFLLM_API infllm_status infllm_build_units(const infllm_config *cfg, int32_t batch, const void *q,
                                  int64_t q_cap, const void *k, int64_t kv_cap, int64_t n_ctx,
@@ -231,8 +238,9 @@ INFLLM_API infllm_status infllm_build_units_qsum(const infllm_config *cfg, int32
  * position; a unit whose last key is at or before n_ctx-1-W (all its keys
  * have left the window of position n_ctx-1) gets exactly what a build of
  * any longer context gives it.  Work and workspace
- * grow with the number of units (plus ceil(W/B)+2 blocks of queries), not
- * with n_ctx.
+ * grow with the number of units (plus ceil(W/B)+1 blocks of queries), not
+ * with n_ctx; one launch (the blocks past the range that its windows reach
+ * get workgroups that only publish their sums).
  *
  *   q, k, n_ctx     as infllm_build_units
  *   u_begin, u_end  0 <= u_begin <= u_end <= infllm_num_units(n_ctx)
@@ -241,7 +249,8 @@ INFLLM_API infllm_status infllm_build_units_qsum(const infllm_config *cfg, int32
  *              (TOKENS; may be NULL for MEAN); other rows untouched
  *   unit_repr  out rows u_begin .. u_end-1 of [batch, H_kv, pool_units, d]
  *   workspace  >= infllm_workspace_size(cfg, INFLLM_CALL_BUILD_RANGE, batch,
- *              u_end - u_begin, 0, 0)
+ *              u_end - u_begin, 0, 0), zero-filled before its first use
+ *              (TOKENS: flags that every call leaves at zero)
  */
 INFLLM_API infllm_status infllm_build_units_range(const infllm_config *cfg, int32_t batch,
                                        const void *q, int64_t q_cap, const void *k,

@@ -268,7 +268,19 @@ def test_workspace_counter_regions():
     assert c0 == 256 and c1 - c0 >= 16 * 8 * 8 * 256 > 65536
     # calls without counters
     assert F.infllm_workspace_layout(c, F.INFLLM_CALL_SCORE, 4, 0, 1, 1) == (0, 0, 0)
-    assert F.infllm_workspace_layout(c, F.INFLLM_CALL_BUILD, 1, 8192)[:2] == (0, 0)
+    # the single-pass build: flags of the published block sums (one int per
+    # block and a counter per (sequence, KV head)) in the region, the sums
+    # after it; 64 KiB up to 16K blocks per head group at 8 KV heads
+    for call, b, n, n_units in ((F.INFLLM_CALL_BUILD, 1, 8192, 63),
+                                (F.INFLLM_CALL_BUILD, 2, 1 << 20, 8191),
+                                (F.INFLLM_CALL_BUILD_RANGE, 4, 1, 1)):
+        c0, c1, total = F.infllm_workspace_layout(c, call, b, n, 0, 0)
+        assert total == F.infllm_workspace_size(c, call, b, n, 0, 0)
+        nbl = n_units + 4096 // 128 + 1
+        assert c0 == 256 and c1 - c0 == max(65536, -(-(b * 8 * (nbl + 1) * 4) // 256) * 256)
+        assert total >= c1 + b * 8 * nbl * 4 * 128 * 8, (call, b, n)   # 4 quarter prefixes
+    mean = cfg(rep_mode=F.INFLLM_REP_MEAN)
+    assert F.infllm_workspace_layout(mean, F.INFLLM_CALL_BUILD, 1, 8192, 0, 0) == (0, 0, 0)
 
 
 def test_qsum_validation_and_workspace():
