@@ -795,7 +795,7 @@ def measure(w: synth.Workload, args, peaks, cpu_seconds: float) -> dict:
             and w.n_ctx >= (1 << 20)):
         rec["offload"] = offload_decode(pipe, args.offload_slots,
                                         min(args.offload_steps, w.decode_steps))
-    if pipe.encode and not args.stream:
+    if pipe.encode and not args.stream and not args.no_sequential:
         # the same encoding pass chunk by chunk (one call of each kind per
         # chunk), as the pages process a context
         n_seq = max(1, min(args.steps, 5))
@@ -856,6 +856,9 @@ def main():
                     help="decode workloads: serving form -- ragged sequence lengths, a device "
                          "position per sequence, units added to the pools as they leave the "
                          "window (streaming unit build)")
+    ap.add_argument("--no-sequential", action="store_true",
+                    help="encoding workloads: skip the chunk-by-chunk pass (profiling runs, "
+                         "so that every attention launch in the trace is the one-call pass)")
     ap.add_argument("--offload-slots", type=int, default=64,
                     help="1M-token decode: also run the decode pass with the K/V in pinned host "
                          "memory and a GPU cache of this many units per (sequence, KV head) "
