@@ -146,24 +146,26 @@ constexpr int kPass2Batch = 8;
 // ascending position order to unit_repr.  Every thread calls it; score is
 // complete (a barrier before).
 template <typename T>
-__device__ __forceinline__ void rep_finish(const double* score, int* picked, int nk, int r_k,
+__device__ __forceinline__ void rep_finish(const double* score, int* picked, int* chosen, int nk,
+                                           int r_k,
                                            int64_t lo, const T* kb, int d, int64_t out_row,
                                            int32_t* __restrict__ rep_idx,
                                            float* __restrict__ unit_repr) {
   const int c = threadIdx.x;
-  // rank each key: #keys ahead of it in (score desc, position asc)
+  // rank each key: #keys ahead of it in (score desc, position asc), a NaN
+  // score (from NaN inputs) behind every number, so that the order is total
+  // and exactly min(nk, r_k) keys are kept
   for (int a = c; a < nk; a += blockDim.x) {
     const double sa = score[a];
     int rank = 0;
     for (int b2 = 0; b2 < nk; ++b2) {
       const double sb = score[b2];
-      rank += (sb > sa) || (sb == sa && b2 < a);
+      rank += (sb > sa) || (sb == sa && b2 < a) || (sa != sa && (sb == sb || b2 < a));
     }
     picked[a] = rank < r_k;
   }
   __syncthreads();
   int32_t* ri = rep_idx + out_row * r_k;
-  __shared__ int chosen[kMaxBlock];     // kept key offsets, ascending
   for (int a = c; a < nk; a += blockDim.x) {
     if (picked[a]) {
       int at = 0;
@@ -209,6 +211,7 @@ __global__ __launch_bounds__(64 * kRepWaves) void k_rep_select(
   __shared__ double seg[2][kRepWaves][64][8];   // per wave: rows added to F(p), to F(e_p)
   __shared__ double score[kMaxBlock];
   __shared__ int picked[kMaxBlock];
+  __shared__ int chosen[kMaxBlock];   // kept key offsets, ascending
 
   // this lane's heads (a head past the group repeats head 0 with weight 0)
   const T* qh[HPL];
@@ -370,7 +373,7 @@ __global__ __launch_bounds__(64 * kRepWaves) void k_rep_select(
   }
   __syncthreads();
 
-  rep_finish(score, picked, nk, r_k, lo, kb, d,
+  rep_finish(score, picked, chosen, nk, r_k, lo, kb, d,
              ((int64_t)bi * Hkv + h) * u_stride + u, rep_idx, unit_repr);
 }
 
@@ -397,6 +400,9 @@ __global__ __launch_bounds__(64 * kRepWaves) void k_rep_select(
 // flags and counter.  Queries are read about once (rows p + W are the rows
 // the block of that position's owner read shortly before).
 constexpr int kWalkSpin = 1 << 10;
+// keys a batch in the walk: four keep the bf16 kernel within 128 registers,
+// four workgroups per CU
+constexpr int kWalkBatch = 4;
 
 struct WalkArgs {
   const void* q;
@@ -417,7 +423,8 @@ __device__ __forceinline__ double ld_dev_f64(const double* p) {
 }
 
 template <typename T, int HPL>
-__global__ __launch_bounds__(64 * kRepWaves) void k_rep_walk(WalkArgs a) {
+__global__ __launch_bounds__(64 * kRepWaves)
+__attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 && HPL == 1 ? 4 : 1))) void k_rep_walk(WalkArgs a) {
   const int lb = a.nbl - 1 - (int)blockIdx.x;   // local block index, last first
   const int h = blockIdx.y, bi = blockIdx.z;
   const int64_t j = a.j_first + lb;
@@ -426,11 +433,19 @@ __global__ __launch_bounds__(64 * kRepWaves) void k_rep_walk(WalkArgs a) {
   const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
   const int cgs = d / 8, cg = lane % cgs, slot = lane / cgs, hs = 64 / cgs;
   const int64_t last = a.n_ctx - 1;
-  __shared__ double part[kRepWaves][64][8];   // per-lane quarter sums
+  // the quarter sums, then (once the window sums are formed) the scores
+  __shared__ union {
+    double part[kRepWaves][64][8];   // per-lane quarter sums
+    struct {
+      double score[kMaxBlock];
+      int picked[kMaxBlock], chosen[kMaxBlock];   // kept keys, ascending
+    } f;
+  } ls;
+  static_assert(sizeof(ls.f) <= sizeof(ls.part), "the scores fit the quarter sums' space");
   __shared__ double mid[2][128];              // sums of the blocks in between (halves)
-  __shared__ double score[kMaxBlock];
-  __shared__ int picked[kMaxBlock];
   __shared__ int all_in;
+  double(&part)[kRepWaves][64][8] = ls.part;
+  double* score = ls.f.score;
 
   const T* qh[HPL];
   bool hv[HPL];
@@ -544,11 +559,11 @@ __global__ __launch_bounds__(64 * kRepWaves) void k_rep_walk(WalkArgs a) {
         __syncthreads();
       }
     }
+    double w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (k0 < k1) {
       // ---- B: the window sum of the wave's first key
       const int64_t p0 = lo + k0;
       const int64_t e0 = p0 + a.W < last ? p0 + a.W : last;
-      double w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       if (pub_ok) {
         const int64_t je = e0 / B, off = e0 - je * B;
         const int qf = (int)((off + 1) / qn);         // whole quarters of je's block up to e0
@@ -586,11 +601,14 @@ __global__ __launch_bounds__(64 * kRepWaves) void k_rep_walk(WalkArgs a) {
           add_rows(jb * B, e0, 1, w);                          // head of e's block
         }
       }
+    }
+    __syncthreads();   // part read for the last time: the scores take its space
+    if (k0 < k1) {
       // ---- C: the walk, a batch's rows requested before any is used
-      for (int o0 = k0; o0 < k1; o0 += kPass2Batch) {
-        Raw8<T> rl[kPass2Batch][HPL], ru[kPass2Batch][HPL], rk[kPass2Batch];
+      for (int o0 = k0; o0 < k1; o0 += kWalkBatch) {
+        Raw8<T> rl[kWalkBatch][HPL], ru[kWalkBatch][HPL], rk[kWalkBatch];
 #pragma unroll
-        for (int y = 0; y < kPass2Batch; ++y) {
+        for (int y = 0; y < kWalkBatch; ++y) {
           const int64_t p = lo + (o0 + y < k1 ? o0 + y : k1 - 1);
           const int64_t pl = p + 1 < last ? p + 1 : last;
           const int64_t pe = p + 1 + a.W < last ? p + 1 + a.W : last;
@@ -601,9 +619,9 @@ __global__ __launch_bounds__(64 * kRepWaves) void k_rep_walk(WalkArgs a) {
           }
           rk[y].load(kb + p * d + cg * 8);
         }
-        double t[kPass2Batch];
+        double t[kWalkBatch];
 #pragma unroll
-        for (int y = 0; y < kPass2Batch; ++y) {
+        for (int y = 0; y < kWalkBatch; ++y) {
           const int64_t p = lo + o0 + y;
           t[y] = 0.0;
           if (o0 + y >= k1) continue;
@@ -618,14 +636,15 @@ __global__ __launch_bounds__(64 * kRepWaves) void k_rep_walk(WalkArgs a) {
           }
         }
 #pragma unroll
-        for (int y = 0; y < kPass2Batch; ++y) {
+        for (int y = 0; y < kWalkBatch; ++y) {
           const double tt = wave_sum_f64_dpp(t[y]);
           if (lane == 0 && o0 + y < k1) score[o0 + y] = tt;
         }
       }
     }
     __syncthreads();
-    rep_finish(score, picked, nk, a.r_k, lo, kb, d, row * a.u_stride + u, a.rep_idx,
+    rep_finish(score, ls.f.picked, ls.f.chosen, nk, a.r_k, lo, kb, d, row * a.u_stride + u,
+               a.rep_idx,
                a.unit_repr);
   }
   // ---- the last workgroup of this (sequence, KV head) clears its flags

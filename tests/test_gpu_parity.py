@@ -169,6 +169,49 @@ def test_build_range_truncated(orc, data, name):
     check_units(orc, w, inp, n_mid, lo, Um, repg, rg[:, :, lo:Um])
 
 
+@pytest.mark.parametrize("name", ["bf16_g4", "bf16_g8_ragged"])
+def test_build_nan_queries_stay_in_rows(data, name):
+    """Query rows holding NaN give some keys NaN scores: every unit still
+    keeps exactly r_k distinct keys of its own (NaN scores rank behind every
+    number), and nothing is written outside the range's rows of the pool --
+    for the range build, the full build and the build with block query sums."""
+    w, inp, dev = data(name)
+    cfg = cfg_of(w)
+    q = dev["q"].clone()
+    q[:, :, 700:705] = float("nan")
+    q[:, 1, 1900] = float("nan")
+    U = F.infllm_num_units(cfg, w.n_ctx)
+    B, n_init, r_k = w.block, w.n_init, w.rep_k
+
+    def check(rep, lo, hi):
+        repg = rep.cpu().numpy()
+        assert (repg[:, :, :lo] == -7).all() and (repg[:, :, hi:] == -7).all()
+        for u in range(lo, hi):
+            first = max((u + n_init // B) * B, n_init)
+            ids = repg[:, :, u].reshape(-1, r_k)
+            for row in ids:
+                assert len(set(row.tolist())) == r_k, (u, row)
+                assert ((row >= first) & (row < (u + n_init // B + 1) * B)).all(), (u, row)
+
+    rep, repr_ = range_pool(cfg, w, U + 3)
+    ws = F.workspace(cfg, F.INFLLM_CALL_BUILD_RANGE, w.batch, U - 2, device="cuda")
+    F.infllm_build_units_range(cfg, q, dev["k"], w.n_ctx, 2, U, rep, repr_, ws)
+    torch.cuda.synchronize()
+    check(rep, 2, U)
+    rep, repr_ = range_pool(cfg, w, U)
+    ws = F.workspace(cfg, F.INFLLM_CALL_BUILD, w.batch, w.n_ctx, device="cuda")
+    F.infllm_build_units(cfg, q, dev["k"], w.n_ctx, rep, repr_, ws)
+    torch.cuda.synchronize()
+    check(rep, 0, U)
+    rep, repr_ = range_pool(cfg, w, U)
+    nb = (w.n_ctx + B - 1) // B
+    bq = torch.empty((w.batch, w.n_kv_heads, nb, w.head_dim), dtype=torch.float64, device="cuda")
+    ws = F.workspace(cfg, F.INFLLM_CALL_BUILD_QSUM, w.batch, w.n_ctx, device="cuda")
+    F.infllm_build_units_qsum(cfg, q, dev["k"], w.n_ctx, rep, repr_, bq, ws)
+    torch.cuda.synchronize()
+    check(rep, 0, U)
+
+
 @pytest.mark.parametrize("name", list(CASES))
 def test_score_and_topk_parity(orc, data, name):
     w, inp, dev = data(name)
