@@ -143,7 +143,11 @@ def test_fullsize_llama3_1m_decode_recall(orc):
     planted = p.inp["planted_units"]                        # absolute blocks [b, H_kv, 8]
     j0 = w.n_init // w.block
     pu = int(planted[0, 0, 0]) - j0
-    check_build(orc, w, p, [(0, 0, pu, pu + 2), (1, 6, U - 6, U)])
+    # units across the whole pool (every tenth of the context) as well as a
+    # planted unit and the truncated windows at the end
+    spread = [(0, 3, f * U // 10, f * U // 10 + 2) for f in (1, 3, 5, 7, 9)]
+    spread += [(1, 2, f * U // 10 + 1, f * U // 10 + 3) for f in (0, 2, 4, 6, 8)]
+    check_build(orc, w, p, [(0, 0, pu, pu + 2), (1, 6, U - 6, U)] + spread)
     qd = p.inp["q_dec"].cpu()
     items = [(s, s, w.n_ctx + s, 1) for s in range(w.decode_steps)]
     sel, orc_sel, _ = check_selections(orc, w, p, qd, p.sel_dec, items)
