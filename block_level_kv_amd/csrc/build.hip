@@ -414,6 +414,8 @@ struct WalkArgs {
   double* S;       // [rows][nbl][4][d] published sums of quarters 0..q-1, q = 1..4
   int* flag;       // [rows][nbl]
   int* count;      // [rows]
+  int* status;     // the workspace header (word 2: units that summed the rows themselves)
+  int spin;        // polls for the published sums (0: always sum the rows)
   int32_t* rep_idx;
   float* unit_repr;
 };
@@ -525,14 +527,16 @@ __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 && HPL == 1 ? 4 : 1))) void k_
       int f = 1;
       const int* fl = a.flag + row * a.nbl + (j + 1 - a.j_first);
       if (tid < n_need) f = __hip_atomic_load(fl + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      bool miss = __syncthreads_or(f == 0);
-      for (int it = 0; it < kWalkSpin && miss; ++it) {
+      bool miss = a.spin == 0 || __syncthreads_or(f == 0);   // spin 0: always the rows
+      for (int it = 1; it < a.spin && miss; ++it) {
         __builtin_amdgcn_s_sleep(2);
         if (tid < n_need && f == 0)
           f = __hip_atomic_load(fl + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         miss = __syncthreads_or(f == 0);
       }
       pub_ok = !miss && n_need <= (int)blockDim.x;
+      if (!pub_ok && tid == 0)
+        __hip_atomic_fetch_add(a.status + 2, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (pub_ok) {
         // full sums of blocks j+1 .. jm-1, blockDim/d threads a column,
         // every load in flight together
@@ -820,6 +824,8 @@ static hipError_t launch_build_t(const BuildArgs& a, hipStream_t st) {
     w.flag = (int*)((char*)a.ws + kWsHeaderBytes);
     w.count = w.flag + rows * nbl;
     w.S = (double*)((char*)a.ws + lay.counters);
+    w.status = (int*)a.ws;
+    w.spin = tuning().build_spin >= 0 ? tuning().build_spin : kWalkSpin;
     w.rep_idx = a.rep_idx;
     w.unit_repr = a.unit_repr;
     const dim3 wgrid((unsigned)nbl, a.Hkv, a.batch);

@@ -30,6 +30,8 @@ const Tuning& tuning() {
     x.step_splits = get("INFLLM_STEP_SPLITS", 2, 64);
     const char* e = getenv("INFLLM_STEP_PRESPIN");
     x.step_prespin = e && atoi(e) >= 0 && atoi(e) <= (1 << 20) ? atoi(e) : -1;
+    e = getenv("INFLLM_BUILD_SPIN");
+    x.build_spin = e && atoi(e) >= 0 && atoi(e) <= (1 << 20) ? atoi(e) : -1;
     return x;
   }();
   return t;

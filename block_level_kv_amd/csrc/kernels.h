@@ -30,6 +30,7 @@ inline size_t ws_counter_region(size_t counter_bytes) {
 struct Tuning {
   int prefill_splits, rows_wgs, step_splits;
   int step_prespin;   // -1: the default bound
+  int build_spin;     // -1: the default bound
 };
 const Tuning& tuning();
 

@@ -47,8 +47,10 @@
  *    chunks, the selection, split attention, the decode step) starts with
  *    a 256-byte header -- its first int32 counts waits of the decode step
  *    that timed out (infllm_workspace_status), its second the rows of the
- *    one-launch step that an attention workgroup selected itself (a
- *    diagnostic; both only grow) -- followed by a counter
+ *    one-launch step that an attention workgroup selected itself, its
+ *    third the units of a TOKENS build that summed their window's query
+ *    rows themselves because a block sum they could have used was not
+ *    published in time (diagnostics; all only grow) -- followed by a counter
  *    region of at least 64 KiB, then the call's data (partial sums and
  *    rows).  It must be zero-filled before its first use; every call
  *    leaves its counters at zero again.  Since every call kind keeps its
@@ -65,7 +67,10 @@
  *    chunk attention, the decode attention and the one-launch decode step
  *    (workgroups per row); INFLLM_STEP_PRESPIN (0 .. 2^20) the polls of
  *    the one-launch step's attention workgroups for the row's selection
- *    before they select it themselves (same result, more work).  They are
+ *    before they select it themselves (same result, more work);
+ *    INFLLM_BUILD_SPIN (0 .. 2^20) the polls of a TOKENS build's unit for
+ *    the block sums it uses before it sums the query rows itself (0: it
+ *    always does; the same selection up to rounding, more work).  They are
  *    read once per process, at the first call that needs them; workspace
  *    sizes follow them.
  *  Units.  Unit u is absolute block j = u + floor(n_init / block); its keys

@@ -74,6 +74,57 @@ def test_build_parity(orc, data, name):
     np.testing.assert_array_equal(rg[same], repr_o.astype(np.float32)[same])
 
 
+def build_rows_fallback_case(orc, name):
+    """test_build_parity for one case on a fresh workspace; returns the
+    workspace's count of units that summed their window's rows themselves
+    (header word 2)."""
+    w = CASES[name]
+    inp = synth.make_inputs(w)
+    cfg = cfg_of(w)
+    q, k = inp["q"].cuda(), inp["k"].cuda()
+    b, U = w.batch, F.infllm_num_units(cfg, w.n_ctx)
+    rep = torch.empty((b, w.n_kv_heads, U, w.rep_k), dtype=torch.int32, device="cuda")
+    repr_ = torch.empty((b, w.n_kv_heads, U, w.head_dim), dtype=torch.float32, device="cuda")
+    ws = F.workspace(cfg, F.INFLLM_CALL_BUILD, b, w.n_ctx)
+    F.infllm_build_units(cfg, q, k, w.n_ctx, rep, repr_, ws)
+    torch.cuda.synchronize()
+    rep_o, repr_o, ks_o = oracle_build(orc, w, inp)
+    ex = check_rep_idx(rep.cpu().numpy(), rep_o, ks_o, w.block, w.n_init)
+    assert len(ex) <= max(2, rep_o.shape[2] // 50)
+    same = np.all(rep.cpu().numpy() == rep_o, axis=-1)
+    np.testing.assert_array_equal(repr_.cpu().numpy()[same], repr_o.astype(np.float32)[same])
+    return int(ws[8:12].view(torch.int32)[0])
+
+
+def test_build_from_rows():
+    """INFLLM_BUILD_SPIN=0: every unit that would take the published block
+    sums of the blocks after it sums its window's query rows itself instead
+    (the path a unit takes when those sums are late): the same selection as
+    the oracle, and the header counts the units that did."""
+    import os
+    import subprocess
+    import sys
+    here = os.path.dirname(os.path.abspath(__file__))
+    code = ("import sys\n"
+            "sys.path[:0] = [%r, %r]\n"
+            "from oracle import oracle as orc\n"
+            "import test_gpu_parity as t\n"
+            "for name in ('bf16_g4', 'f32_g1', 'bf16_g2_d64', 'bf16_g4_unit'):\n"
+            "    print('case', name, flush=True)\n"
+            "    print('from rows', name, t.build_rows_fallback_case(orc, name), flush=True)\n"
+            "print('ok', flush=True)\n") % (here, os.path.dirname(here))
+    env = dict(os.environ, INFLLM_BUILD_SPIN="0")
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout + r.stderr
+    for line in r.stdout.splitlines():
+        if line.startswith("from rows"):
+            name, n = line.split()[2], int(line.split()[3])
+            w = CASES[name]
+            U = F.infllm_num_units(cfg_of(w), w.n_ctx)
+            assert 0 < n <= w.batch * w.n_kv_heads * U, line
+
+
 def check_units(orc, w, inp, n_ctx, u_lo, u_hi, rep_g, repr_g):
     """GPU rows u_lo .. u_hi-1 (rep_g / repr_g: [b, H_kv, u_hi-u_lo, .]) against
     the oracle's build of a context of n_ctx tokens, per (batch, KV head)."""
