@@ -1030,13 +1030,15 @@ void k_select_attend(ScoreArgs s, AttendArgs a, StepPlan p, StepPtrs w) {
   r.finish(j, N, y.merge, 1, w.sync + (int64_t)row * kStepSyncInts, kStepSyncInts, stale);
 }
 
-// Plan of a fused step.  At most kStepTargetWGs workgroups per launch (3 per
-// CU, so that all of them are resident at once), a selector and n_splits
-// attention workgroups per row.  Scoring workgroups take the fewest units (64 .. 256) that leave
+// Plan of a fused step.  One, two or three workgroups per CU in all (a
+// whole number per CU, so that every CU ends together, and at most what is
+// resident at once), a selector and n_splits attention workgroups per row.
+// Scoring workgroups take the fewest units (64 .. 256) that leave
 // at least a sixteenth of a row's workgroups without a slice; every
 // workgroup takes an equal share of the units' keys, and the local keys
 // are shared so that every workgroup moves about the same number of bytes.
-constexpr int64_t kStepTargetWGs = 768;
+constexpr int64_t kStepCUs = 256;                // MI355X compute units
+constexpr int64_t kStepBytesPerWave = 64ll << 20;   // step bytes per workgroup per CU
 constexpr int kStepMaxCand = 8 * kRowsThreads;   // candidates of a row: 8 per lane
 
 int64_t step_rows(const AttendArgs& a) { return (int64_t)a.batch * a.Hkv * a.n_pos; }
@@ -1051,7 +1053,16 @@ bool select_attend_plan(const ScoreArgs& s, const AttendArgs& a, StepPlan* p) {
   if (G != 1 && G != 2 && G != 4 && G != 8) return false;
   const int64_t rows = step_rows(a);
   if (rows > ((int64_t)1 << 24)) return false;
-  int64_t n = kStepTargetWGs / rows - 1;   // attention workgroups (the selector is one more)
+  // one, two or three workgroups per CU, about one per CU for every 64 MiB
+  // the step moves (measured at 128K, 153 MB: 43.3 us with 2 per CU, 44.2
+  // with 3; Mistral 64K, 36 MB: 24.0 us with 1, 26.4 with 2; a grid that is
+  // not a whole number of workgroups per CU leaves some CUs one more and
+  // ends late: 49-52 us at 128K with 576 or 640)
+  const double row_bytes = (double)s.U * (a.d + 1) * 4.0 +
+                           ((double)a.n_init + a.W + (double)a.k_m * a.B) * 2.0 * a.d * 2.0;
+  int64_t per_cu = (int64_t)(rows * row_bytes / (double)kStepBytesPerWave + 0.5);
+  per_cu = per_cu < 1 ? 1 : (per_cu > 3 ? 3 : per_cu);
+  int64_t n = kStepCUs * per_cu / rows - 1;   // attention workgroups (the selector is one more)
   if (tuning().step_splits > 0) n = tuning().step_splits;
   n = n < 2 ? 2 : (n > kMaxSplits ? kMaxSplits : n);
   int up = 0;

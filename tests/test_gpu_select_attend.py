@@ -114,20 +114,20 @@ ANY_PLAN = "any"   # a plan whose shape the test does not fix
 # one-launch shape infllm_step_plan must report, (workgroups per row,
 # scoring workgroups, units each), or None for the two separate calls
 SHAPES = [
-    (8, 2, 128, 47, 8, 1, 1024, 128, False, "bf16", (64, 1, 64)),      # one scorer per row
-    (4, 4, 128, 300, 16, 2, 512, 128, False, "bf16", (47, 5, 64)),     # G = 1, two positions
-    (8, 4, 64, 200, 6, 3, 384, 100, False, "bf16", (31, 4, 64)),       # G = 2, d = 64, sinks not B-aligned
-    (16, 2, 128, 100, 4, 1, 512, 128, True, "bf16", (64, 2, 64)),      # G = 8, a position per sequence
-    (8, 2, 128, 1024, 32, 1, 1024, 128, False, "bf16", (64, 16, 64)),  # 512 candidates per row
+    (8, 2, 128, 47, 8, 1, 1024, 128, False, "bf16", (63, 1, 64)),      # one scorer per row
+    (4, 4, 128, 300, 16, 2, 512, 128, False, "bf16", (15, 5, 64)),     # G = 1, two positions
+    (8, 4, 64, 200, 6, 3, 384, 100, False, "bf16", (9, 4, 64)),       # G = 2, d = 64, sinks not B-aligned
+    (16, 2, 128, 100, 4, 1, 512, 128, True, "bf16", (63, 2, 64)),      # G = 8, a position per sequence
+    (8, 2, 128, 1024, 32, 1, 1024, 128, False, "bf16", (63, 16, 64)),  # 512 candidates per row
     (8, 1, 128, 2048, 32, 1, 512, 128, False, "bf16", (64, 32, 64)),   # 32 scorers
-    (8, 2, 128, 1500, 32, 8, 512, 128, False, "bf16", (23, 12, 128)),  # 128 units per scorer
+    (8, 2, 128, 1500, 32, 8, 512, 128, False, "bf16", (15, 12, 128)),  # 128 units per scorer
     (8, 2, 128, 1500, 32, 16, 512, 128, False, "bf16", (11, 8, 192)),  # 192 units per scorer
     (4, 2, 128, 4000, 32, 1, 512, 128, False, "bf16", None),  # more scores than one search: two calls
-    (4, 2, 128, 300, 8, 16, 512, 128, False, "bf16", (11, 5, 64)),     # few workgroups per row
-    (4, 2, 128, 30, 40, 1, 512, 128, False, "bf16", (64, 1, 64)),      # k_m > units
-    (4, 2, 128, 600, 256, 1, 512, 128, False, "bf16", (64, 10, 64)),   # the largest k_m
-    (8, 2, 128, 64, 2, 1, 4096, 128, False, "bf16", (64, 1, 64)),      # nearly all keys local
-    (32, 8, 128, 300, 8, 32, 512, 128, False, "bf16", (3, 2, 256)),    # 1,536 workgroups: twice what fits at once
+    (4, 2, 128, 300, 8, 16, 512, 128, False, "bf16", (3, 2, 192)),     # few workgroups per row
+    (4, 2, 128, 30, 40, 1, 512, 128, False, "bf16", (63, 1, 64)),      # k_m > units
+    (4, 2, 128, 600, 256, 1, 512, 128, False, "bf16", (63, 10, 64)),   # the largest k_m
+    (8, 2, 128, 64, 2, 1, 4096, 128, False, "bf16", (63, 1, 64)),      # nearly all keys local
+    (32, 8, 128, 300, 8, 32, 512, 128, False, "bf16", (3, 2, 256)),    # 2,048 workgroups: more than fit at once
     (4, 2, 128, 4095, 256, 1, 512, 128, False, "bf16", None),          # 4,096 candidates: separate calls
     (2, 1, 64, 40, 4, 1, 512, 64, False, "f32", None),                 # fp32: separate calls
 ]
@@ -222,7 +222,7 @@ SELF_SELECT_SHAPES = [
     (8, 2, 128, 1024, 32, 1, 1024, 128, False, "bf16"),   # 16 scorers, 512 candidates
     (16, 2, 128, 100, 4, 1, 512, 128, True, "bf16"),      # G = 8, a position per sequence
     (4, 2, 128, 600, 256, 1, 512, 128, False, "bf16"),    # the largest k_m
-    (32, 8, 128, 300, 8, 32, 512, 128, False, "bf16"),    # 1,536 workgroups
+    (32, 8, 128, 300, 8, 32, 512, 128, False, "bf16"),    # 2,048 workgroups
     (8, 4, 64, 200, 6, 3, 384, 100, False, "bf16"),       # d = 64, sinks not B-aligned
 ]
 
