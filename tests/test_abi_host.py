@@ -247,6 +247,25 @@ def test_step_plan(b, Hkv, G, U, k_m, n_pos):
     assert total >= c1 + rows * S * C * 8 + N * b * Hq * n_pos * (d * 4 + 8)
 
 
+
+@pytest.mark.parametrize("b,Hkv,U,n_pos,per_cu", [
+    (4, 8, 1023, 1, 2),     # 128K decode: 153 MB per step, two workgroups per CU
+    (1, 8, 511, 1, 1),      # Mistral 64K decode: 36 MB, one per CU
+    (1, 4, 1023, 1, 1),     # a light step: one per CU (64 workgroups a row)
+    (8, 8, 1023, 1, 3),     # 306 MB: three per CU (the most resident at once)
+    (2, 8, 2047, 2, 3)])    # 171 MB: three per CU
+def test_step_plan_grid(b, Hkv, U, n_pos, per_cu):
+    """The one-launch decode step's grid is a whole number of workgroups per
+    CU of the MI355X's 256, one to three, about one per CU for every 64 MiB
+    the step moves: a grid with some CUs holding one workgroup more than
+    others ends when those do.  (Rows of fewer than 4 rows a call stop at
+    64 attention workgroups a row.)"""
+    c = cfg(n_q_heads=4 * Hkv, n_kv_heads=Hkv, top_k=32)
+    p = F.infllm_step_plan(c, b, U, n_pos)
+    assert p["fused"] == 1
+    rows = b * Hkv * n_pos
+    assert (p["n_splits"] + 1) * rows == 256 * per_cu
+
 def test_workspace_counter_regions():
     """Every call kind keeps its counters in [256, 256 + region) with a
     region of at least 64 KiB, and its data after it: a zero-filled
