@@ -59,12 +59,16 @@ PEAK_F32_TFLOPS = 157.3       # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
 
-def cfg_of(w: synth.Workload) -> F.infllm_config:
+def cfg_of(w: synth.Workload, rope_theta: float = 0.0) -> F.infllm_config:
+    """The library configuration of a workload; rope_theta > 0: the attention
+    re-positions q and k inside the working context (keys otherwise arrive
+    turned at their absolute positions)."""
     return F.make_config(n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, head_dim=w.head_dim,
                          block=w.block, n_init=w.n_init, window=w.window, rep_k=w.rep_k,
                          top_k=w.top_k,
                          rep_mode=F.INFLLM_REP_MEAN if w.rep_mode == "mean" else F.INFLLM_REP_TOKENS,
-                         dtype=F.INFLLM_F32 if w.dtype == "f32" else F.INFLLM_BF16)
+                         dtype=F.INFLLM_F32 if w.dtype == "f32" else F.INFLLM_BF16,
+                         rope_theta=rope_theta)
 
 
 def attended_counts(w: synth.Workload, t0: int, L: int, sel: np.ndarray) -> np.ndarray:
@@ -94,8 +98,8 @@ class Pipeline:
     pool.  Selections and outputs of the last step are kept for checking."""
 
     def __init__(self, w: synth.Workload, dev: str = "cuda", layers: int = 1,
-                 fused_step: bool = True):
-        self.w, self.cfg, self.dev = w, cfg_of(w), dev
+                 fused_step: bool = True, rope_theta: float = 0.0):
+        self.w, self.cfg, self.dev = w, cfg_of(w, rope_theta), dev
         t = time.time()
         self.inp = synth.make_inputs(w, device=dev)
         torch.cuda.synchronize()
@@ -298,8 +302,9 @@ class StreamPipeline:
 
     encode, decode = False, True
 
-    def __init__(self, w: synth.Workload, dev: str = "cuda", layers: int = 1):
-        self.w, self.cfg, self.dev = w, cfg_of(w), dev
+    def __init__(self, w: synth.Workload, dev: str = "cuda", layers: int = 1,
+                 rope_theta: float = 0.0):
+        self.w, self.cfg, self.dev = w, cfg_of(w, rope_theta), dev
         cfg = self.cfg
         self.inp = synth.make_inputs(w, device=dev)
         self.q_all = synth.make_stream_queries(w, self.inp["q"])
@@ -708,8 +713,9 @@ def measure(w: synth.Workload, args, peaks, cpu_seconds: float) -> dict:
     bench line's fields for this workload)."""
     decode_only = w.chunk == 0
     layers = (args.layers or 4) if decode_only else 1
-    pipe = (StreamPipeline(w, layers=layers) if args.stream else
-            Pipeline(w, layers=layers, fused_step=not args.separate_decode))
+    pipe = (StreamPipeline(w, layers=layers, rope_theta=args.rope_theta) if args.stream else
+            Pipeline(w, layers=layers, fused_step=not args.separate_decode,
+                     rope_theta=args.rope_theta))
     if not pipe.encode:
         pipe.build_all()        # decode-only: the pools are built once, beforehand
     # Untimed settling before the warm-up steps: the GPU's clocks ramp up
@@ -765,6 +771,10 @@ def measure(w: synth.Workload, args, peaks, cpu_seconds: float) -> dict:
                               span_ms("dec_sel", "dec_end") / w.decode_steps, w.decode_steps,
                               peaks, getattr(pipe, "fused", False))),
     }
+    if args.rope_theta > 0:
+        # the committed profiles cover the as-given kernels, not the turning ones
+        rec["config"]["rope_theta"] = args.rope_theta
+        rec["roofline"].update(traffic=None, profile_avg_launch_us=None, frac_from_profile=None)
     if args.stream:
         rec["config"]["stream"] = {"lengths": pipe.lens, "pool_units": pipe.U,
                                    "unit_build_calls_per_step": pipe.n_builds * len(pipe.layers)}
@@ -791,6 +801,9 @@ def measure(w: synth.Workload, args, peaks, cpu_seconds: float) -> dict:
             rec["decode_roofline"] = roofline(w, "decode", work["decode"],
                                               span_ms("dec_sel", "dec_end") / w.decode_steps,
                                               w.decode_steps, peaks, pipe.fused)
+            if args.rope_theta > 0:
+                rec["decode_roofline"].update(traffic=None, profile_avg_launch_us=None,
+                                              frac_from_profile=None)
     if (pipe.decode and not pipe.encode and not args.stream and args.offload_slots > 0
             and w.n_ctx >= (1 << 20)):
         rec["offload"] = offload_decode(pipe, args.offload_slots,
@@ -865,6 +878,9 @@ def main():
                          "(0 to skip)")
     ap.add_argument("--offload-steps", type=int, default=16,
                     help="decode steps of that pass (each miss moves a unit over the host link)")
+    ap.add_argument("--rope-theta", type=float, default=0.0, metavar="THETA",
+                    help="RoPE base: the attention re-positions q and k inside each working "
+                         "context (timing only: no oracle baseline, no offload record)")
     ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
                     help="after timing, run one plain device copy of MIB MiB (untimed), the "
                          "reference kernel for scaling HBM byte counters")
@@ -874,6 +890,12 @@ def main():
               "pool resident; runs on %d GPUs are not part of this benchmark" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
+    if args.rope_theta < 0:
+        print("--rope-theta must be >= 0", file=sys.stderr)
+        sys.exit(2)
+    if args.rope_theta > 0:
+        # the oracle baseline and the offload record time the as-given form
+        args.no_cpu_baseline, args.offload_slots = True, 0
     torch.cuda.set_device(0)
     names = [args.workload] if args.workload else ALL_WORKLOADS
     if args.stream and any(synth.WORKLOADS[n].chunk > 0 for n in names):

@@ -906,12 +906,15 @@ __device__ __forceinline__ bool step_wait(const ScoreArgs& s, const StepPlan& p,
   return ss.last;
 }
 
-template <typename T, int D, int G, int NSUB, int VPT>
-__global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(3)))
+// ROPE: keys turned to their places in the working context; the turned
+// keys' registers fit two workgroups per CU (the plan puts at most two
+// there), the others three.
+template <typename T, int D, int G, int NSUB, int VPT, bool ROPE>
+__global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(ROPE ? 2 : 3)))
 void k_select_attend(ScoreArgs s, AttendArgs a, StepPlan p, StepPtrs w) {
   static_assert(kRowsThreads == kScoreThreads, "one workgroup size for both roles");
-  using Attn = RowsAttn<T, D, G>;
-  __shared__ RowsShared<G, D> sh;
+  using Attn = RowsAttn<T, D, G, ROPE>;
+  __shared__ RowsShared<G, D, ROPE> sh;
   __shared__ StepShared ss;
   const int N = p.n_splits, S = p.s_score;
   // row = (sequence * H_kv + KV head) * positions + position; one chunk per
@@ -972,6 +975,7 @@ void k_select_attend(ScoreArgs s, AttendArgs a, StepPlan p, StepPtrs w) {
     step_score<T, G, D, NSUB, false>(s, p, j, row, pos, h, bi, y, w, ss);
   }
   Attn r(a, sh, pos, h, bi);
+  if constexpr (ROPE) __syncthreads();   // the frequency table, before the first turn
   const int64_t l_lo = j < S ? (int64_t)j * p.w_score
                              : (int64_t)S * p.w_score + (int64_t)(j - S) * p.w_unit;
   r.shares(l_lo, l_lo + (j < S ? p.w_score : p.w_unit),
@@ -1045,12 +1049,14 @@ int64_t step_rows(const AttendArgs& a) { return (int64_t)a.batch * a.Hkv * a.n_p
 
 bool select_attend_plan(const ScoreArgs& s, const AttendArgs& a, StepPlan* p) {
   if (!a.bf16 || a.L != 1 || s.U < 1 || a.k_m < 1 || a.k_m > kMaxTopK) return false;
-  // re-positioned keys take the attention launch: turning them here needs
-  // ~40 more VGPRs than the three resident workgroups per CU leave (with
-  // the spills, 96 against 53 us per step at 128K in two launches)
-  if (a.rope_theta > 0.0) return false;
   const int G = a.Hq / a.Hkv;
   if (G != 1 && G != 2 && G != 4 && G != 8) return false;
+  // re-positioned keys (head_dim 128, up to 4 query heads a KV head):
+  // turning them needs ~40 more VGPRs than three workgroups per CU leave
+  // (with the spills, 96 against 53 us per step at 128K in two launches),
+  // so such a launch holds at most two; with 8 heads they spill even then
+  const bool rope = a.rope_theta > 0.0;
+  if (rope && (a.d != 128 || G > 4)) return false;
   const int64_t rows = step_rows(a);
   if (rows > ((int64_t)1 << 24)) return false;
   // one, two or three workgroups per CU, about one per CU for every 64 MiB
@@ -1061,7 +1067,7 @@ bool select_attend_plan(const ScoreArgs& s, const AttendArgs& a, StepPlan* p) {
   const double row_bytes = (double)s.U * (a.d + 1) * 4.0 +
                            ((double)a.n_init + a.W + (double)a.k_m * a.B) * 2.0 * a.d * 2.0;
   int64_t per_cu = (int64_t)(rows * row_bytes / (double)kStepBytesPerWave + 0.5);
-  per_cu = per_cu < 1 ? 1 : (per_cu > 3 ? 3 : per_cu);
+  per_cu = per_cu < 1 ? 1 : (per_cu > (rope ? 2 : 3) ? (rope ? 2 : 3) : per_cu);
   int64_t n = kStepCUs * per_cu / rows - 1;   // attention workgroups (the selector is one more)
   if (tuning().step_splits > 0) n = tuning().step_splits;
   n = n < 2 ? 2 : (n > kMaxSplits ? kMaxSplits : n);
@@ -1115,7 +1121,13 @@ static hipError_t launch_step_dgn(const ScoreArgs& s, const AttendArgs& a, const
                                   const StepPtrs& w, hipStream_t st) {
   const dim3 grid((unsigned)(step_rows(a) * (p.n_splits + 1)));
   static_assert(kStepMaxCand <= 8 * kRowsThreads, "candidate keys per lane");
-  k_select_attend<bf16_t, D, G, NSUB, 8><<<grid, kRowsThreads, 0, st>>>(s, a, p, w);
+  if constexpr (D == 128) {
+    if (a.rope_theta > 0.0) {
+      k_select_attend<bf16_t, D, G, NSUB, 8, true><<<grid, kRowsThreads, 0, st>>>(s, a, p, w);
+      return hipGetLastError();
+    }
+  }
+  k_select_attend<bf16_t, D, G, NSUB, 8, false><<<grid, kRowsThreads, 0, st>>>(s, a, p, w);
   return hipGetLastError();
 }
 

@@ -446,8 +446,9 @@ INFLLM_API infllm_status infllm_attend_varlen(const infllm_config *cfg, int32_t 
  * its selection: scores and sel are identical; out and lse equal up to fp32
  * rounding (the attention is split over workgroups differently).
  *
- * Where the shapes allow (bf16, rope_theta 0, k_m >= 1, and a row's scores
- * few enough to be searched at once: up to 2,048 units) it is one launch: in each
+ * Where the shapes allow (bf16, k_m >= 1, a row's scores few enough to be
+ * searched at once: up to 2,048 units; with rope_theta > 0 also head_dim
+ * 128 and at most 4 query heads per KV head) it is one launch: in each
  * (sequence, KV head, position) row some workgroups score a slice of units
  * each and publish the scores, a selector workgroup selects the row's units
  * from them and publishes the selection, and every attention workgroup

@@ -235,35 +235,53 @@ def test_rope_varlen(orc, data):
         assert_close(out[b:b + 1], o_ref, tolerance(torch.bfloat16, o_ref), "varlen %d" % b)
 
 
-def test_rope_select_attend(orc, data):
-    """The decode step with rope_theta set runs the selection and the
-    attention calls: its selection equals infllm_select_units and its output
-    the attention of that selection, bit for bit, and the oracle's."""
-    w, theta, inp, dev = data("bf16_g4")
+@pytest.mark.parametrize("name,one_launch", [("bf16_g4", True), ("bf16_g8_ragged", False)])
+def test_rope_select_attend(orc, data, name, one_launch):
+    """The decode step with rope_theta set: in one launch where it fits
+    (bf16, head_dim 128, up to 4 query heads a KV head), else the selection
+    and attention calls.  Its selection and scores equal infllm_select_units
+    bit for bit; its output equals the attention of that selection (bit for
+    bit for the two calls, up to fp32 rounding in one launch, which splits
+    the attention differently) and the oracle's; two calls on one workspace
+    give the same bits."""
+    w, theta, inp, dev = data(name)
     cfg = cfg_of(w, rope_theta=theta)
     plan = F.infllm_step_plan(cfg, w.batch, orc.num_units(w.n_ctx, w.block, w.n_init), 4)
-    assert plan["fused"] == 0   # separate calls
+    assert plan["fused"] == int(one_launch)
     n_pos, t0 = 4, w.n_ctx - 4
     U = orc.num_units(w.n_ctx, w.block, w.n_init)
     _, repr_o, _ = orc.build_units_all(inp["q"], inp["k"], w.n_ctx, B=w.block, n_init=w.n_init,
                                        W=w.window, r_k=w.rep_k, mode=w.rep_mode)
     repr_d = torch.from_numpy(repr_o.astype(np.float32)).cuda()
-    scores = torch.empty((w.batch, w.n_kv_heads, n_pos, U), dtype=torch.float32, device="cuda")
-    sel = torch.empty((w.batch, w.n_kv_heads, n_pos, w.top_k), dtype=torch.int32, device="cuda")
-    out = torch.empty((w.batch, w.n_q_heads, n_pos, w.head_dim), dtype=torch.bfloat16,
-                      device="cuda")
-    lse = torch.empty((w.batch, w.n_q_heads, n_pos), dtype=torch.float32, device="cuda")
     ws = F.workspace(cfg, F.INFLLM_CALL_SELECT_ATTEND, w.batch, U, 1, n_pos)
-    F.infllm_select_attend(cfg, dev["q"], t0, t0, n_pos, repr_d, dev["k"], dev["v"], scores, sel,
-                           out, lse, ws=ws)
+    runs = []
+    for _ in range(2):
+        scores = torch.empty((w.batch, w.n_kv_heads, n_pos, U), dtype=torch.float32,
+                             device="cuda")
+        sel = torch.empty((w.batch, w.n_kv_heads, n_pos, w.top_k), dtype=torch.int32,
+                          device="cuda")
+        out = torch.empty((w.batch, w.n_q_heads, n_pos, w.head_dim), dtype=torch.bfloat16,
+                          device="cuda")
+        lse = torch.empty((w.batch, w.n_q_heads, n_pos), dtype=torch.float32, device="cuda")
+        F.infllm_select_attend(cfg, dev["q"], t0, t0, n_pos, repr_d, dev["k"], dev["v"], scores,
+                               sel, out, lse, ws=ws)
+        runs.append((scores, sel, out, lse))
+    scores, sel, out, lse = runs[0]
     s2 = torch.empty_like(scores)
     sel2 = torch.empty_like(sel)
     F.infllm_select_units(cfg, dev["q"], t0, t0, 1, n_pos, repr_d, s2, sel2,
                           ws=F.workspace(cfg, F.INFLLM_CALL_SELECT, w.batch, U, 1, n_pos))
     o2, l2 = gpu_attend(cfg, dev["q"], t0, t0, 1, n_pos, dev["k"], dev["v"], sel2)
     torch.cuda.synchronize()
+    assert all(torch.equal(x, y) for x, y in zip(runs[0], runs[1]))
     assert torch.equal(sel, sel2) and torch.equal(scores, s2)
-    assert torch.equal(out, o2) and torch.equal(lse, l2)
+    if one_launch:
+        o2h = o2.float().cpu().numpy()
+        assert_close(out, o2h, tolerance(torch.bfloat16, o2h), "one launch vs two calls")
+        assert_close(lse, l2.cpu().numpy(), 1e-4, "lse, one launch vs two calls")
+        assert F.infllm_workspace_status(ws) == 0
+    else:
+        assert torch.equal(out, o2) and torch.equal(lse, l2)
     sel_h = sel.cpu().numpy()
     check_chunks(orc, w, theta, inp, out, lse, sel_h, [t0 + i for i in range(n_pos)], 1,
                  "select_attend")
