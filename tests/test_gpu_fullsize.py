@@ -21,9 +21,11 @@ from gpu_helpers import assert_close, check_selection, tolerance
 pytestmark = pytest.mark.gpu
 
 
-def run(name):
+def run(name, rope_theta=0.0, **over):
     w = synth.WORKLOADS[name]
-    p = bench.Pipeline(w)
+    if over:
+        w = w.replace(**over)
+    p = bench.Pipeline(w, rope_theta=rope_theta)
     if not p.encode:
         p.build()
     p.step()
@@ -78,13 +80,14 @@ def check_selections(orc, w, p, q_cpu, sel_log, items):
     return sel, orc_sel, exemptions
 
 
-def check_outputs(orc, w, q_cpu, k_cpu, v_cpu, out_gpu, sel_log, points):
+def check_outputs(orc, w, q_cpu, k_cpu, v_cpu, out_gpu, sel_log, points, rope_theta=0.0):
     """points: (index into sel_log, query row, position)."""
     sel = sel_log.cpu().numpy()[:, :, :, 0]
     worst = 0.0
     for i, row, pos in points:
         o_ref, l_ref = orc.attend_all(q_cpu[:, :, row:row + 1], pos, k_cpu, v_cpu, sel[i],
-                                      B=w.block, n_init=w.n_init, W=w.window)
+                                      B=w.block, n_init=w.n_init, W=w.window,
+                                      rope_theta=rope_theta)
         got = out_gpu[:, :, row:row + 1]
         worst = max(worst, assert_close(got, o_ref, tolerance(q_cpu.dtype, o_ref),
                                         "%s position %d" % (w.name, pos)))
@@ -114,6 +117,24 @@ def test_fullsize_llama3_128k_decode(orc):
     k, v = p.inp["k"].cpu(), p.inp["v"].cpu()
     check_outputs(orc, w, qd, k, v, p.out_dec, p.sel_dec,
                   [(s, s, w.n_ctx + s) for s in (0, 1, 128, 255)])
+
+
+def test_fullsize_llama3_128k_decode_rope(orc):
+    """The 128K decode steps with positions inside the working context
+    (rope_theta 500,000, Llama-3's base), in the form bench.py --rope-theta
+    times (one launch per step): selections re-derived from the oracle's
+    scores, sampled outputs against the oracle's re-positioned attention.
+    Entries of std 1 instead of 1/sqrt(128): logits of order 10, so that a
+    wrong turn moves the softmax weights by far more than the tolerance."""
+    theta = 500000.0
+    w, p = run("llama3_8b_128k_decode", rope_theta=theta, scale=1.0)
+    assert p.fused
+    qd = p.inp["q_dec"].cpu()
+    items = [(s, s, w.n_ctx + s, 1) for s in range(0, w.decode_steps, 17)]
+    check_selections(orc, w, p, qd, p.sel_dec, items)
+    k, v = p.inp["k"].cpu(), p.inp["v"].cpu()
+    check_outputs(orc, w, qd, k, v, p.out_dec, p.sel_dec,
+                  [(s, s, w.n_ctx + s) for s in (0, 1, 128, 255)], rope_theta=theta)
 
 
 def test_fullsize_llama3_128k_range_build(orc):
