@@ -243,6 +243,11 @@ void counter_region(const infllm_config* cfg, int32_t call, int32_t batch, int64
       if (region == 0) return;
       break;
     }
+    case INFLLM_CALL_BUILD_QSUM: {
+      region = build_qsum_counter_region(build_args(cfg, batch, n));
+      if (region == 0) return;
+      break;
+    }
     case INFLLM_CALL_SCORE:
     case INFLLM_CALL_SELECT: {
       ScoreArgs a = score_args(cfg, batch, chunk_len, n_chunks);

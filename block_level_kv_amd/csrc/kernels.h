@@ -131,6 +131,7 @@ size_t build_workspace_bytes(const BuildArgs& a);
 size_t build_range_workspace_bytes(const BuildArgs& a, int64_t n_units);
 size_t build_counter_region(const BuildArgs& a, int64_t n_units);   // bytes after the header
 size_t build_qsum_workspace_bytes(const BuildArgs& a);
+size_t build_qsum_counter_region(const BuildArgs& a);   // bytes after the header
 hipError_t launch_build(const BuildArgs& a, hipStream_t st);
 size_t score_workspace_bytes(const ScoreArgs& a);
 size_t select_workspace_bytes(const ScoreArgs& a);

@@ -225,7 +225,8 @@ INFLLM_API infllm_status infllm_build_units(const infllm_config *cfg, int32_t ba
  *   q          required in both modes
  *   block_qsum out [batch, H_kv, ceil(n_ctx/B), d] fp64, 16-byte aligned
  *   workspace  >= infllm_workspace_size(cfg, INFLLM_CALL_BUILD_QSUM, batch,
- *              n_ctx, 0, 0)
+ *              n_ctx, 0, 0), zero-filled before its first use (TOKENS), as
+ *              for infllm_build_units
  * Other arguments, outputs and errors as infllm_build_units.
  */
 INFLLM_API infllm_status infllm_build_units_qsum(const infllm_config *cfg, int32_t batch,
