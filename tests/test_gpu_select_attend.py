@@ -44,7 +44,7 @@ def fused(cfg, q, q_off, q_pos, n_pos, repr_, k, v, ws, pos=None):
     return scores, sel, out, lse
 
 
-def compare(orc, cfg, got, ref, q_c, q_off, t_list, k_c, v_c, bad=()):
+def compare(orc, cfg, got, ref, q_c, q_off, t_list, k_c, v_c, bad=(), rope_theta=0.0):
     """got (fused) against ref (separate calls) and the oracle; t_list[b] is
     the position of query row q_off of sequence b; q_c, k_c, v_c: the inputs
     on the host."""
@@ -70,7 +70,7 @@ def compare(orc, cfg, got, ref, q_c, q_off, t_list, k_c, v_c, bad=()):
             o_ref, l_ref = orc.attend_all(q_c[b:b + 1, :, q_off + c:q_off + c + 1],
                                           t_list[b] + c, k_c[b:b + 1], v_c[b:b + 1],
                                           selg[b:b + 1, :, c], B=cfg.block, n_init=cfg.n_init,
-                                          W=cfg.window)
+                                          W=cfg.window, rope_theta=rope_theta)
             tol = tolerance(out.dtype, o_ref)
             assert_close(out[b:b + 1, :, c:c + 1], o_ref, tol, "seq %d pos %d" % (b, c))
             assert_close(lse[b:b + 1, :, c:c + 1], l_ref, 1e-3, "lse seq %d pos %d" % (b, c))
@@ -138,16 +138,20 @@ def test_select_attend_shapes(orc, Hq, Hkv, d, U, k_m, n_pos, W, n_init, varlen,
     run_shape(orc, Hq, Hkv, d, U, k_m, n_pos, W, n_init, varlen, dt, plan)
 
 
-def run_shape(orc, Hq, Hkv, d, U, k_m, n_pos, W, n_init, varlen, dt, plan, cut=False):
+def run_shape(orc, Hq, Hkv, d, U, k_m, n_pos, W, n_init, varlen, dt, plan, cut=False,
+              rope_theta=0.0):
     """Random unit representations and K/V; the last position sees every unit
     eligible, a second sequence (varlen) sits mid-context.  Two calls in a
     row on one workspace, bit for bit equal; no wait hits its bound.  cut:
-    the plan must have every slice publish fewer candidates than units."""
+    the plan must have every slice publish fewer candidates than units.
+    rope_theta > 0: positions inside the working context, q and k of std 1
+    (logits of order 10, so that a wrong turn shows)."""
     b, B = 2, 128
     dtype = torch.bfloat16 if dt == "bf16" else torch.float32
     cfg = F.make_config(n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, block=B, n_init=n_init,
                         window=W, rep_k=4, top_k=k_m,
-                        dtype=F.INFLLM_BF16 if dt == "bf16" else F.INFLLM_F32)
+                        dtype=F.INFLLM_BF16 if dt == "bf16" else F.INFLLM_F32,
+                        rope_theta=rope_theta)
     got_plan = F.infllm_step_plan(cfg, b, U, n_pos)
     if plan is None:
         assert got_plan["fused"] == 0
@@ -159,7 +163,7 @@ def run_shape(orc, Hq, Hkv, d, U, k_m, n_pos, W, n_init, varlen, dt, plan, cut=F
     n_units_ctx = U + n_init // B                       # blocks before the window
     t0 = n_units_ctx * B + W + 17                       # every unit eligible
     cap = t0 + n_pos + 5
-    scale = d ** -0.5
+    scale = 1.0 if rope_theta > 0 else d ** -0.5
     q = (torch.randn((b, Hq, n_pos + 2, d), generator=gen) * scale).to(dtype)
     k = (torch.randn((b, Hkv, cap, d), generator=gen) * scale).to(dtype)
     v = (torch.randn((b, Hkv, cap, d), generator=gen) * scale).to(dtype)
@@ -175,13 +179,31 @@ def run_shape(orc, Hq, Hkv, d, U, k_m, n_pos, W, n_init, varlen, dt, plan, cut=F
     first = None
     for _ in range(2):
         got = fused(cfg, qg, 2, t0, n_pos, rg, kg, vg, ws, pos=pos)
-        compare(orc, cfg, got, ref, q, 2, t_list, k, v)
+        compare(orc, cfg, got, ref, q, 2, t_list, k, v, rope_theta=rope_theta)
         if first is None:
             first = got
         else:   # the same bits on the second call (fixed merge order)
             assert all(torch.equal(x, y) for x, y in zip(first, got))
     assert F.infllm_workspace_status(ws) == 0
     return ws
+
+
+# positions inside the working context (rope_theta > 0): one launch with at
+# most two workgroups per CU for up to 4 query heads per KV head at head_dim
+# 128, the two calls otherwise
+ROPE_SHAPES = [
+    (4, 4, 128, 300, 16, 2, 512, 128, False, "bf16", (15, 5, 64)),    # G = 1, two positions
+    (8, 4, 128, 200, 6, 3, 384, 100, True, "bf16", (9, 4, 64)),       # G = 2, sinks not B-aligned
+    (8, 2, 128, 1500, 32, 8, 512, 128, False, "bf16", (15, 12, 128)), # G = 4, eight positions
+    (8, 2, 128, 600, 256, 1, 512, 128, True, "bf16", (63, 10, 64)),   # the largest k_m
+    (16, 2, 128, 100, 4, 1, 512, 128, True, "bf16", None),            # G = 8: the two calls
+    (8, 4, 64, 200, 6, 1, 384, 100, False, "bf16", None),             # d = 64: the two calls
+]
+
+
+@pytest.mark.parametrize("Hq,Hkv,d,U,k_m,n_pos,W,n_init,varlen,dt,plan", ROPE_SHAPES)
+def test_select_attend_rope_shapes(orc, Hq, Hkv, d, U, k_m, n_pos, W, n_init, varlen, dt, plan):
+    run_shape(orc, Hq, Hkv, d, U, k_m, n_pos, W, n_init, varlen, dt, plan, rope_theta=500000.0)
 
 
 # one launch for rows with more scores than one search takes (as at the
