@@ -33,6 +33,11 @@ CASES = {
     # (not only which keys are attended) are checked on the MFMA path
     "bf16_g4_unit": LL.replace(n_ctx=2560, n_q_heads=8, n_kv_heads=2, window=384, top_k=4,
                                chunk=256, scale=1.0),
+    # bf16, G=4, 2 sequences x 8 KV heads x 17 blocks (the last one partial):
+    # a grid large enough for the build with block query sums to take the
+    # single pass
+    "bf16_g4_b2": LL.replace(n_ctx=2112, batch=2, n_q_heads=32, n_kv_heads=8, window=512,
+                             top_k=4, chunk=256),
 }
 
 
