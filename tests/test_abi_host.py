@@ -266,6 +266,20 @@ def test_step_plan_grid(b, Hkv, U, n_pos, per_cu):
     rows = b * Hkv * n_pos
     assert (p["n_splits"] + 1) * rows == 256 * per_cu
 
+def test_step_plan_rope():
+    """With positions inside the working context the one-launch step holds
+    at most two workgroups per CU (its turned keys take the registers of a
+    third), and takes the two calls with 8 query heads per KV head or
+    head_dim 64."""
+    for b, Hkv, U, per_cu in [(8, 8, 1023, 2), (4, 8, 1023, 2), (1, 8, 511, 1)]:
+        c = cfg(n_q_heads=4 * Hkv, n_kv_heads=Hkv, top_k=32, rope_theta=500000.0)
+        p = F.infllm_step_plan(c, b, U, 1)
+        assert p["fused"] == 1 and (p["n_splits"] + 1) * b * Hkv == 256 * per_cu
+    for G, d in [(8, 128), (4, 64)]:
+        c = cfg(n_q_heads=G * 2, n_kv_heads=2, head_dim=d, top_k=8, rope_theta=10000.0)
+        assert F.infllm_step_plan(c, 1, 300, 1)["fused"] == 0
+
+
 def test_workspace_counter_regions():
     """Every call kind keeps its counters in [256, 256 + region) with a
     region of at least 64 KiB, and its data after it: a zero-filled
