@@ -1121,7 +1121,7 @@ static hipError_t launch_step_dgn(const ScoreArgs& s, const AttendArgs& a, const
                                   const StepPtrs& w, hipStream_t st) {
   const dim3 grid((unsigned)(step_rows(a) * (p.n_splits + 1)));
   static_assert(kStepMaxCand <= 8 * kRowsThreads, "candidate keys per lane");
-  if constexpr (D == 128) {
+  if constexpr (D == 128 && G <= 4) {   // the shapes the plan takes with rope_theta > 0
     if (a.rope_theta > 0.0) {
       k_select_attend<bf16_t, D, G, NSUB, 8, true><<<grid, kRowsThreads, 0, st>>>(s, a, p, w);
       return hipGetLastError();
