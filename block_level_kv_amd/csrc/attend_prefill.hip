@@ -73,6 +73,8 @@ __device__ __forceinline__ float max3(float a, float b, float c) {
 constexpr int kWaitRing = 0x0078;
 // s_waitcnt lgkmcnt(0) alone (vmcnt and expcnt at their maxima)
 constexpr int kWaitLgkm0 = 0xC07F;
+// vmcnt(0) lgkmcnt(0): the paired ring's wait before each barrier
+constexpr int kWaitPair = 0x0070;
 static_assert(kStages == 4, "kWaitRing encodes 4 loads x 2 tiles in flight");
 
 __device__ __forceinline__ int swap_bits23(int m) {
@@ -412,7 +414,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_prefill(AttendArgs a, Pr
     const int* tl = tiles + tile_begin;
     load_tile(tl[0], lds_k0, lds_v0);
     load_tile(tl[1 < nt ? 1 : nt - 1], lds_k1, lds_v1);
-    load_tile(tl[2 < nt ? 2 : nt - 1], lds_k2, lds_v2);
+    if constexpr (ROPE) load_tile(tl[2 < nt ? 2 : nt - 1], lds_k2, lds_v2);
   }
   if constexpr (ROPE) {
     turn_table(0);
@@ -422,7 +424,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_prefill(AttendArgs a, Pr
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   }
-  ring_barrier(0, lds_k0);   // tile 0 landed
+  if constexpr (ROPE) {
+    ring_barrier(0, lds_k0);   // tile 0 landed
+  } else {
+    __builtin_amdgcn_s_waitcnt(kWaitPair);   // tiles 0 and 1 landed
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  }
 
   // One tile: issue the loads of tile i+3, then the math on tile i.  The
   // ring buffers are separate variables and the loop below is unrolled over
@@ -432,8 +441,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_prefill(AttendArgs a, Pr
   auto tile_step = [&](const int* tl, const bf16_t* kb, const bf16_t* vb, bf16_t* kn,
                        bf16_t* vn, int i) {
     const int desc = tl[i];
-    load_tile(tl[i + kStages - 1 < nt ? i + kStages - 1 : nt - 1], kn, vn);
-    if constexpr (ROPE) turn_table(i + 2);
+    if constexpr (ROPE) {
+      load_tile(tl[i + kStages - 1 < nt ? i + kStages - 1 : nt - 1], kn, vn);
+      turn_table(i + 2);
+    }
 
     // S^T = K Q^T for 64 keys x 32 rows: two 32-key sub-tiles
     f32x16 s0 = f32x16{}, s1 = f32x16{};
@@ -523,7 +534,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_prefill(AttendArgs a, Pr
   // unrolled over the ring so that every copy names fixed buffers; after
   // each tile: tile i+1 landed (this lane's part), and the barrier makes
   // all parts visible and frees buffer i for the loads of the next tile
-  {
+  if constexpr (ROPE) {
     const int* tl = tiles + tile_begin;
     for (int i = 0; i < nt; i += kStages) {
       tile_step(tl, lds_k0, lds_v0, lds_k3, lds_v3, i);
@@ -537,6 +548,32 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_prefill(AttendArgs a, Pr
       if (i + 3 >= nt) break;
       tile_step(tl, lds_k3, lds_v3, lds_k2, lds_v2, i + 3);
       ring_barrier(i + 4, lds_k0);
+    }
+  } else {
+    // Without RoPE the ring is taken in pairs of tiles, one barrier per
+    // pair: buffers 0-1 and 2-3 alternate, each pair's math first issues
+    // the loads of the next pair into the other two buffers (freed by the
+    // barrier just passed), and the barrier after it waits for them.
+    const int* tl = tiles + tile_begin;
+    auto pair_barrier = [&]() {
+      __builtin_amdgcn_s_waitcnt(kWaitPair);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+    for (int i = 0; i < nt; i += kStages) {
+      load_tile(tl[i + 2 < nt ? i + 2 : nt - 1], lds_k2, lds_v2);
+      load_tile(tl[i + 3 < nt ? i + 3 : nt - 1], lds_k3, lds_v3);
+      tile_step(tl, lds_k0, lds_v0, nullptr, nullptr, i);
+      if (i + 1 < nt) tile_step(tl, lds_k1, lds_v1, nullptr, nullptr, i + 1);
+      if (i + 2 >= nt) break;
+      pair_barrier();
+      load_tile(tl[i + 4 < nt ? i + 4 : nt - 1], lds_k0, lds_v0);
+      load_tile(tl[i + 5 < nt ? i + 5 : nt - 1], lds_k1, lds_v1);
+      tile_step(tl, lds_k2, lds_v2, nullptr, nullptr, i + 2);
+      if (i + 3 < nt) tile_step(tl, lds_k3, lds_v3, nullptr, nullptr, i + 3);
+      if (i + 4 >= nt) break;
+      pair_barrier();
     }
   }
   // the repeat loads past the end must land before the workgroup's LDS can
