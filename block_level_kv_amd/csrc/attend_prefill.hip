@@ -185,6 +185,22 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_prefill(AttendArgs a, Pr
   const int64_t lo_ctx = rope_local_start(base + (int64_t)ch * a.L, a.n_init, a.W);
   const int e_sink = (int)(a.n_init + (int64_t)a.k_m * a.B - lo_ctx);
 
+  // ---------------------------------------------------------- this lane's row
+  // (its Q loads go out first: their latency runs beside the tile list's)
+  const int row = wave * 32 + n;            // 0..255
+  const int g = row / TQ, qi = row % TQ;    // head within the group, query within tile
+  const bool row_ok = qi < nq;
+  const int64_t t_row = ta + qi;
+  const int64_t qh = (int64_t)bi * a.Hq + (int64_t)h * G + g;
+  const bf16_t* Q = (const bf16_t*)a.q;
+  const int64_t q_row = a.q_off + (int64_t)ch * a.L + q_first + (row_ok ? qi : 0);
+  bf16x8 qreg[8];
+  {
+    const bf16_t* qp = Q + (qh * a.q_cap + q_row) * kD + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qreg[ks] = *(const bf16x8*)(qp + ks * 16);
+  }
+
   // ---------------------------------------------------------- tile list
   // [initial-token tiles][unit tiles, in sel order][window-band tiles];
   // thread m handles sel entry m (k_m <= kThreads), a block scan places them.
@@ -260,20 +276,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_prefill(AttendArgs a, Pr
   const int tile_begin = (int)((int64_t)n_tiles * split / geo.splits);
   const int tile_end = (int)((int64_t)n_tiles * (split + 1) / geo.splits);
 
-  // ---------------------------------------------------------- this lane's row
-  const int row = wave * 32 + n;            // 0..255
-  const int g = row / TQ, qi = row % TQ;    // head within the group, query within tile
-  const bool row_ok = qi < nq;
-  const int64_t t_row = ta + qi;
-  const int64_t qh = (int64_t)bi * a.Hq + (int64_t)h * G + g;
-  const bf16_t* Q = (const bf16_t*)a.q;
-  const int64_t q_row = a.q_off + (int64_t)ch * a.L + q_first + (row_ok ? qi : 0);
-  bf16x8 qreg[8];
-  {
-    const bf16_t* qp = Q + (qh * a.q_cap + q_row) * kD + half * 8;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qreg[ks] = *(const bf16x8*)(qp + ks * 16);
-  }
   if constexpr (ROPE) {
     // a query before n_init sees initial tokens only, which are turned by
     // -E_s: turn it by -E_s too.  qreg[ks] holds columns 8 (2 ks + half) ..
